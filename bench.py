@@ -1,0 +1,219 @@
+"""Benchmark of the delta-rule chunked forward (+ decode step) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one whole chunked forward (WY prep + state scan/output kernels)
+over the long-context workload: bf16 q/k/v, B=1, H=32, L=65536,
+d_k=d_v=128, C=128, fp32 beta/state, zero initial state, fp32 o, seeded
+synthetic inputs resident in HBM before the timed region.  The decode step
+(B=256 sequences x H=32 heads, d=128, fp32 state of 512 MiB) is timed as well
+and reported under "decode".
+
+Prints ONE JSON line.  value = tokens/s of the chunked forward (B*L tokens per
+step; a token counts once across heads).  Model TFLOP/s follow the cost model
+2 L d_k d_v + 2 L C d_k per head.  Rooflines use algorithmic bytes (each input
+read once, each output written once) divided by the kernel's average duration
+from HIP events recorded on the launch stream around every launch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def chunk_bytes(w, in_bytes=2, out_bytes=4, s0=False):
+    """Algorithmic bytes of one chunked forward: q, k, v, beta read once, o and
+    S_final written once (S0 read once if given)."""
+    tok_heads = w.B * w.H * w.L
+    b = tok_heads * (2 * w.d_k + w.d_v) * in_bytes + tok_heads * 4 + tok_heads * w.d_v * out_bytes
+    state = w.B * w.H * w.d_k * w.d_v * 4
+    return b + state * (2 if s0 else 1)
+
+
+def scan_kernel_bytes(w, in_bytes=2, out_bytes=4):
+    """Algorithmic bytes of the scan kernel alone: q, k, v read once, o and
+    S_final written once (beta is consumed by the prep kernel)."""
+    tok_heads = w.B * w.H * w.L
+    return (tok_heads * (2 * w.d_k + w.d_v) * in_bytes + tok_heads * w.d_v * out_bytes
+            + w.B * w.H * w.d_k * w.d_v * 4)
+
+
+def model_flops(w):
+    return w.B * w.H * (2 * w.L * w.d_k * w.d_v + 2 * w.L * w.C * w.d_k)
+
+
+def decode_bytes(w, in_bytes=2, out_bytes=4):
+    bh = w.B * w.H
+    return 2 * bh * w.d_k * w.d_v * 4 + bh * ((2 * w.d_k + w.d_v) * in_bytes + 4 + w.d_v * out_bytes)
+
+
+def cpu_baseline(w, x, seconds_hint):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload:
+    all H heads of batch 0, the first `n_tok` tokens, single thread."""
+    from threadpoolctl import threadpool_limits
+
+    from deltanet_delta_rule_chunk_amd.inputs import to_f64
+    from oracle import delta_rule_forward
+
+    n_tok = 32768
+    q = to_f64(x["q"][:1, :, :n_tok])
+    k = to_f64(x["k"][:1, :, :n_tok])
+    v = to_f64(x["v"][:1, :, :n_tok])
+    beta = to_f64(x["beta"][:1, :, :n_tok])
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        delta_rule_forward(q, k, v, beta, None)
+        dt = time.perf_counter() - t0
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"B=1, H={w.H}, first {n_tok} tokens of L={w.L}, d={w.d_k}; "
+                      f"fp64 numpy token loop, {dt:.1f} s, one thread"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads would shard with no communication; see the design notes).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from deltanet_delta_rule_chunk_amd import binding, inputs
+
+    binding.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = inputs.WORKLOADS[3]
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    x = inputs.make_chunk_inputs(w, seed=a.seed)
+    g = {k: (None if t is None else t.to(dev)) for k, t in x.items()}
+    o = torch.empty(w.B, w.H, w.L, w.d_v, device=dev, dtype=torch.float32)
+    S_final = torch.empty(w.B, w.H, w.d_k, w.d_v, device=dev, dtype=torch.float32)
+    ws = torch.empty(binding.workspace_bytes(w.B, w.H, w.L, w.d_k, w.d_v, w.C), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        binding.chunk_fwd(g["q"], g["k"], g["v"], g["beta"], None, w.C, o=o, S_final=S_final,
+                          workspace=ws)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(S_final).all()
+
+    print(f"[bench] timing {a.steps} chunked-forward steps", file=sys.stderr, flush=True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    binding.profile_start()
+    t_wall = time.perf_counter()
+    ev0.record()
+    for _ in range(a.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    prof = binding.profile_stop()
+    ms_step = ev0.elapsed_time(ev1) / a.steps
+
+    tokens_s = w.B * w.L / (ms_step * 1e-3)
+    flops = model_flops(w)
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    kern = {name: tot / n for name, (tot, n) in prof.items()}
+    dom = max((k for k in kern if k.startswith("chunk")), key=lambda k: kern[k])
+    dom_bytes = scan_kernel_bytes(w) if dom == "chunk_scan" else (
+        w.B * w.H * w.L * (2 * w.d_k * 2 + 4))
+    achieved = dom_bytes / (kern[dom] * 1e-3) / 1e9
+    path_gbs = chunk_bytes(w) / (ms_step * 1e-3) / 1e9
+
+    result = {
+        "metric": "delta-rule chunk fwd tokens/s + TFLOP/s (% bf16 MFMA peak); decode GB/s % HBM",
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: q,v ~ N(0,1); k ~ N(0,1) L2-normalised; beta = sigmoid(N(0,1)))",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d_k": w.d_k, "d_v": w.d_v,
+                   "C": w.C, "in_dtype": "bf16", "state_dtype": "f32", "out_dtype": "f32",
+                   "global_batch": w.B, "seq_len": w.L, "parallelism": "single GPU"},
+        "model_tflops": tflops,
+        "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "path_alg_gbs": path_gbs,
+        "pct_hbm_peak_path": 100.0 * path_gbs / PEAK_HBM_GBS,
+        "kernels_ms": kern,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+        "wall_s_timed": t_wall,
+    }
+
+    if not a.no_decode:
+        wd = inputs.WORKLOADS[4]
+        print(f"[bench] decode {wd.name}: {a.decode_steps} steps", file=sys.stderr, flush=True)
+        Sd = inputs.make_decode_state(wd, seed=a.seed).to(dev)
+        ring = [inputs.make_decode_step_inputs(wd, s, seed=a.seed) for s in range(8)]
+        ring = [{k: t.to(dev) for k, t in r.items()} for r in ring]
+        od = torch.empty(wd.B, wd.H, wd.d_v, device=dev, dtype=torch.float32)
+        for s in range(3):
+            r = ring[s % 8]
+            binding.decode_step(r["q"], r["k"], r["v"], r["beta"], Sd, o=od)
+        torch.cuda.synchronize()
+        binding.profile_start()
+        ev0.record()
+        for s in range(a.decode_steps):
+            r = ring[s % 8]
+            binding.decode_step(r["q"], r["k"], r["v"], r["beta"], Sd, o=od)
+        ev1.record()
+        torch.cuda.synchronize()
+        dprof = binding.profile_stop()
+        assert torch.isfinite(od).all()
+        ms_dec = ev0.elapsed_time(ev1) / a.decode_steps
+        k_ms = dprof["decode"][0] / dprof["decode"][1]
+        db = decode_bytes(wd)
+        result["decode"] = {
+            "workload": wd.name, "steps": a.decode_steps, "ms_per_step": ms_dec,
+            "kernel_ms": k_ms, "tokens_per_s": wd.B / (ms_dec * 1e-3),
+            "alg_gbs": db / (ms_dec * 1e-3) / 1e9,
+            "pct_hbm_peak": 100.0 * db / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "roofline": {"bound": "hbm", "kernel": "decode", "achieved": db / (k_ms * 1e-3) / 1e9,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": db / (k_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None},
+            "inputs": "8 seeded step inputs cycled; state carried across all steps",
+        }
+
+    if not a.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, x, 20)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

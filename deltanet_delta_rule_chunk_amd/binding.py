@@ -1,0 +1,199 @@
+"""Thin ctypes binding of libdeltanet.so (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; this module
+checks tensors (device, dtype, contiguity, shape), allocates outputs and the
+workspace through PyTorch's caching allocator, and passes raw device pointers
+and the current HIP stream to the C ABI.  If the library is missing it raises:
+there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdeltanet.so")
+
+DN_OK = 0
+DN_F32 = 0
+DN_BF16 = 1
+STATUS_NAMES = {0: "DN_OK", 1: "DN_ERR_NULL_ARG", 2: "DN_ERR_BAD_SHAPE", 3: "DN_ERR_UNSUPPORTED",
+                4: "DN_ERR_MISALIGNED", 5: "DN_ERR_ALIASING", 6: "DN_ERR_WORKSPACE",
+                7: "DN_ERR_HIP"}
+# Every symbol include/deltanet.h declares.
+EXPORTS = ("deltanet_chunk_fwd", "deltanet_chunk_fwd_workspace_bytes", "deltanet_decode_step",
+           "deltanet_status_string", "deltanet_last_hip_error", "deltanet_version",
+           "deltanet_profile_start", "deltanet_profile_stop")
+PROFILE_SLOTS = ("chunk_prep", "chunk_scan", "decode")
+
+_lib = None
+
+
+class DeltaNetError(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({detail})")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library once and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m deltanet_delta_rule_chunk_amd.build`"
+            " (there is no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.deltanet_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.deltanet_chunk_fwd.restype = i
+    lib.deltanet_chunk_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.deltanet_chunk_fwd_workspace_bytes.restype = sz
+    lib.deltanet_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.deltanet_decode_step.restype = i
+    lib.deltanet_status_string.argtypes = [i]
+    lib.deltanet_status_string.restype = ctypes.c_char_p
+    lib.deltanet_last_hip_error.argtypes = []
+    lib.deltanet_last_hip_error.restype = i
+    lib.deltanet_version.argtypes = []
+    lib.deltanet_version.restype = i
+    lib.deltanet_profile_start.argtypes = []
+    lib.deltanet_profile_start.restype = i
+    lib.deltanet_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(ctypes.c_int), i]
+    lib.deltanet_profile_stop.restype = i
+    _lib = lib
+    return lib
+
+
+def _code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return DN_F32
+    if dt == torch.bfloat16:
+        return DN_BF16
+    raise TypeError(f"unsupported dtype {dt} (float32 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _raise(lib, status: int, what: str):
+    detail = lib.deltanet_status_string(status).decode()
+    if status == 7:
+        detail += f"; hipError {lib.deltanet_last_hip_error()}"
+    raise DeltaNetError(status, what, detail)
+
+
+def _stream(device: torch.device, stream) -> int:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def workspace_bytes(B: int, H: int, L: int, d_k: int, d_v: int, C: int,
+                    in_dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(load().deltanet_chunk_fwd_workspace_bytes(B, H, L, d_k, d_v, C, _code(in_dtype)))
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+              S0: Optional[torch.Tensor] = None, C: int = 64, *,
+              out_dtype: torch.dtype = torch.float32, o: Optional[torch.Tensor] = None,
+              S_final: Optional[torch.Tensor] = None, want_state: bool = True,
+              workspace: Optional[torch.Tensor] = None, stream=None
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked delta-rule forward.  q,k ``[B,H,L,d_k]``, v ``[B,H,L,d_v]`` (fp32 or
+    bf16, same dtype), beta ``[B,H,L]`` fp32, S0 ``[B,H,d_k,d_v]`` fp32 or None.
+    Returns ``(o, S_final)``; S_final is None when ``want_state`` is False."""
+    lib = load()
+    B, H, L, d_k = q.shape
+    d_v = v.shape[-1]
+    dev = q.device
+    _check(q, "q", (B, H, L, d_k), device=dev)
+    _check(k, "k", (B, H, L, d_k), q.dtype, dev)
+    _check(v, "v", (B, H, L, d_v), q.dtype, dev)
+    _check(beta, "beta", (B, H, L), torch.float32, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, d_k, d_v), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, L, d_v), dtype=out_dtype, device=dev)
+    _check(o, "o", (B, H, L, d_v), out_dtype, dev)
+    if S_final is None and want_state:
+        S_final = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=dev)
+    if S_final is not None:
+        _check(S_final, "S_final", (B, H, d_k, d_v), torch.float32, dev)
+    in_code = _code(q.dtype)
+    need = int(lib.deltanet_chunk_fwd_workspace_bytes(B, H, L, d_k, d_v, C, in_code))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.deltanet_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(o),
+                                _ptr(S_final), B, H, L, d_k, d_v, C, in_code,
+                                _code(out_dtype), _ptr(workspace), ws_bytes, _stream(dev, stream))
+    if st != DN_OK:
+        _raise(lib, st, "deltanet_chunk_fwd")
+    return o, S_final
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                S: torch.Tensor, *, out_dtype: torch.dtype = torch.float32,
+                o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step; updates S ``[B,H,d_k,d_v]`` in place and returns o
+    ``[B,H,d_v]`` = q S_new."""
+    lib = load()
+    B, H, d_k = q.shape
+    d_v = v.shape[-1]
+    dev = q.device
+    _check(q, "q", (B, H, d_k), device=dev)
+    _check(k, "k", (B, H, d_k), q.dtype, dev)
+    _check(v, "v", (B, H, d_v), q.dtype, dev)
+    _check(beta, "beta", (B, H), torch.float32, dev)
+    _check(S, "S", (B, H, d_k, d_v), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, d_v), dtype=out_dtype, device=dev)
+    _check(o, "o", (B, H, d_v), out_dtype, dev)
+    st = lib.deltanet_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(o),
+                                  B, H, d_k, d_v, _code(q.dtype), _code(out_dtype),
+                                  _stream(dev, stream))
+    if st != DN_OK:
+        _raise(lib, st, "deltanet_decode_step")
+    return o
+
+
+def profile_start() -> None:
+    """Start bracketing this thread's kernel launches with HIP events."""
+    st = load().deltanet_profile_start()
+    if st != DN_OK:
+        _raise(load(), st, "deltanet_profile_start")
+
+
+def profile_stop() -> dict:
+    """Stop, wait for the recorded events and return
+    ``{slot: (total_ms, launches)}`` for the slots that launched."""
+    lib = load()
+    n = len(PROFILE_SLOTS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    st = lib.deltanet_profile_stop(ms, cnt, n)
+    if st != DN_OK:
+        _raise(lib, st, "deltanet_profile_stop")
+    return {PROFILE_SLOTS[i]: (ms[i], cnt[i]) for i in range(n) if cnt[i]}

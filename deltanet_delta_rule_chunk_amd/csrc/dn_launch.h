@@ -1,0 +1,44 @@
+// dn_launch.h -- host-side launch descriptors between the C ABI layer and the
+// kernel translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace dn {
+
+struct DecodeArgs {
+  const void *q, *k, *v;
+  const float* beta;
+  float* S;
+  void* o;
+  int B, H, d_k, d_v, in_dtype, out_dtype;
+  hipStream_t stream;
+};
+
+struct ChunkArgs {
+  const void *q, *k, *v;
+  const float* beta;
+  const float* S0;  // may be null (zero state)
+  void* o;
+  float* S_final;   // may be null
+  int B, H, L, d_k, d_v, C, in_dtype, out_dtype;
+  void* workspace;  // at least chunk_workspace_bytes(...) bytes
+  hipStream_t stream;
+};
+
+hipError_t launch_decode(const DecodeArgs& a);
+
+// Kernel slots of the profiling hook (see deltanet_profile_start).
+enum ProfSlot { kSlotChunkPrep = 0, kSlotChunkScan = 1, kSlotDecode = 2, kNumSlots = 3 };
+
+// Records a HIP event on `s` before (end = false) or after (end = true) the
+// kernel of `slot`, when profiling is on for the calling thread; a no-op
+// otherwise.
+void prof_mark(int slot, bool end, hipStream_t s);
+
+// Chunked forward: bytes of scratch it needs, and the launch sequence.
+size_t chunk_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int in_dtype);
+hipError_t launch_chunk_fwd(const ChunkArgs& a);
+
+}  // namespace dn

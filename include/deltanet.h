@@ -1,0 +1,125 @@
+/*
+ * deltanet.h -- C ABI of the MI355X (gfx950) DeltaNet delta-rule library.
+ *
+ * The operation.  Per (batch b, head h) the state S is a d_k x d_v matrix and
+ * every token t, in order, does
+ *     v_old = k_t S                    (read what the state holds at key k_t)
+ *     u_t   = beta_t (v_t - v_old)     (gated delta)
+ *     S     = S + k_t^T u_t            (outer-product write)
+ *     o_t   = q_t S                    (read after the write, no scale)
+ * This is the sequential delta-rule prefill loop of the page
+ * "GPT-2 から Kimi K3 まで、AI モデルの進化を解説" (news.ainew.jp), section
+ * "DeltaNet (Parallelizing linear transformers with delta rule)", and, at
+ * one token, that page's layer forward in "DeltaNet (Fast weight
+ * programmers)".  The chunked forward computes exactly this result (up to
+ * floating-point rounding) with the chunkwise-parallel generalised-Householder
+ * form the same section describes.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never frees or retains them.  Tensors are dense, row-major, C-contiguous,
+ *    with the shapes given below (last index fastest), 16-byte aligned.
+ *  - beta and the state are always fp32.  q, k, v are fp32 or bf16
+ *    (in_dtype).  o is fp32 or bf16 (out_dtype).
+ *  - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *    without synchronising.  Faults during execution surface at the caller's
+ *    next synchronisation.
+ *  - Every argument is validated before anything is launched: on any non-OK
+ *    status nothing has been launched and no output has been written.
+ *  - The library keeps no state between calls besides loaded code objects;
+ *    calls on different streams with disjoint buffers may run concurrently.
+ */
+#ifndef DELTANET_H_
+#define DELTANET_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DN_OK = 0,
+  DN_ERR_NULL_ARG = 1,     /* a required pointer is NULL                       */
+  DN_ERR_BAD_SHAPE = 2,    /* a size is negative/zero where it must be >= 1     */
+  DN_ERR_UNSUPPORTED = 3,  /* d_k, d_v, C or a dtype outside the built set      */
+  DN_ERR_MISALIGNED = 4,   /* a pointer is not 16-byte aligned                  */
+  DN_ERR_ALIASING = 5,     /* an output overlaps an input it must not overlap   */
+  DN_ERR_WORKSPACE = 6,    /* workspace given but smaller than required         */
+  DN_ERR_HIP = 7           /* a HIP runtime call failed; see deltanet_last_hip_error */
+} dn_status;
+
+typedef enum { DN_F32 = 0, DN_BF16 = 1 } dn_dtype;
+
+/*
+ * Chunkwise-parallel delta-rule forward over a whole sequence.
+ *
+ *   q, k   : [B, H, L, d_k]   in_dtype
+ *   v      : [B, H, L, d_v]   in_dtype
+ *   beta   : [B, H, L]        fp32, per-token write strength
+ *   S0     : [B, H, d_k, d_v] fp32 initial state, or NULL for the zero state
+ *   o      : [B, H, L, d_v]   out_dtype, written (o_t read after token t's write)
+ *   S_final: [B, H, d_k, d_v] fp32 state after the last token, or NULL to skip.
+ *            S_final may be the same buffer as S0 (in-place state update);
+ *            any other overlap with an input is rejected.
+ *   L      : any length >= 0 (L = 0 copies S0 (or zeros) to S_final; a
+ *            ragged last chunk is handled by masking, an exact no-op).
+ *   d_k, d_v in {64, 128}; C (chunk length) in {64, 128}.
+ *   workspace: device scratch of at least deltanet_chunk_fwd_workspace_bytes()
+ *            bytes, or NULL to let the library allocate and free it on
+ *            `stream` (stream-ordered).  Its contents on entry do not matter.
+ *
+ * Returns DN_OK or the first failing check's status.
+ */
+int deltanet_chunk_fwd(const void* q, const void* k, const void* v, const float* beta,
+                       const float* S0, void* o, float* S_final,
+                       int B, int H, int L, int d_k, int d_v, int C,
+                       int in_dtype, int out_dtype,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace deltanet_chunk_fwd needs for these sizes (0 if the
+ * sizes are invalid or unsupported). */
+size_t deltanet_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
+                                          int in_dtype);
+
+/*
+ * One decode step for B sequences x H heads (the recurrence at one token),
+ * updating the state in place.
+ *
+ *   q, k : [B, H, d_k] in_dtype;  v : [B, H, d_v] in_dtype
+ *   beta : [B, H] fp32
+ *   S    : [B, H, d_k, d_v] fp32, read and overwritten with the new state
+ *   o    : [B, H, d_v] out_dtype, o = q S_new
+ *   d_k, d_v in {64, 128}.  o must not overlap S or any input.
+ */
+int deltanet_decode_step(const void* q, const void* k, const void* v, const float* beta,
+                         float* S, void* o, int B, int H, int d_k, int d_v,
+                         int in_dtype, int out_dtype, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* deltanet_status_string(int status);
+
+/* The hipError_t behind the last DN_ERR_HIP returned on this thread (0 if none). */
+int deltanet_last_hip_error(void);
+
+/*
+ * Profiling hook.  Between deltanet_profile_start() and
+ * deltanet_profile_stop() on the same host thread, every kernel the library
+ * launches from that thread is bracketed by two HIP events recorded on the
+ * call's stream.  deltanet_profile_stop() waits for those events and writes,
+ * per kernel slot, the summed elapsed milliseconds and the launch count
+ * (nslots entries each; slots: 0 = chunk WY-prep kernel, 1 = chunk scan
+ * kernel, 2 = decode kernel).  Recording adds two event records per launch.
+ */
+int deltanet_profile_start(void);
+int deltanet_profile_stop(double* ms_per_slot, int* launches_per_slot, int nslots);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int deltanet_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DELTANET_H_ */

@@ -1,0 +1,151 @@
+"""Chunked forward on the GPU (through the C ABI) against the fp64 oracle."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from deltanet_delta_rule_chunk_amd import inputs as I
+from deltanet_delta_rule_chunk_amd.binding import chunk_fwd
+from oracle import delta_rule_forward
+from parity import assert_parity, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _note(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _run(x, C, out_dtype=torch.float32):
+    g = {k: (None if t is None else t.to(DEV)) for k, t in x.items()}
+    o, S = chunk_fwd(g["q"], g["k"], g["v"], g["beta"], g["S0"], C, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o.cpu(), S.cpu()
+
+
+def _oracle(x, heads=None):
+    """Oracle on all heads, or on the listed (b, h) pairs (heads are independent)."""
+    sel = (lambda t: t) if heads is None else (lambda t: t[[b for b, _ in heads], [h for _, h in heads]][None])
+    q, k, v, beta = (sel(to64(x[n])) for n in ("q", "k", "v", "beta"))
+    S0 = None if x["S0"] is None else sel(to64(x["S0"]))
+    return delta_rule_forward(q, k, v, beta, S0)
+
+
+SMALL = [
+    # name, dtype, B, H, L, dk, dv, C, S0
+    ("f32_d64_C64_L256", "f32", 1, 2, 256, 64, 64, 64, False),
+    ("f32_d128_C128_ragged", "f32", 1, 2, 300, 128, 128, 128, True),
+    ("f32_dk64_dv128_ragged", "f32", 2, 1, 200, 64, 128, 64, True),
+    ("f32_dk128_dv64_C64", "f32", 1, 2, 192, 128, 64, 64, True),
+    ("bf16_dk128_dv64_C128_ragged", "bf16", 1, 3, 333, 128, 64, 128, True),
+    ("bf16_d64_C64_ragged", "bf16", 2, 2, 64 * 5 + 7, 64, 64, 64, False),
+    ("bf16_d128_C64_S0", "bf16", 1, 2, 640, 128, 128, 64, True),
+    ("bf16_d128_C128", "bf16", 1, 2, 512, 128, 128, 128, False),
+    ("bf16_L_below_C", "bf16", 1, 2, 37, 128, 128, 128, True),
+    ("f32_L1", "f32", 1, 1, 1, 64, 64, 64, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: c[0])
+def test_small_parity(gpu_lib, case):
+    name, dt, B, H, L, dk, dv, C, s0 = case
+    _note(f"[chunk] {name}")
+    w = I.ChunkWorkload(name, B, H, L, dk, dv, C, dt, s0_std=0.1 if s0 else None)
+    x = I.make_chunk_inputs(w, seed=11)
+    o, S = _run(x, C)
+    o_ref, S_ref = _oracle(x)
+    assert_parity(o, o_ref, dt, f"{name} o")
+    assert_parity(S, S_ref, dt, f"{name} S_final")
+
+
+def test_workload0_fp32(gpu_lib):
+    w = I.WORKLOADS[0]
+    _note(f"[chunk] {w.name}")
+    x = I.make_chunk_inputs(w, seed=0)
+    o, S = _run(x, w.C)
+    o_ref, S_ref = _oracle(x)
+    assert_parity(o, o_ref, "f32", "o")
+    assert_parity(S, S_ref, "f32", "S_final")
+
+
+def test_workload1_gpt2_heads(gpu_lib):
+    w = I.WORKLOADS[1]
+    _note(f"[chunk] {w.name}")
+    x = I.make_chunk_inputs(w, seed=0)
+    o, S = _run(x, w.C)
+    o_ref, S_ref = _oracle(x)
+    e = assert_parity(o, o_ref, "bf16", "o")
+    assert_parity(S, S_ref, "bf16", "S_final")
+    _note(f"  o err/RMS = {e:.3e}")
+
+
+def test_workload2_overwrite_heads(gpu_lib):
+    """Full-size GPU run; oracle on sampled heads from both halves (beta == 1
+    heads and sigmoid heads)."""
+    w = I.WORKLOADS[2]
+    _note(f"[chunk] {w.name}")
+    x = I.make_chunk_inputs(w, seed=0)
+    o, S = _run(x, w.C)
+    heads = [(0, 0), (1, 7), (0, 8), (1, 15)]
+    o_ref, S_ref = _oracle(x, heads)
+    idx_b = [b for b, _ in heads]
+    idx_h = [h for _, h in heads]
+    e = assert_parity(o[idx_b, idx_h][None], o_ref, "bf16", "o")
+    assert_parity(S[idx_b, idx_h][None], S_ref, "bf16", "S_final")
+    _note(f"  o err/RMS = {e:.3e}")
+
+
+def test_workload3_long_context(gpu_lib):
+    """L = 65536 at full size on the GPU; oracle on two sampled heads."""
+    w = I.WORKLOADS[3]
+    _note(f"[chunk] {w.name}")
+    x = I.make_chunk_inputs(w, seed=0)
+    o, S = _run(x, w.C)
+    assert torch.isfinite(o).all() and torch.isfinite(S).all()
+    heads = [(0, 3), (0, 30)]
+    o_ref, S_ref = _oracle(x, heads)
+    e = assert_parity(o[0, [3, 30]][None], o_ref, "bf16", "o")
+    assert_parity(S[0, [3, 30]][None], S_ref, "bf16", "S_final")
+    _note(f"  o err/RMS = {e:.3e}")
+
+
+def test_empty_sequence_copies_state(gpu_lib):
+    B, H, dk, dv = 2, 3, 64, 128
+    S0 = torch.randn(B, H, dk, dv, device=DEV)
+    q = torch.empty(B, H, 0, dk, device=DEV, dtype=torch.bfloat16)
+    v = torch.empty(B, H, 0, dv, device=DEV, dtype=torch.bfloat16)
+    beta = torch.empty(B, H, 0, device=DEV)
+    o, S = chunk_fwd(q, q, v, beta, S0, 64)
+    torch.cuda.synchronize()
+    assert o.shape == (B, H, 0, dv)
+    assert torch.equal(S, S0)
+    o, S = chunk_fwd(q, q, v, beta, None, 64)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S) == 0
+
+
+def test_in_place_state_update(gpu_lib):
+    w = I.ChunkWorkload("inplace", 1, 2, 200, 64, 64, 64, "f32", s0_std=0.1)
+    x = I.make_chunk_inputs(w, seed=5)
+    g = {k: t.to(DEV) for k, t in x.items()}
+    S = g["S0"].clone()
+    o, S_out = chunk_fwd(g["q"], g["k"], g["v"], g["beta"], S, 64, S_final=S)
+    torch.cuda.synchronize()
+    assert S_out.data_ptr() == S.data_ptr()
+    o_ref, S_ref = _oracle(x)
+    assert_parity(o.cpu(), o_ref, "f32", "o")
+    assert_parity(S.cpu(), S_ref, "f32", "S")
+
+
+def test_bf16_output(gpu_lib):
+    """o stored as bf16: the bar still holds at a moderate size."""
+    w = I.ChunkWorkload("bf16out", 1, 4, 512, 64, 64, 64, "bf16")
+    x = I.make_chunk_inputs(w, seed=9)
+    o, S = _run(x, 64, out_dtype=torch.bfloat16)
+    assert o.dtype == torch.bfloat16
+    o_ref, S_ref = _oracle(x)
+    assert_parity(o, o_ref, "bf16", "o (bf16)")
+    assert_parity(S, S_ref, "bf16", "S_final")

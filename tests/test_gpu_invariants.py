@@ -1,0 +1,128 @@
+"""Properties of the HIP path that hold at any size (GPU)."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from deltanet_delta_rule_chunk_amd import inputs as I
+from deltanet_delta_rule_chunk_amd.binding import chunk_fwd, decode_step
+from oracle import delta_rule_forward
+from parity import assert_parity, err_f32, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _note(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _dev(x):
+    return {k: (None if t is None else t.to(DEV)) for k, t in x.items()}
+
+
+def test_chunk_size_invariance(gpu_lib):
+    """C = 64 and C = 128 compute the same recurrence (bf16 inputs)."""
+    _note("[inv] chunk size")
+    w = I.ChunkWorkload("cinv", 1, 2, 1000, 128, 128, 64, "bf16", s0_std=0.1)
+    g = _dev(I.make_chunk_inputs(w, seed=21))
+    o64, S64 = chunk_fwd(g["q"], g["k"], g["v"], g["beta"], g["S0"], 64)
+    o128, S128 = chunk_fwd(g["q"], g["k"], g["v"], g["beta"], g["S0"], 128)
+    torch.cuda.synchronize()
+    assert_parity(o64.cpu(), o128.cpu(), "bf16", "o C64 vs C128")
+    assert_parity(S64.cpu(), S128.cpu(), "bf16", "S C64 vs C128")
+
+
+def test_split_invariance(gpu_lib):
+    """Two calls chained through S_final -> S0 equal one call (state passing
+    between chunks), fp32 inputs, split at a chunk boundary and off it."""
+    _note("[inv] split")
+    w = I.ChunkWorkload("split", 2, 2, 384, 64, 64, 64, "f32", s0_std=0.1)
+    g = _dev(I.make_chunk_inputs(w, seed=22))
+    o, S = chunk_fwd(g["q"], g["k"], g["v"], g["beta"], g["S0"], 64)
+    for cut in (128, 150):
+        a = {k: g[k][:, :, :cut].contiguous() for k in ("q", "k", "v", "beta")}
+        b = {k: g[k][:, :, cut:].contiguous() for k in ("q", "k", "v", "beta")}
+        o1, S1 = chunk_fwd(a["q"], a["k"], a["v"], a["beta"], g["S0"], 64)
+        o2, S2 = chunk_fwd(b["q"], b["k"], b["v"], b["beta"], S1, 64)
+        torch.cuda.synchronize()
+        assert err_f32(torch.cat([o1, o2], 2).cpu(), o.cpu()) < 1e-5
+        assert err_f32(S2.cpu(), S.cpu()) < 1e-5
+
+
+def test_decode_equals_chunk(gpu_lib):
+    """L decode steps equal one chunked forward over the same L tokens."""
+    _note("[inv] decode vs chunk")
+    w = I.ChunkWorkload("dvc", 2, 3, 70, 128, 64, 64, "f32", s0_std=0.1)
+    g = _dev(I.make_chunk_inputs(w, seed=23))
+    o, S = chunk_fwd(g["q"], g["k"], g["v"], g["beta"], g["S0"], 64)
+    Sd = g["S0"].clone()
+    outs = []
+    for t in range(w.L):
+        outs.append(decode_step(*(g[n][:, :, t].contiguous() for n in ("q", "k", "v", "beta")), Sd))
+    torch.cuda.synchronize()
+    assert err_f32(torch.stack(outs, 2).cpu(), o.cpu()) < 1e-4
+    assert err_f32(Sd.cpu(), S.cpu()) < 1e-4
+
+
+def test_linearity_in_values_and_state(gpu_lib):
+    """For fixed q, k, beta the map (V, S0) -> (O, S_final) is linear."""
+    _note("[inv] linearity")
+    w = I.ChunkWorkload("lin", 1, 2, 200, 64, 64, 64, "f32", s0_std=0.1)
+    g1 = _dev(I.make_chunk_inputs(w, seed=24))
+    g2 = _dev(I.make_chunk_inputs(w, seed=25))
+    a, b = 0.75, -1.5
+    v = (a * g1["v"] + b * g2["v"]).contiguous()
+    S0 = (a * g1["S0"] + b * g2["S0"]).contiguous()
+    o, S = chunk_fwd(g1["q"], g1["k"], v, g1["beta"], S0, 64)
+    o1, S1 = chunk_fwd(g1["q"], g1["k"], g1["v"], g1["beta"], g1["S0"], 64)
+    o2, S2 = chunk_fwd(g1["q"], g1["k"], g2["v"], g1["beta"], g2["S0"], 64)
+    torch.cuda.synchronize()
+    assert err_f32((a * o1 + b * o2).cpu(), o.cpu()) < 1e-4
+    assert err_f32((a * S1 + b * S2).cpu(), S.cpu()) < 1e-4
+
+
+def test_bitwise_determinism(gpu_lib):
+    """No atomics and a fixed reduction order: two runs match bit for bit."""
+    _note("[inv] determinism")
+    w = I.ChunkWorkload("det", 2, 4, 1024, 128, 128, 128, "bf16", s0_std=0.1)
+    g = _dev(I.make_chunk_inputs(w, seed=26))
+    o1, S1 = chunk_fwd(g["q"], g["k"], g["v"], g["beta"], g["S0"], 128)
+    o2, S2 = chunk_fwd(g["q"], g["k"], g["v"], g["beta"], g["S0"], 128)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_beta_zero_on_gpu(gpu_lib):
+    """beta = 0 (fp32): the state never moves and o = q S0."""
+    _note("[inv] beta zero")
+    w = I.ChunkWorkload("b0", 1, 2, 300, 128, 128, 128, "f32", s0_std=0.1)
+    g = _dev(I.make_chunk_inputs(w, seed=27))
+    beta = torch.zeros_like(g["beta"])
+    o, S = chunk_fwd(g["q"], g["k"], g["v"], beta, g["S0"], 128)
+    torch.cuda.synchronize()
+    q, S0 = to64(g["q"]), to64(g["S0"])
+    assert_parity(o.cpu(), q @ S0, "f32", "o")
+    assert_parity(S.cpu(), S0, "f32", "S")
+
+
+def test_orthonormal_overwrite_on_gpu(gpu_lib):
+    """beta = 1, orthonormal keys (fp32), S0 = 0: queries equal to earlier keys
+    read back those keys' values."""
+    _note("[inv] overwrite")
+    rng = np.random.default_rng(28)
+    d, H = 128, 2
+    Q = np.zeros((1, H, d, d)); K = np.zeros((1, H, d, d)); V = rng.standard_normal((1, H, d, d))
+    want = np.zeros_like(V)
+    for h in range(H):
+        m, r = np.linalg.qr(rng.standard_normal((d, d)))
+        K[0, h] = (m * np.sign(np.diag(r))).T
+        pick = np.array([rng.integers(0, t + 1) for t in range(d)])
+        Q[0, h] = K[0, h][pick]
+        want[0, h] = V[0, h][pick]
+    t = lambda a: torch.from_numpy(a).to(DEV, torch.float32).contiguous()
+    o, S = chunk_fwd(t(Q), t(K), t(V), torch.ones(1, H, d, device=DEV), None, 64)
+    torch.cuda.synchronize()
+    assert_parity(o.cpu(), want, "f32", "retrieval")
