@@ -1,4 +1,9 @@
-// dn_chunk.hip -- chooses the kernel sequence for the chunked forward.
+// dn_chunk.hip -- picks the kernel sequence for the chunked forward.
+//
+// bf16 inputs run on the matrix cores (dn_chunk_mfma.hip): every fp32
+// operand is split into a (hi, lo) bf16 pair, which keeps the products at
+// roughly fp32 accuracy.  fp32 inputs are not exact in bf16, so they run on
+// the fp32 vector-ALU kernels (dn_chunk_valu.hip).
 
 #include "dn_common.h"
 #include "dn_launch.h"
@@ -7,12 +12,18 @@ namespace dn {
 
 size_t chunk_workspace_bytes_valu(int B, int H, int L, int C);
 hipError_t launch_chunk_fwd_valu(const ChunkArgs& a);
+size_t chunk_workspace_bytes_mfma(int B, int H, int L, int C);
+hipError_t launch_chunk_fwd_mfma(const ChunkArgs& a);
 
 size_t chunk_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int in_dtype) {
-  (void)d_k; (void)d_v; (void)in_dtype;
-  return chunk_workspace_bytes_valu(B, H, L, C);
+  (void)d_k;
+  (void)d_v;
+  return in_dtype == 1 ? chunk_workspace_bytes_mfma(B, H, L, C)
+                       : chunk_workspace_bytes_valu(B, H, L, C);
 }
 
-hipError_t launch_chunk_fwd(const ChunkArgs& a) { return launch_chunk_fwd_valu(a); }
+hipError_t launch_chunk_fwd(const ChunkArgs& a) {
+  return a.in_dtype == 1 ? launch_chunk_fwd_mfma(a) : launch_chunk_fwd_valu(a);
+}
 
 }  // namespace dn
