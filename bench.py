@@ -67,7 +67,7 @@ def cpu_baseline(w, x, seconds_hint):
     from deltanet_delta_rule_chunk_amd.inputs import to_f64
     from oracle import delta_rule_forward
 
-    n_tok = 32768
+    n_tok = 4096
     q = to_f64(x["q"][:1, :, :n_tok])
     k = to_f64(x["k"][:1, :, :n_tok])
     v = to_f64(x["v"][:1, :, :n_tok])
@@ -90,6 +90,9 @@ def main(argv=None) -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (the known-size "
+                         "reference for the HBM byte counters) and exit")
     a = ap.parse_args(argv)
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -98,6 +101,16 @@ def main(argv=None) -> int:
         return 2
 
     import torch
+
+    if a.copy_calibration:
+        n = a.copy_calibration << 20
+        src = torch.ones(n // 4, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
+        return 0
 
     from deltanet_delta_rule_chunk_amd import binding, inputs
 
