@@ -318,18 +318,14 @@ __device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ q,
   for (int i = 0; i < RPT; ++i) {
     const int r = sr0 + i;
     const size_t rr = tok0 + min(r, valid - 1);
-    const uint4 kv = *reinterpret_cast<const uint4*>(k + rr * DK + sd0);
-    const uint4 qv = *reinterpret_cast<const uint4*>(q + rr * DK + sd0);
-    const uint32_t m = r < valid ? 0xffffffffu : 0u;
-    kst[i] = make_uint4(kv.x & m, kv.y & m, kv.z & m, kv.w & m);
-    qst[i] = make_uint4(qv.x & m, qv.y & m, qv.z & m, qv.w & m);
+    kst[i] = *reinterpret_cast<const uint4*>(k + rr * DK + sd0);
+    qst[i] = *reinterpret_cast<const uint4*>(q + rr * DK + sd0);
   }
   if (rt >= 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * rt + 4 * g + r;
-      const uint32_t vv = v[(tok0 + min(row, valid - 1)) * DV + j0 + i16];
-      vst[r] = row < valid ? vv : 0u;
+      vst[r] = v[(tok0 + min(row, valid - 1)) * DV + j0 + i16];
     }
     const uint4* tb =
         Tfrag + ((size_t)bh * nc + cc) * Frag<C>::chunk_u4 + (size_t)Frag<C>::base(rt) * 2 * 64;
@@ -405,8 +401,13 @@ __global__ __launch_bounds__((ScanCfg<C, DK>::NTHR)) void scan_kernel(
     const size_t tok0 = (size_t)bh * L + t0;
 
     // (1) Staged k, q -> LDS (k both ways); state slice -> split operand.
+    // Rows past L were loaded from a clamped (valid) row; they are zeroed
+    // here, at first use, so the loads above stay in flight until now.
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
+      const uint32_t m = (sr0 + i) < valid ? 0xffffffffu : 0u;
+      kst[i] = make_uint4(kst[i].x & m, kst[i].y & m, kst[i].z & m, kst[i].w & m);
+      qst[i] = make_uint4(qst[i].x & m, qst[i].y & m, qst[i].z & m, qst[i].w & m);
       *reinterpret_cast<uint4*>(Ks + (sr0 + i) * KLD + sd0) = kst[i];
       *reinterpret_cast<uint4*>(Qs + (sr0 + i) * KLD + sd0) = qst[i];
     }
@@ -426,7 +427,7 @@ __global__ __launch_bounds__((ScanCfg<C, DK>::NTHR)) void scan_kernel(
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vcur[i] = vst[i];
+    for (int i = 0; i < 4; ++i) vcur[i] = (16 * rt + 4 * g + i) < valid ? vst[i] : 0u;
 #pragma unroll
     for (int i = 0; i < 2 * NKB; ++i) tcur[i] = tst[i];
     if (has_dt) {
