@@ -33,10 +33,11 @@
 //
 // LDS: the chunk's K tile (double buffered; 16-byte chunks XOR-swizzled per
 // row so that row reads and the transposing reads of K^T are free of bank
-// conflicts), a ring of state snapshots S_b, R and Delta (Delta double
-// buffered).  The snapshots, R and Delta are stored as split-bf16 operand
-// planes (hi = bf16(x), lo = bf16(x - hi)); q and k are exact in bf16, so
-// every product keeps roughly fp32 accuracy.
+// conflicts), the state snapshots, R and Delta (Delta double buffered).  The
+// entering state, R and Delta are stored as split-bf16 operand planes
+// (hi = bf16(x), lo = bf16(x - hi)); the states inside a chunk are stored as
+// fp32 and split by their reader.  q and k are exact in bf16, so every
+// product keeps roughly fp32 accuracy.
 // A ragged last chunk loads clamped rows and zeroes them at first use
 // (k, v rows and beta = 0 make those rows of R, Delta and T zero: no-ops);
 // outputs past L are not stored.
@@ -62,16 +63,22 @@ struct Cfg {
   static constexpr int NTHR = 512;     // 8 waves
   static constexpr int RPW = NRT / NCW;       // row tiles per chain wave
   static constexpr int DPW = DK / 16 / NCW;   // state tiles per chain wave
-  static constexpr int NSLOT = NSB + 1;       // snapshot ring
+  // State snapshots: the state entering a chunk, S_c, as split planes in a
+  // 2-slot ring (slot c & 1); the states inside the chunk, S_{c,b} for
+  // b = 1 .. NSB-1, as plain fp32 (split by the output waves that read them).
+  static constexpr int NFSNAP = NSB - 1;
   static constexpr int SPT = C * DK / (8 * NTHR);  // staged 16-byte k pieces per thread
   static constexpr int KELEMS = C * DK;       // one K buffer (bf16 elements)
   static constexpr int SPLANE = DK * 16;      // one plane of a state snapshot
   static constexpr int RPLANE = C * 16;       // one plane of R or Delta
   static constexpr int OFF_K = 0;
-  static constexpr int OFF_SNAP = OFF_K + 2 * KELEMS;
-  static constexpr int OFF_R = OFF_SNAP + NSLOT * 2 * SPLANE;
+  static constexpr int OFF_SNAP = OFF_K + 2 * KELEMS;          // [2][hi, lo planes]
+  static constexpr int OFF_FSNAP = OFF_SNAP + 2 * 2 * SPLANE;   // [NFSNAP][DK*16 fp32]
+  static constexpr int OFF_R = OFF_FSNAP + NFSNAP * 2 * SPLANE;
   static constexpr int OFF_D = OFF_R + 2 * RPLANE;
-  static constexpr int TOTAL = OFF_D + 2 * 2 * RPLANE;
+  static constexpr int OFF_V = OFF_D + 2 * 2 * RPLANE;   // [2][C][16] bf16 v slice
+  static constexpr int OFF_O = OFF_V + 2 * C * 16;       // [4 waves][32][16] fp32 out tile
+  static constexpr int TOTAL = OFF_O + 4 * 32 * 16 * 2;
   static constexpr size_t bytes = (size_t)TOTAL * sizeof(uint16_t);
   static_assert(RPW >= 1 && DPW >= 1 && SPT >= 1, "shape");
   static_assert(bytes <= 160 * 1024, "LDS budget");
@@ -127,7 +134,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     float* __restrict__ S_final, const uint4* __restrict__ Tfrag, int L, int nc, int BH) {
   using CF = Cfg<C, DK, DV>;
   constexpr int NRT = CF::NRT, NSB = CF::NSB, NKB = CF::NKB, NCT = CF::NCT;
-  constexpr int RPW = CF::RPW, DPW = CF::DPW, SPT = CF::SPT, NSLOT = CF::NSLOT;
+  constexpr int RPW = CF::RPW, DPW = CF::DPW, SPT = CF::SPT;
   constexpr int SPLANE = CF::SPLANE, RPLANE = CF::RPLANE, KELEMS = CF::KELEMS;
   constexpr int TB0 = 2;        // T blocks of a chain wave's first row tile (tiles 0..3)
   constexpr int TB1 = NRT / 2;  // ... of its second row tile (tiles NRT-4 .. NRT-1)
@@ -136,8 +143,10 @@ __global__ __launch_bounds__(512) void scan_kernel(
   uint16_t* const lds = reinterpret_cast<uint16_t*>(smem_raw);
   uint16_t* const Kbuf = lds + CF::OFF_K;
   uint16_t* const Snap = lds + CF::OFF_SNAP;
+  float* const Fsnap = reinterpret_cast<float*>(lds + CF::OFF_FSNAP);
   uint16_t* const Rb = lds + CF::OFF_R;
   uint16_t* const Db = lds + CF::OFF_D;
+  uint16_t* const Vbuf = lds + CF::OFF_V;
 
   const int flat = blockIdx.x, xcd = flat & 7, sl = flat >> 3;
   const int ct = sl % NCT, bh = (sl / NCT) * 8 + xcd;
@@ -145,32 +154,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
   const int j0 = ct * 16;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, i16 = lane & 15;
   const bool chain = w < CF::NCW;
-  const int a = w - CF::NCW;  // output wave index = sub-block
-  const bool outw = !chain && a < NSB;
-
   const size_t sbase = (size_t)bh * DK * DV;
   const size_t tokh = (size_t)bh * L;
-  const int rt0 = w, rt1 = NRT - 1 - w;  // chain row tiles (rt1 only if RPW == 2)
-
-  // ---- chain state -------------------------------------------------------
-  f32x4 sa[DPW], sb[DPW];
-#pragma unroll
-  for (int i = 0; i < DPW; ++i) { sa[i] = zero4(); sb[i] = zero4(); }
-  uint32_t vreg[RPW][4];
-  // One register array serves both roles (a wave is either a chain wave or
-  // an output wave, so the compiler must not keep both sets live):
-  //   chain waves:  the chunk's T fragments for the wave's row tiles;
-  //   output waves: the q rows of the chunk whose outputs are due.
-  constexpr int NTREG = 2 * TB0 + (RPW == 2 ? 2 * TB1 : 0);
-  constexpr int NBANK = NTREG > 2 * NKB ? NTREG : 2 * NKB;
-  uint4 bank[NBANK];
-  uint4* const t0h = bank;
-  uint4* const t0l = bank + TB0;
-  uint4* const t1h = bank + 2 * TB0;
-  uint4* const t1l = bank + 2 * TB0 + TB1;
-  auto qreg = [&](int h, int kb) -> uint4& { return bank[h * NKB + kb]; };
-  // ---- staging of the next chunk's k tile (all threads) ------------------
-  uint4 kst[SPT];
 
   if (nc == 0) {
     if (chain && S_final) {
@@ -188,8 +173,11 @@ __global__ __launch_bounds__(512) void scan_kernel(
   }
 
   auto valid_of = [&](int cc) { return min(C, L - cc * C); };
-  auto slot_of = [&](int n) { return n % NSLOT; };
 
+  // Staging of a chunk's k tile into LDS, shared by all 512 threads.  The
+  // global loads of the next chunk are issued early and consumed by the
+  // store one or two phases later; rows past L are zeroed at the store.
+  uint4 kst[SPT];
   auto stage_load = [&](int cc) {
     const int valid = valid_of(cc);
     const size_t t0 = tokh + (size_t)cc * C;
@@ -201,123 +189,60 @@ __global__ __launch_bounds__(512) void scan_kernel(
   };
   auto stage_store = [&](int cc, uint16_t* dst) {
     const int valid = valid_of(cc);
+    if (valid == C) {
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int e = i * CF::NTHR + tid, row = e / (DK / 8), ch = e % (DK / 8);
-      const uint32_t m = row < valid ? 0xffffffffu : 0u;
-      *reinterpret_cast<uint4*>(dst + koff<DK>(row, ch)) =
-          make_uint4(kst[i].x & m, kst[i].y & m, kst[i].z & m, kst[i].w & m);
-    }
-  };
-  auto v_load = [&](int cc) {
-    const int valid = valid_of(cc);
-    const size_t t0 = tokh + (size_t)cc * C;
+      for (int i = 0; i < SPT; ++i) {
+        const int e = i * CF::NTHR + tid, row = e / (DK / 8), ch = e % (DK / 8);
+        *reinterpret_cast<uint4*>(dst + koff<DK>(row, ch)) = kst[i];
+      }
+    } else {
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int rt = i == 0 ? rt0 : rt1;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * rt + 4 * g + r;
-        vreg[i][r] = v[(t0 + min(row, valid - 1)) * DV + j0 + i16];
+      for (int i = 0; i < SPT; ++i) {
+        const int e = i * CF::NTHR + tid, row = e / (DK / 8), ch = e % (DK / 8);
+        const uint32_t m = row < valid ? 0xffffffffu : 0u;
+        *reinterpret_cast<uint4*>(dst + koff<DK>(row, ch)) =
+            make_uint4(kst[i].x & m, kst[i].y & m, kst[i].z & m, kst[i].w & m);
       }
     }
   };
-  auto t_load = [&](int cc) {
-    const uint4* tb = Tfrag + ((size_t)bh * nc + cc) * Frag<C>::chunk_u4;
-    const uint4* p0 = tb + (size_t)Frag<C>::base(rt0) * 128 + lane;
+
+  // Each role runs its own loop with the same three barriers per chunk, and
+  // every global load inside a loop is unconditional (the chunk index is
+  // clamped on the last step), so the compiler's wait counts stay exact and
+  // the loads of the next chunk remain in flight across phases.
+  if (chain) {
+    // ======================= chain waves =====================================
+    __builtin_amdgcn_s_setprio(2);
+    const int rt0 = w, rt1 = NRT - 1 - w;  // row tiles (rt1 only if RPW == 2)
+    f32x4 sa[DPW], sb[DPW];
+    uint4 t0h[TB0], t0l[TB0], t1h[TB1], t1l[TB1];
+    // Slots past a tile's last block re-read block 0 (unused).
+    auto t_load = [&](int cc) {
+      const uint4* tb = Tfrag + ((size_t)bh * nc + cc) * Frag<C>::chunk_u4 + lane;
+      const uint4* p0 = tb + (size_t)Frag<C>::base(rt0) * 128;
 #pragma unroll
-    for (int cb = 0; cb < TB0; ++cb) {
-      if (cb <= rt0 / 2) {
-        t0h[cb] = p0[(2 * cb) * 64];
-        t0l[cb] = p0[(2 * cb + 1) * 64];
+      for (int cb = 0; cb < TB0; ++cb) {
+        const int blk = cb <= rt0 / 2 ? cb : 0;
+        t0h[cb] = p0[(2 * blk) * 64];
+        t0l[cb] = p0[(2 * blk + 1) * 64];
       }
-    }
-    if constexpr (RPW == 2) {
-      const uint4* p1 = tb + (size_t)Frag<C>::base(rt1) * 128 + lane;
+      if constexpr (RPW == 2) {
+        const uint4* p1 = tb + (size_t)Frag<C>::base(rt1) * 128;
 #pragma unroll
-      for (int cb = 0; cb < TB1; ++cb) {
-        if (cb <= rt1 / 2) {
-          t1h[cb] = p1[(2 * cb) * 64];
-          t1l[cb] = p1[(2 * cb + 1) * 64];
+        for (int cb = 0; cb < TB1; ++cb) {
+          const int blk = cb <= rt1 / 2 ? cb : 0;
+          t1h[cb] = p1[(2 * blk) * 64];
+          t1l[cb] = p1[(2 * blk + 1) * 64];
         }
       }
-    }
-  };
-  auto q_load = [&](int cc) {
-    const int valid = valid_of(cc);
-    const size_t t0 = tokh + (size_t)cc * C;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = min(32 * a + 16 * h + i16, valid - 1);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        qreg(h, kb) = *reinterpret_cast<const uint4*>(q + (t0 + row) * DK + 32 * kb + 8 * g);
-    }
-  };
+    };
 
-  // Outputs of chunk cc for sub-block a: Q_a S_a + tril(Q_a K_a^T) Delta_a,
-  // with the q rows in qreg and chunk cc's k tile still in its LDS buffer.
-  auto outputs = [&](int cc) {
-    const int valid = valid_of(cc);
-    const size_t t0 = tokh + (size_t)cc * C;
-    const uint16_t* Kc = Kbuf + (cc & 1) * KELEMS;
-    const uint16_t* Sn = Snap + slot_of(cc * NSB + a) * 2 * SPLANE;
-    const uint16_t* Dc = Db + (cc & 1) * 2 * RPLANE;
-    // Diagonal 32 x 32 block of Q K^T as transposed 16 x 16 tiles: lane
-    // (i16, g) register r holds P[q = i16][k = 4 g + r] of its tile; the two
-    // diagonal tiles keep k <= q, the tile above the diagonal is not needed.
-    f32x4 p00 = zero4(), p01 = zero4(), p11 = zero4();
-    f32x4 o0h = zero4(), o0l = zero4(), o1h = zero4(), o1l = zero4();
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const bf16x8 K0 = lds16(Kc + koff<DK>(32 * a + i16, 4 * kb + g));
-      const bf16x8 K1 = lds16(Kc + koff<DK>(32 * a + 16 + i16, 4 * kb + g));
-      const bf16x8 Q0 = as_bf16x8(qreg(0, kb)), Q1 = as_bf16x8(qreg(1, kb));
-      p00 = mfma16(K0, Q0, p00);
-      p01 = mfma16(K0, Q1, p01);
-      p11 = mfma16(K1, Q1, p11);
-      const bf16x8 Sh = lds16(Sn + fo_b(kb, g, i16)), Sl = lds16(Sn + SPLANE + fo_b(kb, g, i16));
-      o0h = mfma16(Q0, Sh, o0h);
-      o0l = mfma16(Q0, Sl, o0l);
-      o1h = mfma16(Q1, Sh, o1h);
-      o1l = mfma16(Q1, Sl, o1l);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (4 * g + r > i16) { p00[r] = 0.f; p11[r] = 0.f; }
-    }
-    // As A operands in the "d4" slot map: slots (g, 0..3) <-> k tile 2a rows
-    // 4g..4g+3, slots (g, 4..7) <-> k tile 2a+1 rows 4g..4g+3.
-    uint2 h00, l00, h01, l01, h11, l11;
-    split4(p00, h00, l00);
-    split4(p01, h01, l01);
-    split4(p11, h11, l11);
-    const uint4 ph0 = make_uint4(h00.x, h00.y, 0u, 0u), pl0 = make_uint4(l00.x, l00.y, 0u, 0u);
-    const uint4 ph1 = make_uint4(h01.x, h01.y, h11.x, h11.y);
-    const uint4 pl1 = make_uint4(l01.x, l01.y, l11.x, l11.y);
-    const bf16x8 Dh = as_bf16x8(lds8(Dc + fo_d(2 * a, g, i16)), lds8(Dc + fo_d(2 * a + 1, g, i16)));
-    const bf16x8 Dl = as_bf16x8(lds8(Dc + RPLANE + fo_d(2 * a, g, i16)),
-                                lds8(Dc + RPLANE + fo_d(2 * a + 1, g, i16)));
-    f32x4 x0 = mfma16(as_bf16x8(ph0), Dh, zero4());
-    f32x4 x1 = mfma16(as_bf16x8(ph1), Dh, zero4());
-    x0 = mfma16(as_bf16x8(ph0), Dl, x0);
-    x1 = mfma16(as_bf16x8(ph1), Dl, x1);
-    x0 = mfma16(as_bf16x8(pl0), Dh, x0);
-    x1 = mfma16(as_bf16x8(pl1), Dh, x1);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row0 = 32 * a + 4 * g + r, row1 = row0 + 16;
-      if (row0 < valid) o[(t0 + row0) * DV + j0 + i16] = from_f32<OT>(o0h[r] + o0l[r] + x0[r]);
-      if (row1 < valid) o[(t0 + row1) * DV + j0 + i16] = from_f32<OT>(o1h[r] + o1l[r] + x1[r]);
-    }
-  };
-
-  // ---- prologue ------------------------------------------------------------
-  if (chain) {
-    __builtin_amdgcn_s_setprio(2);
+    t_load(0);
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int dt = DPW * w + i;
+      sa[i] = zero4();
+      sb[i] = zero4();
       if (S0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -325,126 +250,354 @@ __global__ __launch_bounds__(512) void scan_kernel(
       }
       put_split(Snap, SPLANE, fo_d(dt, g, i16), sa[i]);
     }
-    v_load(0);
-    t_load(0);
-  }
-  stage_load(0);
-  stage_store(0, Kbuf);
-  __syncthreads();
+    stage_load(0);
+    stage_store(0, Kbuf);
+    __syncthreads();
 
-  for (int c = 0; c < nc; ++c) {
-    const bool more = c + 1 < nc;
-    const int valid = valid_of(c);
-    const uint16_t* Kc = Kbuf + (c & 1) * KELEMS;
-    uint16_t* Dc = Db + (c & 1) * 2 * RPLANE;
+    const int m = i16 >> 2, ap = i16 & 3;
+    for (int c = 0; c < nc; ++c) {
+      const int cn = min(c + 1, nc - 1);
+      const uint16_t* Kc = Kbuf + (c & 1) * KELEMS;
+      uint16_t* Dc = Db + (c & 1) * 2 * RPLANE;
 
-    // ---- phase A: R = V - K S (chain); outputs of chunk c-1 (output waves)
-    if (more) stage_load(c + 1);
-    if (chain) {
-      const uint16_t* Sc = Snap + slot_of(c * NSB) * 2 * SPLANE;
-      f32x4 rh[RPW], rl[RPW];
+      // ---- phase A: R = V - K S ----------------------------------------------
+      stage_load(cn);
+      {
+        const uint16_t* Sc = Snap + (c & 1) * 2 * SPLANE;
+        // All LDS operands of the phase are read up front, then multiplied.
+        bf16x8 Sh[NKB], Sl[NKB], Ka[RPW][NKB];
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) { rh[i] = zero4(); rl[i] = zero4(); }
+        for (int kb = 0; kb < NKB; ++kb) {
+          Sh[kb] = lds16(Sc + fo_b(kb, g, i16));
+          Sl[kb] = lds16(Sc + SPLANE + fo_b(kb, g, i16));
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 Sh = lds16(Sc + fo_b(kb, g, i16)), Sl = lds16(Sc + SPLANE + fo_b(kb, g, i16));
+          for (int i = 0; i < RPW; ++i)
+            Ka[i][kb] = lds16(Kc + koff<DK>(16 * (i == 0 ? rt0 : rt1) + i16, 4 * kb + g));
+        }
+        f32x4 rh[RPW], rl[RPW];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) { rh[i] = zero4(); rl[i] = zero4(); }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int i = 0; i < RPW; ++i) {
+            rh[i] = mfma16(Ka[i][kb], Sh[kb], rh[i]);
+            rl[i] = mfma16(Ka[i][kb], Sl[kb], rl[i]);
+          }
+        }
+        // v in the D layout straight from the staged row-major slice: the
+        // transposing read gives lane (i16, g) rows 16 rt + 4 g .. + 3 of
+        // column i16 (rows past L were staged as zero).
+        const uint16_t* Vc = Vbuf + (c & 1) * C * 16;
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
           const int rt = i == 0 ? rt0 : rt1;
-          const bf16x8 Ka = lds16(Kc + koff<DK>(16 * rt + i16, 4 * kb + g));
-          rh[i] = mfma16(Ka, Sh, rh[i]);
-          rl[i] = mfma16(Ka, Sl, rl[i]);
+          const uint2 vv = lds_tr(Vc + (16 * rt + 4 * g + m) * 16 + 4 * ap);
+          const float v4[4] = {bf16_to_f32(vv.x & 0xffffu), bf16_to_f32(vv.x >> 16),
+                               bf16_to_f32(vv.y & 0xffffu), bf16_to_f32(vv.y >> 16)};
+          f32x4 R;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) R[r] = v4[r] - (rh[i][r] + rl[i][r]);
+          put_split(Rb, RPLANE, fo_d(rt, g, i16), R);
         }
       }
-#pragma unroll
-      for (int i = 0; i < RPW; ++i) {
-        const int rt = i == 0 ? rt0 : rt1;
-        f32x4 R;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float vv = (16 * rt + 4 * g + r) < valid ? bf16_to_f32(vreg[i][r]) : 0.f;
-          R[r] = vv - (rh[i][r] + rl[i][r]);
-        }
-        put_split(Rb, RPLANE, fo_d(rt, g, i16), R);
-      }
-    } else if (outw) {
-      if (c > 0) outputs(c - 1);
-      q_load(c);
-    }
-    __syncthreads();
+      __syncthreads();
 
-    // ---- phase B: Delta = T R (chain) ---------------------------------------
-    if (chain) {
-      if (more) v_load(c + 1);
+      // ---- phase B: Delta = T R ------------------------------------------------
       {
+        constexpr int NRB = RPW == 2 ? TB1 : TB0;  // R blocks any tile of this wave needs
+        const int nrb = (RPW == 2 ? rt1 : rt0) / 2 + 1;
+        bf16x8 Rh[NRB], Rl[NRB];
+#pragma unroll
+        for (int cb = 0; cb < NRB; ++cb) {
+          if (cb < nrb) {
+            Rh[cb] = lds16(Rb + fo_b(cb, g, i16));
+            Rl[cb] = lds16(Rb + RPLANE + fo_b(cb, g, i16));
+          }
+        }
         f32x4 d0 = zero4(), d1 = zero4(), d2 = zero4();
 #pragma unroll
         for (int cb = 0; cb < TB0; ++cb) {
           if (cb <= rt0 / 2) {
-            const bf16x8 Rh = lds16(Rb + fo_b(cb, g, i16)), Rl = lds16(Rb + RPLANE + fo_b(cb, g, i16));
-            d0 = mfma16(as_bf16x8(t0h[cb]), Rh, d0);
-            d1 = mfma16(as_bf16x8(t0h[cb]), Rl, d1);
-            d2 = mfma16(as_bf16x8(t0l[cb]), Rh, d2);
+            d0 = mfma16(as_bf16x8(t0h[cb]), Rh[cb], d0);
+            d1 = mfma16(as_bf16x8(t0h[cb]), Rl[cb], d1);
+            d2 = mfma16(as_bf16x8(t0l[cb]), Rh[cb], d2);
           }
+        }
+        if constexpr (RPW == 2) {
+          f32x4 e0 = zero4(), e1 = zero4(), e2 = zero4();
+#pragma unroll
+          for (int cb = 0; cb < TB1; ++cb) {
+            if (cb <= rt1 / 2) {
+              e0 = mfma16(as_bf16x8(t1h[cb]), Rh[cb], e0);
+              e1 = mfma16(as_bf16x8(t1h[cb]), Rl[cb], e1);
+              e2 = mfma16(as_bf16x8(t1l[cb]), Rh[cb], e2);
+            }
+          }
+          put_split(Dc, RPLANE, fo_d(rt1, g, i16), e0 + e1 + e2);
         }
         put_split(Dc, RPLANE, fo_d(rt0, g, i16), d0 + d1 + d2);
       }
-      if constexpr (RPW == 2) {
-        f32x4 d0 = zero4(), d1 = zero4(), d2 = zero4();
+      __syncthreads();
+
+      // ---- phase C: S += K^T Delta, snapshot after every sub-block -------------
+      t_load(cn);
+      {
+        bf16x8 Dh[NSB], Dl[NSB], Kt[NSB][DPW];
 #pragma unroll
-        for (int cb = 0; cb < TB1; ++cb) {
-          if (cb <= rt1 / 2) {
-            const bf16x8 Rh = lds16(Rb + fo_b(cb, g, i16)), Rl = lds16(Rb + RPLANE + fo_b(cb, g, i16));
-            d0 = mfma16(as_bf16x8(t1h[cb]), Rh, d0);
-            d1 = mfma16(as_bf16x8(t1h[cb]), Rl, d1);
-            d2 = mfma16(as_bf16x8(t1l[cb]), Rh, d2);
+        for (int b = 0; b < NSB; ++b) {
+          Dh[b] = lds16(Dc + fo_b(b, g, i16));
+          Dl[b] = lds16(Dc + RPLANE + fo_b(b, g, i16));
+          const int row = 32 * b + 8 * g + m;
+#pragma unroll
+          for (int i = 0; i < DPW; ++i) {
+            const int ch = 2 * (DPW * w + i) + (ap >> 1), sub = 4 * (ap & 1);
+            Kt[b][i] = as_bf16x8(lds_tr(Kc + koff<DK>(row, ch) + sub),
+                                 lds_tr(Kc + koff<DK>(row + 4, ch) + sub));
           }
         }
-        put_split(Dc, RPLANE, fo_d(rt1, g, i16), d0 + d1 + d2);
-      }
-    }
-    __syncthreads();
-
-    // ---- phase C: S += K^T Delta with sub-block snapshots (chain);
-    //      stage k of chunk c+1 (all waves).
-    if (chain) {
-      if (more) t_load(c + 1);
-      const int m = i16 >> 2, ap = i16 & 3;
 #pragma unroll
-      for (int b = 0; b < NSB; ++b) {
-        const bf16x8 Dh = lds16(Dc + fo_b(b, g, i16)), Dl = lds16(Dc + RPLANE + fo_b(b, g, i16));
-        const int row = 32 * b + 8 * g + m;
+        for (int b = 0; b < NSB; ++b) {
 #pragma unroll
-        for (int i = 0; i < DPW; ++i) {
-          const int dt = DPW * w + i;
-          const int ch = 2 * dt + (ap >> 1), sub = 4 * (ap & 1);
-          const uint2 lo4 = lds_tr(Kc + koff<DK>(row, ch) + sub);
-          const uint2 hi4 = lds_tr(Kc + koff<DK>(row + 4, ch) + sub);
-          const bf16x8 A = as_bf16x8(lo4, hi4);
-          sa[i] = mfma16(A, Dh, sa[i]);
-          sb[i] = mfma16(A, Dl, sb[i]);
+          for (int i = 0; i < DPW; ++i) {
+            sa[i] = mfma16(Kt[b][i], Dh[b], sa[i]);
+            sb[i] = mfma16(Kt[b][i], Dl[b], sb[i]);
+          }
+          if (b + 1 < NSB) {
+            float* dst = Fsnap + b * DK * 16;
+#pragma unroll
+            for (int i = 0; i < DPW; ++i)
+              *reinterpret_cast<f32x4*>(dst + fo_d(DPW * w + i, g, i16)) = sa[i] + sb[i];
+          } else {
+            uint16_t* dst = Snap + ((c + 1) & 1) * 2 * SPLANE;
+#pragma unroll
+            for (int i = 0; i < DPW; ++i)
+              put_split(dst, SPLANE, fo_d(DPW * w + i, g, i16), sa[i] + sb[i]);
+          }
         }
-        uint16_t* dst = Snap + slot_of(c * NSB + b + 1) * 2 * SPLANE;
-#pragma unroll
-        for (int i = 0; i < DPW; ++i) put_split(dst, SPLANE, fo_d(DPW * w + i, g, i16), sa[i] + sb[i]);
       }
 #pragma unroll
       for (int i = 0; i < DPW; ++i) { sa[i] = sa[i] + sb[i]; sb[i] = zero4(); }
+      stage_store(cn, Kbuf + ((c + 1) & 1) * KELEMS);
+      __syncthreads();
     }
-    if (more) stage_store(c + 1, Kbuf + ((c + 1) & 1) * KELEMS);
-    __syncthreads();
-  }
 
-  // ---- epilogue ------------------------------------------------------------
-  if (outw) outputs(nc - 1);
-  if (chain && S_final) {
+    if (S_final) {
 #pragma unroll
-    for (int i = 0; i < DPW; ++i) {
-      const int dt = DPW * w + i;
+      for (int i = 0; i < DPW; ++i) {
+        const int dt = DPW * w + i;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        S_final[sbase + (size_t)(16 * dt + 4 * g + r) * DV + j0 + i16] = sa[i][r];
+        for (int r = 0; r < 4; ++r)
+          S_final[sbase + (size_t)(16 * dt + 4 * g + r) * DV + j0 + i16] = sa[i][r];
+      }
     }
+  } else {
+    // ======================= output waves ====================================
+    // Wave 4 + a owns sub-block a (row tiles 2a, 2a+1).  With C = 64 only
+    // waves 4 and 5 have a sub-block; the others load and stage like the rest
+    // but skip the arithmetic.
+    const int a = w - CF::NCW;
+    const bool outw = a < NSB;
+    const int aq = outw ? a : 0;
+    uint4 qreg[2][NKB];
+    // The chunk's 16-column v slice is staged row-major into LDS by the
+    // output waves' 256 threads (16 bytes each: row tl / 2, half tl % 2);
+    // rows past L are stored as zero.
+    const int tl = tid - CF::NCW * 64;  // 0 .. 255
+    const int vrow = min(tl >> 1, C - 1), vhalf = tl & 1;
+    uint4 vst;
+    auto v_stage_load = [&](int cc) {
+      const int valid = valid_of(cc);
+      const size_t t0 = tokh + (size_t)cc * C;
+      vst = *reinterpret_cast<const uint4*>(v + (t0 + min(vrow, valid - 1)) * DV + j0 + 8 * vhalf);
+    };
+    auto v_stage_store = [&](int cc, uint16_t* dst) {
+      const int valid = valid_of(cc);
+      if (tl < 2 * C) {
+        const uint32_t msk = vrow < valid ? 0xffffffffu : 0u;
+        *reinterpret_cast<uint4*>(dst + vrow * 16 + 8 * vhalf) =
+            make_uint4(vst.x & msk, vst.y & msk, vst.z & msk, vst.w & msk);
+      }
+    };
+    auto q_load = [&](int cc) {
+      const int valid = valid_of(cc);
+      const size_t t0 = tokh + (size_t)cc * C;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = min(32 * aq + 16 * h + i16, valid - 1);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          qreg[h][kb] = *reinterpret_cast<const uint4*>(q + (t0 + row) * DK + 32 * kb + 8 * g);
+      }
+    };
+    // Diagonal 32 x 32 block of Q K^T of chunk cc for sub-block a, as split
+    // A operands of the P Delta product.  Computed as transposed 16 x 16
+    // tiles: lane (i16, g) register r holds P[q = i16][k = 4 g + r] of its
+    // tile; the two diagonal tiles keep k <= q, the tile above the diagonal is
+    // not needed.  "d4" slot map: slots (g, 0..3) <-> k tile 2a rows
+    // 4g..4g+3, slots (g, 4..7) <-> k tile 2a+1 rows 4g..4g+3.
+    uint4 ph0, pl0, ph1, pl1;
+    auto diag_qk = [&](int cc) {
+      const uint16_t* Kc = Kbuf + (cc & 1) * KELEMS;
+      bf16x8 K0[NKB], K1[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        K0[kb] = lds16(Kc + koff<DK>(32 * a + i16, 4 * kb + g));
+        K1[kb] = lds16(Kc + koff<DK>(32 * a + 16 + i16, 4 * kb + g));
+      }
+      f32x4 p00 = zero4(), p01 = zero4(), p11 = zero4();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 Q0 = as_bf16x8(qreg[0][kb]), Q1 = as_bf16x8(qreg[1][kb]);
+        p00 = mfma16(K0[kb], Q0, p00);
+        p01 = mfma16(K0[kb], Q1, p01);
+        p11 = mfma16(K1[kb], Q1, p11);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (4 * g + r > i16) { p00[r] = 0.f; p11[r] = 0.f; }
+      }
+      uint2 h00, l00, h01, l01, h11, l11;
+      split4(p00, h00, l00);
+      split4(p01, h01, l01);
+      split4(p11, h11, l11);
+      ph0 = make_uint4(h00.x, h00.y, 0u, 0u);
+      pl0 = make_uint4(l00.x, l00.y, 0u, 0u);
+      ph1 = make_uint4(h01.x, h01.y, h11.x, h11.y);
+      pl1 = make_uint4(l01.x, l01.y, l11.x, l11.y);
+    };
+    // Outputs of chunk cc for sub-block a: Q_a S_a + tril(Q_a K_a^T) Delta_a,
+    // with chunk cc's q rows in qreg and its diagonal Q K^T block in ph/pl.
+    auto outputs = [&](int cc) {
+      const int valid = valid_of(cc);
+      const size_t t0 = tokh + (size_t)cc * C;
+      const uint16_t* Dc = Db + (cc & 1) * 2 * RPLANE;
+      bf16x8 Sh[NKB], Sl[NKB];
+      if (a == 0) {
+        const uint16_t* Sn = Snap + (cc & 1) * 2 * SPLANE;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          Sh[kb] = lds16(Sn + fo_b(kb, g, i16));
+          Sl[kb] = lds16(Sn + SPLANE + fo_b(kb, g, i16));
+        }
+      } else {
+        const float* Sn = Fsnap + (a - 1) * DK * 16;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(Sn + fo_b(kb, g, i16));
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(Sn + fo_b(kb, g, i16) + 4);
+          uint2 h0, l0, h1, l1;
+          split4(x0, h0, l0);
+          split4(x1, h1, l1);
+          Sh[kb] = as_bf16x8(h0, h1);
+          Sl[kb] = as_bf16x8(l0, l1);
+        }
+      }
+      const bf16x8 Dh = as_bf16x8(lds8(Dc + fo_d(2 * a, g, i16)), lds8(Dc + fo_d(2 * a + 1, g, i16)));
+      const bf16x8 Dl = as_bf16x8(lds8(Dc + RPLANE + fo_d(2 * a, g, i16)),
+                                  lds8(Dc + RPLANE + fo_d(2 * a + 1, g, i16)));
+      f32x4 o0h = zero4(), o0l = zero4(), o1h = zero4(), o1l = zero4();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 Q0 = as_bf16x8(qreg[0][kb]), Q1 = as_bf16x8(qreg[1][kb]);
+        o0h = mfma16(Q0, Sh[kb], o0h);
+        o0l = mfma16(Q0, Sl[kb], o0l);
+        o1h = mfma16(Q1, Sh[kb], o1h);
+        o1l = mfma16(Q1, Sl[kb], o1l);
+      }
+      f32x4 x0 = mfma16(as_bf16x8(ph0), Dh, zero4());
+      f32x4 x1 = mfma16(as_bf16x8(ph1), Dh, zero4());
+      x0 = mfma16(as_bf16x8(ph0), Dl, x0);
+      x1 = mfma16(as_bf16x8(ph1), Dl, x1);
+      x0 = mfma16(as_bf16x8(pl0), Dh, x0);
+      x1 = mfma16(as_bf16x8(pl1), Dh, x1);
+      // Transpose the 32 x 16 output tile through this wave's LDS tile so
+      // each lane stores 4 consecutive columns of one row (16-byte groups of
+      // a row XOR-swizzled by row / 4 to keep both accesses conflict-free).
+      float* Ot = reinterpret_cast<float*>(lds + CF::OFF_O) + a * 32 * 16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row0 = 4 * g + r, row1 = row0 + 16;
+        Ot[row0 * 16 + ((((i16 >> 2) ^ (row0 >> 2)) & 3) << 2) + (i16 & 3)] = o0h[r] + o0l[r] + x0[r];
+        Ot[row1 * 16 + ((((i16 >> 2) ^ (row1 >> 2)) & 3) << 2) + (i16 & 3)] = o1h[r] + o1l[r] + x1[r];
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 16 * h + (lane >> 2), cg = lane & 3;
+        const f32x4 val = *reinterpret_cast<const f32x4*>(Ot + row * 16 + (((cg ^ (row >> 2)) & 3) << 2));
+        if (32 * a + row < valid) {
+          OT* dst = o + (t0 + 32 * a + row) * DV + j0 + 4 * cg;
+          if constexpr (sizeof(OT) == 4) {
+            *reinterpret_cast<f32x4*>(dst) = val;
+          } else {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16(val[0], val[1]), pack_bf16(val[2], val[3]));
+          }
+        }
+      }
+    };
+
+    // L2 prefetch: the 64-byte sectors of chunk cc's k, q, v and T data are
+    // split over the head's column-slice workgroups (which share an XCD and
+    // its L2); output-wave thread t touches sectors ct + NCT (t + 256 j) with
+    // one dword load each.  The values are folded into pf_acc one chunk later,
+    // so the loads never stall anything, and pf_acc is only ever stored under
+    // a condition that is false.
+    constexpr int LK = C * DK / 32, LV = C * DV / 32, LT = (int)(Frag<C>::chunk_u4 / 4);
+    constexpr int NLINES = 2 * LK + LV + LT;
+    constexpr int NPF = (NLINES / NCT + 255) / 256;
+    uint32_t pf_acc = 0, pf_val[NPF];
+#pragma unroll
+    for (int j = 0; j < NPF; ++j) pf_val[j] = 0;
+    auto prefetch = [&](int cc) {
+      const int valid = valid_of(cc);
+      const size_t t0 = tokh + (size_t)cc * C;
+#pragma unroll
+      for (int j = 0; j < NPF; ++j) {
+        const int n = min(ct + NCT * (tl + 256 * j), NLINES - 1);
+        const uint32_t* src;
+        if (n < 2 * LK) {
+          const int e = (n % LK) * 32, row = min(e / DK, valid - 1);
+          const uint16_t* base = n < LK ? k : q;
+          src = reinterpret_cast<const uint32_t*>(base + (t0 + row) * DK + e % DK);
+        } else if (n < 2 * LK + LV) {
+          const int e = (n - 2 * LK) * 32, row = min(e / DV, valid - 1);
+          src = reinterpret_cast<const uint32_t*>(v + (t0 + row) * DV + e % DV);
+        } else {
+          src = reinterpret_cast<const uint32_t*>(Tfrag + ((size_t)bh * nc + cc) * Frag<C>::chunk_u4 +
+                                                  4 * (n - 2 * LK - LV));
+        }
+        pf_val[j] = *src;
+      }
+    };
+
+    v_stage_load(0);
+    stage_load(0);
+    v_stage_store(0, Vbuf);
+    stage_store(0, Kbuf);
+    __syncthreads();
+    for (int c = 0; c < nc; ++c) {
+      const int cn = min(c + 1, nc - 1);
+      // ---- phase A: outputs of chunk c-1; q rows of chunk c ------------------
+      stage_load(cn);
+      v_stage_load(cn);
+      if (outw && c > 0) outputs(c - 1);
+      q_load(c);
+      __syncthreads();
+      // ---- phase B: L2 prefetch of chunk c+2 ------------------------------------
+#pragma unroll
+      for (int j = 0; j < NPF; ++j) pf_acc ^= pf_val[j];
+      prefetch(min(c + 2, nc - 1));
+      __syncthreads();
+      // ---- phase C: diagonal Q K^T block of chunk c ------------------------------
+      if (outw) diag_qk(c);
+      v_stage_store(cn, Vbuf + ((c + 1) & 1) * C * 16);
+      stage_store(cn, Kbuf + ((c + 1) & 1) * KELEMS);
+      __syncthreads();
+    }
+    if (outw) outputs(nc - 1);
+#pragma unroll
+    for (int j = 0; j < NPF; ++j) pf_acc ^= pf_val[j];
+    if (nc < 0) S_final[0] = __uint_as_float(pf_acc);
   }
 }
 
