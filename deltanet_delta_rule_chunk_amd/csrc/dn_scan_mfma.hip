@@ -45,6 +45,7 @@
 #include "dn_common.h"
 #include "dn_launch.h"
 #include "dn_mfma.h"
+#include "dn_ktile.h"
 #include "dn_tfrag.h"
 
 namespace dn {
@@ -83,19 +84,6 @@ struct Cfg {
   static_assert(RPW >= 1 && DPW >= 1 && SPT >= 1, "shape");
   static_assert(bytes <= 160 * 1024, "LDS budget");
 };
-
-// XOR swizzle of the 16-byte chunks of K-tile row `row` (conflict-free for
-// 16-lane row reads and for the transposing 8-byte reads used for K^T).
-template <int DK>
-__device__ __forceinline__ int kswz(int row) {
-  if constexpr (DK == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-  else return ((row >> 2) & 3) | ((row & 2) << 1);
-}
-// Element offset of 16-byte chunk `ch` (elements 8 ch .. 8 ch + 7) of row `row`.
-template <int DK>
-__device__ __forceinline__ int koff(int row, int ch) {
-  return row * DK + ((ch ^ kswz<DK>(row)) << 3);
-}
 
 // Operand planes of a [rows x 16] split matrix: element (x, j) at
 // ((x / 8) * 16 + j) * 8 + x % 8.
@@ -310,9 +298,10 @@ __global__ __launch_bounds__(512) void scan_kernel(
         bf16x8 Rh[NRB], Rl[NRB];
 #pragma unroll
         for (int cb = 0; cb < NRB; ++cb) {
-          if (cb < nrb) {
-            Rh[cb] = lds16(Rb + fo_b(cb, g, i16));
-            Rl[cb] = lds16(Rb + RPLANE + fo_b(cb, g, i16));
+          if (cb < nrb) {  // d4 slot map, matching the T fragments
+            Rh[cb] = as_bf16x8(lds8(Rb + fo_d(2 * cb, g, i16)), lds8(Rb + fo_d(2 * cb + 1, g, i16)));
+            Rl[cb] = as_bf16x8(lds8(Rb + RPLANE + fo_d(2 * cb, g, i16)),
+                               lds8(Rb + RPLANE + fo_d(2 * cb + 1, g, i16)));
           }
         }
         f32x4 d0 = zero4(), d1 = zero4(), d2 = zero4();
