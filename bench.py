@@ -32,6 +32,41 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
+CSRC = os.path.join(ROOT, "deltanet_delta_rule_chunk_amd", "csrc")
+# Source files each kernel is built from (a change to any of them makes the
+# committed counter measurement stale).
+KERNEL_SOURCES = {
+    "chunk_scan": ["dn_scan_mfma.hip", "dn_ktile.h", "dn_tfrag.h", "dn_mfma.h", "dn_common.h"],
+    "chunk_prep": ["dn_chunk_mfma.hip", "dn_ktile.h", "dn_tfrag.h", "dn_mfma.h", "dn_common.h"],
+    "decode": ["dn_decode.hip", "dn_common.h"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_hash(kernel):
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter
+    reads for a copy kernel of known size), or None when there is none or
+    the kernel's sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    return rec["bytes_per_launch"]
+
 
 def chunk_bytes(w, in_bytes=2, out_bytes=4, s0=False):
     """Algorithmic bytes of one chunked forward: q, k, v, beta read once, o and
@@ -48,6 +83,16 @@ def scan_kernel_bytes(w, in_bytes=2, out_bytes=4):
     tok_heads = w.B * w.H * w.L
     return (tok_heads * (2 * w.d_k + w.d_v) * in_bytes + tok_heads * w.d_v * out_bytes
             + w.B * w.H * w.d_k * w.d_v * 4)
+
+
+def prep_bytes(w, in_bytes=2):
+    """Algorithmic bytes of the WY-prep kernel: k and beta read once, the
+    chunk's T fragments written once (C/32 (C/32 + 1) blocks of 2 KiB per
+    chunk: the lower triangle at 16 x 32 granularity, hi and lo planes)."""
+    tok_heads = w.B * w.H * w.L
+    nc = -(-w.L // w.C)
+    blocks = (w.C // 32) * (w.C // 32 + 1)
+    return tok_heads * (w.d_k * in_bytes + 4) + w.B * w.H * nc * blocks * 2048
 
 
 def model_flops(w):
@@ -67,7 +112,7 @@ def cpu_baseline(w, x, seconds_hint):
     from deltanet_delta_rule_chunk_amd.inputs import to_f64
     from oracle import delta_rule_forward
 
-    n_tok = 4096
+    n_tok = 16384
     q = to_f64(x["q"][:1, :, :n_tok])
     k = to_f64(x["k"][:1, :, :n_tok])
     v = to_f64(x["v"][:1, :, :n_tok])
@@ -155,8 +200,7 @@ def main(argv=None) -> int:
     tflops = flops / (ms_step * 1e-3) / 1e12
     kern = {name: tot / n for name, (tot, n) in prof.items()}
     dom = max((k for k in kern if k.startswith("chunk")), key=lambda k: kern[k])
-    dom_bytes = scan_kernel_bytes(w) if dom == "chunk_scan" else (
-        w.B * w.H * w.L * (2 * w.d_k * 2 + 4))
+    dom_bytes = scan_kernel_bytes(w) if dom == "chunk_scan" else prep_bytes(w)
     achieved = dom_bytes / (kern[dom] * 1e-3) / 1e9
     path_gbs = chunk_bytes(w) / (ms_step * 1e-3) / 1e9
 
@@ -181,8 +225,14 @@ def main(argv=None) -> int:
         "path_alg_gbs": path_gbs,
         "pct_hbm_peak_path": 100.0 * path_gbs / PEAK_HBM_GBS,
         "kernels_ms": kern,
+        "prep_roofline": {"bound": "hbm", "kernel": "chunk_prep",
+                          "achieved": prep_bytes(w) / (kern["chunk_prep"] * 1e-3) / 1e9,
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": prep_bytes(w) / (kern["chunk_prep"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                          "traffic": measured_traffic("chunk_prep")},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": measured_traffic(dom)},
         "wall_s_timed": t_wall,
     }
 
@@ -216,7 +266,8 @@ def main(argv=None) -> int:
             "pct_hbm_peak": 100.0 * db / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "roofline": {"bound": "hbm", "kernel": "decode", "achieved": db / (k_ms * 1e-3) / 1e9,
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": db / (k_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None},
+                         "frac": db / (k_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "traffic": measured_traffic("decode")},
             "inputs": "8 seeded step inputs cycled; state carried across all steps",
         }
 

@@ -203,29 +203,34 @@ __global__ __launch_bounds__(512) void scan_kernel(
     __builtin_amdgcn_s_setprio(2);
     const int rt0 = w, rt1 = NRT - 1 - w;  // row tiles (rt1 only if RPW == 2)
     f32x4 sa[DPW], sb[DPW];
-    uint4 t0h[TB0], t0l[TB0], t1h[TB1], t1l[TB1];
+    // T fragments of one chunk for this wave's row tiles, loaded at the very
+    // start of the chunk's step (ahead of every other wave's loads of that
+    // step) and used in its Delta phase.
+    struct TRegs {
+      uint4 h0[TB0], l0[TB0], h1[TB1], l1[TB1];
+    };
+    TRegs tA;
     // Slots past a tile's last block re-read block 0 (unused).
-    auto t_load = [&](int cc) {
+    auto t_load = [&](int cc, TRegs& t) {
       const uint4* tb = Tfrag + ((size_t)bh * nc + cc) * Frag<C>::chunk_u4 + lane;
       const uint4* p0 = tb + (size_t)Frag<C>::base(rt0) * 128;
 #pragma unroll
       for (int cb = 0; cb < TB0; ++cb) {
         const int blk = cb <= rt0 / 2 ? cb : 0;
-        t0h[cb] = p0[(2 * blk) * 64];
-        t0l[cb] = p0[(2 * blk + 1) * 64];
+        t.h0[cb] = p0[(2 * blk) * 64];
+        t.l0[cb] = p0[(2 * blk + 1) * 64];
       }
       if constexpr (RPW == 2) {
         const uint4* p1 = tb + (size_t)Frag<C>::base(rt1) * 128;
 #pragma unroll
         for (int cb = 0; cb < TB1; ++cb) {
           const int blk = cb <= rt1 / 2 ? cb : 0;
-          t1h[cb] = p1[(2 * blk) * 64];
-          t1l[cb] = p1[(2 * blk + 1) * 64];
+          t.h1[cb] = p1[(2 * blk) * 64];
+          t.l1[cb] = p1[(2 * blk + 1) * 64];
         }
       }
     };
 
-    t_load(0);
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int dt = DPW * w + i;
@@ -243,12 +248,13 @@ __global__ __launch_bounds__(512) void scan_kernel(
     __syncthreads();
 
     const int m = i16 >> 2, ap = i16 & 3;
-    for (int c = 0; c < nc; ++c) {
+    auto step = [&](int c, TRegs& tc) {
       const int cn = min(c + 1, nc - 1);
       const uint16_t* Kc = Kbuf + (c & 1) * KELEMS;
       uint16_t* Dc = Db + (c & 1) * 2 * RPLANE;
 
       // ---- phase A: R = V - K S ----------------------------------------------
+      t_load(c, tc);
       stage_load(cn);
       {
         const uint16_t* Sc = Snap + (c & 1) * 2 * SPLANE;
@@ -308,9 +314,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
         for (int cb = 0; cb < TB0; ++cb) {
           if (cb <= rt0 / 2) {
-            d0 = mfma16(as_bf16x8(t0h[cb]), Rh[cb], d0);
-            d1 = mfma16(as_bf16x8(t0h[cb]), Rl[cb], d1);
-            d2 = mfma16(as_bf16x8(t0l[cb]), Rh[cb], d2);
+            d0 = mfma16(as_bf16x8(tc.h0[cb]), Rh[cb], d0);
+            d1 = mfma16(as_bf16x8(tc.h0[cb]), Rl[cb], d1);
+            d2 = mfma16(as_bf16x8(tc.l0[cb]), Rh[cb], d2);
           }
         }
         if constexpr (RPW == 2) {
@@ -318,9 +324,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
           for (int cb = 0; cb < TB1; ++cb) {
             if (cb <= rt1 / 2) {
-              e0 = mfma16(as_bf16x8(t1h[cb]), Rh[cb], e0);
-              e1 = mfma16(as_bf16x8(t1h[cb]), Rl[cb], e1);
-              e2 = mfma16(as_bf16x8(t1l[cb]), Rh[cb], e2);
+              e0 = mfma16(as_bf16x8(tc.h1[cb]), Rh[cb], e0);
+              e1 = mfma16(as_bf16x8(tc.h1[cb]), Rl[cb], e1);
+              e2 = mfma16(as_bf16x8(tc.l1[cb]), Rh[cb], e2);
             }
           }
           put_split(Dc, RPLANE, fo_d(rt1, g, i16), e0 + e1 + e2);
@@ -330,7 +336,6 @@ __global__ __launch_bounds__(512) void scan_kernel(
       __syncthreads();
 
       // ---- phase C: S += K^T Delta, snapshot after every sub-block -------------
-      t_load(cn);
       {
         bf16x8 Dh[NSB], Dl[NSB], Kt[NSB][DPW];
 #pragma unroll
@@ -369,7 +374,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
       for (int i = 0; i < DPW; ++i) { sa[i] = sa[i] + sb[i]; sb[i] = zero4(); }
       stage_store(cn, Kbuf + ((c + 1) & 1) * KELEMS);
       __syncthreads();
-    }
+    };
+    for (int c = 0; c < nc; ++c) step(c, tA);
 
     if (S_final) {
 #pragma unroll
