@@ -12,12 +12,13 @@
 // so that (I + A) T = diag(beta), T is lower triangular and diag(T) = beta.
 //
 // prep_kernel: one 4-wave workgroup per (chunk, head), all chunks in
-// parallel, ~68 KB of LDS so two workgroups share a CU.  With 16 x 16 tiles
-// (NT = C / 16 tile rows):
-//   1. k rows -> LDS (swizzled, dn_ktile.h).
-//   2. Gram tiles on bf16 MFMA (bf16 products are exact, sums fp32); the
-//      off-diagonal tiles of A are kept as split-bf16 MFMA operands, the
-//      diagonal tiles' strictly lower parts N_i as fp32.
+// parallel, ~52 KB of LDS so three workgroups share a CU.  With 16 x 16
+// tiles (NT = C / 16 tile rows):
+//   1-2. k rows -> LDS (swizzled, dn_ktile.h) 64 columns of d_k at a time,
+//      and the Gram tiles on bf16 MFMA accumulated over the slices (bf16
+//      products are exact, sums fp32), the next slice's loads in flight
+//      meanwhile.  The off-diagonal tiles of A are kept as split-bf16 MFMA
+//      operands, the diagonal tiles' strictly lower parts N_i as fp32.
 //   3. The unit-lower 16 x 16 inverses Linv_i = (I + N_i)^{-1} by fp32
 //      forward substitution, one lane per column.
 //   4. Column tiles of T by block forward substitution: tile column j of
@@ -38,6 +39,8 @@
 #include "dn_mfma.h"
 #include "dn_tfrag.h"
 
+#include <type_traits>
+
 namespace dn {
 
 hipError_t launch_scan_mfma(const ChunkArgs& a, const uint4* Tfrag);
@@ -47,12 +50,14 @@ namespace prep {
 template <int C, int DK>
 struct Cfg {
   static constexpr int NT = C / 16;                    // 16-row tiles
-  static constexpr int NKB = DK / 32;                  // 32-wide blocks of d_k
+  static constexpr int KW = 64;                        // d_k columns staged at a time
+  static constexpr int NH = DK / KW;                   // staging passes over d_k
   static constexpr int NOFF = NT * (NT - 1) / 2;       // off-diagonal lower tiles
-  static constexpr int SPT = C * DK / (8 * 256);       // staged 16-byte k pieces per thread
-  // LDS, in bytes.  Region 0 holds the k tile, later the two fp32 layouts of
-  // the diagonal inverses.
-  static constexpr int R0 = C * DK * 2 > NT * 2048 ? C * DK * 2 : NT * 2048;
+  static constexpr int SPT = C * KW / (8 * 256);       // staged 16-byte k pieces per thread
+  // LDS, in bytes.  Region 0 holds a C x 64 slice of the k tile, later the
+  // two fp32 layouts of the diagonal inverses; ~52 KB in all, so three
+  // workgroups share a CU.
+  static constexpr int R0 = C * KW * 2 > NT * 2048 ? C * KW * 2 : NT * 2048;
   static constexpr int OFF_A = R0;                     // NOFF tiles x 2 planes x 512 B
   static constexpr int OFF_N = OFF_A + NOFF * 1024;    // NT tiles x 1 KB fp32
   static constexpr int OFF_BETA = OFF_N + NT * 1024;   // C floats
@@ -67,12 +72,146 @@ __device__ __forceinline__ bf16x8 lds16(const uint16_t* p) {
   return as_bf16x8(*reinterpret_cast<const uint4*>(p));
 }
 
+// Gram tile columns of wave W: tile (i, kk), kk <= i, computed as
+// K_kk K_i^T so that lane (i16, g) register r holds
+// G[16 i + i16][16 kk + 4 g + r]: A_{i,kk} in row layout.  Columns
+// kk = W and NT - 1 - W (NT + 1 tiles in all).  Each call adds the products
+// over one 64-column slice of k (staged in Ks); the final call writes the
+// off-diagonal tiles of A = diag(beta) G to Atl as split operands and the
+// strictly lower part of the diagonal tile to Nd (fp32, column-major:
+// Nd[i][col][row] = N_i[row][col]).
+template <int C, int W, bool FINAL>
+__device__ __forceinline__ void gram_wave(const uint16_t* Ks, f32x4 (&acc)[2][C / 16], uint2* Atl,
+                                          float* Nd, const float* bs, int lane, int g, int i16) {
+  constexpr int NT = C / 16, KW = 64, NKB = KW / 32;
+  if constexpr (W < NT / 2) {
+#pragma unroll
+    for (int gc = 0; gc < 2; ++gc) {
+      const int kk = gc == 0 ? W : NT - 1 - W;
+      bf16x8 Ak[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) Ak[kb] = lds16(Ks + koff<KW>(16 * kk + i16, 4 * kb + g));
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        if (i < kk) continue;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          acc[gc][i] = mfma16(Ak[kb], lds16(Ks + koff<KW>(16 * i + i16, 4 * kb + g)), acc[gc][i]);
+      }
+      if constexpr (FINAL) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          if (i < kk) continue;
+          const float b = bs[16 * i + i16];
+          if (i > kk) {
+            uint2 hi, lo;
+            split4(acc[gc][i] * b, hi, lo);
+            Atl[tidx(i, kk) * 128 + lane] = hi;
+            Atl[tidx(i, kk) * 128 + 64 + lane] = lo;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int col = 4 * g + r;
+              Nd[i * 256 + col * 16 + i16] = col < i16 ? acc[gc][i][r] * b : 0.f;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// Tile columns j = W and NT - 1 - W of T (waves W >= NT / 2 have none):
+//     T_jj = Linv_j diag(beta_j),
+//     T_ij = Linv_i R_ij,  R_ij = -sum_{j <= k < i} A_ik T_kj   (i > j),
+// the two columns' row chains advancing together.  T_kj is kept split in
+// column layout (lane (i16, g) holds T_kj[4 g + r][i16]), the B operand of
+// the next rows; each T_ij is also formed transposed, R_ij^T Linv_i^T, which
+// is its row layout, and stored as half of fragment block (i, j / 2).
+template <int C, int W>
+__device__ __forceinline__ void cols_wave(const uint2* Atl, const float* Lrow, const float* Lcol,
+                                          const float* bs, uint4* out, int lane, int g, int i16) {
+  constexpr int NT = C / 16;
+  if constexpr (W < NT / 2) {
+    constexpr int J[2] = {W, NT - 1 - W};
+    auto tstore = [&](int i, int j, uint2 hi, uint2 lo) {
+      uint2* blk = reinterpret_cast<uint2*>(out + (size_t)(Frag<C>::base(i) + j / 2) * 128);
+      blk[2 * lane + (j & 1)] = hi;
+      blk[128 + 2 * lane + (j & 1)] = lo;
+    };
+    const uint2 z = make_uint2(0u, 0u);
+    uint2 th[2][NT], tl[2][NT];
+#pragma unroll
+    for (int cw = 0; cw < 2; ++cw) {
+      const int j = J[cw];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) { th[cw][t] = z; tl[cw][t] = z; }
+      const f32x4 lc = *reinterpret_cast<const f32x4*>(Lcol + j * 256 + lane * 4);
+      split4(lc * bs[16 * j + i16], th[cw][j], tl[cw][j]);
+      const f32x4 lr = *reinterpret_cast<const f32x4*>(Lrow + j * 256 + lane * 4);
+      const float4 brow = *reinterpret_cast<const float4*>(bs + 16 * j + 4 * g);
+      f32x4 trow;
+      trow[0] = lr[0] * brow.x; trow[1] = lr[1] * brow.y;
+      trow[2] = lr[2] * brow.z; trow[3] = lr[3] * brow.w;
+      uint2 hi, lo;
+      split4(trow, hi, lo);
+      tstore(j, j, hi, lo);
+      if (j & 1) tstore(j - 1, j, z, z);
+    }
+#pragma unroll
+    for (int i = 1; i < NT; ++i) {
+      const f32x4 lr = *reinterpret_cast<const f32x4*>(Lrow + i * 256 + lane * 4);
+      uint2 lh, ll;
+      split4(lr, lh, ll);
+      const bf16x8 Lh = as_bf16x8(lh, z), Ll = as_bf16x8(ll, z);
+#pragma unroll
+      for (int cw = 0; cw < 2; ++cw) {
+        const int j = J[cw];
+        if (i <= j) continue;
+        // R_ij = -sum_k A_ik T_kj over tile pairs (2p, 2p + 1); T_kj = 0 for
+        // k < j and A_ik is only taken for k < i.
+        f32x4 a0 = zero4(), a1 = zero4(), a2 = zero4();
+#pragma unroll
+        for (int p = 0; p < NT / 2; ++p) {
+          if (2 * p > i - 1 || 2 * p + 1 < j) continue;
+          const uint2 ah0 = Atl[tidx(i, 2 * p) * 128 + lane], al0 = Atl[tidx(i, 2 * p) * 128 + 64 + lane];
+          const bool two = 2 * p + 1 < i;
+          const uint2 ah1 = two ? Atl[tidx(i, 2 * p + 1) * 128 + lane] : z;
+          const uint2 al1 = two ? Atl[tidx(i, 2 * p + 1) * 128 + 64 + lane] : z;
+          const bf16x8 Ah = as_bf16x8(ah0, ah1), Al = as_bf16x8(al0, al1);
+          const bf16x8 Bh = as_bf16x8(th[cw][2 * p], th[cw][2 * p + 1]);
+          const bf16x8 Bl = as_bf16x8(tl[cw][2 * p], tl[cw][2 * p + 1]);
+          a0 = mfma16(Ah, Bh, a0);
+          a1 = mfma16(Ah, Bl, a1);
+          a2 = mfma16(Al, Bh, a2);
+        }
+        const f32x4 R = -(a0 + a1 + a2);
+        uint2 rh, rl;
+        split4(R, rh, rl);
+        const bf16x8 Rh = as_bf16x8(rh, z), Rl = as_bf16x8(rl, z);
+        // T_ij = Linv_i R_ij (column layout, kept for the next rows).
+        f32x4 tc = mfma16(Lh, Rh, zero4());
+        tc = mfma16(Lh, Rl, tc);
+        tc = mfma16(Ll, Rh, tc);
+        split4(tc, th[cw][i], tl[cw][i]);
+        // T_ij^T = R_ij^T Linv_i^T (row layout, stored).
+        f32x4 tr = mfma16(Rh, Lh, zero4());
+        tr = mfma16(Rh, Ll, tr);
+        tr = mfma16(Rl, Lh, tr);
+        uint2 hi, lo;
+        split4(tr, hi, lo);
+        tstore(i, j, hi, lo);
+      }
+    }
+  }
+}
+
 template <int C, int DK>
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ k,
                                                    const float* __restrict__ beta, int L,
                                                    int nc, uint4* __restrict__ Tfrag) {
   using CF = Cfg<C, DK>;
-  constexpr int NT = CF::NT, NKB = CF::NKB;
+  constexpr int NT = CF::NT;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   uint16_t* const Ks = reinterpret_cast<uint16_t*>(smem_raw);
   float* const Lrow = reinterpret_cast<float*>(smem_raw);             // after step 2
@@ -86,54 +225,56 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   const int t0 = c * C, valid = min(C, L - t0);
   const size_t tok0 = (size_t)bh * L + t0;
 
-  // ---- 1. k tile and beta -> LDS --------------------------------------------
-  {
-    uint4 kv[CF::SPT];
+  // ---- 1-2. k tile (64 columns at a time) and Gram tiles -------------------
+  // The next slice's loads are in flight while the current one is used.
+  constexpr int KW = CF::KW, NH = CF::NH, SPT = CF::SPT;
+  uint4 kv[SPT];
+  auto kload = [&](int h) {
 #pragma unroll
-    for (int i = 0; i < CF::SPT; ++i) {
-      const int e = i * 256 + tid, row = e / (DK / 8), ch = e % (DK / 8);
-      kv[i] = *reinterpret_cast<const uint4*>(k + (tok0 + min(row, valid - 1)) * DK + ch * 8);
+    for (int i = 0; i < SPT; ++i) {
+      const int e = i * 256 + tid, row = e / (KW / 8), ch = e % (KW / 8);
+      kv[i] = *reinterpret_cast<const uint4*>(k + (tok0 + min(row, valid - 1)) * DK + h * KW + ch * 8);
     }
-    if (tid < C) bs[tid] = tid < valid ? beta[tok0 + tid] : 0.f;
+  };
+  auto kstore = [&]() {
 #pragma unroll
-    for (int i = 0; i < CF::SPT; ++i) {
-      const int e = i * 256 + tid, row = e / (DK / 8), ch = e % (DK / 8);
+    for (int i = 0; i < SPT; ++i) {
+      const int e = i * 256 + tid, row = e / (KW / 8), ch = e % (KW / 8);
       const uint32_t m = row < valid ? 0xffffffffu : 0u;
-      *reinterpret_cast<uint4*>(Ks + koff<DK>(row, ch)) =
+      *reinterpret_cast<uint4*>(Ks + koff<KW>(row, ch)) =
           make_uint4(kv[i].x & m, kv[i].y & m, kv[i].z & m, kv[i].w & m);
     }
-  }
-  __syncthreads();
-
-  // ---- 2. Gram tiles -----------------------------------------------------------
-  // Tile (i, kk), kk <= i, computed as K_kk K_i^T so that lane (i16, g)
-  // register r holds G[16 i + i16][16 kk + 4 g + r]: A_{i,kk} in row layout.
-  constexpr int NTT = NT * (NT + 1) / 2;
-  for (int p = w; p < NTT; p += 4) {
-    int i = 0;
-    while ((i + 1) * (i + 2) / 2 <= p) ++i;
-    const int kk = p - i * (i + 1) / 2;
-    f32x4 acc = zero4();
+  };
+  kload(0);
+  if (tid < C) bs[tid] = tid < valid ? beta[tok0 + tid] : 0.f;
+  kstore();
+  f32x4 acc[2][NT];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const bf16x8 Ak = lds16(Ks + koff<DK>(16 * kk + i16, 4 * kb + g));
-      const bf16x8 Bi = lds16(Ks + koff<DK>(16 * i + i16, 4 * kb + g));
-      acc = mfma16(Ak, Bi, acc);
+  for (int gc = 0; gc < 2; ++gc)
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[gc][i] = zero4();
+  // Wave w owns the Gram tile columns kk = w and kk = NT - 1 - w; the wave
+  // index is made a compile-time constant so every loop below is static and
+  // the compiler can interleave the independent tiles.
+  auto gram = [&](auto final_tag) {
+    constexpr bool F = decltype(final_tag)::value;
+    switch (w) {
+      case 0: gram_wave<C, 0, F>(Ks, acc, Atl, Nd, bs, lane, g, i16); break;
+      case 1: gram_wave<C, 1, F>(Ks, acc, Atl, Nd, bs, lane, g, i16); break;
+      case 2: gram_wave<C, 2, F>(Ks, acc, Atl, Nd, bs, lane, g, i16); break;
+      default: gram_wave<C, 3, F>(Ks, acc, Atl, Nd, bs, lane, g, i16); break;
     }
-    const float b = bs[16 * i + i16];
-    if (i > kk) {
-      uint2 hi, lo;
-      split4(acc * b, hi, lo);
-      Atl[tidx(i, kk) * 128 + lane] = hi;
-      Atl[tidx(i, kk) * 128 + 64 + lane] = lo;
-    } else {
-      // Strictly lower part of the diagonal tile, stored column-major:
-      // Nd[i][col][row] = N_i[row][col].
+  };
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int col = 4 * g + r;
-        Nd[i * 256 + col * 16 + i16] = col < i16 ? acc[r] * b : 0.f;
-      }
+  for (int h = 0; h < NH; ++h) {
+    if (h + 1 < NH) kload(h + 1);
+    __syncthreads();
+    if (h + 1 < NH) {
+      gram(std::integral_constant<bool, false>{});
+      __syncthreads();
+      kstore();
+    } else {
+      gram(std::integral_constant<bool, true>{});
     }
   }
   __syncthreads();
@@ -170,78 +311,11 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
 
   // ---- 4. tile columns of T ------------------------------------------------------
   uint4* const out = Tfrag + ((size_t)bh * nc + c) * Frag<C>::chunk_u4;
-  // 8-byte half (j & 1) of block (i, j / 2), both planes, this lane.
-  auto tstore = [&](int i, int j, uint2 hi, uint2 lo) {
-    uint2* blk = reinterpret_cast<uint2*>(out + (size_t)(Frag<C>::base(i) + j / 2) * 128);
-    blk[2 * lane + (j & 1)] = hi;
-    blk[128 + 2 * lane + (j & 1)] = lo;
-  };
-  constexpr int NCOLW = NT > 4 ? 2 : 1;  // tile columns per wave
-#pragma unroll
-  for (int cw = 0; cw < NCOLW; ++cw) {
-    const int j = cw == 0 ? w : NT - 1 - w;
-    // Column layout of T_kj (lane (i16, g) holds T_kj[4 g + r][i16]), split.
-    uint2 th[NT], tl[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) { th[t] = make_uint2(0u, 0u); tl[t] = th[t]; }
-    {
-      const f32x4 lc = *reinterpret_cast<const f32x4*>(Lcol + j * 256 + lane * 4);
-      const float bcol = bs[16 * j + i16];
-      uint2 hi, lo;
-      split4(lc * bcol, hi, lo);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) if (t == j) { th[t] = hi; tl[t] = lo; }
-      const f32x4 lr = *reinterpret_cast<const f32x4*>(Lrow + j * 256 + lane * 4);
-      const float4 brow = *reinterpret_cast<const float4*>(bs + 16 * j + 4 * g);
-      f32x4 trow;
-      trow[0] = lr[0] * brow.x; trow[1] = lr[1] * brow.y;
-      trow[2] = lr[2] * brow.z; trow[3] = lr[3] * brow.w;
-      split4(trow, hi, lo);
-      tstore(j, j, hi, lo);
-      if (j & 1) tstore(j - 1, j, make_uint2(0u, 0u), make_uint2(0u, 0u));
-    }
-#pragma unroll
-    for (int i = 1; i < NT; ++i) {
-      if (i <= j) continue;
-      // R_ij = -sum_k A_ik T_kj over tile pairs (2p, 2p + 1); T_kj = 0 for
-      // k < j and A_ik is only taken for k < i.
-      f32x4 a0 = zero4(), a1 = zero4(), a2 = zero4();
-#pragma unroll
-      for (int p = 0; p < NT / 2; ++p) {
-        if (2 * p > i - 1 || 2 * p + 1 < j) continue;
-        const uint2 z = make_uint2(0u, 0u);
-        const uint2 ah0 = Atl[tidx(i, 2 * p) * 128 + lane], al0 = Atl[tidx(i, 2 * p) * 128 + 64 + lane];
-        const bool two = 2 * p + 1 < i;
-        const uint2 ah1 = two ? Atl[tidx(i, 2 * p + 1) * 128 + lane] : z;
-        const uint2 al1 = two ? Atl[tidx(i, 2 * p + 1) * 128 + 64 + lane] : z;
-        const bf16x8 Ah = as_bf16x8(ah0, ah1), Al = as_bf16x8(al0, al1);
-        const bf16x8 Bh = as_bf16x8(th[2 * p], th[2 * p + 1]), Bl = as_bf16x8(tl[2 * p], tl[2 * p + 1]);
-        a0 = mfma16(Ah, Bh, a0);
-        a1 = mfma16(Ah, Bl, a1);
-        a2 = mfma16(Al, Bh, a2);
-      }
-      const f32x4 R = -(a0 + a1 + a2);
-      uint2 rh, rl;
-      split4(R, rh, rl);
-      const f32x4 lr = *reinterpret_cast<const f32x4*>(Lrow + i * 256 + lane * 4);
-      uint2 lh, ll;
-      split4(lr, lh, ll);
-      const uint2 z = make_uint2(0u, 0u);
-      const bf16x8 Lh = as_bf16x8(lh, z), Ll = as_bf16x8(ll, z);
-      const bf16x8 Rh = as_bf16x8(rh, z), Rl = as_bf16x8(rl, z);
-      // T_ij = Linv_i R_ij (column layout, kept for the next rows).
-      f32x4 tc = mfma16(Lh, Rh, zero4());
-      tc = mfma16(Lh, Rl, tc);
-      tc = mfma16(Ll, Rh, tc);
-      split4(tc, th[i], tl[i]);
-      // T_ij^T = R_ij^T Linv_i^T (row layout, stored).
-      f32x4 tr = mfma16(Rh, Lh, zero4());
-      tr = mfma16(Rh, Ll, tr);
-      tr = mfma16(Rl, Lh, tr);
-      uint2 hi, lo;
-      split4(tr, hi, lo);
-      tstore(i, j, hi, lo);
-    }
+  switch (w) {
+    case 0: cols_wave<C, 0>(Atl, Lrow, Lcol, bs, out, lane, g, i16); break;
+    case 1: cols_wave<C, 1>(Atl, Lrow, Lcol, bs, out, lane, g, i16); break;
+    case 2: cols_wave<C, 2>(Atl, Lrow, Lcol, bs, out, lane, g, i16); break;
+    default: cols_wave<C, 3>(Atl, Lrow, Lcol, bs, out, lane, g, i16); break;
   }
 }
 
