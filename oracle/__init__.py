@@ -1,5 +1,7 @@
 """CPU oracle (test infrastructure only; see delta_rule.py)."""
 
-from .delta_rule import delta_rule_decode_step, delta_rule_forward
+from .delta_rule import (delta_rule_decode_step, delta_rule_forward, gated_delta_rule_decode_step,
+                         gated_delta_rule_forward)
 
-__all__ = ["delta_rule_forward", "delta_rule_decode_step"]
+__all__ = ["delta_rule_forward", "delta_rule_decode_step", "gated_delta_rule_forward",
+           "gated_delta_rule_decode_step"]

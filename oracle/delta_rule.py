@@ -30,6 +30,17 @@ state is d_k x d_v with the row-vector convention (v_old = k S); the output
 is read after the write; a length that is not a multiple of any chunk size is
 simply run token by token.
 
+* ``gated_delta_rule_forward`` / ``gated_delta_rule_decode_step`` add the
+  scalar gate of Gated DeltaNet from the article "How a Baseten Engineer
+  Traced 7 Years of Attention Mechanism Evolution", section on Gated DeltaNet:
+  the old state is first decayed by alpha_t in [0, 1] and the precise delta
+  write then acts on the decayed state:
+      S <- alpha_t S;  v_old = k_t S;  u_t = beta_t (v_t - v_old);
+      S <- S + k_t^T u_t;  o_t = q_t S.
+  alpha = 1 is the plain delta rule and alpha = 0 wipes the memory before the
+  write (both as the article states).  Reading taken: the delta reads the
+  decayed state ("decay first, then precise write").
+
 Pins (tests/test_oracle_pins.py) tie this oracle to facts other than
 itself: beta = 0 leaves the state alone; v_t = k_t S leaves it alone; with
 beta = 1 and orthonormal keys the state returns the latest value written at a
@@ -92,6 +103,52 @@ def delta_rule_decode_step(q, k, v, beta, S) -> Tuple[np.ndarray, np.ndarray]:
     k_row = k[:, :, None, :]
     v_old = k_row @ S
     u = beta[:, :, None, None] * (v[:, :, None, :] - v_old)
+    S_new = S + np.swapaxes(k_row, -1, -2) @ u
+    o = (q[:, :, None, :] @ S_new)[:, :, 0, :]
+    return o, S_new
+
+
+def gated_delta_rule_forward(q, k, v, alpha, beta, S0: Optional[np.ndarray] = None
+                             ) -> Tuple[np.ndarray, np.ndarray]:
+    """Token-by-token gated delta-rule forward in fp64 (decay, then the delta
+    write on the decayed state, then the read).
+
+    alpha: ``[B, H, L]`` per-token decay in [0, 1]; the other arguments and
+    the result are as in ``delta_rule_forward``.
+    """
+    q, k, v, beta, alpha = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(beta), _as_f64(alpha)
+    B, H, L, d_k = k.shape
+    d_v = v.shape[-1]
+    if (q.shape != (B, H, L, d_k) or v.shape[:3] != (B, H, L) or beta.shape != (B, H, L)
+            or alpha.shape != (B, H, L)):
+        raise ValueError("shape mismatch among q, k, v, alpha, beta")
+    if S0 is None:
+        S = np.zeros((B, H, d_k, d_v))
+    else:
+        S = _as_f64(S0).copy()
+        if S.shape != (B, H, d_k, d_v):
+            raise ValueError("S0 must be [B, H, d_k, d_v]")
+    o = np.empty((B, H, L, d_v))
+    for t in range(L):
+        S = alpha[:, :, t, None, None] * S                # decay first
+        k_t = k[:, :, t, None, :]
+        v_old = k_t @ S                                   # read the decayed state
+        u_t = beta[:, :, t, None, None] * (v[:, :, t, None, :] - v_old)
+        S = S + np.swapaxes(k_t, -1, -2) @ u_t            # precise write
+        o[:, :, t, :] = (q[:, :, t, None, :] @ S)[:, :, 0, :]
+    return o, S
+
+
+def gated_delta_rule_decode_step(q, k, v, alpha, beta, S) -> Tuple[np.ndarray, np.ndarray]:
+    """One gated decode step in fp64: the gated forward at a single token.
+
+    alpha, beta: ``[B, H]``; the rest as in ``delta_rule_decode_step``.
+    """
+    q, k, v, beta, alpha, S = (_as_f64(q), _as_f64(k), _as_f64(v), _as_f64(beta),
+                               _as_f64(alpha), _as_f64(S))
+    S = alpha[:, :, None, None] * S
+    k_row = k[:, :, None, :]
+    u = beta[:, :, None, None] * (v[:, :, None, :] - k_row @ S)
     S_new = S + np.swapaxes(k_row, -1, -2) @ u
     o = (q[:, :, None, :] @ S_new)[:, :, 0, :]
     return o, S_new

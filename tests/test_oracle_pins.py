@@ -106,3 +106,67 @@ def test_wy_T_is_inverse_and_lower_triangular():
     assert np.abs((np.eye(C) + A) @ T - np.diag(beta)).max() < 1e-12
     assert np.abs(np.triu(T, 1)).max() == 0.0
     assert np.allclose(np.diag(T), beta)
+
+
+# ---- gated (Gated DeltaNet) oracle ------------------------------------------
+
+from oracle import gated_delta_rule_decode_step, gated_delta_rule_forward  # noqa: E402
+from pins_gated import ALL_GATED_PINS  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", ALL_GATED_PINS, ids=lambda p: p.__name__)
+def test_gated_oracle_pin(pin):
+    rng = np.random.default_rng(4321)
+    err = pin(gated_delta_rule_forward, rng)
+    assert err < PIN_TOL, f"{pin.__name__}: max deviation {err:.3e}"
+
+
+def test_gated_decode_step_is_forward_at_one_token():
+    rng = np.random.default_rng(17)
+    B, H, L, dk, dv = 2, 3, 7, 6, 4
+    q, k = rng.standard_normal((B, H, L, dk)), rng.standard_normal((B, H, L, dk))
+    v = rng.standard_normal((B, H, L, dv))
+    alpha, beta = rng.uniform(0, 1, (B, H, L)), rng.uniform(0, 1, (B, H, L))
+    S0 = rng.standard_normal((B, H, dk, dv)) * 0.1
+    o_ref, S_ref = gated_delta_rule_forward(q, k, v, alpha, beta, S0)
+    S = S0
+    for t in range(L):
+        o_t, S = gated_delta_rule_decode_step(q[:, :, t], k[:, :, t], v[:, :, t], alpha[:, :, t],
+                                              beta[:, :, t], S)
+        assert np.abs(o_t - o_ref[:, :, t]).max() < 1e-12
+    assert np.abs(S - S_ref).max() < 1e-12
+
+
+def test_gated_decode_step_identity():
+    """o = q S_new = alpha q S + (q . k) u with u = beta (v - alpha k S): the
+    single-read form the gated decode kernel uses."""
+    rng = np.random.default_rng(18)
+    B, H, dk, dv = 2, 2, 5, 3
+    q, k = rng.standard_normal((B, H, dk)), rng.standard_normal((B, H, dk))
+    v = rng.standard_normal((B, H, dv))
+    alpha, beta = rng.uniform(0, 1, (B, H)), rng.uniform(0, 1, (B, H))
+    S = rng.standard_normal((B, H, dk, dv))
+    o, S_new = gated_delta_rule_decode_step(q, k, v, alpha, beta, S)
+    r = np.einsum("bhk,bhkv->bhv", k, S)
+    p = np.einsum("bhk,bhkv->bhv", q, S)
+    u = beta[..., None] * (v - alpha[..., None] * r)
+    o2 = alpha[..., None] * p + np.einsum("bhk,bhk->bh", q, k)[..., None] * u
+    assert np.abs(o - o2).max() < 1e-12
+    S2 = alpha[..., None, None] * S + k[..., :, None] * u[..., None, :]
+    assert np.abs(S_new - S2).max() < 1e-12
+
+
+@pytest.mark.parametrize("C,SB", [(1, None), (7, None), (16, None), (64, None), (64, 32), (128, 32)])
+@pytest.mark.parametrize("L", [150, 64])
+def test_gated_chunked_form_equals_recurrence(C, SB, L):
+    from wy_model import gated_chunked_forward
+    rng = np.random.default_rng(C * 100 + L)
+    q, k, v, beta, S0 = _rand_head(rng, L, 16, 12)
+    alpha = rng.uniform(0.5, 1.0, L)
+    alpha[::13] = 1.0
+    alpha[5] = 0.0                       # one memory wipe
+    o_ref, S_ref = gated_delta_rule_forward(q[None, None], k[None, None], v[None, None],
+                                            alpha[None, None], beta[None, None], S0[None, None])
+    o, S = gated_chunked_forward(q, k, v, alpha, beta, S0, C, SB)
+    assert np.abs(o - o_ref[0, 0]).max() < 1e-10
+    assert np.abs(S - S_ref[0, 0]).max() < 1e-10

@@ -73,3 +73,65 @@ def chunked_forward_wu(q, k, v, beta, S0, C):
         o[sl] = Qc @ S + np.tril(Qc @ Kc.T) @ D
         S = S + Kc.T @ D
     return o, S
+
+
+# ---- gated (Gated DeltaNet) chunked form --------------------------------------
+#
+# Decay first, then the delta write on the decayed state.  Within a chunk, with
+# g_r = log(alpha_1) + ... + log(alpha_r) (local rows 1..C, g_0 = 0) and the
+# entering state S:
+#   S_r = e^{g_r} S + sum_{i<=r} e^{g_r - g_i} k_i^T delta_i
+#   delta_r = beta_r (v_r - e^{g_r} k_r S - sum_{i<r} e^{g_r - g_i} (k_r . k_i) delta_i)
+#   => (I + A) Delta = diag(beta) (V - diag(e^g) K S),  A_ri = beta_r e^{g_r - g_i} (k_r . k_i), i < r
+#      O  = diag(e^g) Q S + (tril(Q K^T) * e^{g_r - g_i}) Delta
+#      S' = e^{g_C} S + K^T diag(e^{g_C - g}) Delta
+# Every exponent is <= 0.  A zero alpha is floored at LOG_FLOOR (its factor
+# e^{-87.3} ~ 1e-38 stands for 0, as in the kernels); padded rows have
+# alpha = 1, k = 0, beta = 0 (exact no-ops).  With sub-blocks of SB rows the
+# state and outputs are regrouped as the matrix-core scan does:
+#   S_{b+1} = e^{G_{b+1} - G_b} S_b + sum_{i in b} e^{G_{b+1} - g_i} k_i^T delta_i,
+#   O_b     = diag(e^{g - G_b}) Q_b S_b + (tril(Q_b K_b^T) * e^{g_r - g_i}) Delta_b,
+# with G_b the g of the last row before sub-block b (G_0 = 0).
+
+LOG_FLOOR = float(np.log(np.float32(1.1754944e-38)))
+
+
+def gated_chunked_forward(q, k, v, alpha, beta, S0, C, SB=None):
+    L, dk = k.shape
+    dv = v.shape[1]
+    n = -(-L // C)
+    pad = n * C - L
+    if pad:
+        q = np.concatenate([q, np.zeros((pad, dk))])
+        k = np.concatenate([k, np.zeros((pad, dk))])
+        v = np.concatenate([v, np.zeros((pad, dv))])
+        beta = np.concatenate([beta, np.zeros(pad)])
+        alpha = np.concatenate([alpha, np.ones(pad)])
+    la = np.maximum(np.log(np.maximum(alpha, 0.0) + 0.0, where=alpha > 0,
+                           out=np.full(alpha.shape, -np.inf)), LOG_FLOOR)
+    S = np.zeros((dk, dv)) if S0 is None else S0.copy()
+    o = np.zeros((n * C, dv))
+    for c in range(n):
+        sl = slice(c * C, (c + 1) * C)
+        Kc, Qc, Vc, bc = k[sl], q[sl], v[sl], beta[sl]
+        g = np.cumsum(la[sl])
+        E = np.exp(np.minimum(g[:, None] - g[None, :], 0.0))   # e^{g_r - g_i}, used for i <= r
+        A = np.tril(bc[:, None] * E * (Kc @ Kc.T), -1)
+        T = np.linalg.solve(np.eye(C) + A, np.diag(bc))
+        D = T @ (Vc - np.exp(g)[:, None] * (Kc @ S))
+        if SB is None:
+            o[sl] = np.exp(g)[:, None] * (Qc @ S) + (np.tril(Qc @ Kc.T) * E) @ D
+            S = np.exp(g[-1]) * S + Kc.T @ (np.exp(g[-1] - g)[:, None] * D)
+        else:
+            Sb, Gb = S, 0.0
+            for b0 in range(0, C, SB):
+                bs = slice(b0, b0 + SB)
+                gb = g[bs]
+                Eb = E[bs, bs]
+                o[c * C + b0:c * C + b0 + SB] = (np.exp(gb - Gb)[:, None] * (Qc[bs] @ Sb)
+                                                 + (np.tril(Qc[bs] @ Kc[bs].T) * Eb) @ D[bs])
+                Gn = gb[-1]
+                Sb = np.exp(Gn - Gb) * Sb + Kc[bs].T @ (np.exp(Gn - gb)[:, None] * D[bs])
+                Gb = Gn
+            S = Sb
+    return o[:L], S
