@@ -26,6 +26,8 @@ STATUS_NAMES = {0: "DN_OK", 1: "DN_ERR_NULL_ARG", 2: "DN_ERR_BAD_SHAPE", 3: "DN_
                 7: "DN_ERR_HIP"}
 # Every symbol include/deltanet.h declares.
 EXPORTS = ("deltanet_chunk_fwd", "deltanet_chunk_fwd_workspace_bytes", "deltanet_decode_step",
+           "deltanet_gated_chunk_fwd", "deltanet_gated_chunk_fwd_workspace_bytes",
+           "deltanet_gated_decode_step",
            "deltanet_status_string", "deltanet_last_hip_error", "deltanet_version",
            "deltanet_profile_start", "deltanet_profile_stop")
 PROFILE_SLOTS = ("chunk_prep", "chunk_scan", "decode")
@@ -56,6 +58,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.deltanet_chunk_fwd_workspace_bytes.restype = sz
     lib.deltanet_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     lib.deltanet_decode_step.restype = i
+    lib.deltanet_gated_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                             vp, sz, vp]
+    lib.deltanet_gated_chunk_fwd.restype = i
+    lib.deltanet_gated_chunk_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.deltanet_gated_chunk_fwd_workspace_bytes.restype = sz
+    lib.deltanet_gated_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.deltanet_gated_decode_step.restype = i
     lib.deltanet_status_string.argtypes = [i]
     lib.deltanet_status_string.restype = ctypes.c_char_p
     lib.deltanet_last_hip_error.argtypes = []
@@ -111,19 +120,24 @@ def _stream(device: torch.device, stream) -> int:
 
 
 def workspace_bytes(B: int, H: int, L: int, d_k: int, d_v: int, C: int,
-                    in_dtype: torch.dtype = torch.bfloat16) -> int:
-    return int(load().deltanet_chunk_fwd_workspace_bytes(B, H, L, d_k, d_v, C, _code(in_dtype)))
+                    in_dtype: torch.dtype = torch.bfloat16, gated: bool = False) -> int:
+    lib = load()
+    fn = lib.deltanet_gated_chunk_fwd_workspace_bytes if gated else lib.deltanet_chunk_fwd_workspace_bytes
+    return int(fn(B, H, L, d_k, d_v, C, _code(in_dtype)))
 
 
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
               S0: Optional[torch.Tensor] = None, C: int = 64, *,
               out_dtype: torch.dtype = torch.float32, o: Optional[torch.Tensor] = None,
               S_final: Optional[torch.Tensor] = None, want_state: bool = True,
-              workspace: Optional[torch.Tensor] = None, stream=None
+              workspace: Optional[torch.Tensor] = None, stream=None,
+              alpha: Optional[torch.Tensor] = None
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked delta-rule forward.  q,k ``[B,H,L,d_k]``, v ``[B,H,L,d_v]`` (fp32 or
     bf16, same dtype), beta ``[B,H,L]`` fp32, S0 ``[B,H,d_k,d_v]`` fp32 or None.
-    Returns ``(o, S_final)``; S_final is None when ``want_state`` is False."""
+    With ``alpha`` (``[B,H,L]`` fp32) the gated form runs
+    (``deltanet_gated_chunk_fwd``).  Returns ``(o, S_final)``; S_final is None
+    when ``want_state`` is False."""
     lib = load()
     B, H, L, d_k = q.shape
     d_v = v.shape[-1]
@@ -132,6 +146,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     _check(k, "k", (B, H, L, d_k), q.dtype, dev)
     _check(v, "v", (B, H, L, d_v), q.dtype, dev)
     _check(beta, "beta", (B, H, L), torch.float32, dev)
+    if alpha is not None:
+        _check(alpha, "alpha", (B, H, L), torch.float32, dev)
     if S0 is not None:
         _check(S0, "S0", (B, H, d_k, d_v), torch.float32, dev)
     if o is None:
@@ -142,23 +158,42 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     if S_final is not None:
         _check(S_final, "S_final", (B, H, d_k, d_v), torch.float32, dev)
     in_code = _code(q.dtype)
-    need = int(lib.deltanet_chunk_fwd_workspace_bytes(B, H, L, d_k, d_v, C, in_code))
+    need = workspace_bytes(B, H, L, d_k, d_v, C, q.dtype, gated=alpha is not None)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.deltanet_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(o),
-                                _ptr(S_final), B, H, L, d_k, d_v, C, in_code,
-                                _code(out_dtype), _ptr(workspace), ws_bytes, _stream(dev, stream))
-    if st != DN_OK:
-        _raise(lib, st, "deltanet_chunk_fwd")
+    if alpha is None:
+        st = lib.deltanet_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(o),
+                                    _ptr(S_final), B, H, L, d_k, d_v, C, in_code,
+                                    _code(out_dtype), _ptr(workspace), ws_bytes,
+                                    _stream(dev, stream))
+        if st != DN_OK:
+            _raise(lib, st, "deltanet_chunk_fwd")
+    else:
+        st = lib.deltanet_gated_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                          _ptr(S0), _ptr(o), _ptr(S_final), B, H, L, d_k, d_v, C,
+                                          in_code, _code(out_dtype), _ptr(workspace), ws_bytes,
+                                          _stream(dev, stream))
+        if st != DN_OK:
+            _raise(lib, st, "deltanet_gated_chunk_fwd")
     return o, S_final
+
+
+def gated_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                    beta: torch.Tensor, S0: Optional[torch.Tensor] = None, C: int = 64, **kw
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Gated (Gated DeltaNet) chunked forward: ``chunk_fwd`` with a per-token
+    decay alpha ``[B,H,L]`` fp32 applied to the state before each write."""
+    return chunk_fwd(q, k, v, beta, S0, C, alpha=alpha, **kw)
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
                 S: torch.Tensor, *, out_dtype: torch.dtype = torch.float32,
-                o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                o: Optional[torch.Tensor] = None, stream=None,
+                alpha: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One decode step; updates S ``[B,H,d_k,d_v]`` in place and returns o
-    ``[B,H,d_v]`` = q S_new."""
+    ``[B,H,d_v]`` = q S_new.  With ``alpha`` (``[B,H]`` fp32) the gated step
+    runs (``deltanet_gated_decode_step``)."""
     lib = load()
     B, H, d_k = q.shape
     d_v = v.shape[-1]
@@ -171,12 +206,26 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.T
     if o is None:
         o = torch.empty((B, H, d_v), dtype=out_dtype, device=dev)
     _check(o, "o", (B, H, d_v), out_dtype, dev)
-    st = lib.deltanet_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(o),
-                                  B, H, d_k, d_v, _code(q.dtype), _code(out_dtype),
-                                  _stream(dev, stream))
-    if st != DN_OK:
-        _raise(lib, st, "deltanet_decode_step")
+    if alpha is None:
+        st = lib.deltanet_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(o),
+                                      B, H, d_k, d_v, _code(q.dtype), _code(out_dtype),
+                                      _stream(dev, stream))
+        if st != DN_OK:
+            _raise(lib, st, "deltanet_decode_step")
+    else:
+        _check(alpha, "alpha", (B, H), torch.float32, dev)
+        st = lib.deltanet_gated_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                            _ptr(S), _ptr(o), B, H, d_k, d_v, _code(q.dtype),
+                                            _code(out_dtype), _stream(dev, stream))
+        if st != DN_OK:
+            _raise(lib, st, "deltanet_gated_decode_step")
     return o
+
+
+def gated_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                      beta: torch.Tensor, S: torch.Tensor, **kw) -> torch.Tensor:
+    """Gated decode step: ``decode_step`` with the per-(b, h) decay alpha."""
+    return decode_step(q, k, v, beta, S, alpha=alpha, **kw)
 
 
 def profile_start() -> None:

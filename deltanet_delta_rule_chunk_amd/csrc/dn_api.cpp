@@ -18,7 +18,7 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 
 int hip_fail(hipError_t e) {
   g_last_hip_error = static_cast<int>(e);
@@ -88,6 +88,77 @@ hipEvent_t prof_event() {
   hipError_t r = hipEventCreate(&e);
   if (r != hipSuccess && g_prof.error == hipSuccess) g_prof.error = r;
   return r == hipSuccess ? e : nullptr;
+}
+
+// Shared body of the plain (alpha = null) and gated chunked forwards.
+int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alpha,
+                   const float* beta, const float* S0, void* o, float* S_final, int B, int H,
+                   int L, int d_k, int d_v, int C, int in_dtype, int out_dtype, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  ChunkSizes s;
+  int st = check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, out_dtype, &s);
+  if (st != DN_OK) return st;
+  if (L > 0 && (!q || !k || !v || !beta || !o)) return DN_ERR_NULL_ARG;
+  const bool gated = alpha != nullptr;
+  const void* ptrs[] = {q, k, v, alpha, beta, S0, o, S_final, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return DN_ERR_MISALIGNED;
+
+  const Span sq{q, s.qk}, sk{k, s.qk}, sv{v, s.v}, sa{alpha, s.beta}, sb{beta, s.beta};
+  const Span ss0{S0, s.state}, so{o, s.o}, ssf{S_final, s.state};
+  const size_t need = dn::chunk_workspace_bytes(B, H, L, d_k, d_v, C, in_dtype, gated);
+  const Span sw{workspace, workspace ? need : 0};
+  for (Span in : {sq, sk, sv, sa, sb, ss0})
+    if (overlap(so, in) || (in.p != S0 && overlap(ssf, in))) return DN_ERR_ALIASING;
+  if (overlap(so, ssf)) return DN_ERR_ALIASING;
+  if (S_final && S0 && S_final != S0 && overlap(ssf, ss0)) return DN_ERR_ALIASING;
+  for (Span x : {sq, sk, sv, sa, sb, ss0, so, ssf})
+    if (overlap(sw, x)) return DN_ERR_ALIASING;
+  if (workspace && workspace_bytes < need) return DN_ERR_WORKSPACE;
+
+  void* ws = workspace;
+  const bool own_ws = (ws == nullptr && need > 0);
+  if (own_ws) {
+    hipError_t e = hipMallocAsync(&ws, need, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  dn::ChunkArgs a{q, k, v, alpha, beta, S0, o, S_final, B, H, L, d_k, d_v, C, in_dtype,
+                  out_dtype, ws, stream};
+  hipError_t e = dn::launch_chunk_fwd(a);
+  if (own_ws) {
+    hipError_t f = hipFreeAsync(ws, stream);
+    if (e == hipSuccess) e = f;
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  return DN_OK;
+}
+
+// Shared body of the plain (alpha = null) and gated decode steps.
+int decode_impl(const void* q, const void* k, const void* v, const float* alpha,
+                const float* beta, float* S, void* o, int B, int H, int d_k, int d_v,
+                int in_dtype, int out_dtype, hipStream_t stream) {
+  if (B < 1 || H < 1 || d_k < 1 || d_v < 1) return DN_ERR_BAD_SHAPE;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return DN_ERR_UNSUPPORTED;
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return DN_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > 0x7fffffff) return DN_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !beta || !S || !o) return DN_ERR_NULL_ARG;
+  const void* ptrs[] = {q, k, v, alpha, beta, S, o};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return DN_ERR_MISALIGNED;
+  const size_t bh = (size_t)B * H;
+  const Span sq{q, bh * d_k * dtype_size(in_dtype)}, sk{k, sq.n};
+  const Span sv{v, bh * d_v * dtype_size(in_dtype)}, sb{beta, bh * sizeof(float)};
+  const Span sa{alpha, bh * sizeof(float)};
+  const Span sS{S, bh * d_k * d_v * sizeof(float)}, so{o, bh * d_v * dtype_size(out_dtype)};
+  for (Span in : {sq, sk, sv, sa, sb, sS})
+    if (overlap(so, in)) return DN_ERR_ALIASING;
+  for (Span in : {sq, sk, sv, sa, sb})
+    if (overlap(sS, in)) return DN_ERR_ALIASING;
+
+  dn::DecodeArgs a{q, k, v, alpha, beta, S, o, B, H, d_k, d_v, in_dtype, out_dtype, stream};
+  hipError_t e = dn::launch_decode(a);
+  if (e != hipSuccess) return hip_fail(e);
+  return DN_OK;
 }
 
 }  // namespace
@@ -172,74 +243,46 @@ size_t deltanet_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v,
                                           int in_dtype) {
   ChunkSizes s;
   if (check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, DN_F32, &s) != DN_OK) return 0;
-  return dn::chunk_workspace_bytes(B, H, L, d_k, d_v, C, in_dtype);
+  return dn::chunk_workspace_bytes(B, H, L, d_k, d_v, C, in_dtype, false);
+}
+
+size_t deltanet_gated_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
+                                                int in_dtype) {
+  ChunkSizes s;
+  if (check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, DN_F32, &s) != DN_OK) return 0;
+  return dn::chunk_workspace_bytes(B, H, L, d_k, d_v, C, in_dtype, true);
 }
 
 int deltanet_chunk_fwd(const void* q, const void* k, const void* v, const float* beta,
                        const float* S0, void* o, float* S_final, int B, int H, int L, int d_k,
                        int d_v, int C, int in_dtype, int out_dtype, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
-  ChunkSizes s;
-  int st = check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, out_dtype, &s);
-  if (st != DN_OK) return st;
-  if (L > 0 && (!q || !k || !v || !beta || !o)) return DN_ERR_NULL_ARG;
-  const void* ptrs[] = {q, k, v, beta, S0, o, S_final, workspace};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return DN_ERR_MISALIGNED;
+  return chunk_fwd_impl(q, k, v, nullptr, beta, S0, o, S_final, B, H, L, d_k, d_v, C, in_dtype,
+                        out_dtype, workspace, workspace_bytes, stream);
+}
 
-  const Span sq{q, s.qk}, sk{k, s.qk}, sv{v, s.v}, sb{beta, s.beta}, ss0{S0, s.state};
-  const Span so{o, s.o}, ssf{S_final, s.state};
-  const size_t need = dn::chunk_workspace_bytes(B, H, L, d_k, d_v, C, in_dtype);
-  const Span sw{workspace, workspace ? need : 0};
-  for (Span in : {sq, sk, sv, sb, ss0})
-    if (overlap(so, in) || (in.p != S0 && overlap(ssf, in))) return DN_ERR_ALIASING;
-  if (overlap(so, ssf)) return DN_ERR_ALIASING;
-  if (S_final && S0 && S_final != S0 && overlap(ssf, ss0)) return DN_ERR_ALIASING;
-  for (Span x : {sq, sk, sv, sb, ss0, so, ssf})
-    if (overlap(sw, x)) return DN_ERR_ALIASING;
-  if (workspace && workspace_bytes < need) return DN_ERR_WORKSPACE;
-
-  void* ws = workspace;
-  const bool own_ws = (ws == nullptr && need > 0);
-  if (own_ws) {
-    hipError_t e = hipMallocAsync(&ws, need, stream);
-    if (e != hipSuccess) return hip_fail(e);
-  }
-  dn::ChunkArgs a{q, k, v, beta, S0, o, S_final, B, H, L, d_k, d_v, C, in_dtype, out_dtype,
-                  ws, stream};
-  hipError_t e = dn::launch_chunk_fwd(a);
-  if (own_ws) {
-    hipError_t f = hipFreeAsync(ws, stream);
-    if (e == hipSuccess) e = f;
-  }
-  if (e != hipSuccess) return hip_fail(e);
-  return DN_OK;
+int deltanet_gated_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, const float* S0, void* o, float* S_final, int B,
+                             int H, int L, int d_k, int d_v, int C, int in_dtype, int out_dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  // With L = 0 there is no token to decay and alpha may be null: the call
+  // only copies the state, as the plain forward does.
+  if (L > 0 && !alpha) return DN_ERR_NULL_ARG;
+  return chunk_fwd_impl(q, k, v, alpha, beta, S0, o, S_final, B, H, L, d_k, d_v, C, in_dtype,
+                        out_dtype, workspace, workspace_bytes, stream);
 }
 
 int deltanet_decode_step(const void* q, const void* k, const void* v, const float* beta,
                          float* S, void* o, int B, int H, int d_k, int d_v, int in_dtype,
                          int out_dtype, hipStream_t stream) {
-  if (B < 1 || H < 1 || d_k < 1 || d_v < 1) return DN_ERR_BAD_SHAPE;
-  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return DN_ERR_UNSUPPORTED;
-  if (!dim_ok(d_k) || !dim_ok(d_v)) return DN_ERR_UNSUPPORTED;
-  if ((int64_t)B * H > 0x7fffffff) return DN_ERR_UNSUPPORTED;
-  if (!q || !k || !v || !beta || !S || !o) return DN_ERR_NULL_ARG;
-  const void* ptrs[] = {q, k, v, beta, S, o};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return DN_ERR_MISALIGNED;
-  const size_t bh = (size_t)B * H;
-  const Span sq{q, bh * d_k * dtype_size(in_dtype)}, sk{k, sq.n};
-  const Span sv{v, bh * d_v * dtype_size(in_dtype)}, sb{beta, bh * sizeof(float)};
-  const Span sS{S, bh * d_k * d_v * sizeof(float)}, so{o, bh * d_v * dtype_size(out_dtype)};
-  for (Span in : {sq, sk, sv, sb, sS})
-    if (overlap(so, in)) return DN_ERR_ALIASING;
-  for (Span in : {sq, sk, sv, sb})
-    if (overlap(sS, in)) return DN_ERR_ALIASING;
+  return decode_impl(q, k, v, nullptr, beta, S, o, B, H, d_k, d_v, in_dtype, out_dtype, stream);
+}
 
-  dn::DecodeArgs a{q, k, v, beta, S, o, B, H, d_k, d_v, in_dtype, out_dtype, stream};
-  hipError_t e = dn::launch_decode(a);
-  if (e != hipSuccess) return hip_fail(e);
-  return DN_OK;
+int deltanet_gated_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, float* S, void* o, int B, int H, int d_k,
+                               int d_v, int in_dtype, int out_dtype, hipStream_t stream) {
+  if (!alpha) return DN_ERR_NULL_ARG;
+  return decode_impl(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, in_dtype, out_dtype, stream);
 }
 
 }  // extern "C"

@@ -32,6 +32,15 @@
 // Every fp32 operand of a product is carried as a (hi, lo) bf16 pair, the
 // product taken as hi*hi + hi*lo + lo*hi.  A ragged last chunk reads zero
 // rows of k and beta = 0, which makes the padded rows and columns of T zero.
+//
+// Gated form (GATED; Gated DeltaNet, article "How a Baseten Engineer Traced 7
+// Years of Attention Mechanism Evolution", Gated DeltaNet section: decay by
+// alpha_t first, then the precise write).  Decaying the state before each
+// write scales every pair (r, i), i < r, of the chunk by the decays between
+// them, e^{g_r - g_i} with g_r = log(alpha_1) + ... + log(alpha_r):
+//     A_ri = beta_r e^{g_r - g_i} (k_r . k_i),
+// and T = (I + A)^{-1} diag(beta) as before.  The kernel also writes the g_r
+// of the chunk (rows past L: alpha = 1) for the scan.
 
 #include "dn_common.h"
 #include "dn_ktile.h"
@@ -43,7 +52,7 @@
 
 namespace dn {
 
-hipError_t launch_scan_mfma(const ChunkArgs& a, const uint4* Tfrag);
+hipError_t launch_scan_mfma(const ChunkArgs& a, const uint4* Tfrag, const float* Gws);
 
 namespace prep {
 
@@ -65,6 +74,24 @@ struct Cfg {
   static_assert(SPT >= 1, "shape");
 };
 
+// Gated form: the chunk's cumulative log-decays live in registers, lane l
+// holding rows GE l .. GE l + GE - 1 (GE = C / 64); any row's value is fetched
+// with a lane shuffle (every lane may ask for a different row).  Keeping them
+// out of LDS keeps the LDS at a size where three workgroups share a CU.
+template <int C>
+struct GRegs {
+  static constexpr int GE = C / 64;
+  float v[GE];
+  __device__ __forceinline__ float at(int row) const {
+    if constexpr (GE == 1) {
+      return __shfl(v[0], row, 64);
+    } else {
+      const float a = __shfl(v[0], row >> 1, 64), b = __shfl(v[1], row >> 1, 64);
+      return (row & 1) ? b : a;
+    }
+  }
+};
+
 // Lower tile (i, k), i > k, of A: index in the off-diagonal list.
 __device__ __forceinline__ int tidx(int i, int k) { return i * (i - 1) / 2 + k; }
 
@@ -79,10 +106,12 @@ __device__ __forceinline__ bf16x8 lds16(const uint16_t* p) {
 // over one 64-column slice of k (staged in Ks); the final call writes the
 // off-diagonal tiles of A = diag(beta) G to Atl as split operands and the
 // strictly lower part of the diagonal tile to Nd (fp32, column-major:
-// Nd[i][col][row] = N_i[row][col]).
-template <int C, int W, bool FINAL>
+// Nd[i][col][row] = N_i[row][col]); in the gated form each element first
+// takes its decay factor e^{g_row - g_col}.
+template <int C, int W, bool FINAL, bool GATED>
 __device__ __forceinline__ void gram_wave(const uint16_t* Ks, f32x4 (&acc)[2][C / 16], uint2* Atl,
-                                          float* Nd, const float* bs, int lane, int g, int i16) {
+                                          float* Nd, const float* bs, const GRegs<C>& gr_, int lane,
+                                          int g, int i16) {
   constexpr int NT = C / 16, KW = 64, NKB = KW / 32;
   if constexpr (W < NT / 2) {
 #pragma unroll
@@ -99,10 +128,20 @@ __device__ __forceinline__ void gram_wave(const uint16_t* Ks, f32x4 (&acc)[2][C 
           acc[gc][i] = mfma16(Ak[kb], lds16(Ks + koff<KW>(16 * i + i16, 4 * kb + g)), acc[gc][i]);
       }
       if constexpr (FINAL) {
+        float gcol[4];
+        if constexpr (GATED) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) gcol[r] = gr_.at(16 * kk + 4 * g + r);
+        }
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
           if (i < kk) continue;
           const float b = bs[16 * i + i16];
+          if constexpr (GATED) {  // e^{g_row - g_col}; only col <= row is kept
+            const float grow = gr_.at(16 * i + i16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[gc][i][r] *= __expf(fminf(grow - gcol[r], 0.f));
+          }
           if (i > kk) {
             uint2 hi, lo;
             split4(acc[gc][i] * b, hi, lo);
@@ -206,10 +245,12 @@ __device__ __forceinline__ void cols_wave(const uint2* Atl, const float* Lrow, c
   }
 }
 
-template <int C, int DK>
+template <int C, int DK, bool GATED>
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ k,
+                                                   const float* __restrict__ alpha,
                                                    const float* __restrict__ beta, int L,
-                                                   int nc, uint4* __restrict__ Tfrag) {
+                                                   int nc, uint4* __restrict__ Tfrag,
+                                                   float* __restrict__ Gws) {
   using CF = Cfg<C, DK>;
   constexpr int NT = CF::NT;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -247,6 +288,33 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   };
   kload(0);
   if (tid < C) bs[tid] = tid < valid ? beta[tok0 + tid] : 0.f;
+  // Gated form: g_r by an inclusive scan over each wave (every wave keeps its
+  // own copy in registers); wave 0 also writes the chunk's g to the workspace.
+  GRegs<C> gr_;
+  if constexpr (GATED) {
+    constexpr int E = GRegs<C>::GE;
+    float run = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int r = E * lane + e;
+      gr_.v[e] = r < valid ? log_decay(alpha[tok0 + r]) : 0.f;
+      run += gr_.v[e];
+    }
+    float x = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float t = __shfl_up(x, off, 64);
+      if (lane >= off) x += t;
+    }
+    float pre = x - run;
+#pragma unroll
+    for (int e = 0; e < E; ++e) gr_.v[e] = pre += gr_.v[e];
+    if (w == 0) {
+      float* const gout = Gws + ((size_t)bh * nc + c) * C;
+#pragma unroll
+      for (int e = 0; e < E; ++e) gout[E * lane + e] = gr_.v[e];
+    }
+  }
   kstore();
   f32x4 acc[2][NT];
 #pragma unroll
@@ -259,10 +327,10 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   auto gram = [&](auto final_tag) {
     constexpr bool F = decltype(final_tag)::value;
     switch (w) {
-      case 0: gram_wave<C, 0, F>(Ks, acc, Atl, Nd, bs, lane, g, i16); break;
-      case 1: gram_wave<C, 1, F>(Ks, acc, Atl, Nd, bs, lane, g, i16); break;
-      case 2: gram_wave<C, 2, F>(Ks, acc, Atl, Nd, bs, lane, g, i16); break;
-      default: gram_wave<C, 3, F>(Ks, acc, Atl, Nd, bs, lane, g, i16); break;
+      case 0: gram_wave<C, 0, F, GATED>(Ks, acc, Atl, Nd, bs, gr_, lane, g, i16); break;
+      case 1: gram_wave<C, 1, F, GATED>(Ks, acc, Atl, Nd, bs, gr_, lane, g, i16); break;
+      case 2: gram_wave<C, 2, F, GATED>(Ks, acc, Atl, Nd, bs, gr_, lane, g, i16); break;
+      default: gram_wave<C, 3, F, GATED>(Ks, acc, Atl, Nd, bs, gr_, lane, g, i16); break;
     }
   };
 #pragma unroll
@@ -319,24 +387,33 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   }
 }
 
+template <int C, int DK, bool GATED>
+hipError_t launch_g(const ChunkArgs& a, uint4* Tfrag, float* Gws) {
+  const int nc = cdiv(a.L, C);
+  const int BH = a.B * a.H;
+  constexpr size_t sm = Cfg<C, DK>::bytes;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<C, DK, GATED>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+  if (e != hipSuccess) return e;
+  prof_mark(kSlotChunkPrep, false, a.stream);
+  hipLaunchKernelGGL((prep_kernel<C, DK, GATED>), dim3(nc, BH), dim3(256), sm, a.stream,
+                     static_cast<const uint16_t*>(a.k), a.alpha, a.beta, a.L, nc, Tfrag, Gws);
+  e = hipGetLastError();
+  prof_mark(kSlotChunkPrep, true, a.stream);
+  return e;
+}
+
 template <int C, int DK>
 hipError_t launch_c(const ChunkArgs& a) {
   const int nc = cdiv(a.L, C);
-  const int BH = a.B * a.H;
   uint4* Tfrag = static_cast<uint4*>(a.workspace);
+  // The gated form's log-decay table follows the T fragments.
+  float* Gws = reinterpret_cast<float*>(Tfrag + (size_t)a.B * a.H * nc * Frag<C>::chunk_u4);
   if (nc > 0) {
-    constexpr size_t sm = Cfg<C, DK>::bytes;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<C, DK>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-    if (e != hipSuccess) return e;
-    prof_mark(kSlotChunkPrep, false, a.stream);
-    hipLaunchKernelGGL((prep_kernel<C, DK>), dim3(nc, BH), dim3(256), sm, a.stream,
-                       static_cast<const uint16_t*>(a.k), a.beta, a.L, nc, Tfrag);
-    e = hipGetLastError();
-    prof_mark(kSlotChunkPrep, true, a.stream);
+    hipError_t e = a.alpha ? launch_g<C, DK, true>(a, Tfrag, Gws) : launch_g<C, DK, false>(a, Tfrag, Gws);
     if (e != hipSuccess) return e;
   }
-  return launch_scan_mfma(a, Tfrag);
+  return launch_scan_mfma(a, Tfrag, a.alpha ? Gws : nullptr);
 }
 
 }  // namespace prep

@@ -21,6 +21,17 @@
 //         left), so slices of d_v are independent scans.
 // A ragged last chunk reads k = q = v = 0 and beta = 0 past L: zero rows of K
 // and beta make those rows of T, Delta and every state contribution zero.
+//
+// Gated form (GATED = true; Gated DeltaNet, article "How a Baseten Engineer
+// Traced 7 Years of Attention Mechanism Evolution", Gated DeltaNet section:
+// decay the state by alpha_t, then the precise write).  With the within-chunk
+// cumulative log-decays g_r = sum_{j<=r} log alpha_j (rows past L: alpha = 1)
+// and E_ri = e^{g_r - g_i} (i <= r, so every factor is <= 1):
+//     A     = tril(diag(beta) (K K^T o E), -1)
+//     Delta = T (V - diag(e^g) K S)
+//     O     = diag(e^g) Q S + (tril(Q K^T) o E) Delta
+//     S'    = e^{g_C} S + K^T diag(e^{g_C - g}) Delta
+// (o = elementwise product).  The prep kernel writes g next to T and P.
 
 #include "dn_common.h"
 #include "dn_launch.h"
@@ -34,7 +45,7 @@ constexpr int NT = 16;  // d_v columns per scan workgroup
 template <int C, int DK>
 struct PrepSmem {
   static constexpr int LD = (C > DK ? C : DK) + 1;  // row pitch in floats
-  static constexpr size_t bytes = 2 * (size_t)C * LD * sizeof(float) + C * sizeof(float);
+  static constexpr size_t bytes = 2 * (size_t)C * LD * sizeof(float) + 2 * C * sizeof(float);
 };
 
 template <typename IT>
@@ -48,18 +59,21 @@ __device__ __forceinline__ void load_rows(float* dst, int ld, const IT* src, int
 
 // One workgroup per (chunk, head).  Writes T[C][C] and P[C][C] (fp32, full
 // squares with zeros above the diagonal) for the chunk.
-template <int C, int DK, typename IT>
+template <int C, int DK, typename IT, bool GATED>
 __global__ __launch_bounds__(256) void prep_kernel(const IT* __restrict__ q,
                                                    const IT* __restrict__ k,
+                                                   const float* __restrict__ alpha,
                                                    const float* __restrict__ beta, int L,
                                                    float* __restrict__ Tws,
-                                                   float* __restrict__ Pws) {
+                                                   float* __restrict__ Pws,
+                                                   float* __restrict__ Gws) {
   constexpr int LD = PrepSmem<C, DK>::LD;
   constexpr int NB = C / BS;
   extern __shared__ float smem[];
   float* buf0 = smem;
   float* buf1 = smem + C * LD;
   float* bs = smem + 2 * C * LD;
+  float* gs = bs + C;  // within-chunk cumulative log-decays (gated form)
 
   const int c = blockIdx.x, bh = blockIdx.y, nc = gridDim.x;
   const int t0 = c * C;
@@ -70,15 +84,26 @@ __global__ __launch_bounds__(256) void prep_kernel(const IT* __restrict__ q,
 
   load_rows(buf0, LD, k + tok0 * DK, valid, C, DK);
   for (int r = threadIdx.x; r < C; r += blockDim.x) bs[r] = r < valid ? beta[tok0 + r] : 0.f;
+  if constexpr (GATED) {
+    for (int r = threadIdx.x; r < C; r += blockDim.x) gs[r] = r < valid ? log_decay(alpha[tok0 + r]) : 0.f;
+    __syncthreads();
+    if (threadIdx.x == 0) {  // prefix sum, in row order
+      float acc = 0.f;
+      for (int r = 0; r < C; ++r) gs[r] = acc += gs[r];
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < C; r += blockDim.x) Gws[((size_t)bh * nc + c) * C + r] = gs[r];
+  }
   __syncthreads();
 
-  // A = tril(diag(beta) K K^T, -1) into buf1.
+  // A = tril(diag(beta) (K K^T o E), -1) into buf1.
   for (int e = threadIdx.x; e < C * C; e += blockDim.x) {
     const int r = e / C, i = e % C;
     float acc = 0.f;
     if (i < r) {
       for (int d = 0; d < DK; ++d) acc += buf0[r * LD + d] * buf0[i * LD + d];
       acc *= bs[r];
+      if constexpr (GATED) acc *= expf(gs[r] - gs[i]);
     }
     buf1[r * LD + i] = acc;
   }
@@ -132,15 +157,17 @@ __global__ __launch_bounds__(256) void prep_kernel(const IT* __restrict__ q,
   }
   __syncthreads();
 
-  // P = tril(Q K^T), diagonal included.
+  // P = tril(Q K^T) (o E in the gated form), diagonal included.
   load_rows(buf1, LD, k + tok0 * DK, valid, C, DK);
   load_rows(buf0, LD, q + tok0 * DK, valid, C, DK);
   __syncthreads();
   for (int e = threadIdx.x; e < C * C; e += blockDim.x) {
     const int r = e / C, i = e % C;
     float acc = 0.f;
-    if (i <= r)
+    if (i <= r) {
       for (int d = 0; d < DK; ++d) acc += buf0[r * LD + d] * buf1[i * LD + d];
+      if constexpr (GATED) acc *= expf(gs[r] - gs[i]);
+    }
     Pc[e] = acc;
   }
 }
@@ -149,15 +176,16 @@ template <int C, int DK>
 struct ScanSmem {
   static constexpr int LDK = DK + 1;
   static constexpr size_t bytes =
-      ((size_t)C * LDK + (size_t)DK * NT + 2 * (size_t)C * NT) * sizeof(float);
+      ((size_t)C * LDK + (size_t)DK * NT + 2 * (size_t)C * NT + C) * sizeof(float);
 };
 
 // One workgroup per (16-column slice of d_v, head).  Walks all chunks.
-template <int C, int DK, int DV, typename IT, typename OT>
+template <int C, int DK, int DV, typename IT, typename OT, bool GATED>
 __global__ __launch_bounds__(256) void scan_kernel(
     const IT* __restrict__ q, const IT* __restrict__ k, const IT* __restrict__ v,
     const float* __restrict__ S0, OT* __restrict__ o, float* __restrict__ S_final, int L,
-    int nc, const float* __restrict__ Tws, const float* __restrict__ Pws) {
+    int nc, const float* __restrict__ Tws, const float* __restrict__ Pws,
+    const float* __restrict__ Gws) {
   constexpr int LDK = ScanSmem<C, DK>::LDK;
   constexpr int RSTRIDE = 256 / NT;   // rows between a thread's outputs
   constexpr int MR = C / RSTRIDE;     // chunk rows per thread
@@ -167,6 +195,7 @@ __global__ __launch_bounds__(256) void scan_kernel(
   float* Ss = Ks + C * LDK;
   float* Rs = Ss + DK * NT;
   float* Ds = Rs + C * NT;
+  float* gs = Ds + C * NT;  // the chunk's cumulative log-decays (gated form)
 
   const int j0 = blockIdx.x * NT, bh = blockIdx.y;
   const int j = threadIdx.x % NT, rb = threadIdx.x / NT;
@@ -184,9 +213,12 @@ __global__ __launch_bounds__(256) void scan_kernel(
     const float* Tc = Tws + ((size_t)bh * nc + c) * C * C;
     const float* Pc = Pws + ((size_t)bh * nc + c) * C * C;
     load_rows(Ks, LDK, k + tok0 * DK, valid, C, DK);
+    if constexpr (GATED)
+      for (int r = threadIdx.x; r < C; r += blockDim.x) gs[r] = Gws[((size_t)bh * nc + c) * C + r];
     __syncthreads();
 
-    // R = V - K S into LDS; O_inter = Q S kept in registers.
+    // R = V - K S into LDS; O_inter = Q S kept in registers (each row scaled
+    // by e^{g_r} in the gated form).
     float oi[MR];
     for (int m = 0; m < MR; ++m) {
       const int r = rb + m * RSTRIDE;
@@ -200,6 +232,11 @@ __global__ __launch_bounds__(256) void scan_kernel(
         }
       }
       const float vr = r < valid ? to_f32(v[(tok0 + r) * DV + j0 + j]) : 0.f;
+      if constexpr (GATED) {
+        const float dr = expf(gs[r]);
+        ks *= dr;
+        qs *= dr;
+      }
       Rs[r * NT + j] = vr - ks;
       oi[m] = qs;
     }
@@ -224,11 +261,17 @@ __global__ __launch_bounds__(256) void scan_kernel(
       }
     }
 
-    // S += K^T Delta.
+    // S += K^T Delta  (gated: S = e^{g_C} S + K^T diag(e^{g_C - g}) Delta).
     for (int m = 0; m < MS; ++m) {
       const int d = rb + m * RSTRIDE;
       float acc = Ss[d * NT + j];
-      for (int r = 0; r < C; ++r) acc += Ks[r * LDK + d] * Ds[r * NT + j];
+      if constexpr (GATED) {
+        const float gC = gs[C - 1];
+        acc *= expf(gC);
+        for (int r = 0; r < C; ++r) acc += Ks[r * LDK + d] * (expf(gC - gs[r]) * Ds[r * NT + j]);
+      } else {
+        for (int r = 0; r < C; ++r) acc += Ks[r * LDK + d] * Ds[r * NT + j];
+      }
       Ss[d * NT + j] = acc;
     }
     __syncthreads();
@@ -243,46 +286,53 @@ __global__ __launch_bounds__(256) void scan_kernel(
   }
 }
 
-template <int C, int DK, int DV, typename IT, typename OT>
+template <int C, int DK, int DV, typename IT, typename OT, bool GATED>
 hipError_t launch_t(const ChunkArgs& a) {
   const int nc = cdiv(a.L, C);
   const int bh = a.B * a.H;
   float* Tws = static_cast<float*>(a.workspace);
   float* Pws = Tws + (size_t)bh * nc * C * C;
+  float* Gws = Pws + (size_t)bh * nc * C * C;  // gated form only
   if (nc > 0) {
     constexpr size_t sm = PrepSmem<C, DK>::bytes;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<C, DK, IT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+    hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<C, DK, IT, GATED>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
     if (e != hipSuccess) return e;
     prof_mark(kSlotChunkPrep, false, a.stream);
-    hipLaunchKernelGGL((prep_kernel<C, DK, IT>), dim3(nc, bh), dim3(256), sm, a.stream,
-                       static_cast<const IT*>(a.q), static_cast<const IT*>(a.k), a.beta, a.L,
-                       Tws, Pws);
+    hipLaunchKernelGGL((prep_kernel<C, DK, IT, GATED>), dim3(nc, bh), dim3(256), sm, a.stream,
+                       static_cast<const IT*>(a.q), static_cast<const IT*>(a.k), a.alpha,
+                       a.beta, a.L, Tws, Pws, Gws);
     e = hipGetLastError();
     prof_mark(kSlotChunkPrep, true, a.stream);
     if (e != hipSuccess) return e;
   }
   constexpr size_t sm2 = ScanSmem<C, DK>::bytes;
   hipError_t e =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<C, DK, DV, IT, OT>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<C, DK, DV, IT, OT, GATED>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm2);
   if (e != hipSuccess) return e;
   prof_mark(kSlotChunkScan, false, a.stream);
-  hipLaunchKernelGGL((scan_kernel<C, DK, DV, IT, OT>), dim3(DV / NT, bh), dim3(256), sm2,
+  hipLaunchKernelGGL((scan_kernel<C, DK, DV, IT, OT, GATED>), dim3(DV / NT, bh), dim3(256), sm2,
                      a.stream, static_cast<const IT*>(a.q), static_cast<const IT*>(a.k),
                      static_cast<const IT*>(a.v), a.S0, static_cast<OT*>(a.o), a.S_final, a.L,
-                     nc, Tws, Pws);
+                     nc, Tws, Pws, Gws);
   e = hipGetLastError();
   prof_mark(kSlotChunkScan, true, a.stream);
   return e;
 }
 
+template <int C, int DK, int DV, typename IT, typename OT>
+hipError_t launch_g(const ChunkArgs& a) {
+  return a.alpha ? launch_t<C, DK, DV, IT, OT, true>(a) : launch_t<C, DK, DV, IT, OT, false>(a);
+}
+
 template <int C, int DK, int DV>
 hipError_t launch_types(const ChunkArgs& a) {
-  if (a.in_dtype == 0 && a.out_dtype == 0) return launch_t<C, DK, DV, float, float>(a);
-  if (a.in_dtype == 0 && a.out_dtype == 1) return launch_t<C, DK, DV, float, bf16>(a);
-  if (a.in_dtype == 1 && a.out_dtype == 0) return launch_t<C, DK, DV, bf16, float>(a);
-  return launch_t<C, DK, DV, bf16, bf16>(a);
+  if (a.in_dtype == 0 && a.out_dtype == 0) return launch_g<C, DK, DV, float, float>(a);
+  if (a.in_dtype == 0 && a.out_dtype == 1) return launch_g<C, DK, DV, float, bf16>(a);
+  if (a.in_dtype == 1 && a.out_dtype == 0) return launch_g<C, DK, DV, bf16, float>(a);
+  return launch_g<C, DK, DV, bf16, bf16>(a);
 }
 
 template <int C>

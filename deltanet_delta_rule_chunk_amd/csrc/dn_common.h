@@ -30,6 +30,14 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
   return bf16{f32_to_bf16_bits(x)};
 }
 
+// log(alpha) of a decay alpha in [0, 1], floored at log(FLT_MIN) so that a
+// zero decay (a full wipe) becomes a factor e^{-87.3} ~ 1e-38 and every
+// difference of summed log-decays stays finite.
+constexpr float kLogDecayFloor = -87.33654f;
+__device__ __forceinline__ float log_decay(float alpha) {
+  return alpha > 0.f ? fmaxf(logf(alpha), kLogDecayFloor) : kLogDecayFloor;
+}
+
 // Ceil-divide for launch geometry.
 __host__ __device__ constexpr inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 

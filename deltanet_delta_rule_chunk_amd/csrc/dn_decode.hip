@@ -6,7 +6,11 @@
 // Reading o after the write needs no second pass over S:
 //     q S_new = q S + (q . k) u,
 // so one streaming read of S yields both r = k S and p = q S, and S is
-// written back once.  The step is bound by HBM bandwidth: per head it moves
+// written back once.  The gated step (Gated DeltaNet, article "How a Baseten
+// Engineer Traced 7 Years of Attention Mechanism Evolution", Gated DeltaNet
+// section: decay first, then the precise write) decays S by alpha before the
+// delta reads it, which the same single read carries as scalars:
+//     u = beta (v - alpha r),  o = alpha p + (q . k) u,  S <- alpha S + k^T u.  The step is bound by HBM bandwidth: per head it moves
 // 2 * d_k * d_v * 4 bytes of state against 6 d_k d_v flops.
 //
 // Work split: persistent 512-thread workgroups, one per compute unit, each
@@ -28,10 +32,11 @@ namespace dn {
 
 typedef float vf4 __attribute__((ext_vector_type(4)));
 
-template <int DK, int DV, typename IT, typename OT>
+template <int DK, int DV, typename IT, typename OT, bool GATED>
 __global__ __launch_bounds__(512) void decode_step_kernel(
     const IT* __restrict__ q, const IT* __restrict__ k, const IT* __restrict__ v,
-    const float* __restrict__ beta, float* __restrict__ S, OT* __restrict__ o, int BH) {
+    const float* __restrict__ alpha, const float* __restrict__ beta, float* __restrict__ S,
+    OT* __restrict__ o, int BH) {
   constexpr int NT = 512;
   constexpr int COLG = DV / 4;          // float4 column groups per row
   constexpr int ROWG = NT / COLG;       // row groups
@@ -86,6 +91,7 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
     __syncthreads();
 
     const float b = beta[bh];
+    const float al = GATED ? alpha[bh] : 1.f;
     for (int c = tid; c < DV; c += NT) {
       const int g = c / 4, e = c % 4;
       float rr = 0.f, pp = 0.f;
@@ -94,9 +100,9 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
         rr += red_r[j][g][e];
         pp += red_p[j][g][e];
       }
-      const float u = b * (vs[c] - rr);
+      const float u = GATED ? b * (vs[c] - al * rr) : b * (vs[c] - rr);
       us[c] = u;
-      o[(size_t)bh * DV + c] = from_f32<OT>(pp + qk_s * u);
+      o[(size_t)bh * DV + c] = from_f32<OT>(GATED ? al * pp + qk_s * u : pp + qk_s * u);
     }
     __syncthreads();
 
@@ -105,13 +111,12 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = rg + i * ROWG;
-      __builtin_nontemporal_store(s[i] + ks[row] * u4,
-                                  reinterpret_cast<vf4*>(Sh + (size_t)row * DV + cg * 4));
+      const vf4 snew = GATED ? al * s[i] + ks[row] * u4 : s[i] + ks[row] * u4;
+      __builtin_nontemporal_store(snew, reinterpret_cast<vf4*>(Sh + (size_t)row * DV + cg * 4));
     }
     __syncthreads();  // the LDS vectors are rewritten for the next head
     if (!more) break;
     bh = nb;
-#pragma unroll
     for (int i = 0; i < RPT; ++i) s[i] = sn[i];
   }
 }
@@ -135,9 +140,16 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   const int BH = a.B * a.H;
   const int grid = BH < cu_count() ? BH : cu_count();
   prof_mark(kSlotDecode, false, a.stream);
-  hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT>), dim3(grid), dim3(512), 0, a.stream,
-                     static_cast<const IT*>(a.q), static_cast<const IT*>(a.k),
-                     static_cast<const IT*>(a.v), a.beta, a.S, static_cast<OT*>(a.o), BH);
+  if (a.alpha)
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT, true>), dim3(grid), dim3(512), 0,
+                       a.stream, static_cast<const IT*>(a.q), static_cast<const IT*>(a.k),
+                       static_cast<const IT*>(a.v), a.alpha, a.beta, a.S, static_cast<OT*>(a.o),
+                       BH);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT, false>), dim3(grid), dim3(512), 0,
+                       a.stream, static_cast<const IT*>(a.q), static_cast<const IT*>(a.k),
+                       static_cast<const IT*>(a.v), a.alpha, a.beta, a.S, static_cast<OT*>(a.o),
+                       BH);
   hipError_t e = hipGetLastError();
   prof_mark(kSlotDecode, true, a.stream);
   return e;

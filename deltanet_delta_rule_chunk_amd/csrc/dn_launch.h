@@ -9,6 +9,7 @@ namespace dn {
 
 struct DecodeArgs {
   const void *q, *k, *v;
+  const float* alpha;  // per-(b, h) decay of the gated step, or null (plain delta rule)
   const float* beta;
   float* S;
   void* o;
@@ -18,6 +19,7 @@ struct DecodeArgs {
 
 struct ChunkArgs {
   const void *q, *k, *v;
+  const float* alpha;  // per-token decay of the gated form, or null (plain delta rule)
   const float* beta;
   const float* S0;  // may be null (zero state)
   void* o;
@@ -38,7 +40,11 @@ enum ProfSlot { kSlotChunkPrep = 0, kSlotChunkScan = 1, kSlotDecode = 2, kNumSlo
 void prof_mark(int slot, bool end, hipStream_t s);
 
 // Chunked forward: bytes of scratch it needs, and the launch sequence.
-size_t chunk_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int in_dtype);
+size_t chunk_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int in_dtype,
+                             bool gated);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
+// Bytes of the gated form's per-chunk log-decay table; it sits at the end of
+// the workspace, after the kernels' other scratch.
+size_t gated_log_decay_bytes(int B, int H, int L, int C);
 
 }  // namespace dn

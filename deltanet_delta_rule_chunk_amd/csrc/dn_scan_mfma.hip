@@ -41,6 +41,21 @@
 // A ragged last chunk loads clamped rows and zeroes them at first use
 // (k, v rows and beta = 0 make those rows of R, Delta and T zero: no-ops);
 // outputs past L are not stored.
+//
+// Gated form (GATED; Gated DeltaNet, article "How a Baseten Engineer Traced 7
+// Years of Attention Mechanism Evolution", Gated DeltaNet section: the state
+// is decayed by alpha_t before each precise write).  With the chunk's
+// cumulative log-decays g_r (from the prep kernel; every factor below has a
+// non-positive exponent) and G_b = g of the last row before sub-block b
+// (G_0 = 0):
+//     R       = V - diag(e^g) K S
+//     S_{b+1} = e^{G_{b+1} - G_b} S_b + K_b^T diag(e^{G_{b+1} - g}) Delta_b
+//     O_b     = diag(e^{g - G_b}) Q_b S_b + (tril(Q_b K_b^T) o e^{g_r - g_i}) Delta_b
+// The chain waves write a second, decayed copy of Delta for the state update;
+// the output waves decay their rows and their diagonal Q K^T block.  The
+// per-row factors e^{g_r}, e^{G_{b+1} - g_r} and e^{g_r - G_b} are computed
+// once per chunk by the output waves while they stage the chunk, and kept in
+// LDS next to g, so the chain waves only multiply.
 
 #include "dn_common.h"
 #include "dn_launch.h"
@@ -79,7 +94,11 @@ struct Cfg {
   static constexpr int OFF_D = OFF_R + 2 * RPLANE;
   static constexpr int OFF_V = OFF_D + 2 * 2 * RPLANE;   // [2][C][16] bf16 v slice
   static constexpr int OFF_O = OFF_V + 2 * C * 16;       // [4 waves][32][16] fp32 out tile
-  static constexpr int TOTAL = OFF_O + 4 * 32 * 16 * 2;
+  static constexpr int OFF_DT = OFF_O + 4 * 32 * 16 * 2;  // decayed Delta planes (gated form)
+  // Gated form: per slot (chunk parity), 4 rows of C fp32: g, e^{g},
+  // e^{G_{b+1} - g}, e^{g - G_b} (b = the row's sub-block).
+  static constexpr int OFF_G = OFF_DT + 2 * RPLANE;
+  static constexpr int TOTAL = OFF_G + 2 * 4 * C * 2;
   static constexpr size_t bytes = (size_t)TOTAL * sizeof(uint16_t);
   static_assert(RPW >= 1 && DPW >= 1 && SPT >= 1, "shape");
   static_assert(bytes <= 160 * 1024, "LDS budget");
@@ -115,11 +134,12 @@ __device__ __forceinline__ void put_split(uint16_t* base, int plane, int off, f3
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
 
-template <int C, int DK, int DV, typename OT>
+template <int C, int DK, int DV, typename OT, bool GATED>
 __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ S0, OT* __restrict__ o,
-    float* __restrict__ S_final, const uint4* __restrict__ Tfrag, int L, int nc, int BH) {
+    float* __restrict__ S_final, const uint4* __restrict__ Tfrag, const float* __restrict__ Gws,
+    int L, int nc, int BH) {
   using CF = Cfg<C, DK, DV>;
   constexpr int NRT = CF::NRT, NSB = CF::NSB, NKB = CF::NKB, NCT = CF::NCT;
   constexpr int RPW = CF::RPW, DPW = CF::DPW, SPT = CF::SPT;
@@ -135,6 +155,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
   uint16_t* const Rb = lds + CF::OFF_R;
   uint16_t* const Db = lds + CF::OFF_D;
   uint16_t* const Vbuf = lds + CF::OFF_V;
+  uint16_t* const DTb = lds + CF::OFF_DT;
+  float* const Gs = reinterpret_cast<float*>(lds + CF::OFF_G);
 
   const int flat = blockIdx.x, xcd = flat & 7, sl = flat >> 3;
   const int ct = sl % NCT, bh = (sl / NCT) * 8 + xcd;
@@ -248,6 +270,12 @@ __global__ __launch_bounds__(512) void scan_kernel(
     __syncthreads();
 
     const int m = i16 >> 2, ap = i16 & 3;
+    // Gated form: Delta rows 16 rt + 4 g + r of chunk c scaled by
+    // e^{G_{b+1} - g_row}, G_{b+1} = g of the last row of the row's sub-block.
+    auto decay_rows = [&](int rt, f32x4 x, int c) {
+      const f32x4 f = *reinterpret_cast<const f32x4*>(Gs + (c & 1) * 4 * C + 2 * C + 16 * rt + 4 * g);
+      return x * f;
+    };
     auto step = [&](int c, TRegs& tc) {
       const int cn = min(c + 1, nc - 1);
       const uint16_t* Kc = Kbuf + (c & 1) * KELEMS;
@@ -291,7 +319,11 @@ __global__ __launch_bounds__(512) void scan_kernel(
                                bf16_to_f32(vv.y & 0xffffu), bf16_to_f32(vv.y >> 16)};
           f32x4 R;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) R[r] = v4[r] - (rh[i][r] + rl[i][r]);
+          for (int r = 0; r < 4; ++r) {
+            float ks = rh[i][r] + rl[i][r];
+            if constexpr (GATED) ks *= Gs[(c & 1) * 4 * C + C + 16 * rt + 4 * g + r];
+            R[r] = v4[r] - ks;
+          }
           put_split(Rb, RPLANE, fo_d(rt, g, i16), R);
         }
       }
@@ -330,18 +362,21 @@ __global__ __launch_bounds__(512) void scan_kernel(
             }
           }
           put_split(Dc, RPLANE, fo_d(rt1, g, i16), e0 + e1 + e2);
+          if constexpr (GATED) put_split(DTb, RPLANE, fo_d(rt1, g, i16), decay_rows(rt1, e0 + e1 + e2, c));
         }
         put_split(Dc, RPLANE, fo_d(rt0, g, i16), d0 + d1 + d2);
+        if constexpr (GATED) put_split(DTb, RPLANE, fo_d(rt0, g, i16), decay_rows(rt0, d0 + d1 + d2, c));
       }
       __syncthreads();
 
       // ---- phase C: S += K^T Delta, snapshot after every sub-block -------------
       {
         bf16x8 Dh[NSB], Dl[NSB], Kt[NSB][DPW];
+        const uint16_t* Du = GATED ? DTb : Dc;  // the state update takes the decayed copy
 #pragma unroll
         for (int b = 0; b < NSB; ++b) {
-          Dh[b] = lds16(Dc + fo_b(b, g, i16));
-          Dl[b] = lds16(Dc + RPLANE + fo_b(b, g, i16));
+          Dh[b] = lds16(Du + fo_b(b, g, i16));
+          Dl[b] = lds16(Du + RPLANE + fo_b(b, g, i16));
           const int row = 32 * b + 8 * g + m;
 #pragma unroll
           for (int i = 0; i < DPW; ++i) {
@@ -352,6 +387,11 @@ __global__ __launch_bounds__(512) void scan_kernel(
         }
 #pragma unroll
         for (int b = 0; b < NSB; ++b) {
+          if constexpr (GATED) {  // S_b -> e^{G_{b+1} - G_b} S_b  (= e^{g - G_b} at the block's last row)
+            const float f = Gs[(c & 1) * 4 * C + 3 * C + 32 * b + 31];
+#pragma unroll
+            for (int i = 0; i < DPW; ++i) { sa[i] *= f; sb[i] *= f; }
+          }
 #pragma unroll
           for (int i = 0; i < DPW; ++i) {
             sa[i] = mfma16(Kt[b][i], Dh[b], sa[i]);
@@ -400,18 +440,43 @@ __global__ __launch_bounds__(512) void scan_kernel(
     // rows past L are stored as zero.
     const int tl = tid - CF::NCW * 64;  // 0 .. 255
     const int vrow = min(tl >> 1, C - 1), vhalf = tl & 1;
+    // (Gated form: the chunk's C log-decays ride along, 16 bytes per thread,
+    // into slot `gslot` of Gs, the parity of the chunk step that uses them.)
     uint4 vst;
+    float4 gst;
+    float gb0, gb1;  // G_b and G_{b+1} of the sub-block of this thread's 4 rows
+    const int grow4 = 4 * (tl % (C / 4)), gblk = grow4 >> 5;
     auto v_stage_load = [&](int cc) {
       const int valid = valid_of(cc);
       const size_t t0 = tokh + (size_t)cc * C;
       vst = *reinterpret_cast<const uint4*>(v + (t0 + min(vrow, valid - 1)) * DV + j0 + 8 * vhalf);
+      if constexpr (GATED) {
+        const float* gsrc = Gws + ((size_t)bh * nc + cc) * C;
+        gst = *reinterpret_cast<const float4*>(gsrc + grow4);
+        gb0 = gsrc[max(32 * gblk - 1, 0)];
+        gb1 = gsrc[32 * gblk + 31];
+      }
     };
-    auto v_stage_store = [&](int cc, uint16_t* dst) {
+    auto v_stage_store = [&](int cc, uint16_t* dst, int gslot) {
       const int valid = valid_of(cc);
       if (tl < 2 * C) {
         const uint32_t msk = vrow < valid ? 0xffffffffu : 0u;
         *reinterpret_cast<uint4*>(dst + vrow * 16 + 8 * vhalf) =
             make_uint4(vst.x & msk, vst.y & msk, vst.z & msk, vst.w & msk);
+      }
+      if constexpr (GATED) {
+        if (tl < C / 4) {
+          const float G0 = gblk > 0 ? gb0 : 0.f;
+          const float gv[4] = {gst.x, gst.y, gst.z, gst.w};
+          float* dst = Gs + gslot * 4 * C + grow4;
+          *reinterpret_cast<float4*>(dst) = gst;
+          *reinterpret_cast<float4*>(dst + C) =
+              make_float4(__expf(gv[0]), __expf(gv[1]), __expf(gv[2]), __expf(gv[3]));
+          *reinterpret_cast<float4*>(dst + 2 * C) =
+              make_float4(__expf(gb1 - gv[0]), __expf(gb1 - gv[1]), __expf(gb1 - gv[2]), __expf(gb1 - gv[3]));
+          *reinterpret_cast<float4*>(dst + 3 * C) =
+              make_float4(__expf(gv[0] - G0), __expf(gv[1] - G0), __expf(gv[2] - G0), __expf(gv[3] - G0));
+        }
       }
     };
     auto q_load = [&](int cc) {
@@ -447,6 +512,17 @@ __global__ __launch_bounds__(512) void scan_kernel(
         p00 = mfma16(K0[kb], Q0, p00);
         p01 = mfma16(K0[kb], Q1, p01);
         p11 = mfma16(K1[kb], Q1, p11);
+      }
+      if constexpr (GATED) {  // P[q][k] e^{g_q - g_k}, k <= q
+        const float* gc = Gs + (cc & 1) * 4 * C + 32 * a;
+        const float gq0 = gc[i16], gq1 = gc[16 + i16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float gk0 = gc[4 * g + r], gk1 = gc[16 + 4 * g + r];
+          p00[r] *= __expf(fminf(gq0 - gk0, 0.f));
+          p01[r] *= __expf(fminf(gq1 - gk0, 0.f));
+          p11[r] *= __expf(fminf(gq1 - gk1, 0.f));
+        }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -513,8 +589,14 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row0 = 4 * g + r, row1 = row0 + 16;
-        Ot[row0 * 16 + ((((i16 >> 2) ^ (row0 >> 2)) & 3) << 2) + (i16 & 3)] = o0h[r] + o0l[r] + x0[r];
-        Ot[row1 * 16 + ((((i16 >> 2) ^ (row1 >> 2)) & 3) << 2) + (i16 & 3)] = o1h[r] + o1l[r] + x1[r];
+        float s0 = o0h[r] + o0l[r], s1 = o1h[r] + o1l[r];
+        if constexpr (GATED) {  // rows of Q_a S_a decayed by e^{g_row - G_a}
+          const float* f3 = Gs + (cc & 1) * 4 * C + 3 * C + 32 * a;
+          s0 *= f3[row0];
+          s1 *= f3[row1];
+        }
+        Ot[row0 * 16 + ((((i16 >> 2) ^ (row0 >> 2)) & 3) << 2) + (i16 & 3)] = s0 + x0[r];
+        Ot[row1 * 16 + ((((i16 >> 2) ^ (row1 >> 2)) & 3) << 2) + (i16 & 3)] = s1 + x1[r];
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -567,7 +649,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
 
     v_stage_load(0);
     stage_load(0);
-    v_stage_store(0, Vbuf);
+    v_stage_store(0, Vbuf, 0);
     stage_store(0, Kbuf);
     __syncthreads();
     for (int c = 0; c < nc; ++c) {
@@ -585,7 +667,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
       __syncthreads();
       // ---- phase C: diagonal Q K^T block of chunk c ------------------------------
       if (outw) diag_qk(c);
-      v_stage_store(cn, Vbuf + ((c + 1) & 1) * C * 16);
+      v_stage_store(cn, Vbuf + ((c + 1) & 1) * C * 16, (c + 1) & 1);
       stage_store(cn, Kbuf + ((c + 1) & 1) * KELEMS);
       __syncthreads();
     }
@@ -596,43 +678,47 @@ __global__ __launch_bounds__(512) void scan_kernel(
   }
 }
 
-template <int C, int DK, int DV, typename OT>
-hipError_t launch_t(const ChunkArgs& a, const uint4* Tfrag) {
+template <int C, int DK, int DV, typename OT, bool GATED>
+hipError_t launch_t(const ChunkArgs& a, const uint4* Tfrag, const float* Gws) {
   using CF = Cfg<C, DK, DV>;
   const int nc = cdiv(a.L, C);
   const int BH = a.B * a.H;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<C, DK, DV, OT>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<C, DK, DV, OT, GATED>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)CF::bytes);
   if (e != hipSuccess) return e;
   const int groups = cdiv(BH, 8) * 8 * CF::NCT;
   prof_mark(kSlotChunkScan, false, a.stream);
-  hipLaunchKernelGGL((scan_kernel<C, DK, DV, OT>), dim3(groups), dim3(CF::NTHR), CF::bytes,
+  hipLaunchKernelGGL((scan_kernel<C, DK, DV, OT, GATED>), dim3(groups), dim3(CF::NTHR), CF::bytes,
                      a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.S0,
-                     static_cast<OT*>(a.o), a.S_final, Tfrag, a.L, nc, BH);
+                     static_cast<OT*>(a.o), a.S_final, Tfrag, Gws, a.L, nc, BH);
   e = hipGetLastError();
   prof_mark(kSlotChunkScan, true, a.stream);
   return e;
 }
 
 template <int C, int DK, int DV>
-hipError_t launch_o(const ChunkArgs& a, const uint4* Tfrag) {
-  return a.out_dtype == 0 ? launch_t<C, DK, DV, float>(a, Tfrag)
-                          : launch_t<C, DK, DV, bf16>(a, Tfrag);
+hipError_t launch_o(const ChunkArgs& a, const uint4* Tfrag, const float* Gws) {
+  if (Gws)
+    return a.out_dtype == 0 ? launch_t<C, DK, DV, float, true>(a, Tfrag, Gws)
+                            : launch_t<C, DK, DV, bf16, true>(a, Tfrag, Gws);
+  return a.out_dtype == 0 ? launch_t<C, DK, DV, float, false>(a, Tfrag, Gws)
+                          : launch_t<C, DK, DV, bf16, false>(a, Tfrag, Gws);
 }
 
 template <int C>
-hipError_t launch_c(const ChunkArgs& a, const uint4* Tfrag) {
-  if (a.d_k == 64 && a.d_v == 64) return launch_o<C, 64, 64>(a, Tfrag);
-  if (a.d_k == 64 && a.d_v == 128) return launch_o<C, 64, 128>(a, Tfrag);
-  if (a.d_k == 128 && a.d_v == 64) return launch_o<C, 128, 64>(a, Tfrag);
-  return launch_o<C, 128, 128>(a, Tfrag);
+hipError_t launch_c(const ChunkArgs& a, const uint4* Tfrag, const float* Gws) {
+  if (a.d_k == 64 && a.d_v == 64) return launch_o<C, 64, 64>(a, Tfrag, Gws);
+  if (a.d_k == 64 && a.d_v == 128) return launch_o<C, 64, 128>(a, Tfrag, Gws);
+  if (a.d_k == 128 && a.d_v == 64) return launch_o<C, 128, 64>(a, Tfrag, Gws);
+  return launch_o<C, 128, 128>(a, Tfrag, Gws);
 }
 
 }  // namespace scan
 
-hipError_t launch_scan_mfma(const ChunkArgs& a, const uint4* Tfrag) {
-  return a.C == 64 ? scan::launch_c<64>(a, Tfrag) : scan::launch_c<128>(a, Tfrag);
+// Gws: the gated form's per-chunk log-decays, or null for the plain delta rule.
+hipError_t launch_scan_mfma(const ChunkArgs& a, const uint4* Tfrag, const float* Gws) {
+  return a.C == 64 ? scan::launch_c<64>(a, Tfrag, Gws) : scan::launch_c<128>(a, Tfrag, Gws);
 }
 
 }  // namespace dn

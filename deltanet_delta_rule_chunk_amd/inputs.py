@@ -26,6 +26,13 @@ memory stays at one slice of fp64.
 Decode steps: the state is drawn from ``default_rng(seed)``; step s draws its
 q, k, v, beta-logit from ``default_rng([seed, s + 1])`` with the same
 transforms, so any step can be made on its own.
+
+Gated form (Gated DeltaNet): the decay alpha comes from a stream of its own,
+``default_rng([seed, 7])`` for a chunked forward (``[B,H,L]`` in C order) and
+``default_rng([seed, s + 1, 7])`` for decode step s (``[B,H]``), as
+alpha = sigmoid(N(3, 1)) in fp64 then cast to fp32 (a decay
+per token on average 0.93, from ~0.25 to ~0.9996), so the draws of the
+other inputs are the same with or without the gate.
 """
 
 from __future__ import annotations
@@ -145,6 +152,21 @@ def make_chunk_inputs(w: ChunkWorkload, seed: int = 0, L: Optional[int] = None) 
         S0 = _draw_normal(rng, (w.B, w.H, w.d_k, w.d_v),
                           lambda a: torch.from_numpy(a * w.s0_std).to(torch.float32))
     return dict(q=q, k=k, v=v, beta=beta, S0=S0)
+
+
+def _alpha_from(rng: np.random.Generator, shape) -> torch.Tensor:
+    return torch.from_numpy(_sigmoid(3.0 + rng.standard_normal(shape))).to(torch.float32)
+
+
+def make_chunk_alpha(w: ChunkWorkload, seed: int = 0, L: Optional[int] = None) -> torch.Tensor:
+    """Per-token decay ``[B,H,L]`` fp32 of the gated forward."""
+    L = w.L if L is None else L
+    return _alpha_from(np.random.default_rng([seed, 7]), (w.B, w.H, L))
+
+
+def make_decode_alpha(w: DecodeWorkload, step: int, seed: int = 0) -> torch.Tensor:
+    """Per-(b, h) decay ``[B,H]`` fp32 of gated decode step ``step``."""
+    return _alpha_from(np.random.default_rng([seed, step + 1, 7]), (w.B, w.H))
 
 
 def make_decode_state(w: DecodeWorkload, seed: int = 0) -> torch.Tensor:

@@ -97,6 +97,45 @@ int deltanet_decode_step(const void* q, const void* k, const void* v, const floa
                          float* S, void* o, int B, int H, int d_k, int d_v,
                          int in_dtype, int out_dtype, hipStream_t stream);
 
+/*
+ * Gated forms (Gated DeltaNet).  The article "How a Baseten Engineer Traced 7
+ * Years of Attention Mechanism Evolution" (wpnews.pro / dev.to), section on
+ * Gated DeltaNet, adds a decay alpha in [0, 1] that is applied to the old
+ * state first, after which the precise delta write acts on the decayed
+ * state; alpha = 1 is the plain delta rule, alpha = 0 wipes the memory.  Per
+ * (b, h) and token t, in order:
+ *     S     = alpha_t S
+ *     v_old = k_t S
+ *     u_t   = beta_t (v_t - v_old)
+ *     S     = S + k_t^T u_t
+ *     o_t   = q_t S
+ * Arguments are those of the plain entry points plus alpha, fp32, one value
+ * per token: [B, H, L] for the chunked forward, [B, H] for the decode step.
+ * alpha must be 16-byte aligned and may not overlap an output; values outside
+ * [0, 1] are not checked (the product is then not a decay).  A zero alpha is
+ * taken as a factor of about 1e-38 inside a chunk (the kernels sum
+ * log(alpha), floored at log(FLT_MIN)), which is a wipe to within fp32.
+ * The chunked forward's workspace is larger than the plain one's: query it
+ * with deltanet_gated_chunk_fwd_workspace_bytes().  With L = 0, alpha may be
+ * NULL.  Status codes and every other rule are as for the plain calls.
+ */
+int deltanet_gated_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, const float* S0, void* o, float* S_final,
+                             int B, int H, int L, int d_k, int d_v, int C,
+                             int in_dtype, int out_dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace deltanet_gated_chunk_fwd needs (0 if the sizes are
+ * invalid or unsupported). */
+size_t deltanet_gated_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
+                                                int in_dtype);
+
+/* One gated decode step, S updated in place; o = q S_new.  alpha: [B, H] fp32. */
+int deltanet_gated_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, float* S, void* o, int B, int H,
+                               int d_k, int d_v, int in_dtype, int out_dtype,
+                               hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* deltanet_status_string(int status);
 

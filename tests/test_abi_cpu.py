@@ -33,7 +33,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.deltanet_version() == 100
+    assert lib.deltanet_version() == 200
     for s in range(8):
         assert lib.deltanet_status_string(s)
     assert lib.deltanet_status_string(99) == b"unknown status"
@@ -101,3 +101,43 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         binding.chunk_fwd(x, x, x, torch.zeros(1, 1, 4))
+
+
+def _gfwd(lib, alpha=BASE + 800 * MB, q=BASE, k=BASE + 100 * MB, v=BASE + 200 * MB,
+          beta=BASE + 300 * MB, S0=None, o=BASE + 400 * MB, Sf=BASE + 500 * MB, B=1, H=2, L=256,
+          dk=64, dv=64, C=64, it=BF16, ot=F32, ws=BASE + 600 * MB, ws_bytes=1 << 40):
+    return lib.deltanet_gated_chunk_fwd(q, k, v, alpha, beta, S0, o, Sf, B, H, L, dk, dv, C, it,
+                                        ot, ws, ws_bytes, None)
+
+
+def test_gated_chunk_fwd_validation(lib):
+    assert _gfwd(lib, alpha=None) == NULL
+    assert _gfwd(lib, q=None) == NULL
+    assert _gfwd(lib, B=0) == SHAPE
+    assert _gfwd(lib, dk=96) == UNSUP
+    assert _gfwd(lib, alpha=BASE + 800 * MB + 4) == ALIGN
+    assert _gfwd(lib, o=BASE + 800 * MB) == ALIAS      # o overlaps alpha
+    assert _gfwd(lib, Sf=BASE + 800 * MB) == ALIAS     # S_final overlaps alpha
+    assert _gfwd(lib, ws=BASE + 800 * MB) == ALIAS     # workspace overlaps alpha
+    plain = lib.deltanet_chunk_fwd_workspace_bytes(1, 2, 256, 64, 64, 64, BF16)
+    need = lib.deltanet_gated_chunk_fwd_workspace_bytes(1, 2, 256, 64, 64, 64, BF16)
+    assert need == plain + 1 * 2 * 256 * 4            # plus one log-decay per token
+    assert _gfwd(lib, ws_bytes=need - 1) == WS
+    assert lib.deltanet_gated_chunk_fwd_workspace_bytes(1, 2, 256, 64, 64, 48, BF16) == 0
+    assert lib.deltanet_last_hip_error() == 0
+
+
+def _gdec(lib, alpha=BASE + 800 * MB, q=BASE, k=BASE + 100 * MB, v=BASE + 200 * MB,
+          beta=BASE + 300 * MB, S=BASE + 400 * MB, o=BASE + 900 * MB, B=2, H=3, dk=128, dv=128,
+          it=BF16, ot=F32):
+    return lib.deltanet_gated_decode_step(q, k, v, alpha, beta, S, o, B, H, dk, dv, it, ot, None)
+
+
+def test_gated_decode_validation(lib):
+    assert _gdec(lib, alpha=None) == NULL
+    assert _gdec(lib, S=None) == NULL
+    assert _gdec(lib, dk=100) == UNSUP
+    assert _gdec(lib, alpha=BASE + 800 * MB + 8) == ALIGN
+    assert _gdec(lib, o=BASE + 800 * MB) == ALIAS     # o overlaps alpha
+    assert _gdec(lib, S=BASE + 800 * MB) == ALIAS     # S overlaps alpha
+    assert lib.deltanet_last_hip_error() == 0

@@ -1,0 +1,157 @@
+"""Gated (Gated DeltaNet) chunked forward and decode step on the GPU, through
+the C ABI, against the fp64 gated oracle."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from deltanet_delta_rule_chunk_amd import inputs as I
+from deltanet_delta_rule_chunk_amd.binding import chunk_fwd, gated_chunk_fwd, gated_decode_step
+from oracle import gated_delta_rule_decode_step, gated_delta_rule_forward
+from parity import assert_parity, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _note(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _run(x, alpha, C, out_dtype=torch.float32):
+    g = {k: (None if t is None else t.to(DEV)) for k, t in x.items()}
+    o, S = gated_chunk_fwd(g["q"], g["k"], g["v"], alpha.to(DEV), g["beta"], g["S0"], C,
+                           out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o.cpu(), S.cpu()
+
+
+def _oracle(x, alpha, heads=None):
+    sel = (lambda t: t) if heads is None else (lambda t: t[[b for b, _ in heads], [h for _, h in heads]][None])
+    q, k, v, beta = (sel(to64(x[n])) for n in ("q", "k", "v", "beta"))
+    S0 = None if x["S0"] is None else sel(to64(x["S0"]))
+    return gated_delta_rule_forward(q, k, v, sel(to64(alpha)), beta, S0)
+
+
+SMALL = [
+    # name, dtype, B, H, L, dk, dv, C, S0
+    ("f32_d64_C64_L256", "f32", 1, 2, 256, 64, 64, 64, False),
+    ("f32_d128_C128_ragged", "f32", 1, 2, 300, 128, 128, 128, True),
+    ("f32_dk64_dv128_ragged", "f32", 2, 1, 200, 64, 128, 64, True),
+    ("bf16_dk128_dv64_C128_ragged", "bf16", 1, 3, 333, 128, 64, 128, True),
+    ("bf16_d64_C64_ragged", "bf16", 2, 2, 64 * 5 + 7, 64, 64, 64, False),
+    ("bf16_d128_C64_S0", "bf16", 1, 2, 640, 128, 128, 64, True),
+    ("bf16_d128_C128", "bf16", 1, 2, 512, 128, 128, 128, True),
+    ("bf16_dk64_dv128_C128", "bf16", 1, 2, 384, 64, 128, 128, True),
+    ("bf16_L_below_C", "bf16", 1, 2, 37, 128, 128, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: c[0])
+def test_gated_small_parity(gpu_lib, case):
+    name, dt, B, H, L, dk, dv, C, s0 = case
+    _note(f"[gated] {name}")
+    w = I.ChunkWorkload(name, B, H, L, dk, dv, C, dt, s0_std=0.1 if s0 else None)
+    x = I.make_chunk_inputs(w, seed=21)
+    alpha = I.make_chunk_alpha(w, seed=21)
+    o, S = _run(x, alpha, C)
+    o_ref, S_ref = _oracle(x, alpha)
+    assert_parity(o, o_ref, dt, f"{name} o")
+    assert_parity(S, S_ref, dt, f"{name} S_final")
+
+
+@pytest.mark.parametrize("dt,C", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_gated_alpha_one_equals_plain(gpu_lib, dt, C):
+    """alpha = 1 is the plain delta rule: every decay factor is exactly 1.
+    On the matrix-core (bf16) path the gated kernels then reproduce the plain
+    kernels' bits.  The fp32 vector-ALU scan is compiled to a different
+    multiply-add grouping once the decay multiplies are present (the plain
+    one folds its sums into one fused chain), so there the two agree to
+    rounding: measured 2e-7 of max|o|, checked at 2e-6."""
+    w = I.ChunkWorkload("a1", 1, 2, 3 * C + 5, 128, 128, C, dt, s0_std=0.1)
+    x = I.make_chunk_inputs(w, seed=3)
+    g = {k: t.to(DEV) for k, t in x.items()}
+    ones = torch.ones_like(g["beta"])
+    o1, S1 = gated_chunk_fwd(g["q"], g["k"], g["v"], ones, g["beta"], g["S0"], C)
+    o2, S2 = chunk_fwd(g["q"], g["k"], g["v"], g["beta"], g["S0"], C)
+    torch.cuda.synchronize()
+    if dt == "bf16":
+        assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    else:
+        assert float((o1 - o2).abs().max()) <= 2e-6 * float(o2.abs().max())
+        assert float((S1 - S2).abs().max()) <= 2e-6 * float(S2.abs().max())
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_gated_wipes_and_mixed_decays(gpu_lib, dt):
+    """Exact zeros (full wipes), exact ones and small decays mixed within
+    chunks, against the oracle (which applies alpha = 0 exactly)."""
+    w = I.ChunkWorkload("wipe", 1, 2, 330, 128, 128, 128 if dt == "bf16" else 64, dt, s0_std=0.1)
+    x = I.make_chunk_inputs(w, seed=4)
+    alpha = I.make_chunk_alpha(w, seed=4)
+    alpha[:, :, ::17] = 0.0
+    alpha[:, :, 5::11] = 1.0
+    alpha[:, 1, 40:60] = 0.05
+    o, S = _run(x, alpha, w.C)
+    o_ref, S_ref = _oracle(x, alpha)
+    assert_parity(o, o_ref, dt, "o")
+    assert_parity(S, S_ref, dt, "S_final")
+
+
+def test_gated_long_context(gpu_lib):
+    """The long-context shape (B=1, H=32, L=65536, d=128, C=128) with the gate,
+    at full size on the GPU; oracle on two sampled heads."""
+    w = I.WORKLOADS[3]
+    _note(f"[gated] {w.name}")
+    x = I.make_chunk_inputs(w, seed=0)
+    alpha = I.make_chunk_alpha(w, seed=0)
+    o, S = _run(x, alpha, w.C)
+    assert torch.isfinite(o).all() and torch.isfinite(S).all()
+    heads = [(0, 5), (0, 26)]
+    o_ref, S_ref = _oracle(x, alpha, heads)
+    e = assert_parity(o[0, [5, 26]][None], o_ref, "bf16", "o")
+    assert_parity(S[0, [5, 26]][None], S_ref, "bf16", "S_final")
+    _note(f"  o err/RMS = {e:.3e}")
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128)])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_gated_decode_small(gpu_lib, dt, dk, dv):
+    w = I.DecodeWorkload("gd", 3, 5, dk, dv, 4, dt, 0.1)
+    S = I.make_decode_state(w, seed=2)
+    S_ref = to64(S)
+    Sg = S.to(DEV)
+    for step in range(w.steps):
+        x = I.make_decode_step_inputs(w, step, seed=2)
+        a = I.make_decode_alpha(w, step, seed=2)
+        if step == 2:
+            a[0] = 0.0
+        o = gated_decode_step(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), a.to(DEV),
+                              x["beta"].to(DEV), Sg)
+        torch.cuda.synchronize()
+        o_ref, S_ref = gated_delta_rule_decode_step(to64(x["q"]), to64(x["k"]), to64(x["v"]),
+                                                    to64(a), to64(x["beta"]), S_ref)
+        assert_parity(o.cpu(), o_ref, dt, f"o step {step}")
+    assert_parity(Sg.cpu(), S_ref, dt, "S")
+
+
+def test_gated_decode_workload_first_steps(gpu_lib):
+    """The decode workload's shape (B=256, H=32, d=128, 512 MiB of state) with
+    the gate, on the full state for the first steps."""
+    w = I.WORKLOADS[4]
+    _note(f"[gated] {w.name}")
+    S = I.make_decode_state(w, seed=0)
+    S_ref = to64(S)
+    Sg = S.to(DEV)
+    for step in range(2):
+        x = I.make_decode_step_inputs(w, step, seed=0)
+        a = I.make_decode_alpha(w, step, seed=0)
+        o = gated_decode_step(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), a.to(DEV),
+                              x["beta"].to(DEV), Sg)
+        torch.cuda.synchronize()
+        o_ref, S_ref = gated_delta_rule_decode_step(to64(x["q"]), to64(x["k"]), to64(x["v"]),
+                                                    to64(a), to64(x["beta"]), S_ref)
+        assert_parity(o.cpu(), o_ref, "bf16", f"o step {step}")
+    assert_parity(Sg.cpu(), S_ref, "bf16", "S")
