@@ -135,6 +135,8 @@ def main(argv=None) -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-gated", action="store_true",
+                    help="skip the gated (Gated DeltaNet) forward and decode measurements")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (the known-size "
                          "reference for the HBM byte counters) and exit")
@@ -270,6 +272,58 @@ def main(argv=None) -> int:
                          "traffic": measured_traffic("decode")},
             "inputs": "8 seeded step inputs cycled; state carried across all steps",
         }
+
+    if not a.no_gated:
+        # The gated form (per-token decay alpha) on the same workloads; a
+        # secondary figure next to the plain path's headline number.
+        print(f"[bench] gated forward {w.name}: {a.steps} steps", file=sys.stderr, flush=True)
+        alpha = inputs.make_chunk_alpha(w, seed=a.seed).to(dev)
+        gws = torch.empty(binding.workspace_bytes(w.B, w.H, w.L, w.d_k, w.d_v, w.C, gated=True),
+                          dtype=torch.uint8, device=dev)
+
+        def gstep():
+            binding.chunk_fwd(g["q"], g["k"], g["v"], g["beta"], None, w.C, o=o, S_final=S_final,
+                              workspace=gws, alpha=alpha)
+
+        for _ in range(a.warmup):
+            gstep()
+        torch.cuda.synchronize()
+        binding.profile_start()
+        ev0.record()
+        for _ in range(a.steps):
+            gstep()
+        ev1.record()
+        torch.cuda.synchronize()
+        gprof = binding.profile_stop()
+        assert torch.isfinite(o).all() and torch.isfinite(S_final).all()
+        ms_g = ev0.elapsed_time(ev1) / a.steps
+        result["gated"] = {
+            "workload": w.name + "_gated", "steps": a.steps, "ms_per_step": ms_g,
+            "tokens_per_s": w.B * w.L / (ms_g * 1e-3),
+            "kernels_ms": {name: tot / n for name, (tot, n) in gprof.items()},
+            "alpha": "sigmoid(N(3, 1)) per token (seeded stream of its own)",
+        }
+        if not a.no_decode:
+            nd = max(1, a.decode_steps // 4)
+            print(f"[bench] gated decode {wd.name}: {nd} steps", file=sys.stderr, flush=True)
+            aring = [inputs.make_decode_alpha(wd, s, seed=a.seed).to(dev) for s in range(8)]
+            binding.profile_start()
+            ev0.record()
+            for s in range(nd):
+                r = ring[s % 8]
+                binding.decode_step(r["q"], r["k"], r["v"], r["beta"], Sd, o=od, alpha=aring[s % 8])
+            ev1.record()
+            torch.cuda.synchronize()
+            gdprof = binding.profile_stop()
+            assert torch.isfinite(od).all()
+            ms_gd = ev0.elapsed_time(ev1) / nd
+            gk = gdprof["decode"][0] / gdprof["decode"][1]
+            gdb = decode_bytes(wd) + wd.B * wd.H * 4
+            result["gated"]["decode"] = {
+                "workload": wd.name + "_gated", "steps": nd, "ms_per_step": ms_gd, "kernel_ms": gk,
+                "tokens_per_s": wd.B / (ms_gd * 1e-3),
+                "pct_hbm_peak": 100.0 * gdb / (gk * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            }
 
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
