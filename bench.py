@@ -40,6 +40,8 @@ KERNEL_SOURCES = {
     "chunk_prep": ["dn_chunk_mfma.hip", "dn_ktile.h", "dn_tfrag.h", "dn_mfma.h", "dn_common.h"],
     "decode": ["dn_decode.hip", "dn_common.h"],
 }
+# The gated instantiations come from the same sources.
+KERNEL_SOURCES.update({"gated_" + k: v for k, v in list(KERNEL_SOURCES.items())})
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
