@@ -144,8 +144,13 @@ __global__ __launch_bounds__(512) void scan_kernel(
   constexpr int NRT = CF::NRT, NSB = CF::NSB, NKB = CF::NKB, NCT = CF::NCT;
   constexpr int RPW = CF::RPW, DPW = CF::DPW, SPT = CF::SPT;
   constexpr int SPLANE = CF::SPLANE, RPLANE = CF::RPLANE, KELEMS = CF::KELEMS;
-  constexpr int TB0 = 2;        // T blocks of a chain wave's first row tile (tiles 0..3)
+  constexpr int TB0 = 2;        // T blocks of a chain wave's first row tile (tiles 0..3) at most
   constexpr int TB1 = NRT / 2;  // ... of its second row tile (tiles NRT-4 .. NRT-1)
+  // Register slots for one chunk's T blocks of a chain wave: row tile rt0's
+  // block cb in slot cb, row tile rt1's block cb in slot NTS - 1 - cb.  The
+  // two tiles of a wave have NRT/2 + 1 blocks together, so every slot is
+  // loaded once and used once, and the indices stay compile-time constants.
+  constexpr int NTS = RPW == 2 ? NRT / 2 + 1 : TB0;
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   uint16_t* const lds = reinterpret_cast<uint16_t*>(smem_raw);
@@ -229,27 +234,19 @@ __global__ __launch_bounds__(512) void scan_kernel(
     // start of the chunk's step (ahead of every other wave's loads of that
     // step) and used in its Delta phase.
     struct TRegs {
-      uint4 h0[TB0], l0[TB0], h1[TB1], l1[TB1];
+      uint4 h[NTS], l[NTS];
     };
     TRegs tA;
-    // Slots past a tile's last block re-read block 0 (unused).
     auto t_load = [&](int cc, TRegs& t) {
       const uint4* tb = Tfrag + ((size_t)bh * nc + cc) * Frag<C>::chunk_u4 + lane;
-      const uint4* p0 = tb + (size_t)Frag<C>::base(rt0) * 128;
 #pragma unroll
-      for (int cb = 0; cb < TB0; ++cb) {
-        const int blk = cb <= rt0 / 2 ? cb : 0;
-        t.h0[cb] = p0[(2 * blk) * 64];
-        t.l0[cb] = p0[(2 * blk + 1) * 64];
-      }
-      if constexpr (RPW == 2) {
-        const uint4* p1 = tb + (size_t)Frag<C>::base(rt1) * 128;
-#pragma unroll
-        for (int cb = 0; cb < TB1; ++cb) {
-          const int blk = cb <= rt1 / 2 ? cb : 0;
-          t.h1[cb] = p1[(2 * blk) * 64];
-          t.l1[cb] = p1[(2 * blk + 1) * 64];
-        }
+      for (int sl = 0; sl < NTS; ++sl) {
+        // (RPW == 1: a slot past the tile's last block re-reads block 0, unused.)
+        const bool first = RPW == 1 || sl <= rt0 / 2;
+        const int blk = RPW == 1 ? (sl <= rt0 / 2 ? sl : 0) : (first ? sl : NTS - 1 - sl);
+        const uint4* p = tb + (size_t)Frag<C>::base(first ? rt0 : rt1) * 128 + (size_t)blk * 128;
+        t.h[sl] = p[0];
+        t.l[sl] = p[64];
       }
     };
 
@@ -346,9 +343,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
         for (int cb = 0; cb < TB0; ++cb) {
           if (cb <= rt0 / 2) {
-            d0 = mfma16(as_bf16x8(tc.h0[cb]), Rh[cb], d0);
-            d1 = mfma16(as_bf16x8(tc.h0[cb]), Rl[cb], d1);
-            d2 = mfma16(as_bf16x8(tc.l0[cb]), Rh[cb], d2);
+            d0 = mfma16(as_bf16x8(tc.h[cb]), Rh[cb], d0);
+            d1 = mfma16(as_bf16x8(tc.h[cb]), Rl[cb], d1);
+            d2 = mfma16(as_bf16x8(tc.l[cb]), Rh[cb], d2);
           }
         }
         if constexpr (RPW == 2) {
@@ -356,9 +353,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
           for (int cb = 0; cb < TB1; ++cb) {
             if (cb <= rt1 / 2) {
-              e0 = mfma16(as_bf16x8(tc.h1[cb]), Rh[cb], e0);
-              e1 = mfma16(as_bf16x8(tc.h1[cb]), Rl[cb], e1);
-              e2 = mfma16(as_bf16x8(tc.l1[cb]), Rh[cb], e2);
+              e0 = mfma16(as_bf16x8(tc.h[NTS - 1 - cb]), Rh[cb], e0);
+              e1 = mfma16(as_bf16x8(tc.h[NTS - 1 - cb]), Rl[cb], e1);
+              e2 = mfma16(as_bf16x8(tc.l[NTS - 1 - cb]), Rh[cb], e2);
             }
           }
           put_split(Dc, RPLANE, fo_d(rt1, g, i16), e0 + e1 + e2);
@@ -613,13 +610,18 @@ __global__ __launch_bounds__(512) void scan_kernel(
       }
     };
 
-    // L2 prefetch: the 64-byte sectors of chunk cc's k, q, v and T data are
+    // L2 prefetch: the 128-byte lines of chunk cc's k, q, v and T data are
     // split over the head's column-slice workgroups (which share an XCD and
-    // its L2); output-wave thread t touches sectors ct + NCT (t + 256 j) with
+    // its L2); output-wave thread t touches lines ct + NCT (t + 256 j) with
     // one dword load each.  The values are folded into pf_acc one chunk later,
     // so the loads never stall anything, and pf_acc is only ever stored under
-    // a condition that is false.
-    constexpr int LK = C * DK / 32, LV = C * DV / 32, LT = (int)(Frag<C>::chunk_u4 / 4);
+    // a condition that is false.  (Whole lines rather than 64-byte sectors:
+    // the kernel runs power-limited, and touching half as many lines was
+    // measured to save ~3.5% of its cycles at the same clock.)
+    constexpr int PFL = 128;                 // line bytes
+    constexpr int EPL = PFL / 2;             // bf16 elements per line
+    constexpr int LK = C * DK / EPL, LV = C * DV / EPL;
+    constexpr int LT = (int)(Frag<C>::chunk_u4 * 16 / PFL);
     constexpr int NLINES = 2 * LK + LV + LT;
     constexpr int NPF = (NLINES / NCT + 255) / 256;
     uint32_t pf_acc = 0, pf_val[NPF];
@@ -633,15 +635,15 @@ __global__ __launch_bounds__(512) void scan_kernel(
         const int n = min(ct + NCT * (tl + 256 * j), NLINES - 1);
         const uint32_t* src;
         if (n < 2 * LK) {
-          const int e = (n % LK) * 32, row = min(e / DK, valid - 1);
+          const int e = (n % LK) * EPL, row = min(e / DK, valid - 1);
           const uint16_t* base = n < LK ? k : q;
           src = reinterpret_cast<const uint32_t*>(base + (t0 + row) * DK + e % DK);
         } else if (n < 2 * LK + LV) {
-          const int e = (n - 2 * LK) * 32, row = min(e / DV, valid - 1);
+          const int e = (n - 2 * LK) * EPL, row = min(e / DV, valid - 1);
           src = reinterpret_cast<const uint32_t*>(v + (t0 + row) * DV + e % DV);
         } else {
           src = reinterpret_cast<const uint32_t*>(Tfrag + ((size_t)bh * nc + cc) * Frag<C>::chunk_u4 +
-                                                  4 * (n - 2 * LK - LV));
+                                                  (PFL / 16) * (n - 2 * LK - LV));
         }
         pf_val[j] = *src;
       }
