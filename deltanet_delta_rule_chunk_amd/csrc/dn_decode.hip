@@ -61,9 +61,10 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
   vf4 s[RPT], sn[RPT];
   load_state(bh, s);
   for (;;) {
-    const int nb = bh + (int)gridDim.x;
-    const bool more = nb < BH;
-    load_state(more ? nb : bh, sn);  // next head's state, in flight meanwhile
+    const long long nbl = (long long)bh + gridDim.x;  // no int overflow near BH = 2^31
+    const bool more = nbl < BH;
+    const int nb = more ? (int)nbl : bh;
+    load_state(nb, sn);  // next head's state, in flight meanwhile
     for (int i = tid; i < DK; i += NT) {
       ks[i] = to_f32(k[(size_t)bh * DK + i]);
       qs[i] = to_f32(q[(size_t)bh * DK + i]);
