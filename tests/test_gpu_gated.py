@@ -10,7 +10,7 @@ import torch
 from deltanet_delta_rule_chunk_amd import inputs as I
 from deltanet_delta_rule_chunk_amd.binding import chunk_fwd, gated_chunk_fwd, gated_decode_step
 from oracle import gated_delta_rule_decode_step, gated_delta_rule_forward
-from parity import assert_parity, to64
+from parity import assert_parity, err_f32, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -155,3 +155,99 @@ def test_gated_decode_workload_first_steps(gpu_lib):
                                                     to64(a), to64(x["beta"]), S_ref)
         assert_parity(o.cpu(), o_ref, "bf16", f"o step {step}")
     assert_parity(Sg.cpu(), S_ref, "bf16", "S")
+
+
+# ---- properties of the gated path that hold at any size -------------------------
+
+def _dev(x):
+    return {k: (None if t is None else t.to(DEV)) for k, t in x.items()}
+
+
+def test_gated_chunk_size_invariance(gpu_lib):
+    """C = 64 and C = 128 compute the same gated recurrence (bf16 inputs)."""
+    w = I.ChunkWorkload("gcinv", 1, 2, 1000, 128, 128, 64, "bf16", s0_std=0.1)
+    g = _dev(I.make_chunk_inputs(w, seed=31))
+    a = I.make_chunk_alpha(w, seed=31).to(DEV)
+    o64, S64 = gated_chunk_fwd(g["q"], g["k"], g["v"], a, g["beta"], g["S0"], 64)
+    o128, S128 = gated_chunk_fwd(g["q"], g["k"], g["v"], a, g["beta"], g["S0"], 128)
+    torch.cuda.synchronize()
+    assert_parity(o64.cpu(), o128.cpu(), "bf16", "o C64 vs C128")
+    assert_parity(S64.cpu(), S128.cpu(), "bf16", "S C64 vs C128")
+
+
+def test_gated_split_invariance(gpu_lib):
+    """Two gated calls chained through S_final -> S0 equal one call (fp32), cut
+    at a chunk boundary and off it: the decay restarts at every chunk start."""
+    w = I.ChunkWorkload("gsplit", 2, 2, 384, 64, 64, 64, "f32", s0_std=0.1)
+    g = _dev(I.make_chunk_inputs(w, seed=32))
+    al = I.make_chunk_alpha(w, seed=32).to(DEV)
+    o, S = gated_chunk_fwd(g["q"], g["k"], g["v"], al, g["beta"], g["S0"], 64)
+    for cut in (128, 150):
+        a = {k: g[k][:, :, :cut].contiguous() for k in ("q", "k", "v", "beta")}
+        b = {k: g[k][:, :, cut:].contiguous() for k in ("q", "k", "v", "beta")}
+        o1, S1 = gated_chunk_fwd(a["q"], a["k"], a["v"], al[:, :, :cut].contiguous(), a["beta"],
+                                 g["S0"], 64)
+        o2, S2 = gated_chunk_fwd(b["q"], b["k"], b["v"], al[:, :, cut:].contiguous(), b["beta"], S1, 64)
+        torch.cuda.synchronize()
+        assert err_f32(torch.cat([o1, o2], 2).cpu(), o.cpu()) < 1e-5
+        assert err_f32(S2.cpu(), S.cpu()) < 1e-5
+
+
+def test_gated_decode_equals_chunk(gpu_lib):
+    """L gated decode steps equal one gated chunked forward over the same L tokens."""
+    w = I.ChunkWorkload("gdvc", 2, 3, 70, 128, 64, 64, "f32", s0_std=0.1)
+    g = _dev(I.make_chunk_inputs(w, seed=33))
+    al = I.make_chunk_alpha(w, seed=33).to(DEV)
+    o, S = gated_chunk_fwd(g["q"], g["k"], g["v"], al, g["beta"], g["S0"], 64)
+    Sd = g["S0"].clone()
+    outs = []
+    for t in range(w.L):
+        outs.append(gated_decode_step(*(g[n][:, :, t].contiguous() for n in ("q", "k", "v")),
+                                      al[:, :, t].contiguous(), g["beta"][:, :, t].contiguous(), Sd))
+    torch.cuda.synchronize()
+    assert err_f32(torch.stack(outs, 2).cpu(), o.cpu()) < 1e-4
+    assert err_f32(Sd.cpu(), S.cpu()) < 1e-4
+
+
+def test_gated_linearity_in_values_and_state(gpu_lib):
+    """For fixed q, k, alpha, beta the gated map (V, S0) -> (O, S_final) is linear."""
+    w = I.ChunkWorkload("glin", 1, 2, 200, 64, 64, 64, "f32", s0_std=0.1)
+    g1 = _dev(I.make_chunk_inputs(w, seed=34))
+    g2 = _dev(I.make_chunk_inputs(w, seed=35))
+    al = I.make_chunk_alpha(w, seed=34).to(DEV)
+    a, b = 0.75, -1.5
+    v = (a * g1["v"] + b * g2["v"]).contiguous()
+    S0 = (a * g1["S0"] + b * g2["S0"]).contiguous()
+    o, S = gated_chunk_fwd(g1["q"], g1["k"], v, al, g1["beta"], S0, 64)
+    o1, S1 = gated_chunk_fwd(g1["q"], g1["k"], g1["v"], al, g1["beta"], g1["S0"], 64)
+    o2, S2 = gated_chunk_fwd(g1["q"], g1["k"], g2["v"], al, g1["beta"], g2["S0"], 64)
+    torch.cuda.synchronize()
+    assert err_f32((a * o1 + b * o2).cpu(), o.cpu()) < 1e-4
+    assert err_f32((a * S1 + b * S2).cpu(), S.cpu()) < 1e-4
+
+
+def test_gated_bitwise_determinism(gpu_lib):
+    w = I.ChunkWorkload("gdet", 2, 4, 1024, 128, 128, 128, "bf16", s0_std=0.1)
+    g = _dev(I.make_chunk_inputs(w, seed=36))
+    al = I.make_chunk_alpha(w, seed=36).to(DEV)
+    o1, S1 = gated_chunk_fwd(g["q"], g["k"], g["v"], al, g["beta"], g["S0"], 128)
+    o2, S2 = gated_chunk_fwd(g["q"], g["k"], g["v"], al, g["beta"], g["S0"], 128)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_gated_decay_only_on_gpu(gpu_lib):
+    """beta = 0: only the decay acts, S_L = (alpha_1 ... alpha_L) S0 and
+    o_t = (alpha_1 ... alpha_t) q_t S0 (bf16 path, long enough for 3 chunks)."""
+    w = I.ChunkWorkload("gdecay", 1, 2, 300, 128, 128, 128, "bf16", s0_std=0.1)
+    g = _dev(I.make_chunk_inputs(w, seed=37))
+    al = I.make_chunk_alpha(w, seed=37)
+    al = 0.5 + 0.5 * al                      # keep the products away from underflow
+    beta = torch.zeros_like(g["beta"])
+    o, S = gated_chunk_fwd(g["q"], g["k"], g["v"], al.to(DEV), beta, g["S0"], 128)
+    torch.cuda.synchronize()
+    cp = np.cumprod(to64(al), axis=-1)
+    want_o = cp[..., None] * (to64(g["q"]) @ to64(g["S0"]))
+    want_S = cp[:, :, -1, None, None] * to64(g["S0"])
+    assert_parity(o.cpu(), want_o, "bf16", "o")
+    assert_parity(S.cpu(), want_S, "bf16", "S")
