@@ -43,6 +43,7 @@ KERNEL_SOURCES = {
 # The gated instantiations come from the same sources.
 KERNEL_SOURCES.update({"gated_" + k: v for k, v in list(KERNEL_SOURCES.items())})
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters.json")
 
 
 def kernel_source_hash(kernel):
@@ -68,6 +69,21 @@ def measured_traffic(kernel):
     if rec.get("source_sha256") != kernel_source_hash(kernel):
         return None
     return rec["bytes_per_launch"]
+
+
+def measured_mfma(kernel):
+    """Executed bf16 MFMA flops per launch of `kernel` and its MFMA-busy share
+    from the committed rocprofv3 counter summary
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, SQ_VALU_MFMA_BUSY_CYCLES), or None
+    when there is none or the kernel's sources changed since it was taken."""
+    try:
+        with open(MFMA_FILE) as fh:
+            rec = json.load(fh)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    return rec
 
 
 def chunk_bytes(w, in_bytes=2, out_bytes=4, s0=False):
@@ -239,6 +255,19 @@ def main(argv=None) -> int:
                      "traffic": measured_traffic(dom)},
         "wall_s_timed": t_wall,
     }
+    # The matrix-core work the kernels really issue (split-precision operands,
+    # the delta rule's three state products, per-slice diagonal blocks) is
+    # well above the pages' cost model: executed flops from the counters,
+    # rate from this run's kernel times.
+    ex = {}
+    for kname in ("chunk_prep", "chunk_scan"):
+        rec = measured_mfma(kname)
+        if rec is not None:
+            tf = rec["bf16_flops"] / (kern[kname] * 1e-3) / 1e12
+            ex[kname] = {"bf16_flops_per_launch": rec["bf16_flops"], "tflops": tf,
+                         "pct_bf16_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS,
+                         "mfma_busy_pct_counters": rec["mfma_busy_pct"]}
+    result["executed_mfma"] = ex or None
 
     if not a.no_decode:
         wd = inputs.WORKLOADS[4]
