@@ -153,6 +153,8 @@ def main(argv=None) -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip timing the two smaller chunked workloads")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the gated (Gated DeltaNet) forward and decode measurements")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -355,6 +357,37 @@ def main(argv=None) -> int:
                 "tokens_per_s": wd.B / (ms_gd * 1e-3),
                 "pct_hbm_peak": 100.0 * gdb / (gk * 1e-3) / 1e9 / PEAK_HBM_GBS,
             }
+
+    if not a.no_other_workloads:
+        # The other chunked workloads (parity cases; timed here for reference).
+        others = []
+        for wo in (inputs.WORKLOADS[1], inputs.WORKLOADS[2]):
+            print(f"[bench] {wo.name}: {a.steps} steps", file=sys.stderr, flush=True)
+            xo = {k: (None if t is None else t.to(dev)) for k, t in inputs.make_chunk_inputs(wo, seed=a.seed).items()}
+            oo = torch.empty(wo.B, wo.H, wo.L, wo.d_v, device=dev, dtype=torch.float32)
+            So = torch.empty(wo.B, wo.H, wo.d_k, wo.d_v, device=dev, dtype=torch.float32)
+            wso = torch.empty(binding.workspace_bytes(wo.B, wo.H, wo.L, wo.d_k, wo.d_v, wo.C),
+                              dtype=torch.uint8, device=dev)
+
+            def ostep():
+                binding.chunk_fwd(xo["q"], xo["k"], xo["v"], xo["beta"], xo["S0"], wo.C, o=oo, S_final=So,
+                                  workspace=wso)
+
+            for _ in range(a.warmup):
+                ostep()
+            torch.cuda.synchronize()
+            ev0.record()
+            for _ in range(a.steps):
+                ostep()
+            ev1.record()
+            torch.cuda.synchronize()
+            assert torch.isfinite(oo).all()
+            mso = ev0.elapsed_time(ev1) / a.steps
+            fo = model_flops(wo)
+            others.append({"workload": wo.name, "ms_per_step": mso, "tokens_per_s": wo.B * wo.L / (mso * 1e-3),
+                           "model_tflops": fo / (mso * 1e-3) / 1e12,
+                           "path_alg_gbs": chunk_bytes(wo, s0=wo.s0_std is not None) / (mso * 1e-3) / 1e9})
+        result["other_workloads"] = others
 
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
