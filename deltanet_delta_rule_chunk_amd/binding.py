@@ -27,10 +27,11 @@ STATUS_NAMES = {0: "DN_OK", 1: "DN_ERR_NULL_ARG", 2: "DN_ERR_BAD_SHAPE", 3: "DN_
 # Every symbol include/deltanet.h declares.
 EXPORTS = ("deltanet_chunk_fwd", "deltanet_chunk_fwd_workspace_bytes", "deltanet_decode_step",
            "deltanet_gated_chunk_fwd", "deltanet_gated_chunk_fwd_workspace_bytes",
-           "deltanet_gated_decode_step",
+           "deltanet_gated_decode_step", "deltanet_feature_prep", "deltanet_chunk_fwd_features",
+           "deltanet_chunk_fwd_features_workspace_bytes", "deltanet_decode_step_features",
            "deltanet_status_string", "deltanet_last_hip_error", "deltanet_version",
            "deltanet_profile_start", "deltanet_profile_stop")
-PROFILE_SLOTS = ("chunk_prep", "chunk_scan", "decode")
+PROFILE_SLOTS = ("chunk_prep", "chunk_scan", "decode", "features")
 
 _lib = None
 
@@ -65,6 +66,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.deltanet_gated_chunk_fwd_workspace_bytes.restype = sz
     lib.deltanet_gated_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     lib.deltanet_gated_decode_step.restype = i
+    lib.deltanet_feature_prep.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.deltanet_feature_prep.restype = i
+    lib.deltanet_chunk_fwd_features.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
+                                                i, i, vp, sz, vp]
+    lib.deltanet_chunk_fwd_features.restype = i
+    lib.deltanet_chunk_fwd_features_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+    lib.deltanet_chunk_fwd_features_workspace_bytes.restype = sz
+    lib.deltanet_decode_step_features.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.deltanet_decode_step_features.restype = i
     lib.deltanet_status_string.argtypes = [i]
     lib.deltanet_status_string.restype = ctypes.c_char_p
     lib.deltanet_last_hip_error.argtypes = []
@@ -120,10 +130,38 @@ def _stream(device: torch.device, stream) -> int:
 
 
 def workspace_bytes(B: int, H: int, L: int, d_k: int, d_v: int, C: int,
-                    in_dtype: torch.dtype = torch.bfloat16, gated: bool = False) -> int:
+                    in_dtype: torch.dtype = torch.bfloat16, gated: bool = False,
+                    features: bool = False) -> int:
     lib = load()
+    if features:
+        return int(lib.deltanet_chunk_fwd_features_workspace_bytes(B, H, L, d_k, d_v, C,
+                                                                    _code(in_dtype), int(gated)))
     fn = lib.deltanet_gated_chunk_fwd_workspace_bytes if gated else lib.deltanet_chunk_fwd_workspace_bytes
     return int(fn(B, H, L, d_k, d_v, C, _code(in_dtype)))
+
+
+def feature_prep(q_raw: torch.Tensor, k_raw: torch.Tensor, beta_logit: torch.Tensor, *,
+                 in_place: bool = False, stream=None
+                 ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """The layer's feature maps: ``normalise(silu(q_raw))``, ``normalise(silu(k_raw))``
+    (``[B,H,L,d_k]``, same dtype as the inputs) and ``sigmoid(beta_logit)``
+    (``[B,H,L]`` fp32), by ``deltanet_feature_prep``.  ``in_place`` writes the
+    results over the inputs."""
+    lib = load()
+    B, H, L, d_k = q_raw.shape
+    dev = q_raw.device
+    _check(q_raw, "q_raw", (B, H, L, d_k), device=dev)
+    _check(k_raw, "k_raw", (B, H, L, d_k), q_raw.dtype, dev)
+    _check(beta_logit, "beta_logit", (B, H, L), torch.float32, dev)
+    if in_place:
+        qh, kh, b = q_raw, k_raw, beta_logit
+    else:
+        qh, kh, b = torch.empty_like(q_raw), torch.empty_like(k_raw), torch.empty_like(beta_logit)
+    st = lib.deltanet_feature_prep(_ptr(q_raw), _ptr(k_raw), _ptr(beta_logit), _ptr(qh), _ptr(kh),
+                                   _ptr(b), B, H, L, d_k, _code(q_raw.dtype), _stream(dev, stream))
+    if st != DN_OK:
+        _raise(lib, st, "deltanet_feature_prep")
+    return qh, kh, b
 
 
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
@@ -131,13 +169,15 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
               out_dtype: torch.dtype = torch.float32, o: Optional[torch.Tensor] = None,
               S_final: Optional[torch.Tensor] = None, want_state: bool = True,
               workspace: Optional[torch.Tensor] = None, stream=None,
-              alpha: Optional[torch.Tensor] = None
+              alpha: Optional[torch.Tensor] = None, features: bool = False
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked delta-rule forward.  q,k ``[B,H,L,d_k]``, v ``[B,H,L,d_v]`` (fp32 or
     bf16, same dtype), beta ``[B,H,L]`` fp32, S0 ``[B,H,d_k,d_v]`` fp32 or None.
     With ``alpha`` (``[B,H,L]`` fp32) the gated form runs
-    (``deltanet_gated_chunk_fwd``).  Returns ``(o, S_final)``; S_final is None
-    when ``want_state`` is False."""
+    (``deltanet_gated_chunk_fwd``).  With ``features`` q, k are the raw
+    projections and beta the logits, mapped by the layer's feature maps first
+    (``deltanet_chunk_fwd_features``).  Returns ``(o, S_final)``; S_final is
+    None when ``want_state`` is False."""
     lib = load()
     B, H, L, d_k = q.shape
     d_v = v.shape[-1]
@@ -158,11 +198,19 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     if S_final is not None:
         _check(S_final, "S_final", (B, H, d_k, d_v), torch.float32, dev)
     in_code = _code(q.dtype)
-    need = workspace_bytes(B, H, L, d_k, d_v, C, q.dtype, gated=alpha is not None)
+    need = workspace_bytes(B, H, L, d_k, d_v, C, q.dtype, gated=alpha is not None,
+                           features=features)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if alpha is None:
+    if features:
+        st = lib.deltanet_chunk_fwd_features(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                             _ptr(S0), _ptr(o), _ptr(S_final), B, H, L, d_k, d_v,
+                                             C, in_code, _code(out_dtype), _ptr(workspace),
+                                             ws_bytes, _stream(dev, stream))
+        if st != DN_OK:
+            _raise(lib, st, "deltanet_chunk_fwd_features")
+    elif alpha is None:
         st = lib.deltanet_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(o),
                                     _ptr(S_final), B, H, L, d_k, d_v, C, in_code,
                                     _code(out_dtype), _ptr(workspace), ws_bytes,
@@ -190,10 +238,12 @@ def gated_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: to
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
                 S: torch.Tensor, *, out_dtype: torch.dtype = torch.float32,
                 o: Optional[torch.Tensor] = None, stream=None,
-                alpha: Optional[torch.Tensor] = None) -> torch.Tensor:
+                alpha: Optional[torch.Tensor] = None, features: bool = False) -> torch.Tensor:
     """One decode step; updates S ``[B,H,d_k,d_v]`` in place and returns o
     ``[B,H,d_v]`` = q S_new.  With ``alpha`` (``[B,H]`` fp32) the gated step
-    runs (``deltanet_gated_decode_step``)."""
+    runs (``deltanet_gated_decode_step``).  With ``features`` q, k are the raw
+    projections and beta the logits, mapped inside the step's kernel
+    (``deltanet_decode_step_features``)."""
     lib = load()
     B, H, d_k = q.shape
     d_v = v.shape[-1]
@@ -206,14 +256,21 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.T
     if o is None:
         o = torch.empty((B, H, d_v), dtype=out_dtype, device=dev)
     _check(o, "o", (B, H, d_v), out_dtype, dev)
-    if alpha is None:
+    if alpha is not None:
+        _check(alpha, "alpha", (B, H), torch.float32, dev)
+    if features:
+        st = lib.deltanet_decode_step_features(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                               _ptr(S), _ptr(o), B, H, d_k, d_v, _code(q.dtype),
+                                               _code(out_dtype), _stream(dev, stream))
+        if st != DN_OK:
+            _raise(lib, st, "deltanet_decode_step_features")
+    elif alpha is None:
         st = lib.deltanet_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(o),
                                       B, H, d_k, d_v, _code(q.dtype), _code(out_dtype),
                                       _stream(dev, stream))
         if st != DN_OK:
             _raise(lib, st, "deltanet_decode_step")
     else:
-        _check(alpha, "alpha", (B, H), torch.float32, dev)
         st = lib.deltanet_gated_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                             _ptr(S), _ptr(o), B, H, d_k, d_v, _code(q.dtype),
                                             _code(out_dtype), _stream(dev, stream))

@@ -18,7 +18,7 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kVersion = 200;  // 0.2.0
+constexpr int kVersion = 300;  // 0.3.0
 
 int hip_fail(hipError_t e) {
   g_last_hip_error = static_cast<int>(e);
@@ -90,15 +90,38 @@ hipEvent_t prof_event() {
   return r == hipSuccess ? e : nullptr;
 }
 
-// Shared body of the plain (alpha = null) and gated chunked forwards.
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace of the chunked forward: the chunk kernels' scratch, then (with
+// the feature maps) the mapped q, k and beta, each 256-byte aligned.
+struct WsLayout {
+  size_t core, qk, beta, total;
+};
+WsLayout ws_layout(int B, int H, int L, int d_k, int d_v, int C, int in_dtype, bool gated,
+                   bool features, const ChunkSizes& s) {
+  WsLayout w{dn::chunk_workspace_bytes(B, H, L, d_k, d_v, C, in_dtype, gated), 0, 0, 0};
+  if (features) {
+    w.core = align256(w.core);
+    w.qk = align256(s.qk);
+    w.beta = align256(s.beta);
+  }
+  w.total = w.core + 2 * w.qk + w.beta;
+  return w;
+}
+
+// Shared body of the chunked forwards: plain (alpha = null) or gated, on
+// mapped operands or (features) on the raw projections, in which case q, k
+// are the raw q, k and beta holds the logits.
 int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alpha,
                    const float* beta, const float* S0, void* o, float* S_final, int B, int H,
                    int L, int d_k, int d_v, int C, int in_dtype, int out_dtype, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream) {
+                   size_t workspace_bytes, hipStream_t stream, bool features = false) {
   ChunkSizes s;
   int st = check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, out_dtype, &s);
   if (st != DN_OK) return st;
   if (L > 0 && (!q || !k || !v || !beta || !o)) return DN_ERR_NULL_ARG;
+  if (features && (long long)B * H * L > dn::feature_max_rows(d_k, in_dtype))
+    return DN_ERR_UNSUPPORTED;
   const bool gated = alpha != nullptr;
   const void* ptrs[] = {q, k, v, alpha, beta, S0, o, S_final, workspace};
   for (const void* p : ptrs)
@@ -106,7 +129,8 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alp
 
   const Span sq{q, s.qk}, sk{k, s.qk}, sv{v, s.v}, sa{alpha, s.beta}, sb{beta, s.beta};
   const Span ss0{S0, s.state}, so{o, s.o}, ssf{S_final, s.state};
-  const size_t need = dn::chunk_workspace_bytes(B, H, L, d_k, d_v, C, in_dtype, gated);
+  const WsLayout wl = ws_layout(B, H, L, d_k, d_v, C, in_dtype, gated, features, s);
+  const size_t need = wl.total;
   const Span sw{workspace, workspace ? need : 0};
   for (Span in : {sq, sk, sv, sa, sb, ss0})
     if (overlap(so, in) || (in.p != S0 && overlap(ssf, in))) return DN_ERR_ALIASING;
@@ -122,9 +146,22 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alp
     hipError_t e = hipMallocAsync(&ws, need, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
-  dn::ChunkArgs a{q, k, v, alpha, beta, S0, o, S_final, B, H, L, d_k, d_v, C, in_dtype,
-                  out_dtype, ws, stream};
-  hipError_t e = dn::launch_chunk_fwd(a);
+  hipError_t e = hipSuccess;
+  if (features && L > 0) {
+    char* base = static_cast<char*>(ws) + wl.core;
+    void *qh = base, *kh = base + wl.qk;
+    float* bh = reinterpret_cast<float*>(base + 2 * wl.qk);
+    dn::FeatureArgs f{q, k, beta, qh, kh, bh, (long long)B * H * L, d_k, in_dtype, stream};
+    e = dn::launch_features(f);
+    q = qh;
+    k = kh;
+    beta = bh;
+  }
+  if (e == hipSuccess) {
+    dn::ChunkArgs a{q, k, v, alpha, beta, S0, o, S_final, B, H, L, d_k, d_v, C, in_dtype,
+                    out_dtype, ws, stream};
+    e = dn::launch_chunk_fwd(a);
+  }
   if (own_ws) {
     hipError_t f = hipFreeAsync(ws, stream);
     if (e == hipSuccess) e = f;
@@ -136,7 +173,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alp
 // Shared body of the plain (alpha = null) and gated decode steps.
 int decode_impl(const void* q, const void* k, const void* v, const float* alpha,
                 const float* beta, float* S, void* o, int B, int H, int d_k, int d_v,
-                int in_dtype, int out_dtype, hipStream_t stream) {
+                int in_dtype, int out_dtype, hipStream_t stream, bool features = false) {
   if (B < 1 || H < 1 || d_k < 1 || d_v < 1) return DN_ERR_BAD_SHAPE;
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return DN_ERR_UNSUPPORTED;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return DN_ERR_UNSUPPORTED;
@@ -155,7 +192,8 @@ int decode_impl(const void* q, const void* k, const void* v, const float* alpha,
   for (Span in : {sq, sk, sv, sa, sb})
     if (overlap(sS, in)) return DN_ERR_ALIASING;
 
-  dn::DecodeArgs a{q, k, v, alpha, beta, S, o, B, H, d_k, d_v, in_dtype, out_dtype, stream};
+  dn::DecodeArgs a{q, k, v, alpha, beta, S, o, B, H, d_k, d_v, in_dtype, out_dtype, stream,
+                   features};
   hipError_t e = dn::launch_decode(a);
   if (e != hipSuccess) return hip_fail(e);
   return DN_OK;
@@ -233,10 +271,63 @@ const char* deltanet_status_string(int status) {
       return "unsupported configuration (d_k, d_v in {64,128}; C in {64,128}; dtype f32/bf16; B*H <= 65535)";
     case DN_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
     case DN_ERR_ALIASING: return "an output overlaps an input";
-    case DN_ERR_WORKSPACE: return "workspace smaller than deltanet_chunk_fwd_workspace_bytes()";
+    case DN_ERR_WORKSPACE: return "workspace smaller than the matching *_workspace_bytes() query";
     case DN_ERR_HIP: return "HIP runtime error (see deltanet_last_hip_error)";
     default: return "unknown status";
   }
+}
+
+int deltanet_feature_prep(const void* q_raw, const void* k_raw, const float* beta_logit,
+                          void* q_hat, void* k_hat, float* beta, int B, int H, int L, int d_k,
+                          int dtype, hipStream_t stream) {
+  if (B < 1 || H < 1 || L < 0 || d_k < 1) return DN_ERR_BAD_SHAPE;
+  if (!dtype_ok(dtype) || !dim_ok(d_k)) return DN_ERR_UNSUPPORTED;
+  const long long rows = (long long)B * H * L;
+  if (rows > dn::feature_max_rows(d_k, dtype)) return DN_ERR_UNSUPPORTED;
+  if (rows == 0) return DN_OK;
+  if (!q_raw || !k_raw || !beta_logit || !q_hat || !k_hat || !beta) return DN_ERR_NULL_ARG;
+  const void* ptrs[] = {q_raw, k_raw, beta_logit, q_hat, k_hat, beta};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return DN_ERR_MISALIGNED;
+  const size_t nqk = (size_t)rows * d_k * dtype_size(dtype), nb = (size_t)rows * sizeof(float);
+  const Span in[] = {{q_raw, nqk}, {k_raw, nqk}, {beta_logit, nb}};
+  const Span out[] = {{q_hat, nqk}, {k_hat, nqk}, {beta, nb}};
+  // An output may be its own input (the maps run in place) and must
+  // overlap nothing else.
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlap(out[i], in[j]) && !(i == j && out[i].p == in[j].p)) return DN_ERR_ALIASING;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(out[i], out[j])) return DN_ERR_ALIASING;
+  }
+  dn::FeatureArgs f{q_raw, k_raw, beta_logit, q_hat, k_hat, beta, rows, d_k, dtype, stream};
+  hipError_t e = dn::launch_features(f);
+  if (e != hipSuccess) return hip_fail(e);
+  return DN_OK;
+}
+
+size_t deltanet_chunk_fwd_features_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
+                                                   int in_dtype, int gated) {
+  ChunkSizes s;
+  if (check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, DN_F32, &s) != DN_OK) return 0;
+  return ws_layout(B, H, L, d_k, d_v, C, in_dtype, gated != 0, true, s).total;
+}
+
+int deltanet_chunk_fwd_features(const void* q_raw, const void* k_raw, const void* v,
+                                const float* alpha, const float* beta_logit, const float* S0,
+                                void* o, float* S_final, int B, int H, int L, int d_k, int d_v,
+                                int C, int in_dtype, int out_dtype, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return chunk_fwd_impl(q_raw, k_raw, v, alpha, beta_logit, S0, o, S_final, B, H, L, d_k, d_v, C,
+                        in_dtype, out_dtype, workspace, workspace_bytes, stream, true);
+}
+
+int deltanet_decode_step_features(const void* q_raw, const void* k_raw, const void* v,
+                                  const float* alpha, const float* beta_logit, float* S, void* o,
+                                  int B, int H, int d_k, int d_v, int in_dtype, int out_dtype,
+                                  hipStream_t stream) {
+  return decode_impl(q_raw, k_raw, v, alpha, beta_logit, S, o, B, H, d_k, d_v, in_dtype,
+                     out_dtype, stream, true);
 }
 
 size_t deltanet_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,

@@ -24,15 +24,42 @@
 // the write stream interleave with the read stream at a higher HBM rate
 // (measured: 78% of peak for this form against 63% with one 256-thread
 // workgroup per head and plain stores).
+//
+// With FEAT the step also applies the layer's feature maps to its inputs
+// (same page and section: q, k = normalise(silu(.)), beta = sigmoid(logit);
+// dn_features.h): waves 0 and 1 map k and q while the others stage v, and
+// the mapped q, k are held in the input dtype, as the streaming feature
+// kernel stores them for the chunked path.  It adds no memory traffic.
 
 #include "dn_common.h"
+#include "dn_features.h"
 #include "dn_launch.h"
 
 namespace dn {
 
 typedef float vf4 __attribute__((ext_vector_type(4)));
 
-template <int DK, int DV, typename IT, typename OT, bool GATED>
+// One head's q or k row through the feature maps by one wave: silu, the
+// row's norm by a wave reduction, the scaled values rounded to the input
+// dtype, into LDS.
+template <int DK, typename IT>
+__device__ __forceinline__ void map_row_to_lds(const IT* __restrict__ x, float* dst, int lane) {
+  constexpr int E = DK / 64;
+  float f[E];
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    f[e] = fast_silu(to_f32(x[lane + 64 * e]));
+    ss += f[e] * f[e];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  const float r = inv_row_norm(ss);
+#pragma unroll
+  for (int e = 0; e < E; ++e) dst[lane + 64 * e] = to_f32(from_f32<IT>(f[e] * r));
+}
+
+template <int DK, int DV, typename IT, typename OT, bool GATED, bool FEAT>
 __global__ __launch_bounds__(512) void decode_step_kernel(
     const IT* __restrict__ q, const IT* __restrict__ k, const IT* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, float* __restrict__ S,
@@ -65,11 +92,20 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
     const bool more = nbl < BH;
     const int nb = more ? (int)nbl : bh;
     load_state(nb, sn);  // next head's state, in flight meanwhile
-    for (int i = tid; i < DK; i += NT) {
-      ks[i] = to_f32(k[(size_t)bh * DK + i]);
-      qs[i] = to_f32(q[(size_t)bh * DK + i]);
+    if (FEAT) {
+      static_assert(DK % 64 == 0, "one wave per feature row");
+      if (tid < 64)
+        map_row_to_lds<DK>(k + (size_t)bh * DK, ks, tid);
+      else if (tid < 128)
+        map_row_to_lds<DK>(q + (size_t)bh * DK, qs, tid - 64);
+      for (int i = tid; i < DV; i += NT) vs[i] = to_f32(v[(size_t)bh * DV + i]);
+    } else {
+      for (int i = tid; i < DK; i += NT) {
+        ks[i] = to_f32(k[(size_t)bh * DK + i]);
+        qs[i] = to_f32(q[(size_t)bh * DK + i]);
+      }
+      for (int i = tid; i < DV; i += NT) vs[i] = to_f32(v[(size_t)bh * DV + i]);
     }
-    for (int i = tid; i < DV; i += NT) vs[i] = to_f32(v[(size_t)bh * DV + i]);
     __syncthreads();
 
     if (tid < 64) {  // q . k by one wave
@@ -91,7 +127,7 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
     red_p[rg][cg] = p;
     __syncthreads();
 
-    const float b = beta[bh];
+    const float b = FEAT ? fast_sigmoid(beta[bh]) : beta[bh];
     const float al = GATED ? alpha[bh] : 1.f;
     for (int c = tid; c < DV; c += NT) {
       const int g = c / 4, e = c % 4;
@@ -141,16 +177,22 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   const int BH = a.B * a.H;
   const int grid = BH < cu_count() ? BH : cu_count();
   prof_mark(kSlotDecode, false, a.stream);
-  if (a.alpha)
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT, true>), dim3(grid), dim3(512), 0,
-                       a.stream, static_cast<const IT*>(a.q), static_cast<const IT*>(a.k),
-                       static_cast<const IT*>(a.v), a.alpha, a.beta, a.S, static_cast<OT*>(a.o),
-                       BH);
+  const IT *q = static_cast<const IT*>(a.q), *k = static_cast<const IT*>(a.k);
+  const IT* v = static_cast<const IT*>(a.v);
+  OT* o = static_cast<OT*>(a.o);
+  const dim3 g(grid), blk(512);
+  if (a.alpha && a.features)
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT, true, true>), g, blk, 0, a.stream, q,
+                       k, v, a.alpha, a.beta, a.S, o, BH);
+  else if (a.alpha)
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT, true, false>), g, blk, 0, a.stream, q,
+                       k, v, a.alpha, a.beta, a.S, o, BH);
+  else if (a.features)
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT, false, true>), g, blk, 0, a.stream, q,
+                       k, v, a.alpha, a.beta, a.S, o, BH);
   else
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT, false>), dim3(grid), dim3(512), 0,
-                       a.stream, static_cast<const IT*>(a.q), static_cast<const IT*>(a.k),
-                       static_cast<const IT*>(a.v), a.alpha, a.beta, a.S, static_cast<OT*>(a.o),
-                       BH);
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT, false, false>), g, blk, 0, a.stream, q,
+                       k, v, a.alpha, a.beta, a.S, o, BH);
   hipError_t e = hipGetLastError();
   prof_mark(kSlotDecode, true, a.stream);
   return e;

@@ -10,11 +10,15 @@ namespace dn {
 struct DecodeArgs {
   const void *q, *k, *v;
   const float* alpha;  // per-(b, h) decay of the gated step, or null (plain delta rule)
-  const float* beta;
+  const float* beta;   // write strength, or its logit when `features` is set
   float* S;
   void* o;
   int B, H, d_k, d_v, in_dtype, out_dtype;
   hipStream_t stream;
+  // Apply the layer's feature maps in-kernel: q, k are the raw projections
+  // (normalise(silu(.)) is taken, the result held in in_dtype) and beta is
+  // the logit (sigmoid is taken).
+  bool features;
 };
 
 struct ChunkArgs {
@@ -31,8 +35,28 @@ struct ChunkArgs {
 
 hipError_t launch_decode(const DecodeArgs& a);
 
+// The layer's feature maps over `rows` rows of d_k (dn_features.hip).
+struct FeatureArgs {
+  const void *q_raw, *k_raw;
+  const float* beta_logit;
+  void *q_hat, *k_hat;
+  float* beta;
+  long long rows;
+  int d_k, dtype;
+  hipStream_t stream;
+};
+hipError_t launch_features(const FeatureArgs& a);
+// Most rows one launch takes (the grid's x extent times rows per workgroup).
+long long feature_max_rows(int d_k, int dtype);
+
 // Kernel slots of the profiling hook (see deltanet_profile_start).
-enum ProfSlot { kSlotChunkPrep = 0, kSlotChunkScan = 1, kSlotDecode = 2, kNumSlots = 3 };
+enum ProfSlot {
+  kSlotChunkPrep = 0,
+  kSlotChunkScan = 1,
+  kSlotDecode = 2,
+  kSlotFeatures = 3,
+  kNumSlots = 4
+};
 
 // Records a HIP event on `s` before (end = false) or after (end = true) the
 // kernel of `slot`, when profiling is on for the calling thread; a no-op

@@ -190,6 +190,41 @@ def make_decode_step_inputs(w: DecodeWorkload, step: int, seed: int = 0) -> dict
     return dict(q=q, k=k, v=v, beta=beta)
 
 
+def make_chunk_raw_inputs(w: ChunkWorkload, seed: int = 0, L: Optional[int] = None) -> dict:
+    """Host tensors for a chunked forward fed by the layer's raw projections
+    (the feature maps run first): dict(q_raw, k_raw, v, beta_logit, S0) with
+    q_raw, k_raw ``[B,H,L,d_k]`` and v ``[B,H,L,d_v]`` standard normal in the
+    storage dtype (a projection's output), beta_logit ``[B,H,L]`` standard
+    normal fp32, S0 as in ``make_chunk_inputs``.  Its own stream,
+    ``default_rng([seed, 11])``, draws in that order."""
+    L = w.L if L is None else L
+    dt = _TORCH_DTYPE[w.dtype]
+    rng = np.random.default_rng([seed, 11])
+    q = _draw_normal(rng, (w.B, w.H, L, w.d_k), _to_storage(dt))
+    k = _draw_normal(rng, (w.B, w.H, L, w.d_k), _to_storage(dt))
+    v = _draw_normal(rng, (w.B, w.H, L, w.d_v), _to_storage(dt))
+    logit = torch.from_numpy(rng.standard_normal((w.B, w.H, L))).to(torch.float32)
+    S0 = None
+    if w.s0_std is not None:
+        S0 = _draw_normal(rng, (w.B, w.H, w.d_k, w.d_v),
+                          lambda a: torch.from_numpy(a * w.s0_std).to(torch.float32))
+    return dict(q_raw=q, k_raw=k, v=v, beta_logit=logit, S0=S0)
+
+
+def make_decode_raw_step_inputs(w: DecodeWorkload, step: int, seed: int = 0) -> dict:
+    """Raw inputs of decode step ``step`` (the feature maps run in the step):
+    q_raw, k_raw ``[B,H,d_k]``, v ``[B,H,d_v]`` standard normal in the
+    storage dtype, beta_logit ``[B,H]`` standard normal fp32, from
+    ``default_rng([seed, step + 1, 11])``."""
+    dt = _TORCH_DTYPE[w.dtype]
+    rng = np.random.default_rng([seed, step + 1, 11])
+    q = torch.from_numpy(rng.standard_normal((w.B, w.H, w.d_k))).to(dt)
+    k = torch.from_numpy(rng.standard_normal((w.B, w.H, w.d_k))).to(dt)
+    v = torch.from_numpy(rng.standard_normal((w.B, w.H, w.d_v))).to(dt)
+    logit = torch.from_numpy(rng.standard_normal((w.B, w.H))).to(torch.float32)
+    return dict(q_raw=q, k_raw=k, v=v, beta_logit=logit)
+
+
 def scaled_chunk_workload(w: ChunkWorkload, **changes) -> ChunkWorkload:
     """A copy of ``w`` with some fields changed (smaller parity cases)."""
     return dataclasses.replace(w, **changes)

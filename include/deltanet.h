@@ -136,6 +136,61 @@ int deltanet_gated_decode_step(const void* q, const void* k, const void* v, cons
                                int d_k, int d_v, int in_dtype, int out_dtype,
                                hipStream_t stream);
 
+/*
+ * The layer's feature maps (page "GPT-2 から Kimi K3 まで、AI モデルの進化を解説",
+ * section "DeltaNet (Fast weight programmers)": before the delta rule the
+ * layer maps its projections to
+ *     q = normalise(silu(q_raw)),  k = normalise(silu(k_raw)),
+ *     beta = sigmoid(beta_logit),
+ * with silu(x) = x sigmoid(x) and normalise(x) = x / max(||x||_2, 1e-12)
+ * along d_k, as PyTorch's F.normalize).  The maps are evaluated in fp32; q
+ * and k are stored in `dtype` (bf16: rounded to nearest, ties to even),
+ * beta in fp32.  Elements of a row beyond ~1e19 overflow its fp32 sum of
+ * squares (the row then maps to zeros).
+ *
+ *   q_raw, k_raw, q_hat, k_hat : [B, H, L, d_k] dtype
+ *   beta_logit, beta            : [B, H, L] fp32
+ *   d_k in {64, 128}.  Every pointer is required when B H L > 0.  An output
+ *   may be the very buffer of its own input (in place); any other overlap is
+ *   rejected.
+ */
+int deltanet_feature_prep(const void* q_raw, const void* k_raw, const float* beta_logit,
+                          void* q_hat, void* k_hat, float* beta,
+                          int B, int H, int L, int d_k, int dtype, hipStream_t stream);
+
+/*
+ * The chunked forward fed by the raw projections: the feature maps above,
+ * then the plain (alpha == NULL) or gated (alpha given) chunked forward on the
+ * mapped q, k, beta.  Arguments are those of deltanet_chunk_fwd /
+ * deltanet_gated_chunk_fwd with q_raw, k_raw in place of q, k and
+ * beta_logit in place of beta.  The mapped operands live in the workspace,
+ * which is therefore larger: query it with
+ * deltanet_chunk_fwd_features_workspace_bytes(..., gated = alpha != NULL).
+ */
+int deltanet_chunk_fwd_features(const void* q_raw, const void* k_raw, const void* v,
+                                const float* alpha, const float* beta_logit, const float* S0,
+                                void* o, float* S_final,
+                                int B, int H, int L, int d_k, int d_v, int C,
+                                int in_dtype, int out_dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace deltanet_chunk_fwd_features needs (gated != 0 when
+ * alpha will be given; 0 if the sizes are invalid or unsupported). */
+size_t deltanet_chunk_fwd_features_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
+                                                   int in_dtype, int gated);
+
+/*
+ * One decode step fed by the raw projections: the feature maps are applied
+ * inside the step's kernel (no extra memory traffic), then the plain
+ * (alpha == NULL) or gated step.  Arguments are those of
+ * deltanet_decode_step / deltanet_gated_decode_step with q_raw, k_raw and
+ * beta_logit in place of q, k and beta.
+ */
+int deltanet_decode_step_features(const void* q_raw, const void* k_raw, const void* v,
+                                  const float* alpha, const float* beta_logit, float* S, void* o,
+                                  int B, int H, int d_k, int d_v, int in_dtype, int out_dtype,
+                                  hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* deltanet_status_string(int status);
 
@@ -149,7 +204,7 @@ int deltanet_last_hip_error(void);
  * call's stream.  deltanet_profile_stop() waits for those events and writes,
  * per kernel slot, the summed elapsed milliseconds and the launch count
  * (nslots entries each; slots: 0 = chunk WY-prep kernel, 1 = chunk scan
- * kernel, 2 = decode kernel).  Recording adds two event records per launch.
+ * kernel, 2 = decode kernel, 3 = feature-map kernel).  Recording adds two event records per launch.
  */
 int deltanet_profile_start(void);
 int deltanet_profile_stop(double* ms_per_slot, int* launches_per_slot, int nslots);

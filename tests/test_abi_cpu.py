@@ -33,7 +33,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.deltanet_version() == 200
+    assert lib.deltanet_version() == 300
     for s in range(8):
         assert lib.deltanet_status_string(s)
     assert lib.deltanet_status_string(99) == b"unknown status"
@@ -140,4 +140,70 @@ def test_gated_decode_validation(lib):
     assert _gdec(lib, alpha=BASE + 800 * MB + 8) == ALIGN
     assert _gdec(lib, o=BASE + 800 * MB) == ALIAS     # o overlaps alpha
     assert _gdec(lib, S=BASE + 800 * MB) == ALIAS     # S overlaps alpha
+    assert lib.deltanet_last_hip_error() == 0
+
+
+def _feat(lib, q=BASE, k=BASE + 100 * MB, bl=BASE + 200 * MB, qh=BASE + 300 * MB,
+          kh=BASE + 400 * MB, b=BASE + 500 * MB, B=2, H=3, L=100, dk=128, dt=BF16):
+    return lib.deltanet_feature_prep(q, k, bl, qh, kh, b, B, H, L, dk, dt, None)
+
+
+def test_feature_prep_validation(lib):
+    for name in ("q", "k", "bl", "qh", "kh", "b"):
+        assert _feat(lib, **{name: None}) == NULL, name
+    assert _feat(lib, q=None, L=0) == OK              # nothing to map: no pointer needed
+    assert _feat(lib, B=0) == SHAPE
+    assert _feat(lib, L=-1) == SHAPE
+    assert _feat(lib, dk=96) == UNSUP
+    assert _feat(lib, dt=2) == UNSUP
+    assert _feat(lib, kh=BASE + 400 * MB + 2) == ALIGN
+    assert _feat(lib, qh=BASE + 100 * MB) == ALIAS     # q_hat over k_raw
+    assert _feat(lib, b=BASE + 400 * MB) == ALIAS      # beta over k_hat
+    assert _feat(lib, qh=BASE + 16) == ALIAS           # partly over its own input
+    assert _feat(lib, L=70000, B=65535, H=65535) == UNSUP  # more rows than one launch takes
+    assert lib.deltanet_last_hip_error() == 0
+
+
+def _ffwd(lib, alpha=None, q=BASE, k=BASE + 100 * MB, v=BASE + 200 * MB, bl=BASE + 300 * MB,
+          S0=None, o=BASE + 400 * MB, Sf=BASE + 500 * MB, B=1, H=2, L=256, dk=64, dv=64, C=64,
+          it=BF16, ot=F32, ws=BASE + 600 * MB, ws_bytes=1 << 40):
+    return lib.deltanet_chunk_fwd_features(q, k, v, alpha, bl, S0, o, Sf, B, H, L, dk, dv, C, it,
+                                           ot, ws, ws_bytes, None)
+
+
+def test_chunk_fwd_features_validation(lib):
+    assert _ffwd(lib, q=None) == NULL
+    assert _ffwd(lib, bl=None) == NULL
+    assert _ffwd(lib, dk=96) == UNSUP
+    assert _ffwd(lib, C=32) == UNSUP
+    assert _ffwd(lib, bl=BASE + 300 * MB + 4) == ALIGN
+    assert _ffwd(lib, o=BASE + 100 * MB) == ALIAS      # o over k_raw
+    assert _ffwd(lib, ws=BASE + 300 * MB) == ALIAS     # workspace over the logits
+    for gated in (0, 1):
+        core = (lib.deltanet_gated_chunk_fwd_workspace_bytes if gated
+                else lib.deltanet_chunk_fwd_workspace_bytes)(1, 2, 256, 64, 64, 64, BF16)
+        need = lib.deltanet_chunk_fwd_features_workspace_bytes(1, 2, 256, 64, 64, 64, BF16, gated)
+        r = lambda n: (n + 255) // 256 * 256
+        # the mapped q, k (bf16) and beta (fp32) follow the core's scratch
+        assert need == r(core) + 2 * r(1 * 2 * 256 * 64 * 2) + r(1 * 2 * 256 * 4)
+        alpha = BASE + 800 * MB if gated else None
+        assert _ffwd(lib, alpha=alpha, ws_bytes=need - 1) == WS
+    assert lib.deltanet_chunk_fwd_features_workspace_bytes(1, 2, 256, 64, 64, 48, BF16, 0) == 0
+    assert lib.deltanet_last_hip_error() == 0
+
+
+def test_decode_step_features_validation(lib):
+    def d(**kw):
+        a = dict(q=BASE, k=BASE + 100 * MB, v=BASE + 200 * MB, alpha=None, bl=BASE + 300 * MB,
+                 S=BASE + 400 * MB, o=BASE + 900 * MB, B=2, H=3, dk=128, dv=128, it=BF16, ot=F32)
+        a.update(kw)
+        return lib.deltanet_decode_step_features(a["q"], a["k"], a["v"], a["alpha"], a["bl"],
+                                                 a["S"], a["o"], a["B"], a["H"], a["dk"],
+                                                 a["dv"], a["it"], a["ot"], None)
+    assert d(bl=None) == NULL
+    assert d(k=None) == NULL
+    assert d(dv=32) == UNSUP
+    assert d(alpha=BASE + 800 * MB + 4) == ALIGN
+    assert d(o=BASE + 300 * MB) == ALIAS               # o over the logits
+    assert d(S=BASE + 100 * MB) == ALIAS               # S over k_raw
     assert lib.deltanet_last_hip_error() == 0
