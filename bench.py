@@ -38,10 +38,13 @@ CSRC = os.path.join(ROOT, "deltanet_delta_rule_chunk_amd", "csrc")
 KERNEL_SOURCES = {
     "chunk_scan": ["dn_scan_mfma.hip", "dn_ktile.h", "dn_tfrag.h", "dn_mfma.h", "dn_common.h"],
     "chunk_prep": ["dn_chunk_mfma.hip", "dn_ktile.h", "dn_tfrag.h", "dn_mfma.h", "dn_common.h"],
-    "decode": ["dn_decode.hip", "dn_common.h"],
+    "decode": ["dn_decode.hip", "dn_features.h", "dn_common.h"],
+    "features": ["dn_features.hip", "dn_features.h", "dn_common.h"],
 }
-# The gated instantiations come from the same sources.
-KERNEL_SOURCES.update({"gated_" + k: v for k, v in list(KERNEL_SOURCES.items())})
+# The gated instantiations, and the decode step that applies the feature
+# maps in-kernel, come from the same sources.
+KERNEL_SOURCES.update({"gated_" + k: v for k, v in list(KERNEL_SOURCES.items()) if k != "features"})
+KERNEL_SOURCES["features_decode"] = KERNEL_SOURCES["decode"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters.json")
 
@@ -113,6 +116,13 @@ def prep_bytes(w, in_bytes=2):
     return tok_heads * (w.d_k * in_bytes + 4) + w.B * w.H * nc * blocks * 2048
 
 
+def feature_bytes(w, in_bytes=2):
+    """Algorithmic bytes of the feature-map kernel: q, k read and written once
+    in the storage dtype, the beta logits read and beta written once (fp32)."""
+    tok_heads = w.B * w.H * w.L
+    return tok_heads * (4 * w.d_k * in_bytes + 8)
+
+
 def model_flops(w):
     return w.B * w.H * (2 * w.L * w.d_k * w.d_v + 2 * w.L * w.C * w.d_k)
 
@@ -157,6 +167,8 @@ def main(argv=None) -> int:
                     help="skip timing the two smaller chunked workloads")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the gated (Gated DeltaNet) forward and decode measurements")
+    ap.add_argument("--no-features", action="store_true",
+                    help="skip the forward and decode fed by raw projections (feature maps)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (the known-size "
                          "reference for the HBM byte counters) and exit")
@@ -356,6 +368,71 @@ def main(argv=None) -> int:
                 "workload": wd.name + "_gated", "steps": nd, "ms_per_step": ms_gd, "kernel_ms": gk,
                 "tokens_per_s": wd.B / (ms_gd * 1e-3),
                 "pct_hbm_peak": 100.0 * gdb / (gk * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            }
+
+    if not a.no_features:
+        # The layer's feature maps (silu + L2-normalise of q, k; sigmoid of the
+        # beta logits) in front of the same forward, from raw projections.
+        print(f"[bench] feature maps + forward {w.name}: {a.steps} steps", file=sys.stderr,
+              flush=True)
+        r = {k: (None if t is None else t.to(dev))
+             for k, t in inputs.make_chunk_raw_inputs(w, seed=a.seed).items()}
+        fws = torch.empty(binding.workspace_bytes(w.B, w.H, w.L, w.d_k, w.d_v, w.C, features=True),
+                          dtype=torch.uint8, device=dev)
+
+        def fstep():
+            binding.chunk_fwd(r["q_raw"], r["k_raw"], r["v"], r["beta_logit"], None, w.C, o=o,
+                              S_final=S_final, workspace=fws, features=True)
+
+        for _ in range(a.warmup):
+            fstep()
+        torch.cuda.synchronize()
+        binding.profile_start()
+        ev0.record()
+        for _ in range(a.steps):
+            fstep()
+        ev1.record()
+        torch.cuda.synchronize()
+        fprof = binding.profile_stop()
+        assert torch.isfinite(o).all() and torch.isfinite(S_final).all()
+        ms_f = ev0.elapsed_time(ev1) / a.steps
+        fk = {name: tot / n for name, (tot, n) in fprof.items()}
+        fb = feature_bytes(w)
+        result["features"] = {
+            "workload": w.name + "_features", "steps": a.steps, "ms_per_step": ms_f,
+            "tokens_per_s": w.B * w.L / (ms_f * 1e-3), "kernels_ms": fk,
+            "roofline": {"bound": "hbm", "kernel": "features",
+                         "achieved": fb / (fk["features"] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s",
+                         "frac": fb / (fk["features"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "traffic": measured_traffic("features")},
+            "inputs": "q_raw, k_raw, v ~ N(0,1) bf16; beta logits ~ N(0,1) fp32 (own seeded stream)",
+        }
+        del r, fws
+        if not a.no_decode:
+            nd = max(1, a.decode_steps // 4)
+            print(f"[bench] decode with feature maps {wd.name}: {nd} steps", file=sys.stderr,
+                  flush=True)
+            fring = [{k: t.to(dev) for k, t in
+                      inputs.make_decode_raw_step_inputs(wd, s, seed=a.seed).items()}
+                     for s in range(8)]
+            binding.profile_start()
+            ev0.record()
+            for s in range(nd):
+                rr = fring[s % 8]
+                binding.decode_step(rr["q_raw"], rr["k_raw"], rr["v"], rr["beta_logit"], Sd, o=od,
+                                    features=True)
+            ev1.record()
+            torch.cuda.synchronize()
+            fdprof = binding.profile_stop()
+            assert torch.isfinite(od).all()
+            ms_fd = ev0.elapsed_time(ev1) / nd
+            fdk = fdprof["decode"][0] / fdprof["decode"][1]
+            result["features"]["decode"] = {
+                "workload": wd.name + "_features", "steps": nd, "ms_per_step": ms_fd,
+                "kernel_ms": fdk, "tokens_per_s": wd.B / (ms_fd * 1e-3),
+                "pct_hbm_peak": 100.0 * decode_bytes(wd) / (fdk * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "traffic": measured_traffic("features_decode"),
             }
 
     if not a.no_other_workloads:

@@ -6,11 +6,14 @@
 
 namespace dn {
 
-// bf16 is carried as its 16-bit pattern; conversions are written out here so
-// the rounding rule is explicit (round to nearest, ties to even).
+// bf16 is carried as its 16-bit pattern.  fp32 -> bf16 rounds to nearest,
+// ties to even (gfx950's v_cvt_pk_bf16_f32, which converts two values per
+// instruction; NaN stays NaN).
 struct bf16 {
   uint16_t bits;
 };
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) {
@@ -18,10 +21,12 @@ __device__ __forceinline__ float to_f32(bf16 x) {
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN stays NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// (a, b) -> bf16 bits of a in the low half, of b in the high half.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);
