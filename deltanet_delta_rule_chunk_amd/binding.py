@@ -29,6 +29,8 @@ EXPORTS = ("deltanet_chunk_fwd", "deltanet_chunk_fwd_workspace_bytes", "deltanet
            "deltanet_gated_chunk_fwd", "deltanet_gated_chunk_fwd_workspace_bytes",
            "deltanet_gated_decode_step", "deltanet_feature_prep", "deltanet_chunk_fwd_features",
            "deltanet_chunk_fwd_features_workspace_bytes", "deltanet_decode_step_features",
+           "deltanet_kda_chunk_fwd", "deltanet_kda_chunk_fwd_workspace_bytes",
+           "deltanet_kda_decode_step",
            "deltanet_status_string", "deltanet_last_hip_error", "deltanet_version",
            "deltanet_profile_start", "deltanet_profile_stop")
 PROFILE_SLOTS = ("chunk_prep", "chunk_scan", "decode", "features")
@@ -75,6 +77,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.deltanet_chunk_fwd_features_workspace_bytes.restype = sz
     lib.deltanet_decode_step_features.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     lib.deltanet_decode_step_features.restype = i
+    lib.deltanet_kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                           vp, sz, vp]
+    lib.deltanet_kda_chunk_fwd.restype = i
+    lib.deltanet_kda_chunk_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.deltanet_kda_chunk_fwd_workspace_bytes.restype = sz
+    lib.deltanet_kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.deltanet_kda_decode_step.restype = i
     lib.deltanet_status_string.argtypes = [i]
     lib.deltanet_status_string.restype = ctypes.c_char_p
     lib.deltanet_last_hip_error.argtypes = []
@@ -138,6 +147,77 @@ def workspace_bytes(B: int, H: int, L: int, d_k: int, d_v: int, C: int,
                                                                     _code(in_dtype), int(gated)))
     fn = lib.deltanet_gated_chunk_fwd_workspace_bytes if gated else lib.deltanet_chunk_fwd_workspace_bytes
     return int(fn(B, H, L, d_k, d_v, C, _code(in_dtype)))
+
+
+def kda_workspace_bytes(B: int, H: int, L: int, d_k: int, d_v: int, C: int = 64,
+                        in_dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(load().deltanet_kda_chunk_fwd_workspace_bytes(B, H, L, d_k, d_v, C,
+                                                             _code(in_dtype)))
+
+
+def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                  beta: torch.Tensor, S0: Optional[torch.Tensor] = None, C: int = 64, *,
+                  out_dtype: torch.dtype = torch.float32, o: Optional[torch.Tensor] = None,
+                  S_final: Optional[torch.Tensor] = None, want_state: bool = True,
+                  workspace: Optional[torch.Tensor] = None, stream=None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked forward with per-dimension decay (``deltanet_kda_chunk_fwd``):
+    ``chunk_fwd``'s arguments with alpha ``[B,H,L,d_k]`` fp32."""
+    lib = load()
+    B, H, L, d_k = q.shape
+    d_v = v.shape[-1]
+    dev = q.device
+    _check(q, "q", (B, H, L, d_k), device=dev)
+    _check(k, "k", (B, H, L, d_k), q.dtype, dev)
+    _check(v, "v", (B, H, L, d_v), q.dtype, dev)
+    _check(alpha, "alpha", (B, H, L, d_k), torch.float32, dev)
+    _check(beta, "beta", (B, H, L), torch.float32, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, d_k, d_v), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, L, d_v), dtype=out_dtype, device=dev)
+    _check(o, "o", (B, H, L, d_v), out_dtype, dev)
+    if S_final is None and want_state:
+        S_final = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=dev)
+    if S_final is not None:
+        _check(S_final, "S_final", (B, H, d_k, d_v), torch.float32, dev)
+    need = kda_workspace_bytes(B, H, L, d_k, d_v, C, q.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.deltanet_kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),
+                                    _ptr(o), _ptr(S_final), B, H, L, d_k, d_v, C, _code(q.dtype),
+                                    _code(out_dtype), _ptr(workspace), ws_bytes,
+                                    _stream(dev, stream))
+    if st != DN_OK:
+        _raise(lib, st, "deltanet_kda_chunk_fwd")
+    return o, S_final
+
+
+def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                    beta: torch.Tensor, S: torch.Tensor, *, out_dtype: torch.dtype = torch.float32,
+                    o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode step with per-dimension decay (``deltanet_kda_decode_step``):
+    alpha ``[B,H,d_k]`` fp32; S updated in place; returns o = q S_new."""
+    lib = load()
+    B, H, d_k = q.shape
+    d_v = v.shape[-1]
+    dev = q.device
+    _check(q, "q", (B, H, d_k), device=dev)
+    _check(k, "k", (B, H, d_k), q.dtype, dev)
+    _check(v, "v", (B, H, d_v), q.dtype, dev)
+    _check(alpha, "alpha", (B, H, d_k), torch.float32, dev)
+    _check(beta, "beta", (B, H), torch.float32, dev)
+    _check(S, "S", (B, H, d_k, d_v), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, d_v), dtype=out_dtype, device=dev)
+    _check(o, "o", (B, H, d_v), out_dtype, dev)
+    st = lib.deltanet_kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S),
+                                      _ptr(o), B, H, d_k, d_v, _code(q.dtype), _code(out_dtype),
+                                      _stream(dev, stream))
+    if st != DN_OK:
+        _raise(lib, st, "deltanet_kda_decode_step")
+    return o
 
 
 def feature_prep(q_raw: torch.Tensor, k_raw: torch.Tensor, beta_logit: torch.Tensor, *,

@@ -18,7 +18,7 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kVersion = 300;  // 0.3.0
+constexpr int kVersion = 400;  // 0.4.0
 
 int hip_fail(hipError_t e) {
   g_last_hip_error = static_cast<int>(e);
@@ -115,7 +115,8 @@ WsLayout ws_layout(int B, int H, int L, int d_k, int d_v, int C, int in_dtype, b
 int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alpha,
                    const float* beta, const float* S0, void* o, float* S_final, int B, int H,
                    int L, int d_k, int d_v, int C, int in_dtype, int out_dtype, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream, bool features = false) {
+                   size_t workspace_bytes, hipStream_t stream, bool features = false,
+                   bool per_dim = false) {
   ChunkSizes s;
   int st = check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, out_dtype, &s);
   if (st != DN_OK) return st;
@@ -127,10 +128,11 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alp
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return DN_ERR_MISALIGNED;
 
-  const Span sq{q, s.qk}, sk{k, s.qk}, sv{v, s.v}, sa{alpha, s.beta}, sb{beta, s.beta};
+  const size_t alpha_bytes = per_dim ? s.beta * d_k : s.beta;
+  const Span sq{q, s.qk}, sk{k, s.qk}, sv{v, s.v}, sa{alpha, alpha_bytes}, sb{beta, s.beta};
   const Span ss0{S0, s.state}, so{o, s.o}, ssf{S_final, s.state};
   const WsLayout wl = ws_layout(B, H, L, d_k, d_v, C, in_dtype, gated, features, s);
-  const size_t need = wl.total;
+  const size_t need = per_dim ? dn::kda_workspace_bytes(B, H, L, d_k) : wl.total;
   const Span sw{workspace, workspace ? need : 0};
   for (Span in : {sq, sk, sv, sa, sb, ss0})
     if (overlap(so, in) || (in.p != S0 && overlap(ssf, in))) return DN_ERR_ALIASING;
@@ -159,7 +161,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alp
   }
   if (e == hipSuccess) {
     dn::ChunkArgs a{q, k, v, alpha, beta, S0, o, S_final, B, H, L, d_k, d_v, C, in_dtype,
-                    out_dtype, ws, stream};
+                    out_dtype, ws, stream, per_dim};
     e = dn::launch_chunk_fwd(a);
   }
   if (own_ws) {
@@ -173,7 +175,8 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alp
 // Shared body of the plain (alpha = null) and gated decode steps.
 int decode_impl(const void* q, const void* k, const void* v, const float* alpha,
                 const float* beta, float* S, void* o, int B, int H, int d_k, int d_v,
-                int in_dtype, int out_dtype, hipStream_t stream, bool features = false) {
+                int in_dtype, int out_dtype, hipStream_t stream, bool features = false,
+                bool per_dim = false) {
   if (B < 1 || H < 1 || d_k < 1 || d_v < 1) return DN_ERR_BAD_SHAPE;
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return DN_ERR_UNSUPPORTED;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return DN_ERR_UNSUPPORTED;
@@ -185,7 +188,7 @@ int decode_impl(const void* q, const void* k, const void* v, const float* alpha,
   const size_t bh = (size_t)B * H;
   const Span sq{q, bh * d_k * dtype_size(in_dtype)}, sk{k, sq.n};
   const Span sv{v, bh * d_v * dtype_size(in_dtype)}, sb{beta, bh * sizeof(float)};
-  const Span sa{alpha, bh * sizeof(float)};
+  const Span sa{alpha, bh * sizeof(float) * (per_dim ? d_k : 1)};
   const Span sS{S, bh * d_k * d_v * sizeof(float)}, so{o, bh * d_v * dtype_size(out_dtype)};
   for (Span in : {sq, sk, sv, sa, sb, sS})
     if (overlap(so, in)) return DN_ERR_ALIASING;
@@ -193,7 +196,7 @@ int decode_impl(const void* q, const void* k, const void* v, const float* alpha,
     if (overlap(sS, in)) return DN_ERR_ALIASING;
 
   dn::DecodeArgs a{q, k, v, alpha, beta, S, o, B, H, d_k, d_v, in_dtype, out_dtype, stream,
-                   features};
+                   features, per_dim};
   hipError_t e = dn::launch_decode(a);
   if (e != hipSuccess) return hip_fail(e);
   return DN_OK;
@@ -328,6 +331,30 @@ int deltanet_decode_step_features(const void* q_raw, const void* k_raw, const vo
                                   hipStream_t stream) {
   return decode_impl(q_raw, k_raw, v, alpha, beta_logit, S, o, B, H, d_k, d_v, in_dtype,
                      out_dtype, stream, true);
+}
+
+size_t deltanet_kda_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
+                                              int in_dtype) {
+  ChunkSizes s;
+  if (check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, DN_F32, &s) != DN_OK) return 0;
+  return dn::kda_workspace_bytes(B, H, L, d_k);
+}
+
+int deltanet_kda_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* S0, void* o, float* S_final, int B,
+                           int H, int L, int d_k, int d_v, int C, int in_dtype, int out_dtype,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (L > 0 && !alpha) return DN_ERR_NULL_ARG;
+  return chunk_fwd_impl(q, k, v, alpha, beta, S0, o, S_final, B, H, L, d_k, d_v, C, in_dtype,
+                        out_dtype, workspace, workspace_bytes, stream, false, true);
+}
+
+int deltanet_kda_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, float* S, void* o, int B, int H, int d_k,
+                             int d_v, int in_dtype, int out_dtype, hipStream_t stream) {
+  if (!alpha) return DN_ERR_NULL_ARG;
+  return decode_impl(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, in_dtype, out_dtype, stream,
+                     false, true);
 }
 
 size_t deltanet_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,

@@ -5,6 +5,9 @@
 // roughly fp32 accuracy.  fp32 inputs are not exact in bf16, so they run on
 // the fp32 vector-ALU kernels (dn_chunk_valu.hip).
 //
+// Per-dimension decay (KDA) runs its own fp32 vector-ALU kernels
+// (dn_kda.hip) for either input dtype.
+//
 // The gated form (a per-token decay alpha) runs the same kernels with the
 // decay compiled in; its workspace adds, per chunk, the C within-chunk
 // cumulative log-decays g_r = log(alpha_1) + ... + log(alpha_r), written by
@@ -34,6 +37,7 @@ size_t chunk_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int i
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a) {
+  if (a.alpha && a.per_dim_alpha) return launch_kda_chunk_fwd(a);
   return a.in_dtype == 1 ? launch_chunk_fwd_mfma(a) : launch_chunk_fwd_valu(a);
 }
 

@@ -35,11 +35,11 @@
 
 #include "dn_common.h"
 #include "dn_launch.h"
+#include "dn_valu_common.h"
 
 namespace dn {
 namespace valu {
 
-constexpr int BS = 16;  // block size of the blocked triangular inverse
 constexpr int NT = 16;  // d_v columns per scan workgroup
 
 template <int C, int DK>
@@ -48,14 +48,6 @@ struct PrepSmem {
   static constexpr size_t bytes = 2 * (size_t)C * LD * sizeof(float) + 2 * C * sizeof(float);
 };
 
-template <typename IT>
-__device__ __forceinline__ void load_rows(float* dst, int ld, const IT* src, int rows_valid,
-                                          int rows, int cols) {
-  for (int e = threadIdx.x; e < rows * cols; e += blockDim.x) {
-    const int r = e / cols, c = e % cols;
-    dst[r * ld + c] = r < rows_valid ? to_f32(src[(size_t)r * cols + c]) : 0.f;
-  }
-}
 
 // One workgroup per (chunk, head).  Writes T[C][C] and P[C][C] (fp32, full
 // squares with zeros above the diagonal) for the chunk.
@@ -68,7 +60,6 @@ __global__ __launch_bounds__(256) void prep_kernel(const IT* __restrict__ q,
                                                    float* __restrict__ Pws,
                                                    float* __restrict__ Gws) {
   constexpr int LD = PrepSmem<C, DK>::LD;
-  constexpr int NB = C / BS;
   extern __shared__ float smem[];
   float* buf0 = smem;
   float* buf1 = smem + C * LD;
@@ -109,46 +100,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const IT* __restrict__ q,
   }
   __syncthreads();
 
-  // X = (I + A)^{-1} into buf0, by 16 x 16 blocks.
-  for (int e = threadIdx.x; e < C * C; e += blockDim.x) buf0[(e / C) * LD + e % C] = 0.f;
-  __syncthreads();
-  // Diagonal blocks: column j depends only on earlier rows of column j.
-  for (int t = threadIdx.x; t < C; t += blockDim.x) {
-    const int j = t, blk_end = (j / BS + 1) * BS;
-    buf0[j * LD + j] = 1.f;
-    for (int r = j + 1; r < blk_end; ++r) {
-      float acc = 0.f;
-      for (int i = j; i < r; ++i) acc += buf1[r * LD + i] * buf0[i * LD + j];
-      buf0[r * LD + j] = -acc;
-    }
-  }
-  __syncthreads();
-  // Off-diagonal block rows in order: X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj.
-  for (int bi = 1; bi < NB; ++bi) {
-    // Y_j = sum_k A_ik X_kj, parked in X_ij's slot.
-    for (int e = threadIdx.x; e < bi * BS * BS; e += blockDim.x) {
-      const int bj = e / (BS * BS), rr = (e / BS) % BS, cc = e % BS;
-      const int row = bi * BS + rr, col = bj * BS + cc;
-      float acc = 0.f;
-      for (int m = bj * BS; m < bi * BS; ++m) acc += buf1[row * LD + m] * buf0[m * LD + col];
-      buf0[row * LD + col] = acc;
-    }
-    __syncthreads();
-    float out[NB];
-    for (int e = threadIdx.x, s = 0; e < bi * BS * BS; e += blockDim.x, ++s) {
-      const int bj = e / (BS * BS), rr = (e / BS) % BS, cc = e % BS;
-      const int row = bi * BS + rr, col = bj * BS + cc;
-      float acc = 0.f;
-      for (int m = 0; m < BS; ++m) acc += buf0[row * LD + bi * BS + m] * buf0[(bi * BS + m) * LD + col];
-      out[s] = -acc;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x, s = 0; e < bi * BS * BS; e += blockDim.x, ++s) {
-      const int bj = e / (BS * BS), rr = (e / BS) % BS, cc = e % BS;
-      buf0[(bi * BS + rr) * LD + bj * BS + cc] = out[s];
-    }
-    __syncthreads();
-  }
+  // X = (I + A)^{-1} into buf0.
+  unit_lower_inverse<C>(buf1, LD, buf0, LD);
 
   // T = X diag(beta).
   for (int e = threadIdx.x; e < C * C; e += blockDim.x) {
@@ -225,6 +178,7 @@ __global__ __launch_bounds__(256) void scan_kernel(
       float ks = 0.f, qs = 0.f;
       if (r < valid) {
         const IT* qr = q + (tok0 + r) * DK;
+#pragma unroll 8
         for (int d = 0; d < DK; ++d) {
           const float sd = Ss[d * NT + j];
           ks += Ks[r * LDK + d] * sd;
@@ -246,6 +200,7 @@ __global__ __launch_bounds__(256) void scan_kernel(
     for (int m = 0; m < MR; ++m) {
       const int r = rb + m * RSTRIDE;
       float acc = 0.f;
+#pragma unroll 8
       for (int i = 0; i <= r; ++i) acc += Tc[r * C + i] * Rs[i * NT + j];
       Ds[r * NT + j] = acc;
     }
@@ -256,6 +211,7 @@ __global__ __launch_bounds__(256) void scan_kernel(
       const int r = rb + m * RSTRIDE;
       if (r < valid) {
         float acc = oi[m];
+#pragma unroll 8
         for (int i = 0; i <= r; ++i) acc += Pc[r * C + i] * Ds[i * NT + j];
         o[(tok0 + r) * DV + j0 + j] = from_f32<OT>(acc);
       }
@@ -268,8 +224,10 @@ __global__ __launch_bounds__(256) void scan_kernel(
       if constexpr (GATED) {
         const float gC = gs[C - 1];
         acc *= expf(gC);
+#pragma unroll 8
         for (int r = 0; r < C; ++r) acc += Ks[r * LDK + d] * (expf(gC - gs[r]) * Ds[r * NT + j]);
       } else {
+#pragma unroll 8
         for (int r = 0; r < C; ++r) acc += Ks[r * LDK + d] * Ds[r * NT + j];
       }
       Ss[d * NT + j] = acc;

@@ -25,6 +25,13 @@
 // (measured: 78% of peak for this form against 63% with one 256-thread
 // workgroup per head and plain stores).
 //
+// Per-dimension decay (DECAY = 2; KDA as the same article describes it: the
+// gate is a vector, one forgetting rate per memory dimension) decays row j of
+// S by alpha[j], the key dimension a read addresses.  The single read then
+// carries k o alpha and q o alpha:
+//     u = beta (v - (k o alpha) S),  o = (q o alpha) S + (q . k) u,
+//     S <- diag(alpha) S + k^T u.
+//
 // With FEAT the step also applies the layer's feature maps to its inputs
 // (same page and section: q, k = normalise(silu(.)), beta = sigmoid(logit);
 // dn_features.h): waves 0 and 1 map k and q while the others stage v, and
@@ -59,7 +66,8 @@ __device__ __forceinline__ void map_row_to_lds(const IT* __restrict__ x, float* 
   for (int e = 0; e < E; ++e) dst[lane + 64 * e] = to_f32(from_f32<IT>(f[e] * r));
 }
 
-template <int DK, int DV, typename IT, typename OT, bool GATED, bool FEAT>
+// DECAY: 0 none, 1 one alpha per (b, h), 2 one alpha per key dimension.
+template <int DK, int DV, typename IT, typename OT, int DECAY, bool FEAT>
 __global__ __launch_bounds__(512) void decode_step_kernel(
     const IT* __restrict__ q, const IT* __restrict__ k, const IT* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, float* __restrict__ S,
@@ -69,8 +77,10 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
   constexpr int ROWG = NT / COLG;       // row groups
   constexpr int RPT = DK / ROWG;        // rows per thread
   static_assert(RPT * ROWG == DK && COLG * ROWG == NT, "tile shape");
+  constexpr bool GATED = DECAY == 1, PERDIM = DECAY == 2;
 
   __shared__ float ks[DK], qs[DK], vs[DV], us[DV];
+  __shared__ float ad[PERDIM ? DK : 1];  // per-dimension decays
   __shared__ vf4 red_r[ROWG][COLG], red_p[ROWG][COLG];
   __shared__ float qk_s;
 
@@ -106,6 +116,8 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
       }
       for (int i = tid; i < DV; i += NT) vs[i] = to_f32(v[(size_t)bh * DV + i]);
     }
+    if (PERDIM)
+      for (int i = tid; i < DK; i += NT) ad[i] = alpha[(size_t)bh * DK + i];
     __syncthreads();
 
     if (tid < 64) {  // q . k by one wave
@@ -120,8 +132,9 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = rg + i * ROWG;
-      r += ks[row] * s[i];
-      p += qs[row] * s[i];
+      const float dr = PERDIM ? ad[row] : 1.f;
+      r += (ks[row] * dr) * s[i];
+      p += (qs[row] * dr) * s[i];
     }
     red_r[rg][cg] = r;
     red_p[rg][cg] = p;
@@ -148,7 +161,9 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = rg + i * ROWG;
-      const vf4 snew = GATED ? al * s[i] + ks[row] * u4 : s[i] + ks[row] * u4;
+      const vf4 snew = GATED    ? al * s[i] + ks[row] * u4
+                       : PERDIM ? ad[row] * s[i] + ks[row] * u4
+                                : s[i] + ks[row] * u4;
       __builtin_nontemporal_store(snew, reinterpret_cast<vf4*>(Sh + (size_t)row * DV + cg * 4));
     }
     __syncthreads();  // the LDS vectors are rewritten for the next head
@@ -181,18 +196,20 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   const IT* v = static_cast<const IT*>(a.v);
   OT* o = static_cast<OT*>(a.o);
   const dim3 g(grid), blk(512);
-  if (a.alpha && a.features)
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT, true, true>), g, blk, 0, a.stream, q,
-                       k, v, a.alpha, a.beta, a.S, o, BH);
-  else if (a.alpha)
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT, true, false>), g, blk, 0, a.stream, q,
-                       k, v, a.alpha, a.beta, a.S, o, BH);
-  else if (a.features)
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT, false, true>), g, blk, 0, a.stream, q,
-                       k, v, a.alpha, a.beta, a.S, o, BH);
-  else
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT, false, false>), g, blk, 0, a.stream, q,
-                       k, v, a.alpha, a.beta, a.S, o, BH);
+  const int decay = a.alpha ? (a.per_dim_alpha ? 2 : 1) : 0;
+#define DN_DECODE_LAUNCH(D, F)                                                                \
+  hipLaunchKernelGGL((decode_step_kernel<DK, DV, IT, OT, D, F>), g, blk, 0, a.stream, q, k, v, \
+                     a.alpha, a.beta, a.S, o, BH)
+  if (a.features) {
+    if (decay == 2) DN_DECODE_LAUNCH(2, true);
+    else if (decay == 1) DN_DECODE_LAUNCH(1, true);
+    else DN_DECODE_LAUNCH(0, true);
+  } else {
+    if (decay == 2) DN_DECODE_LAUNCH(2, false);
+    else if (decay == 1) DN_DECODE_LAUNCH(1, false);
+    else DN_DECODE_LAUNCH(0, false);
+  }
+#undef DN_DECODE_LAUNCH
   hipError_t e = hipGetLastError();
   prof_mark(kSlotDecode, true, a.stream);
   return e;

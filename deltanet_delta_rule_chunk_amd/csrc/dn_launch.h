@@ -9,7 +9,7 @@ namespace dn {
 
 struct DecodeArgs {
   const void *q, *k, *v;
-  const float* alpha;  // per-(b, h) decay of the gated step, or null (plain delta rule)
+  const float* alpha;  // decay of the gated step, or null (plain delta rule)
   const float* beta;   // write strength, or its logit when `features` is set
   float* S;
   void* o;
@@ -19,18 +19,23 @@ struct DecodeArgs {
   // (normalise(silu(.)) is taken, the result held in in_dtype) and beta is
   // the logit (sigmoid is taken).
   bool features;
+  // alpha holds d_k decays per (b, h), one per key dimension (KDA), instead
+  // of one.
+  bool per_dim_alpha;
 };
 
 struct ChunkArgs {
   const void *q, *k, *v;
-  const float* alpha;  // per-token decay of the gated form, or null (plain delta rule)
+  const float* alpha;  // per-token decay of the gated form, or null (plain delta rule);
+                       // [B,H,L,d_k] when per_dim_alpha
   const float* beta;
   const float* S0;  // may be null (zero state)
   void* o;
   float* S_final;   // may be null
   int B, H, L, d_k, d_v, C, in_dtype, out_dtype;
-  void* workspace;  // at least chunk_workspace_bytes(...) bytes
+  void* workspace;  // at least chunk_workspace_bytes(...) bytes (kda_workspace_bytes)
   hipStream_t stream;
+  bool per_dim_alpha;  // one decay per key dimension (KDA, dn_kda.hip)
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
@@ -67,6 +72,9 @@ void prof_mark(int slot, bool end, hipStream_t s);
 size_t chunk_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int in_dtype,
                              bool gated);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
+// The per-dimension-decay (KDA) chunked forward: its workspace and launches.
+size_t kda_workspace_bytes(int B, int H, int L, int d_k);
+hipError_t launch_kda_chunk_fwd(const ChunkArgs& a);
 // Bytes of the gated form's per-chunk log-decay table; it sits at the end of
 // the workspace, after the kernels' other scratch.
 size_t gated_log_decay_bytes(int B, int H, int L, int C);

@@ -169,6 +169,18 @@ def make_decode_alpha(w: DecodeWorkload, step: int, seed: int = 0) -> torch.Tens
     return _alpha_from(np.random.default_rng([seed, step + 1, 7]), (w.B, w.H))
 
 
+def make_chunk_kda_alpha(w: ChunkWorkload, seed: int = 0, L: Optional[int] = None) -> torch.Tensor:
+    """Per-token, per-key-dimension decay ``[B,H,L,d_k]`` fp32 of the KDA
+    forward: sigmoid(N(3, 1)) per element, from ``default_rng([seed, 13])``."""
+    L = w.L if L is None else L
+    return _alpha_from(np.random.default_rng([seed, 13]), (w.B, w.H, L, w.d_k))
+
+
+def make_decode_kda_alpha(w: DecodeWorkload, step: int, seed: int = 0) -> torch.Tensor:
+    """Per-key-dimension decay ``[B,H,d_k]`` fp32 of KDA decode step ``step``."""
+    return _alpha_from(np.random.default_rng([seed, step + 1, 13]), (w.B, w.H, w.d_k))
+
+
 def make_decode_state(w: DecodeWorkload, seed: int = 0) -> torch.Tensor:
     """Initial decode state ``[B,H,d_k,d_v]`` fp32, std ``w.s_std``."""
     rng = np.random.default_rng(seed)

@@ -137,6 +137,44 @@ int deltanet_gated_decode_step(const void* q, const void* k, const void* v, cons
                                hipStream_t stream);
 
 /*
+ * Per-dimension decay (KDA).  The same article describes Kimi Linear's KDA as
+ * Gated DeltaNet with the scalar gate turned into a vector: each dimension of
+ * the memory forgets at its own rate.  The gate acts on the key dimension,
+ * the rows of S.  Per (b, h) and token t, in order:
+ *     S     = diag(alpha_t) S          alpha_t in [0, 1]^{d_k}
+ *     v_old = k_t S
+ *     u_t   = beta_t (v_t - v_old)
+ *     S     = S + k_t^T u_t
+ *     o_t   = q_t S
+ * Arguments are those of the gated entry points with alpha one fp32 per key
+ * dimension: [B, H, L, d_k] for the chunked forward, [B, H, d_k] for the
+ * decode step.  alpha must be 16-byte aligned and may not overlap an output;
+ * zeros are floored inside a chunk as for the scalar gate.  The chunked
+ * forward runs fp32 vector-ALU kernels for either input dtype, in 64-token
+ * chunks whatever C names (the result does not depend on the chunk size; C
+ * must still be 64 or 128).  Its workspace is larger than the other forms':
+ * query deltanet_kda_chunk_fwd_workspace_bytes().  With L = 0, alpha may be
+ * NULL.
+ */
+int deltanet_kda_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* S0, void* o, float* S_final,
+                           int B, int H, int L, int d_k, int d_v, int C,
+                           int in_dtype, int out_dtype,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace deltanet_kda_chunk_fwd needs (0 if the sizes are invalid
+ * or unsupported). */
+size_t deltanet_kda_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
+                                              int in_dtype);
+
+/* One decode step with per-dimension decay, S updated in place; o = q S_new.
+ * alpha: [B, H, d_k] fp32. */
+int deltanet_kda_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, float* S, void* o, int B, int H,
+                             int d_k, int d_v, int in_dtype, int out_dtype,
+                             hipStream_t stream);
+
+/*
  * The layer's feature maps (page "GPT-2 から Kimi K3 まで、AI モデルの進化を解説",
  * section "DeltaNet (Fast weight programmers)": before the delta rule the
  * layer maps its projections to

@@ -33,7 +33,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.deltanet_version() == 300
+    assert lib.deltanet_version() == 400
     for s in range(8):
         assert lib.deltanet_status_string(s)
     assert lib.deltanet_status_string(99) == b"unknown status"
@@ -206,4 +206,53 @@ def test_decode_step_features_validation(lib):
     assert d(alpha=BASE + 800 * MB + 4) == ALIGN
     assert d(o=BASE + 300 * MB) == ALIAS               # o over the logits
     assert d(S=BASE + 100 * MB) == ALIAS               # S over k_raw
+    assert lib.deltanet_last_hip_error() == 0
+
+
+def _kfwd(lib, alpha=BASE + 800 * MB, q=BASE, k=BASE + 100 * MB, v=BASE + 200 * MB,
+          beta=BASE + 300 * MB, S0=None, o=BASE + 400 * MB, Sf=BASE + 500 * MB, B=1, H=2, L=256,
+          dk=64, dv=64, C=64, it=BF16, ot=F32, ws=BASE + 600 * MB, ws_bytes=1 << 40):
+    return lib.deltanet_kda_chunk_fwd(q, k, v, alpha, beta, S0, o, Sf, B, H, L, dk, dv, C, it, ot,
+                                      ws, ws_bytes, None)
+
+
+def test_kda_chunk_fwd_validation(lib):
+    assert _kfwd(lib, alpha=None) == NULL
+    # L = 0: no token to decay, alpha may be NULL (the later alignment check
+    # is what stops this call, so the NULL alpha passed)
+    assert _kfwd(lib, alpha=None, L=0, S0=BASE + 4) == ALIGN
+    assert _kfwd(lib, v=None) == NULL
+    assert _kfwd(lib, dk=32) == UNSUP
+    assert _kfwd(lib, C=96) == UNSUP
+    assert _kfwd(lib, alpha=BASE + 800 * MB + 4) == ALIGN
+    # alpha is [B, H, L, d_k] fp32 = 128 KiB here: an output just past one
+    # scalar per token still overlaps it
+    assert _kfwd(lib, o=BASE + 800 * MB + 4096) == ALIAS
+    assert _kfwd(lib, ws=BASE + 800 * MB + 64 * 1024) == ALIAS
+    need = lib.deltanet_kda_chunk_fwd_workspace_bytes(1, 2, 256, 64, 64, 64, BF16)
+    # o right after the gate does not overlap it (the workspace check after
+    # the aliasing checks is what stops this call)
+    assert _kfwd(lib, o=BASE + 800 * MB + 1 * 2 * 256 * 64 * 4, ws_bytes=need - 1) == WS
+    # per 64-token chunk: T and P (64 x 64), three 64 x d_k decayed operands,
+    # the d_k end-of-chunk decays, all fp32
+    assert need == 1 * 2 * 4 * (2 * 64 * 64 + 3 * 64 * 64 + 64) * 4
+    assert lib.deltanet_kda_chunk_fwd_workspace_bytes(1, 2, 256, 64, 64, 128, BF16) == need
+    assert _kfwd(lib, ws_bytes=need - 1) == WS
+    assert lib.deltanet_last_hip_error() == 0
+
+
+def test_kda_decode_validation(lib):
+    def d(**kw):
+        a = dict(q=BASE, k=BASE + 100 * MB, v=BASE + 200 * MB, alpha=BASE + 800 * MB,
+                 beta=BASE + 300 * MB, S=BASE + 400 * MB, o=BASE + 900 * MB, B=2, H=3, dk=128,
+                 dv=128, it=BF16, ot=F32)
+        a.update(kw)
+        return lib.deltanet_kda_decode_step(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S"],
+                                            a["o"], a["B"], a["H"], a["dk"], a["dv"], a["it"],
+                                            a["ot"], None)
+    assert d(alpha=None) == NULL
+    assert d(dk=100) == UNSUP
+    assert d(alpha=BASE + 800 * MB + 8) == ALIGN
+    assert d(o=BASE + 800 * MB + 2 * 3 * 4 * 64) == ALIAS   # inside the [B, H, d_k] gate
+    assert d(S=BASE + 800 * MB + 1024) == ALIAS
     assert lib.deltanet_last_hip_error() == 0
