@@ -45,6 +45,9 @@ KERNEL_SOURCES = {
 # maps in-kernel, come from the same sources.
 KERNEL_SOURCES.update({"gated_" + k: v for k, v in list(KERNEL_SOURCES.items()) if k != "features"})
 KERNEL_SOURCES["features_decode"] = KERNEL_SOURCES["decode"]
+KERNEL_SOURCES["kda_decode"] = KERNEL_SOURCES["decode"]
+KERNEL_SOURCES["kda_chunk_prep"] = KERNEL_SOURCES["kda_chunk_scan"] = [
+    "dn_kda.hip", "dn_valu_common.h", "dn_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters.json")
 
@@ -167,6 +170,8 @@ def main(argv=None) -> int:
                     help="skip timing the two smaller chunked workloads")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the gated (Gated DeltaNet) forward and decode measurements")
+    ap.add_argument("--no-kda", action="store_true",
+                    help="skip the per-dimension-decay (KDA) forward and decode measurements")
     ap.add_argument("--no-features", action="store_true",
                     help="skip the forward and decode fed by raw projections (feature maps)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -368,6 +373,62 @@ def main(argv=None) -> int:
                 "workload": wd.name + "_gated", "steps": nd, "ms_per_step": ms_gd, "kernel_ms": gk,
                 "tokens_per_s": wd.B / (ms_gd * 1e-3),
                 "pct_hbm_peak": 100.0 * gdb / (gk * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            }
+
+    if not a.no_kda:
+        # Per-dimension decay (KDA): fp32 vector-ALU chunk kernels, and the
+        # decode step with a d_k-vector gate per (b, h).
+        print(f"[bench] kda forward {w.name}: {a.steps} steps", file=sys.stderr, flush=True)
+        kalpha = inputs.make_chunk_kda_alpha(w, seed=a.seed).to(dev)
+        kws = torch.empty(binding.kda_workspace_bytes(w.B, w.H, w.L, w.d_k, w.d_v, w.C),
+                          dtype=torch.uint8, device=dev)
+
+        def kstep():
+            binding.kda_chunk_fwd(g["q"], g["k"], g["v"], kalpha, g["beta"], None, w.C, o=o,
+                                  S_final=S_final, workspace=kws)
+
+        kstep()
+        torch.cuda.synchronize()
+        binding.profile_start()
+        ev0.record()
+        for _ in range(a.steps):
+            kstep()
+        ev1.record()
+        torch.cuda.synchronize()
+        kprof = binding.profile_stop()
+        assert torch.isfinite(o).all() and torch.isfinite(S_final).all()
+        ms_k = ev0.elapsed_time(ev1) / a.steps
+        result["kda"] = {
+            "workload": w.name + "_kda", "steps": a.steps, "ms_per_step": ms_k,
+            "tokens_per_s": w.B * w.L / (ms_k * 1e-3),
+            "kernels_ms": {name: tot / n for name, (tot, n) in kprof.items()},
+            "path": "fp32 vector ALU, 64-token chunks",
+            "alpha": "sigmoid(N(3, 1)) per token and key dimension (seeded stream of its own)",
+        }
+        del kws, kalpha
+        if not a.no_decode:
+            nd = max(1, a.decode_steps // 4)
+            print(f"[bench] kda decode {wd.name}: {nd} steps", file=sys.stderr, flush=True)
+            kring = [inputs.make_decode_kda_alpha(wd, s, seed=a.seed).to(dev) for s in range(8)]
+            binding.profile_start()
+            ev0.record()
+            for s in range(nd):
+                r = ring[s % 8]
+                binding.kda_decode_step(r["q"], r["k"], r["v"], kring[s % 8], r["beta"], Sd, o=od)
+            ev1.record()
+            torch.cuda.synchronize()
+            kdprof = binding.profile_stop()
+            assert torch.isfinite(od).all()
+            ms_kd = ev0.elapsed_time(ev1) / nd
+            kk = kdprof["decode"][0] / kdprof["decode"][1]
+            kdb = decode_bytes(wd) + wd.B * wd.H * wd.d_k * 4
+            result["kda"]["decode"] = {
+                "workload": wd.name + "_kda", "steps": nd, "ms_per_step": ms_kd, "kernel_ms": kk,
+                "tokens_per_s": wd.B / (ms_kd * 1e-3),
+                "roofline": {"bound": "hbm", "kernel": "kda_decode",
+                             "achieved": kdb / (kk * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": kdb / (kk * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                             "traffic": measured_traffic("kda_decode")},
             }
 
     if not a.no_features:

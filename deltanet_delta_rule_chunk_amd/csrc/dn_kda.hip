@@ -29,8 +29,8 @@
 //        sum per dimension, then T, P and the decayed operands
 //        K o e^g, Q o e^g, K o e^{g_C - g} and e^{g_C} into the workspace;
 //   scan (one workgroup per (head, 16 columns of d_v)): walks the chunks in
-//        order with its state columns in LDS; the columns of S evolve
-//        independently.
+//        order with its state columns in LDS (the columns of S evolve
+//        independently), staging each chunk's operands into LDS first.
 
 #include "dn_common.h"
 #include "dn_launch.h"
@@ -40,8 +40,11 @@ namespace dn {
 namespace kda {
 
 using valu::load_rows;
-constexpr int C = 64;   // chunk rows
-constexpr int NT = 16;  // d_v columns per scan workgroup
+constexpr int C = 64;      // chunk rows
+constexpr int NT = 16;     // d_v columns per scan workgroup
+constexpr int NTHR = 1024; // threads per workgroup: the LDS a chunk needs
+                           // allows one workgroup per CU, so it brings 16
+                           // waves to hide LDS and memory latency
 
 // Workspace per (head, chunk), in floats: T, P (C x C each), K o e^g,
 // Q o e^g, K o e^{g_C - g} (C x d_k each), e^{g_C} (d_k).
@@ -58,7 +61,7 @@ struct PrepSmem {
 };
 
 template <int DK, typename IT>
-__global__ __launch_bounds__(256) void prep_kernel(const IT* __restrict__ q,
+__global__ __launch_bounds__(NTHR) void prep_kernel(const IT* __restrict__ q,
                                                    const IT* __restrict__ k,
                                                    const float* __restrict__ alpha,
                                                    const float* __restrict__ beta, int L,
@@ -135,28 +138,42 @@ __global__ __launch_bounds__(256) void prep_kernel(const IT* __restrict__ q,
 
 template <int DK>
 struct ScanSmem {
-  static constexpr int LDK = DK + 1;
-  static constexpr size_t bytes =
-      ((size_t)C * LDK + (size_t)DK * NT + 2 * (size_t)C * NT + DK) * sizeof(float);
+  static constexpr int LDK = DK + 1;  // row pitch of the C x d_k tiles
+  static constexpr int LDC = C + 1;   // row pitch of T and P
+  static constexpr size_t floats = 3 * (size_t)C * LDK + 2 * (size_t)C * LDC + (size_t)DK * NT +
+                                   2 * (size_t)C * NT + DK;
+  static constexpr size_t bytes = floats * sizeof(float);
+  static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
-// One workgroup per (16-column slice of d_v, head).  Walks all chunks.
+// One workgroup per (16-column slice of d_v, head).  Walks all chunks.  Each
+// chunk's workspace block (T, P, the three decayed tiles, e^{g_C}: 145 KB
+// at d_k = 128) is contiguous; it is staged into LDS with 16-byte loads, all
+// issued before any use, and every product then runs from LDS.
 template <int DK, int DV, typename IT, typename OT>
-__global__ __launch_bounds__(256) void scan_kernel(const IT* __restrict__ v,
+__global__ __launch_bounds__(NTHR) void scan_kernel(const IT* __restrict__ v,
                                                    const float* __restrict__ S0,
                                                    OT* __restrict__ o,
                                                    float* __restrict__ S_final, int L, int nc,
                                                    const float* __restrict__ ws) {
-  constexpr int LDK = ScanSmem<DK>::LDK;
-  constexpr int RSTRIDE = 256 / NT;  // rows between a thread's outputs
+  constexpr int LDK = ScanSmem<DK>::LDK, LDC = ScanSmem<DK>::LDC;
+  constexpr int RSTRIDE = NTHR / NT;  // rows between a thread's outputs
   constexpr int MR = C / RSTRIDE;    // chunk rows per thread
   constexpr int MS = DK / RSTRIDE;   // state rows per thread
+  static_assert(MR >= 1 && MS >= 1 && MR * RSTRIDE == C && MS * RSTRIDE == DK, "thread map");
+  constexpr int NF4 = (int)(chunk_floats(DK) / 4);
+  static_assert(chunk_floats(DK) % 4 == 0 && (C * C) % 4 == 0 && (C * DK) % 4 == 0 && DK % 4 == 0,
+                "16-byte pieces never straddle two tiles");
   extern __shared__ float smem[];
-  float* Ks = smem;            // K o e^g, then K o e^{g_C - g}
-  float* Ss = Ks + C * LDK;    // state columns j0 .. j0 + 15
+  float* Ts = smem;              // T
+  float* Ps = Ts + C * LDC;      // P
+  float* Kd = Ps + C * LDC;      // K o e^g
+  float* Qd = Kd + C * LDK;      // Q o e^g
+  float* Ku = Qd + C * LDK;      // K o e^{g_C - g}
+  float* Ss = Ku + C * LDK;      // state columns j0 .. j0 + 15
   float* Rs = Ss + DK * NT;
   float* Ds = Rs + C * NT;
-  float* gam = Ds + C * NT;    // e^{g_C}
+  float* gam = Ds + C * NT;      // e^{g_C}
 
   const int j0 = blockIdx.x * NT, bh = blockIdx.y;
   const int j = threadIdx.x % NT, rb = threadIdx.x / NT;
@@ -171,13 +188,32 @@ __global__ __launch_bounds__(256) void scan_kernel(const IT* __restrict__ v,
     const int t0 = c * C;
     const int valid = min(C, L - t0);
     const size_t tok0 = (size_t)bh * L + t0;
-    const float* Tc = ws + ((size_t)bh * nc + c) * chunk_floats(DK);
-    const float* Pc = Tc + C * C;
-    const float* Kd = Pc + C * C;
-    const float* Qd = Kd + C * DK;
-    const float* Ku = Qd + C * DK;
-    load_rows(Ks, LDK, Kd, C, C, DK);
-    for (int d = threadIdx.x; d < DK; d += blockDim.x) gam[d] = Ku[C * DK + d];
+    const float4* src = reinterpret_cast<const float4*>(ws + ((size_t)bh * nc + c) * chunk_floats(DK));
+#pragma unroll 8
+    for (int e4 = threadIdx.x; e4 < NF4; e4 += NTHR) {
+      const float4 x = src[e4];
+      int f = 4 * e4;
+      float* dst;
+      if (f < C * C) {
+        dst = Ts + (f / C) * LDC + f % C;
+      } else if ((f -= C * C) < C * C) {
+        dst = Ps + (f / C) * LDC + f % C;
+      } else if ((f -= C * C) < 3 * C * DK) {
+        const int t = f / (C * DK), g = f % (C * DK);
+        dst = Kd + t * C * LDK + (g / DK) * LDK + g % DK;
+      } else {
+        dst = gam + (f - 3 * C * DK);
+      }
+      dst[0] = x.x;
+      dst[1] = x.y;
+      dst[2] = x.z;
+      dst[3] = x.w;
+    }
+    float vr[MR];
+    for (int m = 0; m < MR; ++m) {
+      const int r = rb + m * RSTRIDE;
+      vr[m] = r < valid ? to_f32(v[(tok0 + r) * DV + j0 + j]) : 0.f;
+    }
     __syncthreads();
 
     // R = V - (K o e^g) S into LDS; (Q o e^g) S kept in registers.
@@ -185,15 +221,13 @@ __global__ __launch_bounds__(256) void scan_kernel(const IT* __restrict__ v,
     for (int m = 0; m < MR; ++m) {
       const int r = rb + m * RSTRIDE;
       float ks = 0.f, qs = 0.f;
-      const float* qr = Qd + (size_t)r * DK;
 #pragma unroll 8
       for (int d = 0; d < DK; ++d) {
         const float sd = Ss[d * NT + j];
-        ks += Ks[r * LDK + d] * sd;
-        qs += qr[d] * sd;
+        ks += Kd[r * LDK + d] * sd;
+        qs += Qd[r * LDK + d] * sd;
       }
-      const float vr = r < valid ? to_f32(v[(tok0 + r) * DV + j0 + j]) : 0.f;
-      Rs[r * NT + j] = vr - ks;
+      Rs[r * NT + j] = vr[m] - ks;
       oi[m] = qs;
     }
     __syncthreads();
@@ -203,33 +237,30 @@ __global__ __launch_bounds__(256) void scan_kernel(const IT* __restrict__ v,
       const int r = rb + m * RSTRIDE;
       float acc = 0.f;
 #pragma unroll 8
-      for (int i = 0; i <= r; ++i) acc += Tc[r * C + i] * Rs[i * NT + j];
+      for (int i = 0; i <= r; ++i) acc += Ts[r * LDC + i] * Rs[i * NT + j];
       Ds[r * NT + j] = acc;
     }
     __syncthreads();
 
-    // O = (Q o e^g) S + P Delta; meanwhile K o e^{g_C - g} replaces K o e^g.
+    // O = (Q o e^g) S + P Delta, and S' = diag(e^{g_C}) S + (K o e^{g_C - g})^T Delta
+    // (both read Delta; the state was last read before the previous barrier).
     for (int m = 0; m < MR; ++m) {
       const int r = rb + m * RSTRIDE;
       if (r < valid) {
         float acc = oi[m];
 #pragma unroll 8
-        for (int i = 0; i <= r; ++i) acc += Pc[r * C + i] * Ds[i * NT + j];
+        for (int i = 0; i <= r; ++i) acc += Ps[r * LDC + i] * Ds[i * NT + j];
         o[(tok0 + r) * DV + j0 + j] = from_f32<OT>(acc);
       }
     }
-    load_rows(Ks, LDK, Ku, C, C, DK);
-    __syncthreads();
-
-    // S' = diag(e^{g_C}) S + (K o e^{g_C - g})^T Delta.
     for (int m = 0; m < MS; ++m) {
       const int d = rb + m * RSTRIDE;
       float acc = gam[d] * Ss[d * NT + j];
 #pragma unroll 8
-      for (int r = 0; r < C; ++r) acc += Ks[r * LDK + d] * Ds[r * NT + j];
+      for (int r = 0; r < C; ++r) acc += Ku[r * LDK + d] * Ds[r * NT + j];
       Ss[d * NT + j] = acc;
     }
-    __syncthreads();
+    __syncthreads();  // the next chunk overwrites every tile
   }
 
   if (S_final) {
@@ -251,7 +282,7 @@ hipError_t launch_t(const ChunkArgs& a) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
     if (e != hipSuccess) return e;
     prof_mark(kSlotChunkPrep, false, a.stream);
-    hipLaunchKernelGGL((prep_kernel<DK, IT>), dim3(nc, bh), dim3(256), sm, a.stream,
+    hipLaunchKernelGGL((prep_kernel<DK, IT>), dim3(nc, bh), dim3(NTHR), sm, a.stream,
                        static_cast<const IT*>(a.q), static_cast<const IT*>(a.k), a.alpha, a.beta,
                        a.L, ws);
     e = hipGetLastError();
@@ -263,7 +294,7 @@ hipError_t launch_t(const ChunkArgs& a) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm2);
   if (e != hipSuccess) return e;
   prof_mark(kSlotChunkScan, false, a.stream);
-  hipLaunchKernelGGL((scan_kernel<DK, DV, IT, OT>), dim3(DV / NT, bh), dim3(256), sm2, a.stream,
+  hipLaunchKernelGGL((scan_kernel<DK, DV, IT, OT>), dim3(DV / NT, bh), dim3(NTHR), sm2, a.stream,
                      static_cast<const IT*>(a.v), a.S0, static_cast<OT*>(a.o), a.S_final, a.L, nc,
                      ws);
   e = hipGetLastError();
