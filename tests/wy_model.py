@@ -135,3 +135,60 @@ def gated_chunked_forward(q, k, v, alpha, beta, S0, C, SB=None):
                 Gb = Gn
             S = Sb
     return o[:L], S
+
+
+def chunked_backward(q, k, v, beta, S0, dO, dS_final, C):
+    """fp64 model of the chunked backward the HIP kernels implement, per
+    chunk with entering state S and exit gradient G' = dL/dS':
+        forward:  X = (I + A)^{-1}, A = tril(diag(beta) K K^T, -1),
+                  T = X diag(beta), R = V - K S, Delta = T R,
+                  M = tril(Q K^T) (diagonal included),
+                  O = Q S + M Delta, S' = S + K^T Delta
+        backward: dDelta = M^T dO + K G',  dR = T^T dDelta,  dV = dR,
+                  dS = G' + Q^T dO - K^T dR,
+                  dM = tril(dO Delta^T),  dQ = dO S^T + dM K,
+                  dT = dDelta R^T,  dX = dT diag(beta),
+                  dbeta_i += sum_r X_ri dT_ri,
+                  dA = -X^T dX X^T (strictly lower part),
+                  W = diag(beta) dA,  dbeta_r += sum_i dA_ri (k_r . k_i),
+                  dK = dM^T Q + Delta G'^T - dR S^T + W K + W^T K.
+    Returns (dq, dk, dv, dbeta, dS0)."""
+    q, k, v, beta, dO = (np.asarray(x, np.float64) for x in (q, k, v, beta, dO))
+    B, H, L, dk_ = k.shape
+    dv_ = v.shape[-1]
+    outs = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros_like(beta),
+            np.zeros((B, H, dk_, dv_))]
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dk_, dv_)) if S0 is None else np.asarray(S0, np.float64)[b, h].copy()
+            saved = []
+            for t0 in range(0, L, C):
+                sl = slice(t0, min(t0 + C, L))
+                K, V, bt = k[b, h, sl], v[b, h, sl], beta[b, h, sl]
+                A = np.tril(bt[:, None] * (K @ K.T), -1)
+                X = np.linalg.inv(np.eye(len(bt)) + A)
+                T = X * bt[None, :]
+                R = V - K @ S
+                D = T @ R
+                saved.append((sl, S.copy(), X, T, R, D))
+                S = S + K.T @ D
+            G = np.zeros((dk_, dv_)) if dS_final is None else np.asarray(dS_final, np.float64)[b, h].copy()
+            for sl, S, X, T, R, D in reversed(saved):
+                Q, K, bt, dOc = q[b, h, sl], k[b, h, sl], beta[b, h, sl], dO[b, h, sl]
+                M = np.tril(Q @ K.T)
+                dD = M.T @ dOc + K @ G
+                dR = T.T @ dD
+                dM = np.tril(dOc @ D.T)
+                dT = dD @ R.T
+                dX = dT * bt[None, :]
+                db = np.sum(X * dT, axis=0)
+                dA = np.tril(-X.T @ dX @ X.T, -1)
+                W = bt[:, None] * dA
+                db = db + np.sum(dA * (K @ K.T), axis=1)
+                outs[0][b, h, sl] = dOc @ S.T + dM @ K
+                outs[1][b, h, sl] = dM.T @ Q + D @ G.T - dR @ S.T + W @ K + W.T @ K
+                outs[2][b, h, sl] = dR
+                outs[3][b, h, sl] = db
+                G = G + Q.T @ dOc - K.T @ dR
+            outs[4][b, h] = G
+    return tuple(outs)
