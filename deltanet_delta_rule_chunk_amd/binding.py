@@ -30,10 +30,11 @@ EXPORTS = ("deltanet_chunk_fwd", "deltanet_chunk_fwd_workspace_bytes", "deltanet
            "deltanet_gated_decode_step", "deltanet_feature_prep", "deltanet_chunk_fwd_features",
            "deltanet_chunk_fwd_features_workspace_bytes", "deltanet_decode_step_features",
            "deltanet_kda_chunk_fwd", "deltanet_kda_chunk_fwd_workspace_bytes",
-           "deltanet_kda_decode_step",
+           "deltanet_kda_decode_step", "deltanet_chunk_bwd", "deltanet_chunk_bwd_workspace_bytes",
            "deltanet_status_string", "deltanet_last_hip_error", "deltanet_version",
            "deltanet_profile_start", "deltanet_profile_stop")
-PROFILE_SLOTS = ("chunk_prep", "chunk_scan", "decode", "features")
+PROFILE_SLOTS = ("chunk_prep", "chunk_scan", "decode", "features", "bwd_prep", "bwd_fwd_scan",
+                 "bwd_scan", "bwd_cc", "bwd_qk")
 
 _lib = None
 
@@ -84,6 +85,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.deltanet_kda_chunk_fwd_workspace_bytes.restype = sz
     lib.deltanet_kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     lib.deltanet_kda_decode_step.restype = i
+    lib.deltanet_chunk_bwd.argtypes = [vp] * 12 + [i] * 7 + [vp, sz, vp]
+    lib.deltanet_chunk_bwd.restype = i
+    lib.deltanet_chunk_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.deltanet_chunk_bwd_workspace_bytes.restype = sz
     lib.deltanet_status_string.argtypes = [i]
     lib.deltanet_status_string.restype = ctypes.c_char_p
     lib.deltanet_last_hip_error.argtypes = []
@@ -147,6 +152,48 @@ def workspace_bytes(B: int, H: int, L: int, d_k: int, d_v: int, C: int,
                                                                     _code(in_dtype), int(gated)))
     fn = lib.deltanet_gated_chunk_fwd_workspace_bytes if gated else lib.deltanet_chunk_fwd_workspace_bytes
     return int(fn(B, H, L, d_k, d_v, C, _code(in_dtype)))
+
+
+def bwd_workspace_bytes(B: int, H: int, L: int, d_k: int, d_v: int, C: int = 64,
+                        in_dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(load().deltanet_chunk_bwd_workspace_bytes(B, H, L, d_k, d_v, C, _code(in_dtype)))
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+              S0: Optional[torch.Tensor], dO: torch.Tensor, dS_final: Optional[torch.Tensor] = None,
+              C: int = 64, *, want_dS0: bool = True, workspace: Optional[torch.Tensor] = None,
+              stream=None):
+    """Gradient of the chunked forward (``deltanet_chunk_bwd``).  q,k ``[B,H,L,d_k]``,
+    v ``[B,H,L,d_v]`` (fp32 or bf16), beta ``[B,H,L]``, S0 ``[B,H,d_k,d_v]`` or None,
+    dO ``[B,H,L,d_v]`` fp32, dS_final ``[B,H,d_k,d_v]`` fp32 or None.  Returns fp32
+    ``(dq, dk, dv, dbeta, dS0)`` (dS0 None when ``want_dS0`` is False)."""
+    lib = load()
+    B, H, L, d_k = q.shape
+    d_v = v.shape[-1]
+    dev = q.device
+    _check(q, "q", (B, H, L, d_k), device=dev)
+    _check(k, "k", (B, H, L, d_k), q.dtype, dev)
+    _check(v, "v", (B, H, L, d_v), q.dtype, dev)
+    _check(beta, "beta", (B, H, L), torch.float32, dev)
+    _check(dO, "dO", (B, H, L, d_v), torch.float32, dev)
+    for t, n in ((S0, "S0"), (dS_final, "dS_final")):
+        if t is not None:
+            _check(t, n, (B, H, d_k, d_v), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dk = torch.empty((B, H, L, d_k), **f32), torch.empty((B, H, L, d_k), **f32)
+    dv, db = torch.empty((B, H, L, d_v), **f32), torch.empty((B, H, L), **f32)
+    dS0 = torch.empty((B, H, d_k, d_v), **f32) if want_dS0 else None
+    need = bwd_workspace_bytes(B, H, L, d_k, d_v, C, q.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.deltanet_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(dO),
+                                _ptr(dS_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(dS0),
+                                B, H, L, d_k, d_v, C, _code(q.dtype), _ptr(workspace), ws_bytes,
+                                _stream(dev, stream))
+    if st != DN_OK:
+        _raise(lib, st, "deltanet_chunk_bwd")
+    return dq, dk, dv, db, dS0
 
 
 def kda_workspace_bytes(B: int, H: int, L: int, d_k: int, d_v: int, C: int = 64,

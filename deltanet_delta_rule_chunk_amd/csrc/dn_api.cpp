@@ -18,7 +18,7 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kVersion = 400;  // 0.4.0
+constexpr int kVersion = 500;  // 0.5.0
 
 int hip_fail(hipError_t e) {
   g_last_hip_error = static_cast<int>(e);
@@ -331,6 +331,61 @@ int deltanet_decode_step_features(const void* q_raw, const void* k_raw, const vo
                                   hipStream_t stream) {
   return decode_impl(q_raw, k_raw, v, alpha, beta_logit, S, o, B, H, d_k, d_v, in_dtype,
                      out_dtype, stream, true);
+}
+
+size_t deltanet_chunk_bwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
+                                          int in_dtype) {
+  ChunkSizes s;
+  if (check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, DN_F32, &s) != DN_OK) return 0;
+  return dn::chunk_bwd_workspace_bytes(B, H, L, d_k, d_v);
+}
+
+int deltanet_chunk_bwd(const void* q, const void* k, const void* v, const float* beta,
+                       const float* S0, const float* dO, const float* dS_final, float* dq,
+                       float* dk, float* dv, float* dbeta, float* dS0, int B, int H, int L,
+                       int d_k, int d_v, int C, int in_dtype, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  ChunkSizes s;
+  int st = check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, DN_F32, &s);
+  if (st != DN_OK) return st;
+  if (L > 0 && (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta))
+    return DN_ERR_NULL_ARG;
+  const void* ptrs[] = {q, k, v, beta, S0, dO, dS_final, dq, dk, dv, dbeta, dS0, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return DN_ERR_MISALIGNED;
+  const size_t tok = (size_t)B * H * (size_t)L;
+  const Span in[] = {{q, s.qk}, {k, s.qk}, {v, s.v}, {beta, s.beta}, {S0, s.state},
+                     {dO, tok * d_v * 4}, {dS_final, s.state}};
+  const Span out[] = {{dq, tok * d_k * 4}, {dk, tok * d_k * 4}, {dv, tok * d_v * 4},
+                      {dbeta, s.beta}, {dS0, s.state}};
+  const size_t need = dn::chunk_bwd_workspace_bytes(B, H, L, d_k, d_v);
+  const Span sw{workspace, workspace ? need : 0};
+  for (int i = 0; i < 5; ++i) {
+    for (const Span& x : in)
+      if (overlap(out[i], x)) return DN_ERR_ALIASING;
+    for (int j = i + 1; j < 5; ++j)
+      if (overlap(out[i], out[j])) return DN_ERR_ALIASING;
+    if (overlap(sw, out[i])) return DN_ERR_ALIASING;
+  }
+  for (const Span& x : in)
+    if (overlap(sw, x)) return DN_ERR_ALIASING;
+  if (workspace && workspace_bytes < need) return DN_ERR_WORKSPACE;
+
+  void* ws = workspace;
+  const bool own_ws = (ws == nullptr && need > 0);
+  if (own_ws) {
+    hipError_t e = hipMallocAsync(&ws, need, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  dn::BwdArgs a{q,  k,  v,     beta, S0, dO, dS_final, dq,        dk, dv, dbeta,
+                dS0, B, H, L, d_k, d_v, in_dtype, ws, stream};
+  hipError_t e = dn::launch_chunk_bwd(a);
+  if (own_ws) {
+    hipError_t f = hipFreeAsync(ws, stream);
+    if (e == hipSuccess) e = f;
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  return DN_OK;
 }
 
 size_t deltanet_kda_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,

@@ -60,7 +60,12 @@ enum ProfSlot {
   kSlotChunkScan = 1,
   kSlotDecode = 2,
   kSlotFeatures = 3,
-  kNumSlots = 4
+  kSlotBwdPrep = 4,
+  kSlotBwdFwdScan = 5,
+  kSlotBwdScan = 6,
+  kSlotBwdCc = 7,
+  kSlotBwdQk = 8,
+  kNumSlots = 9
 };
 
 // Records a HIP event on `s` before (end = false) or after (end = true) the
@@ -72,6 +77,22 @@ void prof_mark(int slot, bool end, hipStream_t s);
 size_t chunk_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int in_dtype,
                              bool gated);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
+// Gradient of the chunked forward (dn_backward.hip).
+struct BwdArgs {
+  const void *q, *k, *v;    // in_dtype
+  const float* beta;
+  const float* S0;          // may be null (zero state)
+  const float* dO;          // [B,H,L,d_v] fp32
+  const float* dS_final;    // may be null (zero)
+  float *dq, *dk, *dv, *dbeta;
+  float* dS0;               // may be null (not written)
+  int B, H, L, d_k, d_v, in_dtype;
+  void* workspace;          // at least chunk_bwd_workspace_bytes(...) bytes
+  hipStream_t stream;
+};
+size_t chunk_bwd_workspace_bytes(int B, int H, int L, int d_k, int d_v);
+hipError_t launch_chunk_bwd(const BwdArgs& a);
+
 // The per-dimension-decay (KDA) chunked forward: its workspace and launches.
 size_t kda_workspace_bytes(int B, int H, int L, int d_k);
 hipError_t launch_kda_chunk_fwd(const ChunkArgs& a);

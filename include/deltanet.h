@@ -137,6 +137,38 @@ int deltanet_gated_decode_step(const void* q, const void* k, const void* v, cons
                                hipStream_t stream);
 
 /*
+ * Gradient of the chunked forward (training).  The pages present the chunked
+ * form as the way to train the delta rule in linear time but print no
+ * backward pass; this one is the reverse-mode derivative of the forward
+ * above (plain delta rule, no gate).  Given the gradients of a loss with
+ * respect to the forward's outputs, it returns those with respect to its
+ * inputs:
+ *   q, k   : [B, H, L, d_k]  in_dtype;   v : [B, H, L, d_v] in_dtype
+ *   beta   : [B, H, L] fp32;  S0 : [B, H, d_k, d_v] fp32 or NULL (zero state)
+ *   dO     : [B, H, L, d_v] fp32, dL/do
+ *   dS_final: [B, H, d_k, d_v] fp32, dL/dS_final, or NULL (zero)
+ *   dq, dk : [B, H, L, d_k] fp32;  dv : [B, H, L, d_v] fp32;
+ *   dbeta  : [B, H, L] fp32;       dS0 : [B, H, d_k, d_v] fp32 or NULL (not
+ *            written)
+ * The forward is recomputed inside (nothing from a previous forward call is
+ * needed).  fp32 vector-ALU kernels for either input dtype, 64-token chunks
+ * whatever C names (C must still be 64 or 128).  Outputs may not overlap
+ * inputs or one another.  The workspace holds, per 64-token chunk, the
+ * entering state and the exit gradient (2 d_k d_v floats) besides per-chunk
+ * matrices: query deltanet_chunk_bwd_workspace_bytes().
+ */
+int deltanet_chunk_bwd(const void* q, const void* k, const void* v, const float* beta,
+                       const float* S0, const float* dO, const float* dS_final,
+                       float* dq, float* dk, float* dv, float* dbeta, float* dS0,
+                       int B, int H, int L, int d_k, int d_v, int C, int in_dtype,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace deltanet_chunk_bwd needs (0 if the sizes are invalid or
+ * unsupported). */
+size_t deltanet_chunk_bwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
+                                          int in_dtype);
+
+/*
  * Per-dimension decay (KDA).  The same article describes Kimi Linear's KDA as
  * Gated DeltaNet with the scalar gate turned into a vector: each dimension of
  * the memory forgets at its own rate.  The gate acts on the key dimension,
@@ -242,7 +274,9 @@ int deltanet_last_hip_error(void);
  * call's stream.  deltanet_profile_stop() waits for those events and writes,
  * per kernel slot, the summed elapsed milliseconds and the launch count
  * (nslots entries each; slots: 0 = chunk WY-prep kernel, 1 = chunk scan
- * kernel, 2 = decode kernel, 3 = feature-map kernel).  Recording adds two event records per launch.
+ * kernel, 2 = decode kernel, 3 = feature-map kernel; the backward's kernels:
+ * 4 = prep, 5 = forward state pass, 6 = reverse state pass, 7 = per-chunk
+ * matrix gradients, 8 = dq / dk).  Recording adds two event records per launch.
  */
 int deltanet_profile_start(void);
 int deltanet_profile_stop(double* ms_per_slot, int* launches_per_slot, int nslots);

@@ -33,7 +33,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.deltanet_version() == 400
+    assert lib.deltanet_version() == 500
     for s in range(8):
         assert lib.deltanet_status_string(s)
     assert lib.deltanet_status_string(99) == b"unknown status"
@@ -255,4 +255,37 @@ def test_kda_decode_validation(lib):
     assert d(alpha=BASE + 800 * MB + 8) == ALIGN
     assert d(o=BASE + 800 * MB + 2 * 3 * 4 * 64) == ALIAS   # inside the [B, H, d_k] gate
     assert d(S=BASE + 800 * MB + 1024) == ALIAS
+    assert lib.deltanet_last_hip_error() == 0
+
+
+def _bwd(lib, **kw):
+    a = dict(q=BASE, k=BASE + 100 * MB, v=BASE + 200 * MB, beta=BASE + 300 * MB, S0=None,
+             dO=BASE + 400 * MB, dSf=None, dq=BASE + 500 * MB, dk=BASE + 600 * MB,
+             dv=BASE + 700 * MB, db=BASE + 800 * MB, dS0=BASE + 900 * MB, B=1, H=2, L=256, dk_=64,
+             dv_=64, C=64, it=BF16, ws=BASE + 1000 * MB, wsb=1 << 40)
+    a.update(kw)
+    return lib.deltanet_chunk_bwd(a["q"], a["k"], a["v"], a["beta"], a["S0"], a["dO"], a["dSf"],
+                                  a["dq"], a["dk"], a["dv"], a["db"], a["dS0"], a["B"], a["H"],
+                                  a["L"], a["dk_"], a["dv_"], a["C"], a["it"], a["ws"], a["wsb"],
+                                  None)
+
+
+def test_chunk_bwd_validation(lib):
+    for name in ("q", "k", "v", "beta", "dO", "dq", "dk", "dv", "db"):
+        assert _bwd(lib, **{name: None}) == NULL, name
+    assert _bwd(lib, B=0) == SHAPE
+    assert _bwd(lib, dk_=80) == UNSUP
+    assert _bwd(lib, C=32) == UNSUP
+    assert _bwd(lib, dO=BASE + 400 * MB + 8) == ALIGN
+    assert _bwd(lib, dS0=BASE + 900 * MB + 4) == ALIGN
+    assert _bwd(lib, dq=BASE + 100 * MB) == ALIAS          # dq over k
+    assert _bwd(lib, dv=BASE + 400 * MB) == ALIAS          # dv over dO
+    assert _bwd(lib, db=BASE + 500 * MB + 64) == ALIAS     # dbeta inside dq
+    assert _bwd(lib, dS0=BASE + 700 * MB) == ALIAS         # dS0 over dv
+    assert _bwd(lib, ws=BASE + 800 * MB) == ALIAS          # workspace over dbeta
+    need = lib.deltanet_chunk_bwd_workspace_bytes(1, 2, 256, 64, 64, 64, BF16)
+    # per 64-token chunk: X, M, dM, W (64 x 64), the entering state and exit
+    # gradient (d_k x d_v), R, Delta, dDelta (64 x d_v), all fp32
+    assert need == 1 * 2 * 4 * (4 * 64 * 64 + 2 * 64 * 64 + 3 * 64 * 64) * 4
+    assert _bwd(lib, wsb=need - 1) == WS
     assert lib.deltanet_last_hip_error() == 0
