@@ -170,6 +170,8 @@ def main(argv=None) -> int:
                     help="skip timing the two smaller chunked workloads")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the gated (Gated DeltaNet) forward and decode measurements")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the chunked backward (gradient) measurement")
     ap.add_argument("--no-kda", action="store_true",
                     help="skip the per-dimension-decay (KDA) forward and decode measurements")
     ap.add_argument("--no-features", action="store_true",
@@ -374,6 +376,39 @@ def main(argv=None) -> int:
                 "tokens_per_s": wd.B / (ms_gd * 1e-3),
                 "pct_hbm_peak": 100.0 * gdb / (gk * 1e-3) / 1e9 / PEAK_HBM_GBS,
             }
+
+    if not a.no_backward:
+        # The gradient of the same forward (recomputing it inside): dO ~ N(0, 1).
+        print(f"[bench] backward {w.name}: {a.steps} steps", file=sys.stderr, flush=True)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(a.seed + 17)
+        dO = torch.randn(w.B, w.H, w.L, w.d_v, device=dev, generator=gen)
+        bws = torch.empty(binding.bwd_workspace_bytes(w.B, w.H, w.L, w.d_k, w.d_v, w.C),
+                          dtype=torch.uint8, device=dev)
+
+        def bstep():
+            return binding.chunk_bwd(g["q"], g["k"], g["v"], g["beta"], None, dO, None, w.C,
+                                     workspace=bws)
+
+        bstep()
+        torch.cuda.synchronize()
+        binding.profile_start()
+        ev0.record()
+        for _ in range(a.steps):
+            grads = bstep()
+        ev1.record()
+        torch.cuda.synchronize()
+        bprof = binding.profile_stop()
+        assert all(torch.isfinite(t).all() for t in grads if t is not None)
+        ms_b = ev0.elapsed_time(ev1) / a.steps
+        result["backward"] = {
+            "workload": w.name + "_backward", "steps": a.steps, "ms_per_step": ms_b,
+            "tokens_per_s": w.B * w.L / (ms_b * 1e-3),
+            "kernels_ms": {name: tot / n for name, (tot, n) in bprof.items()},
+            "path": "fp32 vector ALU, 64-token chunks, forward recomputed inside",
+            "grads_in": "dO ~ N(0, 1) (torch generator seeded), no dS_final",
+        }
+        del bws, dO, grads
 
     if not a.no_kda:
         # Per-dimension decay (KDA): fp32 vector-ALU chunk kernels, and the
