@@ -72,6 +72,30 @@ __device__ __forceinline__ void load_f32(float* dst, int ld, const float* src, i
   }
 }
 
+// A workgroup's ROWS x COLS tile held in registers, NTHR-strided (element
+// e = threadIdx.x + p NTHR): the scans fetch the next chunk's operands into
+// one while they compute the current chunk, then deposit it into LDS.
+template <int ROWS, int COLS, typename T>
+struct RegTile {
+  static constexpr int N = ROWS * COLS / NTHR;
+  static_assert(N * NTHR == ROWS * COLS, "tile");
+  float x[N];
+  __device__ __forceinline__ void load(const T* src, int rows_valid) {
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+      const int e = threadIdx.x + p * NTHR, r = e / COLS;
+      x[p] = r < rows_valid ? to_f32(src[e]) : 0.f;
+    }
+  }
+  __device__ __forceinline__ void store(float* dst, int ld) const {
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+      const int e = threadIdx.x + p * NTHR;
+      dst[(e / COLS) * ld + e % COLS] = x[p];
+    }
+  }
+};
+
 // ---- prep: X = (I + A)^{-1} and M = tril(Q K^T) ---------------------------
 template <int DK>
 struct PrepSmem {
@@ -149,19 +173,30 @@ __global__ __launch_bounds__(NTHR) void fwd_scan_kernel(const IT* __restrict__ k
     const int d = r + m * RS;
     Ss[d * NT + j] = S0 ? S0[((size_t)bh * DK + d) * DV + j0 + j] : 0.f;
   }
+  RegTile<C, DK, IT> tk;
+  RegTile<C, C, float> tx;
+  float pb = 0.f, pv = 0.f;
+  auto fetch = [&](int cc) {
+    const int vc = min(C, L - cc * C);
+    const size_t t0 = (size_t)bh * L + (size_t)cc * C;
+    tk.load(k + t0 * DK, vc);
+    tx.load(ws + ((size_t)bh * nc + cc) * W.per_chunk() + W.X(), C);
+    pb = (int)threadIdx.x < vc ? beta[t0 + threadIdx.x] : 0.f;
+    pv = r < vc ? to_f32(v[(t0 + r) * DV + j0 + j]) : 0.f;
+  };
+  if (nc > 0) fetch(0);
   for (int c = 0; c < nc; ++c) {
-    const int valid = min(C, L - c * C);
-    const size_t tok0 = (size_t)bh * L + (size_t)c * C;
     float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
-    load_rows(Ks, LD, k + tok0 * DK, valid, C, DK);
-    load_f32(Xs, LDC, blk + W.X(), C, C, C, C);
-    for (int i = threadIdx.x; i < C; i += blockDim.x) bs[i] = i < valid ? beta[tok0 + i] : 0.f;
+    tk.store(Ks, LD);
+    tx.store(Xs, LDC);
+    if (threadIdx.x < C) bs[threadIdx.x] = pb;
+    float acc = pv;
     __syncthreads();
+    if (c + 1 < nc) fetch(c + 1);  // in flight while this chunk computes
     for (int m = 0; m < MS; ++m) {  // the entering state
       const int d = r + m * RS;
       blk[W.S() + (size_t)d * DV + j0 + j] = Ss[d * NT + j];
     }
-    float acc = r < valid ? to_f32(v[(tok0 + r) * DV + j0 + j]) : 0.f;
     for (int d = 0; d < DK; ++d) acc -= Ks[r * LD + d] * Ss[d * NT + j];
     Rs[r * NT + j] = acc;
     blk[W.R() + (size_t)r * DV + j0 + j] = acc;
@@ -216,17 +251,33 @@ __global__ __launch_bounds__(NTHR) void bwd_scan_kernel(
     const int d = r + m * RS;
     Gs[d * NT + j] = dS_final ? dS_final[((size_t)bh * DK + d) * DV + j0 + j] : 0.f;
   }
+  RegTile<C, DK, IT> tq, tk;
+  RegTile<C, C, float> tm, tx;
+  float pb = 0.f, pd = 0.f;
+  auto fetch = [&](int cc) {
+    const int vc = min(C, L - cc * C);
+    const size_t t0 = (size_t)bh * L + (size_t)cc * C;
+    const float* b = ws + ((size_t)bh * nc + cc) * W.per_chunk();
+    tq.load(q + t0 * DK, vc);
+    tk.load(k + t0 * DK, vc);
+    tm.load(b + W.M(), C);
+    tx.load(b + W.X(), C);
+    pb = (int)threadIdx.x < vc ? beta[t0 + threadIdx.x] : 0.f;
+    pd = r < vc ? dO[(t0 + r) * DV + j0 + j] : 0.f;
+  };
+  if (nc > 0) fetch(nc - 1);
   for (int c = nc - 1; c >= 0; --c) {
     const int valid = min(C, L - c * C);
     const size_t tok0 = (size_t)bh * L + (size_t)c * C;
     float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
-    load_rows(Qs, LD, q + tok0 * DK, valid, C, DK);
-    load_rows(Ks, LD, k + tok0 * DK, valid, C, DK);
-    load_f32(Ms, LDC, blk + W.M(), C, C, C, C);
-    load_f32(Xs, LDC, blk + W.X(), C, C, C, C);
-    for (int i = threadIdx.x; i < C; i += blockDim.x) bs[i] = i < valid ? beta[tok0 + i] : 0.f;
-    dOs[r * NT + j] = r < valid ? dO[(tok0 + r) * DV + j0 + j] : 0.f;
+    tq.store(Qs, LD);
+    tk.store(Ks, LD);
+    tm.store(Ms, LDC);
+    tx.store(Xs, LDC);
+    if (threadIdx.x < C) bs[threadIdx.x] = pb;
+    dOs[r * NT + j] = pd;
     __syncthreads();
+    if (c > 0) fetch(c - 1);  // in flight while this chunk computes
     for (int m = 0; m < MS; ++m) {  // the exit gradient
       const int d = r + m * RS;
       blk[W.G() + (size_t)d * DV + j0 + j] = Gs[d * NT + j];
@@ -302,21 +353,27 @@ __global__ __launch_bounds__(NTHR) void cc_grad_kernel(const IT* __restrict__ k,
     load_f32(P1, LDH, dO + tok0 * DV + h, DV, valid, C, HW);
     load_f32(P2, LDH, blk + W.D() + h, DV, C, C, HW);
     __syncthreads();
-    for (int p = 0; p < PER; ++p) {
-      const int e = threadIdx.x + p * NTHR, r = e / C, i = e % C;
-      if (i <= r)
-        #pragma unroll 8
-        for (int jj = 0; jj < HW; ++jj) am[p] += P1[r * LDH + jj] * P2[i * LDH + jj];
+    {  // a thread's PER entries share the column i = threadIdx.x mod C
+      const int i = threadIdx.x % C;
+#pragma unroll 4
+      for (int jj = 0; jj < HW; ++jj) {
+        const float b = P2[i * LDH + jj];
+#pragma unroll
+        for (int p = 0; p < PER; ++p) am[p] += P1[((threadIdx.x + p * NTHR) / C) * LDH + jj] * b;
+      }
     }
     __syncthreads();
     load_f32(P1, LDH, blk + W.dD() + h, DV, C, C, HW);
     load_f32(P2, LDH, blk + W.R() + h, DV, C, C, HW);
     __syncthreads();
-    for (int p = 0; p < PER; ++p) {
-      const int e = threadIdx.x + p * NTHR, r = e / C, i = e % C;
-      if (i <= r)
-        #pragma unroll 8
-        for (int jj = 0; jj < HW; ++jj) at[p] += P1[r * LDH + jj] * P2[i * LDH + jj];
+    {  // a thread's PER entries share the column i = threadIdx.x mod C
+      const int i = threadIdx.x % C;
+#pragma unroll 4
+      for (int jj = 0; jj < HW; ++jj) {
+        const float b = P2[i * LDH + jj];
+#pragma unroll
+        for (int p = 0; p < PER; ++p) at[p] += P1[((threadIdx.x + p * NTHR) / C) * LDH + jj] * b;
+      }
     }
     __syncthreads();
   }
@@ -325,9 +382,10 @@ __global__ __launch_bounds__(NTHR) void cc_grad_kernel(const IT* __restrict__ k,
   for (int i = threadIdx.x; i < C; i += blockDim.x) bs[i] = i < valid ? beta[tok0 + i] : 0.f;
   for (int p = 0; p < PER; ++p) {
     const int e = threadIdx.x + p * NTHR, r = e / C, i = e % C;
-    dMs[r * LDC + i] = am[p];  // zero above the diagonal
-    dTs[r * LDC + i] = at[p];
-    blk[W.dM() + e] = am[p];
+    const float m_ = i <= r ? am[p] : 0.f, t_ = i <= r ? at[p] : 0.f;  // lower triangles
+    dMs[r * LDC + i] = m_;
+    dTs[r * LDC + i] = t_;
+    blk[W.dM() + e] = m_;
   }
   __syncthreads();
   // dbeta_i from T = X diag(beta), then dX = dT diag(beta) in place.
@@ -346,7 +404,7 @@ __global__ __launch_bounds__(NTHR) void cc_grad_kernel(const IT* __restrict__ k,
   for (int p = 0; p < PER; ++p) {
     const int e = threadIdx.x + p * NTHR, a = e / C, b = e % C;
     float s = 0.f;
-    #pragma unroll 8
+#pragma unroll 8
     for (int r = a > b ? a : b; r < C; ++r) s += Xs[r * LDC + a] * dTs[r * LDC + b];
     Ys[a * LDC + b] = s;
   }
@@ -356,7 +414,7 @@ __global__ __launch_bounds__(NTHR) void cc_grad_kernel(const IT* __restrict__ k,
     const int e = threadIdx.x + p * NTHR, r = e / C, i = e % C;
     float s = 0.f;
     if (i < r)
-      #pragma unroll 8
+#pragma unroll 8
       for (int b = 0; b <= i; ++b) s -= Ys[r * LDC + b] * Xs[i * LDC + b];
     dTs[r * LDC + i] = s;
     blk[W.W() + e] = bs[r] * s;
@@ -369,7 +427,7 @@ __global__ __launch_bounds__(NTHR) void cc_grad_kernel(const IT* __restrict__ k,
     float s = 0.f;
     for (int i = l; i < r; i += 16) {
       float kk = 0.f;
-      #pragma unroll 8
+#pragma unroll 8
       for (int d = 0; d < DK; ++d) kk += Ks[r * LD + d] * Ks[i * LD + d];
       s += dTs[r * LDC + i] * kk;
     }
@@ -422,17 +480,17 @@ __global__ __launch_bounds__(NTHR) void qk_grad_kernel(
       load_f32(Dh, LDH, blk + W.D() + h, DV, C, C, HW);
       load_f32(dRh, LDH, dv + tok0 * DV + h, DV, valid, C, HW);
       __syncthreads();
-      for (int m = 0; m < MC; ++m) {
-        const int d = cg + m * NCG;
-        float sq = 0.f, sk = 0.f;
-        #pragma unroll 8
-        for (int jj = 0; jj < HW; ++jj) {
-          const float s = Sh[d * LDH + jj];
-          sq += dOh[r * LDH + jj] * s;
-          sk += Dh[r * LDH + jj] * Gh[d * LDH + jj] - dRh[r * LDH + jj] * s;
+      // One read of this row's dO, Delta, dR per column feeds all MC outputs.
+#pragma unroll 2
+      for (int jj = 0; jj < HW; ++jj) {
+        const float o_ = dOh[r * LDH + jj], dl = Dh[r * LDH + jj], rr = dRh[r * LDH + jj];
+#pragma unroll
+        for (int m = 0; m < MC; ++m) {
+          const int d = cg + m * NCG;
+          const float sv = Sh[d * LDH + jj];
+          aq[m] += o_ * sv;
+          ak[m] += dl * Gh[d * LDH + jj] - rr * sv;
         }
-        aq[m] += sq;
-        ak[m] += sk;
       }
       __syncthreads();
     }
@@ -447,17 +505,19 @@ __global__ __launch_bounds__(NTHR) void qk_grad_kernel(
     load_f32(dMs, LDC, blk + W.dM(), C, C, C, C);
     load_f32(Wm, LDC, blk + W.W(), C, C, C, C);
     __syncthreads();
-    for (int m = 0; m < MC; ++m) {
-      const int d = cg + m * NCG;
-      float sq = 0.f, sk = 0.f;
-      #pragma unroll 8
-      for (int i = 0; i <= r; ++i) sq += dMs[r * LDC + i] * Ks[i * LD + d];
-      #pragma unroll 8
-      for (int a = r; a < C; ++a) sk += dMs[a * LDC + r] * Qs[a * LD + d];
-      #pragma unroll 8
-      for (int a = 0; a < C; ++a) sk += (Wm[r * LDC + a] + Wm[a * LDC + r]) * Ks[a * LD + d];
-      aq[m] += sq;
-      ak[m] += sk;
+    // dM and W hold zeros outside their triangles, so every row a can be
+    // summed: dM_ra (a <= r), dM_ar (a >= r), W_ra + W_ar.
+#pragma unroll 2
+    for (int a = 0; a < C; ++a) {
+      const float mra = dMs[r * LDC + a], mar = dMs[a * LDC + r];
+      const float w = Wm[r * LDC + a] + Wm[a * LDC + r];
+#pragma unroll
+      for (int m = 0; m < MC; ++m) {
+        const int d = cg + m * NCG;
+        const float kv = Ks[a * LD + d];
+        aq[m] += mra * kv;
+        ak[m] += mar * Qs[a * LD + d] + w * kv;
+      }
     }
   }
   if (r < valid)
