@@ -48,6 +48,8 @@ KERNEL_SOURCES["features_decode"] = KERNEL_SOURCES["decode"]
 KERNEL_SOURCES["kda_decode"] = KERNEL_SOURCES["decode"]
 KERNEL_SOURCES["kda_chunk_prep"] = KERNEL_SOURCES["kda_chunk_scan"] = [
     "dn_kda.hip", "dn_valu_common.h", "dn_common.h"]
+for _k in ("bwd_prep", "bwd_fwd_scan", "bwd_scan", "bwd_cc", "bwd_qk"):
+    KERNEL_SOURCES[_k] = ["dn_backward.hip", "dn_valu_common.h", "dn_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters.json")
 
