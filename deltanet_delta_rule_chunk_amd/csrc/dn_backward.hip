@@ -1,5 +1,6 @@
-// dn_backward.hip -- gradient of the chunked delta-rule forward, fp32
-// vector-ALU kernels.
+// dn_backward.hip -- gradient of the chunked delta-rule forward: fp32
+// vector-ALU kernels, with the two state scans on the matrix cores for bf16
+// inputs (dn_backward_mfma.hip).
 //
 // The pages present the chunked form as the way to train the delta rule in
 // linear time (page "GPT-2 から Kimi K3 まで、AI モデルの進化を解説", section
@@ -30,6 +31,7 @@
 //   qk_grad   (chunk, head): dQ and dK.
 // A ragged last chunk reads zero rows (k = q = 0, beta = 0, dO = 0).
 
+#include "dn_backward.h"
 #include "dn_common.h"
 #include "dn_launch.h"
 #include "dn_valu_common.h"
@@ -38,29 +40,9 @@ namespace dn {
 namespace bwd {
 
 using valu::load_rows;
-constexpr int C = 64;      // chunk rows
-constexpr int NT = 16;     // d_v columns per scan workgroup
 constexpr int HV = 64;     // d_v columns staged at a time by the gradient kernels
 constexpr int NTHR = 1024;
 constexpr int LDC = C + 1;
-
-// Workspace per (head, chunk), in floats.
-struct Ws {
-  int dk, dv;
-  __host__ __device__ constexpr size_t per_chunk() const {
-    return 4 * (size_t)C * C + 2 * (size_t)dk * dv + 3 * (size_t)C * dv;
-  }
-  // Offsets inside a chunk's block.
-  __host__ __device__ constexpr size_t X() const { return 0; }
-  __host__ __device__ constexpr size_t M() const { return (size_t)C * C; }
-  __host__ __device__ constexpr size_t dM() const { return 2 * (size_t)C * C; }
-  __host__ __device__ constexpr size_t W() const { return 3 * (size_t)C * C; }
-  __host__ __device__ constexpr size_t S() const { return 4 * (size_t)C * C; }
-  __host__ __device__ constexpr size_t G() const { return S() + (size_t)dk * dv; }
-  __host__ __device__ constexpr size_t R() const { return G() + (size_t)dk * dv; }
-  __host__ __device__ constexpr size_t D() const { return R() + (size_t)C * dv; }
-  __host__ __device__ constexpr size_t dD() const { return D() + (size_t)C * dv; }
-};
 
 // rows x cols of an fp32 matrix (row pitch src_ld) into LDS (row pitch ld);
 // rows at or past rows_valid read as zero.
@@ -548,6 +530,9 @@ hipError_t launch_t(const BwdArgs& a) {
   const IT *q = static_cast<const IT*>(a.q), *k = static_cast<const IT*>(a.k);
   const IT* v = static_cast<const IT*>(a.v);
   const dim3 chunks(nc, bh), slices(DV / NT, bh), blk(NTHR);
+  // bf16 q, k, v: the state scans run on the matrix cores
+  // (dn_backward_mfma.hip); fp32 inputs keep the vector-ALU scans.
+  constexpr bool kMatrixCores = sizeof(IT) == 2;
   if (nc > 0) {
     DN_TRY(set_smem(&prep_kernel<DK, DV, IT>, PrepSmem<DK>::bytes));
     prof_mark(kSlotBwdPrep, false, a.stream);
@@ -555,18 +540,27 @@ hipError_t launch_t(const BwdArgs& a) {
                        a.beta, a.L, ws);
     DN_TRY(hipGetLastError());
     prof_mark(kSlotBwdPrep, true, a.stream);
-    DN_TRY(set_smem(&fwd_scan_kernel<DK, DV, IT>, FwdSmem<DK>::bytes));
     prof_mark(kSlotBwdFwdScan, false, a.stream);
-    hipLaunchKernelGGL((fwd_scan_kernel<DK, DV, IT>), slices, blk, FwdSmem<DK>::bytes, a.stream, k,
-                       v, a.beta, a.S0, a.L, nc, ws);
-    DN_TRY(hipGetLastError());
+    if (kMatrixCores) {
+      DN_TRY(launch_fwd_scan_mfma(DK, DV, k, v, a.beta, a.S0, a.L, nc, bh, ws, a.stream));
+    } else {
+      DN_TRY(set_smem(&fwd_scan_kernel<DK, DV, IT>, FwdSmem<DK>::bytes));
+      hipLaunchKernelGGL((fwd_scan_kernel<DK, DV, IT>), slices, blk, FwdSmem<DK>::bytes, a.stream,
+                         k, v, a.beta, a.S0, a.L, nc, ws);
+      DN_TRY(hipGetLastError());
+    }
     prof_mark(kSlotBwdFwdScan, true, a.stream);
   }
-  DN_TRY(set_smem(&bwd_scan_kernel<DK, DV, IT>, BwdSmem<DK>::bytes));
   prof_mark(kSlotBwdScan, false, a.stream);
-  hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, IT>), slices, blk, BwdSmem<DK>::bytes, a.stream, q, k,
-                     a.beta, a.dO, a.dS_final, a.dv, a.dS0, a.L, nc, ws);
-  DN_TRY(hipGetLastError());
+  if (kMatrixCores && nc > 0) {
+    DN_TRY(launch_bwd_scan_mfma(DK, DV, q, k, a.beta, a.dO, a.dS_final, a.dv, a.dS0, a.L, nc, bh,
+                                ws, a.stream));
+  } else {
+    DN_TRY(set_smem(&bwd_scan_kernel<DK, DV, IT>, BwdSmem<DK>::bytes));
+    hipLaunchKernelGGL((bwd_scan_kernel<DK, DV, IT>), slices, blk, BwdSmem<DK>::bytes, a.stream, q,
+                       k, a.beta, a.dO, a.dS_final, a.dv, a.dS0, a.L, nc, ws);
+    DN_TRY(hipGetLastError());
+  }
   prof_mark(kSlotBwdScan, true, a.stream);
   if (nc > 0) {
     DN_TRY(set_smem(&cc_grad_kernel<DK, DV, IT>, CcSmem<DK>::bytes));

@@ -1,0 +1,475 @@
+// dn_backward_mfma.hip -- the backward's two state scans on the gfx950
+// matrix cores, for bf16 q, k, v.
+//
+// The products are those of the vector-ALU scans in dn_backward.hip (the
+// chunk algebra is derived there), taken as 16 x 16 x 32 bf16 MFMAs with
+// fp32 accumulation.  q and k are exact in bf16; every fp32 operand (the
+// state S, its gradient G', X, M, dO, R, Delta, dDelta, dR) is carried as a
+// split (hi, lo) bf16 pair (dn_mfma.h), so each product keeps roughly fp32
+// accuracy.
+//
+// One 4-wave workgroup per (head, 16 columns of d_v).  The slice of the
+// state lives in MFMA accumulators: wave w holds the d_k / 64 row tiles
+// w * d_k / 64 ...  Each chunk step is four phases separated by barriers:
+//   0  the staged operands of the chunk go into LDS (transposed copies where
+//      a product contracts over chunk rows), the state is written out and
+//      published to LDS as a split B operand;
+//   1  wave w forms row tile w (16 chunk rows) of the first product;
+//   2  wave w forms row tile w of the second;
+//   3  every wave advances its state tiles.
+// The next chunk's operands are loaded into registers right after phase 0,
+// so their latency hides behind phases 1-3.
+//
+// LDS operand arrays are bf16 with rows padded by 16 bytes.  A fragment
+// read `frag(a, P, r0, kb)` gives lane l the 8 contraction slots
+// kb + 8 (l / 16) ... of row r0 + l % 16, which is the A layout of the MFMA
+// and, for an array stored [column][contraction], also its B layout.
+
+#include "dn_backward.h"
+#include "dn_common.h"
+#include "dn_mfma.h"
+
+namespace dn {
+namespace bwd {
+namespace mf {
+
+constexpr int NTH = 256;   // 4 waves
+constexpr int PC = C + 8;  // pitch (bf16) of arrays whose contraction runs over chunk rows
+
+__device__ __forceinline__ bf16x8 frag(const uint16_t* a, int P, int r0, int kb) {
+  const int l = threadIdx.x & 63;
+  return as_bf16x8(*reinterpret_cast<const uint4*>(a + (r0 + (l & 15)) * P + kb + 8 * (l >> 4)));
+}
+
+// A D tile (lane: column l % 16, rows r0 + 4 (l / 16) + e) split into hi and
+// lo and stored transposed, hi[column * P + row].
+__device__ __forceinline__ void put_split_t(uint16_t* hi, uint16_t* lo, int P, int r0, f32x4 v) {
+  const int l = threadIdx.x & 63;
+  uint2 h, o;
+  split4(v, h, o);
+  const int off = (l & 15) * P + r0 + 4 * (l >> 4);
+  *reinterpret_cast<uint2*>(hi + off) = h;
+  *reinterpret_cast<uint2*>(lo + off) = o;
+}
+
+// bf16 element e (0..7) of 16 bytes.
+__device__ __forceinline__ uint16_t elem8(const uint4& x, int e) {
+  const uint32_t w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
+  return static_cast<uint16_t>(w >> (16 * (e & 1)));
+}
+
+// Loads of one chunk's C x DK bf16 tile (q or k): 16 bytes per thread per
+// step, the chunk row fastest across lanes; rows at or past `valid` read as
+// zero (the load itself is clamped to a valid row).
+template <int DK>
+struct RowTile {
+  static constexpr int N = C * DK / 8 / NTH;
+  uint4 x[N];
+  __device__ __forceinline__ void load(const bf16* src, int valid) {
+    const uint4* s = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+      const int f = threadIdx.x + p * NTH, r = f % C, c8 = f / C;
+      const uint4 v = s[min(r, valid - 1) * (DK / 8) + c8];
+      x[p] = r < valid ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  // Row-major copy [C][DK + 8].
+  __device__ __forceinline__ void put_rows(uint16_t* dst) const {
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+      const int f = threadIdx.x + p * NTH, r = f % C, c8 = f / C;
+      *reinterpret_cast<uint4*>(dst + r * (DK + 8) + 8 * c8) = x[p];
+    }
+  }
+  // Transposed copy [DK][PC].
+  __device__ __forceinline__ void put_cols(uint16_t* dst) const {
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+      const int f = threadIdx.x + p * NTH, r = f % C, c8 = f / C;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[(8 * c8 + e) * PC + r] = elem8(x[p], e);
+    }
+  }
+};
+
+// Loads of one chunk's C x C fp32 block of the workspace (X or M).
+struct SqTile {
+  static constexpr int N = C * C / 4 / NTH;
+  float4 x[N];
+  __device__ __forceinline__ void load(const float* src) {
+    const float4* s = reinterpret_cast<const float4*>(src);
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+      const int f = threadIdx.x + p * NTH, r = f % C, c4 = f / C;
+      x[p] = s[r * (C / 4) + c4];
+    }
+  }
+  // Split, row-major [C][PC].
+  __device__ __forceinline__ void put_rows(uint16_t* hi, uint16_t* lo) const {
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+      const int f = threadIdx.x + p * NTH, r = f % C, c4 = f / C;
+      uint2 h, o;
+      split4(x[p], h, o);
+      *reinterpret_cast<uint2*>(hi + r * PC + 4 * c4) = h;
+      *reinterpret_cast<uint2*>(lo + r * PC + 4 * c4) = o;
+    }
+  }
+  // Split, transposed [C][PC]: hi[column * PC + row].
+  __device__ __forceinline__ void put_cols(uint16_t* hi, uint16_t* lo) const {
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+      const int f = threadIdx.x + p * NTH, r = f % C, c4 = f / C;
+      uint2 h, o;
+      split4(x[p], h, o);
+      hi[(4 * c4 + 0) * PC + r] = static_cast<uint16_t>(h.x);
+      hi[(4 * c4 + 1) * PC + r] = static_cast<uint16_t>(h.x >> 16);
+      hi[(4 * c4 + 2) * PC + r] = static_cast<uint16_t>(h.y);
+      hi[(4 * c4 + 3) * PC + r] = static_cast<uint16_t>(h.y >> 16);
+      lo[(4 * c4 + 0) * PC + r] = static_cast<uint16_t>(o.x);
+      lo[(4 * c4 + 1) * PC + r] = static_cast<uint16_t>(o.x >> 16);
+      lo[(4 * c4 + 2) * PC + r] = static_cast<uint16_t>(o.y);
+      lo[(4 * c4 + 3) * PC + r] = static_cast<uint16_t>(o.y >> 16);
+    }
+  }
+};
+
+// ---- forward state pass -----------------------------------------------------
+template <int DK>
+struct FwdLds {
+  static constexpr int PK = DK + 8;
+  static constexpr int PV = NT + 1;
+  static constexpr size_t halves = (size_t)C * PK + (size_t)DK * PC + 2 * (size_t)C * PC +
+                                   2 * (size_t)NT * PK + 4 * (size_t)NT * PC;
+  static constexpr size_t bytes = halves * 2 + ((size_t)C * PV + C) * sizeof(float);
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ k,
+                                                       const bf16* __restrict__ v,
+                                                       const float* __restrict__ beta,
+                                                       const float* __restrict__ S0, int L,
+                                                       int nc, float* __restrict__ ws) {
+  using LD = FwdLds<DK>;
+  constexpr int PK = LD::PK, PV = LD::PV;
+  constexpr Ws W{DK, DV};
+  constexpr int TPW = DK / 64;  // state row tiles per wave
+  extern __shared__ uint4 lds_u4[];
+  uint16_t* Kb = reinterpret_cast<uint16_t*>(lds_u4);  // K rows     [C][PK]
+  uint16_t* Kt = Kb + C * PK;                           // K^T        [DK][PC]
+  uint16_t* Xh = Kt + DK * PC;                          // X          [C][PC]
+  uint16_t* Xl = Xh + C * PC;
+  uint16_t* Sh = Xl + C * PC;                           // -S^T       [NT][PK]
+  uint16_t* Sl = Sh + NT * PK;
+  uint16_t* Rh = Sl + NT * PK;                          // (beta R)^T [NT][PC]
+  uint16_t* Rl = Rh + NT * PC;
+  uint16_t* Dh = Rl + NT * PC;                          // Delta^T    [NT][PC]
+  uint16_t* Dl = Dh + NT * PC;
+  float* Vs = reinterpret_cast<float*>(Dl + NT * PC);   // V slice    [C][PV]
+  float* bs = Vs + C * PV;
+
+  const int j0 = blockIdx.x * NT, bh = blockIdx.y;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
+
+  f32x4 S[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int d0 = 16 * (w * TPW + i) + 4 * g;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) S[i][e] = S0 ? S0[((size_t)bh * DK + d0 + e) * DV + j0 + n] : 0.f;
+  }
+
+  RowTile<DK> tk;
+  SqTile tx;
+  uint2 pv;
+  float pb = 0.f;
+  auto fetch = [&](int cc) {
+    const int vc = min(C, L - cc * C);
+    const size_t t0 = (size_t)bh * L + (size_t)cc * C;
+    tk.load(k + t0 * DK, vc);
+    tx.load(ws + ((size_t)bh * nc + cc) * W.per_chunk() + W.X());
+    const int r = t % C, c4 = t / C;
+    const uint2 x = *reinterpret_cast<const uint2*>(v + (t0 + min(r, vc - 1)) * DV + j0 + 4 * c4);
+    pv = r < vc ? x : make_uint2(0u, 0u);
+    if (t < C) pb = t < vc ? beta[t0 + t] : 0.f;
+  };
+
+  fetch(0);
+  for (int c = 0; c < nc; ++c) {
+    float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
+    // Phase 0: operands into LDS; the entering state out and into LDS.
+    tk.put_rows(Kb);
+    tk.put_cols(Kt);
+    tx.put_rows(Xh, Xl);
+    {
+      const int r = t % C, c4 = t / C;
+      Vs[r * PV + 4 * c4 + 0] = __uint_as_float(pv.x << 16);
+      Vs[r * PV + 4 * c4 + 1] = __uint_as_float(pv.x & 0xffff0000u);
+      Vs[r * PV + 4 * c4 + 2] = __uint_as_float(pv.y << 16);
+      Vs[r * PV + 4 * c4 + 3] = __uint_as_float(pv.y & 0xffff0000u);
+    }
+    if (t < C) bs[t] = pb;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int d0 = 16 * (w * TPW + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) blk[W.S() + (size_t)(d0 + 4 * g + e) * DV + j0 + n] = S[i][e];
+      put_split_t(Sh, Sl, PK, d0, -S[i]);
+    }
+    __syncthreads();
+    if (c + 1 < nc) fetch(c + 1);
+
+    // Phase 1: R = V - K S, row tile w.
+    const int r0 = 16 * w;
+    f32x4 acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = Vs[(r0 + 4 * g + e) * PV + n];
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks)
+      acc = mfma_split2(frag(Kb, PK, r0, 32 * ks), frag(Sh, PK, 0, 32 * ks), frag(Sl, PK, 0, 32 * ks),
+                        acc);
+    f32x4 rb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      blk[W.R() + (size_t)(r0 + 4 * g + e) * DV + j0 + n] = acc[e];
+      rb[e] = acc[e] * bs[r0 + 4 * g + e];
+    }
+    put_split_t(Rh, Rl, PC, r0, rb);
+    __syncthreads();
+
+    // Phase 2: Delta = X diag(beta) R, row tile w (X is lower triangular, so
+    // the contraction stops at the tile's last row).
+    acc = zero4();
+#pragma unroll
+    for (int ks = 0; ks <= w / 2; ++ks)
+      acc = mfma_split3(frag(Xh, PC, r0, 32 * ks), frag(Xl, PC, r0, 32 * ks), frag(Rh, PC, 0, 32 * ks),
+                        frag(Rl, PC, 0, 32 * ks), acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) blk[W.D() + (size_t)(r0 + 4 * g + e) * DV + j0 + n] = acc[e];
+    put_split_t(Dh, Dl, PC, r0, acc);
+    __syncthreads();
+
+    // Phase 3: S += K^T Delta.
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int ks = 0; ks < C / 32; ++ks)
+        S[i] = mfma_split2(frag(Kt, PC, 16 * (w * TPW + i), 32 * ks), frag(Dh, PC, 0, 32 * ks),
+                           frag(Dl, PC, 0, 32 * ks), S[i]);
+    __syncthreads();
+  }
+}
+
+// ---- reverse state pass -----------------------------------------------------
+template <int DK>
+struct BwdLds {
+  static constexpr int PK = DK + 8;
+  static constexpr size_t halves = (size_t)C * PK + 2 * (size_t)DK * PC + 4 * (size_t)C * PC +
+                                   2 * (size_t)NT * PK + 6 * (size_t)NT * PC;
+  static constexpr size_t bytes = halves * 2 + (size_t)C * sizeof(float);
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NTH) void bwd_scan_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ beta,
+    const float* __restrict__ dO, const float* __restrict__ dS_final, float* __restrict__ dv,
+    float* __restrict__ dS0, int L, int nc, float* __restrict__ ws) {
+  using LD = BwdLds<DK>;
+  constexpr int PK = LD::PK;
+  constexpr Ws W{DK, DV};
+  constexpr int TPW = DK / 64;
+  extern __shared__ uint4 lds_u4[];
+  uint16_t* Kb = reinterpret_cast<uint16_t*>(lds_u4);  // K rows        [C][PK]
+  uint16_t* Kt = Kb + C * PK;                           // K^T           [DK][PC]
+  uint16_t* Qt = Kt + DK * PC;                          // Q^T           [DK][PC]
+  uint16_t* Mh = Qt + DK * PC;                          // M^T           [C][PC]
+  uint16_t* Ml = Mh + C * PC;
+  uint16_t* Xh = Ml + C * PC;                           // X^T           [C][PC]
+  uint16_t* Xl = Xh + C * PC;
+  uint16_t* Gh = Xl + C * PC;                           // G'^T          [NT][PK]
+  uint16_t* Gl = Gh + NT * PK;
+  uint16_t* Oh = Gl + NT * PK;                          // dO^T          [NT][PC]
+  uint16_t* Ol = Oh + NT * PC;
+  uint16_t* Eh = Ol + NT * PC;                          // dDelta^T      [NT][PC]
+  uint16_t* El = Eh + NT * PC;
+  uint16_t* Fh = El + NT * PC;                          // -dR^T         [NT][PC]
+  uint16_t* Fl = Fh + NT * PC;
+  float* bs = reinterpret_cast<float*>(Fl + NT * PC);
+
+  const int j0 = blockIdx.x * NT, bh = blockIdx.y;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
+
+  f32x4 G[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int d0 = 16 * (w * TPW + i) + 4 * g;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      G[i][e] = dS_final ? dS_final[((size_t)bh * DK + d0 + e) * DV + j0 + n] : 0.f;
+  }
+
+  RowTile<DK> tq, tk;
+  SqTile tm, tx;
+  float4 pd;
+  float pb = 0.f;
+  auto fetch = [&](int cc) {
+    const int vc = min(C, L - cc * C);
+    const size_t t0 = (size_t)bh * L + (size_t)cc * C;
+    const float* b = ws + ((size_t)bh * nc + cc) * W.per_chunk();
+    tq.load(q + t0 * DK, vc);
+    tk.load(k + t0 * DK, vc);
+    tm.load(b + W.M());
+    tx.load(b + W.X());
+    const int r = t % C, c4 = t / C;
+    const float4 x = *reinterpret_cast<const float4*>(dO + (t0 + min(r, vc - 1)) * DV + j0 + 4 * c4);
+    pd = r < vc ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < C) pb = t < vc ? beta[t0 + t] : 0.f;
+  };
+
+  fetch(nc - 1);
+  for (int c = nc - 1; c >= 0; --c) {
+    const int valid = min(C, L - c * C);
+    const size_t tok0 = (size_t)bh * L + (size_t)c * C;
+    float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
+    // Phase 0.
+    tk.put_rows(Kb);
+    tk.put_cols(Kt);
+    tq.put_cols(Qt);
+    tm.put_cols(Mh, Ml);
+    tx.put_cols(Xh, Xl);
+    {
+      const int r = t % C, c4 = t / C;
+      uint2 h, o;
+      split4(pd, h, o);
+      Oh[(4 * c4 + 0) * PC + r] = static_cast<uint16_t>(h.x);
+      Oh[(4 * c4 + 1) * PC + r] = static_cast<uint16_t>(h.x >> 16);
+      Oh[(4 * c4 + 2) * PC + r] = static_cast<uint16_t>(h.y);
+      Oh[(4 * c4 + 3) * PC + r] = static_cast<uint16_t>(h.y >> 16);
+      Ol[(4 * c4 + 0) * PC + r] = static_cast<uint16_t>(o.x);
+      Ol[(4 * c4 + 1) * PC + r] = static_cast<uint16_t>(o.x >> 16);
+      Ol[(4 * c4 + 2) * PC + r] = static_cast<uint16_t>(o.y);
+      Ol[(4 * c4 + 3) * PC + r] = static_cast<uint16_t>(o.y >> 16);
+    }
+    if (t < C) bs[t] = pb;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int d0 = 16 * (w * TPW + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) blk[W.G() + (size_t)(d0 + 4 * g + e) * DV + j0 + n] = G[i][e];
+      put_split_t(Gh, Gl, PK, d0, G[i]);
+    }
+    __syncthreads();
+    if (c > 0) fetch(c - 1);
+
+    // Phase 1: dDelta = M^T dO + K G', row tile w (M^T is upper triangular,
+    // so the first product starts at the tile's first row).
+    const int r0 = 16 * w;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int ks = w / 2; ks < C / 32; ++ks)
+      acc = mfma_split3(frag(Mh, PC, r0, 32 * ks), frag(Ml, PC, r0, 32 * ks), frag(Oh, PC, 0, 32 * ks),
+                        frag(Ol, PC, 0, 32 * ks), acc);
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks)
+      acc = mfma_split2(frag(Kb, PK, r0, 32 * ks), frag(Gh, PK, 0, 32 * ks), frag(Gl, PK, 0, 32 * ks),
+                        acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) blk[W.dD() + (size_t)(r0 + 4 * g + e) * DV + j0 + n] = acc[e];
+    put_split_t(Eh, El, PC, r0, acc);
+    __syncthreads();
+
+    // Phase 2: dR = diag(beta) X^T dDelta, row tile w; dv = dR.
+    acc = zero4();
+#pragma unroll
+    for (int ks = w / 2; ks < C / 32; ++ks)
+      acc = mfma_split3(frag(Xh, PC, r0, 32 * ks), frag(Xl, PC, r0, 32 * ks), frag(Eh, PC, 0, 32 * ks),
+                        frag(El, PC, 0, 32 * ks), acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = r0 + 4 * g + e;
+      acc[e] *= bs[r];
+      if (r < valid) dv[(tok0 + r) * DV + j0 + n] = acc[e];
+    }
+    put_split_t(Fh, Fl, PC, r0, -acc);
+    __syncthreads();
+
+    // Phase 3: G = G' + Q^T dO - K^T dR.
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int d0 = 16 * (w * TPW + i);
+#pragma unroll
+      for (int ks = 0; ks < C / 32; ++ks) {
+        G[i] = mfma_split2(frag(Qt, PC, d0, 32 * ks), frag(Oh, PC, 0, 32 * ks), frag(Ol, PC, 0, 32 * ks),
+                           G[i]);
+        G[i] = mfma_split2(frag(Kt, PC, d0, 32 * ks), frag(Fh, PC, 0, 32 * ks), frag(Fl, PC, 0, 32 * ks),
+                           G[i]);
+      }
+    }
+    __syncthreads();
+  }
+  if (dS0)
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int d0 = 16 * (w * TPW + i) + 4 * g;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dS0[((size_t)bh * DK + d0 + e) * DV + j0 + n] = G[i][e];
+    }
+}
+
+template <typename K>
+static hipError_t set_lds(K* kernel, size_t bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int DK, int DV>
+hipError_t fwd_t(const void* k, const void* v, const float* beta, const float* S0, int L, int nc,
+                 int bh, float* ws, hipStream_t s) {
+  auto* kern = &fwd_scan_kernel<DK, DV>;
+  hipError_t e = set_lds(kern, FwdLds<DK>::bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(DV / NT, bh), dim3(NTH), FwdLds<DK>::bytes, s,
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), beta, S0, L, nc, ws);
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t bwd_t(const void* q, const void* k, const float* beta, const float* dO,
+                 const float* dS_final, float* dv, float* dS0, int L, int nc, int bh, float* ws,
+                 hipStream_t s) {
+  auto* kern = &bwd_scan_kernel<DK, DV>;
+  hipError_t e = set_lds(kern, BwdLds<DK>::bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(DV / NT, bh), dim3(NTH), BwdLds<DK>::bytes, s,
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k), beta, dO, dS_final,
+                     dv, dS0, L, nc, ws);
+  return hipGetLastError();
+}
+
+}  // namespace mf
+
+hipError_t launch_fwd_scan_mfma(int d_k, int d_v, const void* k, const void* v,
+                                const float* beta, const float* S0, int L, int nc, int bh,
+                                float* ws, hipStream_t stream) {
+  if (d_k == 64 && d_v == 64) return mf::fwd_t<64, 64>(k, v, beta, S0, L, nc, bh, ws, stream);
+  if (d_k == 64 && d_v == 128) return mf::fwd_t<64, 128>(k, v, beta, S0, L, nc, bh, ws, stream);
+  if (d_k == 128 && d_v == 64) return mf::fwd_t<128, 64>(k, v, beta, S0, L, nc, bh, ws, stream);
+  return mf::fwd_t<128, 128>(k, v, beta, S0, L, nc, bh, ws, stream);
+}
+
+hipError_t launch_bwd_scan_mfma(int d_k, int d_v, const void* q, const void* k,
+                                const float* beta, const float* dO, const float* dS_final,
+                                float* dv, float* dS0, int L, int nc, int bh, float* ws,
+                                hipStream_t stream) {
+  if (d_k == 64 && d_v == 64)
+    return mf::bwd_t<64, 64>(q, k, beta, dO, dS_final, dv, dS0, L, nc, bh, ws, stream);
+  if (d_k == 64 && d_v == 128)
+    return mf::bwd_t<64, 128>(q, k, beta, dO, dS_final, dv, dS0, L, nc, bh, ws, stream);
+  if (d_k == 128 && d_v == 64)
+    return mf::bwd_t<128, 64>(q, k, beta, dO, dS_final, dv, dS0, L, nc, bh, ws, stream);
+  return mf::bwd_t<128, 128>(q, k, beta, dO, dS_final, dv, dS0, L, nc, bh, ws, stream);
+}
+
+}  // namespace bwd
+}  // namespace dn
