@@ -569,11 +569,15 @@ hipError_t launch_t(const BwdArgs& a) {
                        a.beta, a.dO, a.dbeta, a.L, ws);
     DN_TRY(hipGetLastError());
     prof_mark(kSlotBwdCc, true, a.stream);
-    DN_TRY(set_smem(&qk_grad_kernel<DK, DV, IT>, QkSmem<DK>::bytes));
     prof_mark(kSlotBwdQk, false, a.stream);
-    hipLaunchKernelGGL((qk_grad_kernel<DK, DV, IT>), chunks, blk, QkSmem<DK>::bytes, a.stream, q, k,
-                       a.dO, a.dv, a.dq, a.dk, a.L, ws);
-    DN_TRY(hipGetLastError());
+    if (kMatrixCores) {
+      DN_TRY(launch_qk_grad_mfma(DK, DV, q, k, a.dO, a.dv, a.dq, a.dk, a.L, nc, bh, ws, a.stream));
+    } else {
+      DN_TRY(set_smem(&qk_grad_kernel<DK, DV, IT>, QkSmem<DK>::bytes));
+      hipLaunchKernelGGL((qk_grad_kernel<DK, DV, IT>), chunks, blk, QkSmem<DK>::bytes, a.stream, q,
+                         k, a.dO, a.dv, a.dq, a.dk, a.L, ws);
+      DN_TRY(hipGetLastError());
+    }
     prof_mark(kSlotBwdQk, true, a.stream);
   }
   return hipSuccess;

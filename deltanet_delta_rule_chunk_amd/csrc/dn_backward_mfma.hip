@@ -61,15 +61,15 @@ __device__ __forceinline__ uint16_t elem8(const uint4& x, int e) {
 // Loads of one chunk's C x DK bf16 tile (q or k): 16 bytes per thread per
 // step, the chunk row fastest across lanes; rows at or past `valid` read as
 // zero (the load itself is clamped to a valid row).
-template <int DK>
+template <int DK, int NTHR = NTH>
 struct RowTile {
-  static constexpr int N = C * DK / 8 / NTH;
+  static constexpr int N = C * DK / 8 / NTHR;
   uint4 x[N];
   __device__ __forceinline__ void load(const bf16* src, int valid) {
     const uint4* s = reinterpret_cast<const uint4*>(src);
 #pragma unroll
     for (int p = 0; p < N; ++p) {
-      const int f = threadIdx.x + p * NTH, r = f % C, c8 = f / C;
+      const int f = threadIdx.x + p * NTHR, r = f % C, c8 = f / C;
       const uint4 v = s[min(r, valid - 1) * (DK / 8) + c8];
       x[p] = r < valid ? v : make_uint4(0u, 0u, 0u, 0u);
     }
@@ -78,7 +78,7 @@ struct RowTile {
   __device__ __forceinline__ void put_rows(uint16_t* dst) const {
 #pragma unroll
     for (int p = 0; p < N; ++p) {
-      const int f = threadIdx.x + p * NTH, r = f % C, c8 = f / C;
+      const int f = threadIdx.x + p * NTHR, r = f % C, c8 = f / C;
       *reinterpret_cast<uint4*>(dst + r * (DK + 8) + 8 * c8) = x[p];
     }
   }
@@ -86,7 +86,7 @@ struct RowTile {
   __device__ __forceinline__ void put_cols(uint16_t* dst) const {
 #pragma unroll
     for (int p = 0; p < N; ++p) {
-      const int f = threadIdx.x + p * NTH, r = f % C, c8 = f / C;
+      const int f = threadIdx.x + p * NTHR, r = f % C, c8 = f / C;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dst[(8 * c8 + e) * PC + r] = elem8(x[p], e);
     }
@@ -417,6 +417,188 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
     }
 }
 
+// ---- dQ and dK -------------------------------------------------------------
+// One workgroup of d_k / 16 waves per (chunk, head); wave w owns column tile
+// w (16 columns of d_k) of both outputs, for all four 16-row tiles.
+//   phase A, over d_v in passes of HJ columns:  dQ += dO S^T,
+//            dK += Delta G'^T - dR S^T.  dO, Delta and -dR rows are staged
+//            split in LDS; the S and G' rows are each wave's own B operands,
+//            loaded from the workspace straight into registers.
+//   phase B, over chunk rows:  dQ += dM K,  dK += dM^T Q + (W + W^T) K,
+//            with dM and W staged in fp32 and split per fragment, K and Q
+//            staged transposed.
+template <int DK>
+struct QkLds {
+  static constexpr int HJ = 64;
+  static constexpr int PJ = HJ + 8;
+  static constexpr int PF = C + 4;
+  static constexpr size_t a_bytes = 6 * (size_t)C * PJ * 2;
+  static constexpr size_t b_bytes = 2 * (size_t)DK * PC * 2 + 2 * (size_t)C * PF * sizeof(float);
+  static constexpr size_t bytes = a_bytes > b_bytes ? a_bytes : b_bytes;
+};
+
+// 8 fp32 values -> split bf16x8 pair.
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+  uint2 h0, l0, h1, l1;
+  split4(make_float4(x[0], x[1], x[2], x[3]), h0, l0);
+  split4(make_float4(x[4], x[5], x[6], x[7]), h1, l1);
+  hi = as_bf16x8(h0, h1);
+  lo = as_bf16x8(l0, l1);
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(DK * 4) void qk_grad_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ dO,
+    const float* __restrict__ dv, float* __restrict__ dq, float* __restrict__ dk, int L,
+    const float* __restrict__ ws) {
+  using LD = QkLds<DK>;
+  constexpr int HJ = LD::HJ < DV ? LD::HJ : DV, PJ = LD::PJ, PF = LD::PF;
+  constexpr Ws W{DK, DV};
+  constexpr int TPW = 1, NTQ = DK * 4;
+  constexpr int KS = HJ / 32;
+  extern __shared__ uint4 lds_u4[];
+  const int c = blockIdx.x, bh = blockIdx.y, nc = gridDim.x;
+  const int valid = min(C, L - c * C);
+  const size_t tok0 = (size_t)bh * L + (size_t)c * C;
+  const float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
+
+  f32x4 aq[4][TPW], ak[4][TPW];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) aq[rt][i] = ak[rt][i] = zero4();
+
+  {  // phase A
+    uint16_t* Oh = reinterpret_cast<uint16_t*>(lds_u4);
+    uint16_t* Ol = Oh + C * PJ;
+    uint16_t* Dh = Ol + C * PJ;
+    uint16_t* Dl = Dh + C * PJ;
+    uint16_t* Rh = Dl + C * PJ;
+    uint16_t* Rl = Rh + C * PJ;
+    for (int h = 0; h < DV; h += HJ) {
+      float4 sv[TPW][KS][2], gv[TPW][KS][2];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const size_t o = (size_t)(16 * (w * TPW + i) + n) * DV + h + 32 * ks + 8 * g;
+          sv[i][ks][0] = *reinterpret_cast<const float4*>(blk + W.S() + o);
+          sv[i][ks][1] = *reinterpret_cast<const float4*>(blk + W.S() + o + 4);
+          gv[i][ks][0] = *reinterpret_cast<const float4*>(blk + W.G() + o);
+          gv[i][ks][1] = *reinterpret_cast<const float4*>(blk + W.G() + o + 4);
+        }
+      if (h > 0) __syncthreads();
+#pragma unroll
+      for (int p = 0; p < C * HJ / 4 / NTQ; ++p) {
+        const int f = t + p * NTQ, r = f / (HJ / 4), c4 = f % (HJ / 4);
+        const size_t go = (tok0 + min(r, valid - 1)) * DV + h + 4 * c4;
+        float4 xo = *reinterpret_cast<const float4*>(dO + go);
+        float4 xr = *reinterpret_cast<const float4*>(dv + go);
+        const float4 xd = *reinterpret_cast<const float4*>(blk + W.D() + (size_t)r * DV + h + 4 * c4);
+        if (r >= valid) xo = xr = make_float4(0.f, 0.f, 0.f, 0.f);
+        xr = make_float4(-xr.x, -xr.y, -xr.z, -xr.w);
+        uint2 hh, ll;
+        split4(xo, hh, ll);
+        *reinterpret_cast<uint2*>(Oh + r * PJ + 4 * c4) = hh;
+        *reinterpret_cast<uint2*>(Ol + r * PJ + 4 * c4) = ll;
+        split4(xd, hh, ll);
+        *reinterpret_cast<uint2*>(Dh + r * PJ + 4 * c4) = hh;
+        *reinterpret_cast<uint2*>(Dl + r * PJ + 4 * c4) = ll;
+        split4(xr, hh, ll);
+        *reinterpret_cast<uint2*>(Rh + r * PJ + 4 * c4) = hh;
+        *reinterpret_cast<uint2*>(Rl + r * PJ + 4 * c4) = ll;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+          uint2 h0, l0, h1, l1;
+          split4(sv[i][ks][0], h0, l0);
+          split4(sv[i][ks][1], h1, l1);
+          const bf16x8 sh = as_bf16x8(h0, h1), sl = as_bf16x8(l0, l1);
+          split4(gv[i][ks][0], h0, l0);
+          split4(gv[i][ks][1], h1, l1);
+          const bf16x8 gh = as_bf16x8(h0, h1), gl = as_bf16x8(l0, l1);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            aq[rt][i] = mfma_split3(frag(Oh, PJ, 16 * rt, 32 * ks), frag(Ol, PJ, 16 * rt, 32 * ks), sh,
+                                    sl, aq[rt][i]);
+            ak[rt][i] = mfma_split3(frag(Dh, PJ, 16 * rt, 32 * ks), frag(Dl, PJ, 16 * rt, 32 * ks), gh,
+                                    gl, ak[rt][i]);
+            ak[rt][i] = mfma_split3(frag(Rh, PJ, 16 * rt, 32 * ks), frag(Rl, PJ, 16 * rt, 32 * ks), sh,
+                                    sl, ak[rt][i]);
+          }
+        }
+    }
+  }
+  __syncthreads();
+  {  // phase B
+    uint16_t* Kt = reinterpret_cast<uint16_t*>(lds_u4);
+    uint16_t* Qt = Kt + DK * PC;
+    float* Ms = reinterpret_cast<float*>(Qt + DK * PC);
+    float* Wm = Ms + C * PF;
+    {
+      RowTile<DK, NTQ> tq, tk;
+      tq.load(q + tok0 * DK, valid);
+      tk.load(k + tok0 * DK, valid);
+#pragma unroll
+      for (int p = 0; p < C * C / 4 / NTQ; ++p) {
+        const int f = t + p * NTQ, r = f / (C / 4), c4 = f % (C / 4);
+        *reinterpret_cast<float4*>(Ms + r * PF + 4 * c4) =
+            *reinterpret_cast<const float4*>(blk + W.dM() + r * C + 4 * c4);
+        *reinterpret_cast<float4*>(Wm + r * PF + 4 * c4) =
+            *reinterpret_cast<const float4*>(blk + W.W() + r * C + 4 * c4);
+      }
+      tq.put_cols(Qt);
+      tk.put_cols(Kt);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < C / 32; ++ks) {
+        const int r = 16 * rt + n, a0 = 32 * ks + 8 * g;
+        float m[8], mt[8], ww[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          m[e] = Ms[r * PF + a0 + e];
+          mt[e] = Ms[(a0 + e) * PF + r];
+          ww[e] = Wm[r * PF + a0 + e] + Wm[(a0 + e) * PF + r];
+        }
+        bf16x8 mh, ml, th, tl, wh, wl;
+        split8(m, mh, ml);
+        split8(mt, th, tl);
+        split8(ww, wh, wl);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+          const int d0 = 16 * (w * TPW + i);
+          const bf16x8 bk = frag(Kt, PC, d0, 32 * ks), bq = frag(Qt, PC, d0, 32 * ks);
+          aq[rt][i] = mfma16(mh, bk, aq[rt][i]);
+          aq[rt][i] = mfma16(ml, bk, aq[rt][i]);
+          ak[rt][i] = mfma16(th, bq, ak[rt][i]);
+          ak[rt][i] = mfma16(tl, bq, ak[rt][i]);
+          ak[rt][i] = mfma16(wh, bk, ak[rt][i]);
+          ak[rt][i] = mfma16(wl, bk, ak[rt][i]);
+        }
+      }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * g + e;
+        if (r < valid) {
+          const size_t o = (tok0 + r) * DK + 16 * (w * TPW + i) + n;
+          dq[o] = aq[rt][i][e];
+          dk[o] = ak[rt][i][e];
+        }
+      }
+}
+
 template <typename K>
 static hipError_t set_lds(K* kernel, size_t bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -447,6 +629,18 @@ hipError_t bwd_t(const void* q, const void* k, const float* beta, const float* d
   return hipGetLastError();
 }
 
+template <int DK, int DV>
+hipError_t qk_t(const void* q, const void* k, const float* dO, const float* dv, float* dq,
+                float* dk, int L, int nc, int bh, const float* ws, hipStream_t s) {
+  auto* kern = &qk_grad_kernel<DK, DV>;
+  hipError_t e = set_lds(kern, QkLds<DK>::bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(nc, bh), dim3(DK * 4), QkLds<DK>::bytes, s,
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k), dO, dv, dq, dk, L,
+                     ws);
+  return hipGetLastError();
+}
+
 }  // namespace mf
 
 hipError_t launch_fwd_scan_mfma(int d_k, int d_v, const void* k, const void* v,
@@ -469,6 +663,15 @@ hipError_t launch_bwd_scan_mfma(int d_k, int d_v, const void* q, const void* k,
   if (d_k == 128 && d_v == 64)
     return mf::bwd_t<128, 64>(q, k, beta, dO, dS_final, dv, dS0, L, nc, bh, ws, stream);
   return mf::bwd_t<128, 128>(q, k, beta, dO, dS_final, dv, dS0, L, nc, bh, ws, stream);
+}
+
+hipError_t launch_qk_grad_mfma(int d_k, int d_v, const void* q, const void* k,
+                               const float* dO, const float* dv, float* dq, float* dk, int L,
+                               int nc, int bh, const float* ws, hipStream_t stream) {
+  if (d_k == 64 && d_v == 64) return mf::qk_t<64, 64>(q, k, dO, dv, dq, dk, L, nc, bh, ws, stream);
+  if (d_k == 64 && d_v == 128) return mf::qk_t<64, 128>(q, k, dO, dv, dq, dk, L, nc, bh, ws, stream);
+  if (d_k == 128 && d_v == 64) return mf::qk_t<128, 64>(q, k, dO, dv, dq, dk, L, nc, bh, ws, stream);
+  return mf::qk_t<128, 128>(q, k, dO, dv, dq, dk, L, nc, bh, ws, stream);
 }
 
 }  // namespace bwd
