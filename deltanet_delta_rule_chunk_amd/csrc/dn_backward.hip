@@ -563,11 +563,15 @@ hipError_t launch_t(const BwdArgs& a) {
   }
   prof_mark(kSlotBwdScan, true, a.stream);
   if (nc > 0) {
-    DN_TRY(set_smem(&cc_grad_kernel<DK, DV, IT>, CcSmem<DK>::bytes));
     prof_mark(kSlotBwdCc, false, a.stream);
-    hipLaunchKernelGGL((cc_grad_kernel<DK, DV, IT>), chunks, blk, CcSmem<DK>::bytes, a.stream, k,
-                       a.beta, a.dO, a.dbeta, a.L, ws);
-    DN_TRY(hipGetLastError());
+    if (kMatrixCores) {
+      DN_TRY(launch_cc_grad_mfma(DK, DV, k, a.beta, a.dO, a.dbeta, a.L, nc, bh, ws, a.stream));
+    } else {
+      DN_TRY(set_smem(&cc_grad_kernel<DK, DV, IT>, CcSmem<DK>::bytes));
+      hipLaunchKernelGGL((cc_grad_kernel<DK, DV, IT>), chunks, blk, CcSmem<DK>::bytes, a.stream, k,
+                         a.beta, a.dO, a.dbeta, a.L, ws);
+      DN_TRY(hipGetLastError());
+    }
     prof_mark(kSlotBwdCc, true, a.stream);
     prof_mark(kSlotBwdQk, false, a.stream);
     if (kMatrixCores) {

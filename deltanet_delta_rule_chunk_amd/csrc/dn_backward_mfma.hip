@@ -599,6 +599,201 @@ __global__ __launch_bounds__(DK * 4) void qk_grad_kernel(
       }
 }
 
+// ---- the C x C gradients: dM, dT, dA, W and dbeta -------------------------
+// One 4-wave workgroup per (chunk, head); wave w owns row tile w of every
+// C x C product.
+//   phase 1, over d_v in passes of 64 columns: dM = tril(dO Delta^T) and
+//            dT = tril(dDelta R^T), all four operands staged split in LDS
+//            (the Delta and R rows are the B operands as stored);
+//   phase 2: dbeta_i = sum_a X_ai dT_ai; Y = X^T dX with dX = dT diag(beta)
+//            (both operands gathered from fp32 LDS columns and split);
+//            dA = -Y X^T (strictly lower) and W = diag(beta) dA; the Gram
+//            tiles K K^T (exact bf16 products) give
+//            dbeta_r += sum_{i<r} dA_ri (k_r . k_i).
+template <int DK>
+struct CcLds {
+  static constexpr int HJ = 64;
+  static constexpr int PJ = HJ + 8;
+  static constexpr int PF = C + 4;
+  static constexpr int PK = DK + 8;
+  static constexpr size_t p1 = 8 * (size_t)C * PJ * 2;
+  static constexpr size_t p2 = 3 * (size_t)C * PF * sizeof(float) + (size_t)C * PK * 2 +
+                               2 * (size_t)C * sizeof(float);
+  static constexpr size_t bytes = p1 > p2 ? p1 : p2;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NTH) void cc_grad_kernel(const bf16* __restrict__ k,
+                                                      const float* __restrict__ beta,
+                                                      const float* __restrict__ dO,
+                                                      float* __restrict__ dbeta, int L,
+                                                      float* __restrict__ ws) {
+  using LD = CcLds<DK>;
+  constexpr int HJ = LD::HJ < DV ? LD::HJ : DV, PJ = LD::PJ, PF = LD::PF, PK = LD::PK;
+  constexpr Ws W{DK, DV};
+  extern __shared__ uint4 lds_u4[];
+  const int c = blockIdx.x, bh = blockIdx.y, nc = gridDim.x;
+  const int valid = min(C, L - c * C);
+  const size_t tok0 = (size_t)bh * L + (size_t)c * C;
+  float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
+  const int r0 = 16 * w;
+
+  f32x4 am[4], at[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) am[ct] = at[ct] = zero4();
+  {  // phase 1
+    uint16_t* Oh = reinterpret_cast<uint16_t*>(lds_u4);
+    uint16_t* Ol = Oh + C * PJ;
+    uint16_t* Dh = Ol + C * PJ;
+    uint16_t* Dl = Dh + C * PJ;
+    uint16_t* Eh = Dl + C * PJ;
+    uint16_t* El = Eh + C * PJ;
+    uint16_t* Rh = El + C * PJ;
+    uint16_t* Rl = Rh + C * PJ;
+    for (int h = 0; h < DV; h += HJ) {
+      if (h > 0) __syncthreads();
+#pragma unroll
+      for (int p = 0; p < C * HJ / 4 / NTH; ++p) {
+        const int f = t + p * NTH, r = f / (HJ / 4), c4 = f % (HJ / 4);
+        const size_t wo = (size_t)r * DV + h + 4 * c4;
+        float4 xo = *reinterpret_cast<const float4*>(dO + (tok0 + min(r, valid - 1)) * DV + h + 4 * c4);
+        if (r >= valid) xo = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 xd = *reinterpret_cast<const float4*>(blk + W.D() + wo);
+        const float4 xe = *reinterpret_cast<const float4*>(blk + W.dD() + wo);
+        const float4 xr = *reinterpret_cast<const float4*>(blk + W.R() + wo);
+        const int o = r * PJ + 4 * c4;
+        uint2 hh, ll;
+        split4(xo, hh, ll);
+        *reinterpret_cast<uint2*>(Oh + o) = hh;
+        *reinterpret_cast<uint2*>(Ol + o) = ll;
+        split4(xd, hh, ll);
+        *reinterpret_cast<uint2*>(Dh + o) = hh;
+        *reinterpret_cast<uint2*>(Dl + o) = ll;
+        split4(xe, hh, ll);
+        *reinterpret_cast<uint2*>(Eh + o) = hh;
+        *reinterpret_cast<uint2*>(El + o) = ll;
+        split4(xr, hh, ll);
+        *reinterpret_cast<uint2*>(Rh + o) = hh;
+        *reinterpret_cast<uint2*>(Rl + o) = ll;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < HJ / 32; ++ks) {
+        const bf16x8 oh = frag(Oh, PJ, r0, 32 * ks), ol = frag(Ol, PJ, r0, 32 * ks);
+        const bf16x8 eh = frag(Eh, PJ, r0, 32 * ks), el = frag(El, PJ, r0, 32 * ks);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          if (ct > w) continue;  // above the diagonal
+          am[ct] = mfma_split3(oh, ol, frag(Dh, PJ, 16 * ct, 32 * ks), frag(Dl, PJ, 16 * ct, 32 * ks),
+                               am[ct]);
+          at[ct] = mfma_split3(eh, el, frag(Rh, PJ, 16 * ct, 32 * ks), frag(Rl, PJ, 16 * ct, 32 * ks),
+                               at[ct]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  float* Xs = reinterpret_cast<float*>(lds_u4);  // X    [C][PF]
+  float* Ts = Xs + C * PF;                        // dT   [C][PF]
+  float* Ys = Ts + C * PF;                        // Y    [C][PF]
+  float* bs = Ys + C * PF;
+  float* dbs = bs + C;
+  uint16_t* Kb = reinterpret_cast<uint16_t*>(dbs + C);  // K rows [C][PK]
+  {
+    RowTile<DK> tk;
+    tk.load(k + tok0 * DK, valid);
+#pragma unroll
+    for (int p = 0; p < C * C / 4 / NTH; ++p) {
+      const int f = t + p * NTH, r = f / (C / 4), c4 = f % (C / 4);
+      *reinterpret_cast<float4*>(Xs + r * PF + 4 * c4) =
+          *reinterpret_cast<const float4*>(blk + W.X() + r * C + 4 * c4);
+    }
+    if (t < C) bs[t] = t < valid ? beta[tok0 + t] : 0.f;
+    tk.put_rows(Kb);
+  }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = r0 + 4 * g + e, i = 16 * ct + n;
+      const float m = i <= r ? am[ct][e] : 0.f, d = i <= r ? at[ct][e] : 0.f;
+      blk[W.dM() + r * C + i] = m;
+      Ts[r * PF + i] = d;
+    }
+  __syncthreads();
+  if (t < C) {  // dbeta_i from T = X diag(beta)
+    float s = 0.f;
+    for (int a = t; a < C; ++a) s += Xs[a * PF + t] * Ts[a * PF + t];
+    dbs[t] = s;
+  }
+  // Y = X^T dX, row tile w: Y_ab = sum_{r >= a} X_ra dT_rb beta_b.
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    f32x4 y = zero4();
+    const int a = r0 + n, b = 16 * ct + n;
+    const float bb = bs[b];
+#pragma unroll
+    for (int ks = w / 2; ks < C / 32; ++ks) {
+      float xa[8], xb[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 32 * ks + 8 * g + e;
+        xa[e] = Xs[r * PF + a];
+        xb[e] = Ts[r * PF + b] * bb;
+      }
+      bf16x8 ah, al, bh_, bl;
+      split8(xa, ah, al);
+      split8(xb, bh_, bl);
+      y = mfma_split3(ah, al, bh_, bl, y);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Ys[(r0 + 4 * g + e) * PF + 16 * ct + n] = y[e];
+  }
+  __syncthreads();
+  // dA = -Y X^T (strictly lower), W = diag(beta) dA, and the dbeta row sums
+  // against the Gram tiles.
+  float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    f32x4 acc = zero4(), gr = zero4();
+    if (ct <= w) {
+#pragma unroll
+      for (int ks = 0; ks <= ct / 2; ++ks) {
+        const float* ya = Ys + (r0 + n) * PF + 32 * ks + 8 * g;
+        const float* xb = Xs + (16 * ct + n) * PF + 32 * ks + 8 * g;
+        float va[8], vb[8];
+        *reinterpret_cast<float4*>(va) = *reinterpret_cast<const float4*>(ya);
+        *reinterpret_cast<float4*>(va + 4) = *reinterpret_cast<const float4*>(ya + 4);
+        *reinterpret_cast<float4*>(vb) = *reinterpret_cast<const float4*>(xb);
+        *reinterpret_cast<float4*>(vb + 4) = *reinterpret_cast<const float4*>(xb + 4);
+        bf16x8 ah, al, bh_, bl;
+        split8(va, ah, al);
+        split8(vb, bh_, bl);
+        acc = mfma_split3(ah, al, bh_, bl, acc);
+      }
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks)
+        gr = mfma16(frag(Kb, PK, r0, 32 * ks), frag(Kb, PK, 16 * ct, 32 * ks), gr);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = r0 + 4 * g + e, i = 16 * ct + n;
+      const float da = i < r ? -acc[e] : 0.f;
+      blk[W.W() + r * C + i] = bs[r] * da;
+      rs[e] += da * gr[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v = rs[e];
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int r = r0 + 4 * g + e;
+    if (n == 0 && r < valid) dbeta[tok0 + r] = dbs[r] + v;
+  }
+}
+
 template <typename K>
 static hipError_t set_lds(K* kernel, size_t bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -641,6 +836,17 @@ hipError_t qk_t(const void* q, const void* k, const float* dO, const float* dv, 
   return hipGetLastError();
 }
 
+template <int DK, int DV>
+hipError_t cc_t(const void* k, const float* beta, const float* dO, float* dbeta, int L, int nc,
+                int bh, float* ws, hipStream_t s) {
+  auto* kern = &cc_grad_kernel<DK, DV>;
+  hipError_t e = set_lds(kern, CcLds<DK>::bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(nc, bh), dim3(NTH), CcLds<DK>::bytes, s,
+                     static_cast<const bf16*>(k), beta, dO, dbeta, L, ws);
+  return hipGetLastError();
+}
+
 }  // namespace mf
 
 hipError_t launch_fwd_scan_mfma(int d_k, int d_v, const void* k, const void* v,
@@ -672,6 +878,15 @@ hipError_t launch_qk_grad_mfma(int d_k, int d_v, const void* q, const void* k,
   if (d_k == 64 && d_v == 128) return mf::qk_t<64, 128>(q, k, dO, dv, dq, dk, L, nc, bh, ws, stream);
   if (d_k == 128 && d_v == 64) return mf::qk_t<128, 64>(q, k, dO, dv, dq, dk, L, nc, bh, ws, stream);
   return mf::qk_t<128, 128>(q, k, dO, dv, dq, dk, L, nc, bh, ws, stream);
+}
+
+hipError_t launch_cc_grad_mfma(int d_k, int d_v, const void* k, const float* beta,
+                               const float* dO, float* dbeta, int L, int nc, int bh, float* ws,
+                               hipStream_t stream) {
+  if (d_k == 64 && d_v == 64) return mf::cc_t<64, 64>(k, beta, dO, dbeta, L, nc, bh, ws, stream);
+  if (d_k == 64 && d_v == 128) return mf::cc_t<64, 128>(k, beta, dO, dbeta, L, nc, bh, ws, stream);
+  if (d_k == 128 && d_v == 64) return mf::cc_t<128, 64>(k, beta, dO, dbeta, L, nc, bh, ws, stream);
+  return mf::cc_t<128, 128>(k, beta, dO, dbeta, L, nc, bh, ws, stream);
 }
 
 }  // namespace bwd
