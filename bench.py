@@ -407,7 +407,7 @@ def main(argv=None) -> int:
             "workload": w.name + "_backward", "steps": a.steps, "ms_per_step": ms_b,
             "tokens_per_s": w.B * w.L / (ms_b * 1e-3),
             "kernels_ms": {name: tot / n for name, (tot, n) in bprof.items()},
-            "path": "64-token chunks, forward recomputed inside; state scans, C x C gradients and dQ/dK on bf16 MFMA (split-precision operands), prep fp32 vector ALU",
+            "path": "64-token chunks, forward recomputed inside; every product on bf16 MFMA (split-precision operands), the 64 x 64 triangular inverse fp32 vector ALU",
             "grads_in": "dO ~ N(0, 1) (torch generator seeded), no dS_final",
         }
         del bws, dO, grads

@@ -33,6 +33,11 @@ struct Ws {
   __host__ __device__ constexpr size_t dD() const { return D() + (size_t)C * dv; }
 };
 
+// X = (I + A)^{-1} and M = tril(Q K^T) of every chunk, the Gram products on
+// the matrix cores (bf16 q, k).  nc >= 1.
+hipError_t launch_prep_mfma(int d_k, int d_v, const void* q, const void* k, const float* beta,
+                            int L, int nc, int bh, float* ws, hipStream_t stream);
+
 // Forward state pass on the matrix cores (bf16 k, v): writes S_c, R and
 // Delta of every chunk into the workspace, whose X blocks the prep kernel
 // has filled.  nc = ceil(L / C) >= 1; bh = B * H.

@@ -1,6 +1,6 @@
-// dn_backward.hip -- gradient of the chunked delta-rule forward: fp32
-// vector-ALU kernels, with the two state scans on the matrix cores for bf16
-// inputs (dn_backward_mfma.hip).
+// dn_backward.hip -- gradient of the chunked delta-rule forward: the fp32
+// vector-ALU kernels (fp32 inputs) and the launch sequence; bf16 inputs run
+// the matrix-core versions of the same five kernels (dn_backward_mfma.hip).
 //
 // The pages present the chunked form as the way to train the delta rule in
 // linear time (page "GPT-2 から Kimi K3 まで、AI モデルの進化を解説", section
@@ -530,15 +530,19 @@ hipError_t launch_t(const BwdArgs& a) {
   const IT *q = static_cast<const IT*>(a.q), *k = static_cast<const IT*>(a.k);
   const IT* v = static_cast<const IT*>(a.v);
   const dim3 chunks(nc, bh), slices(DV / NT, bh), blk(NTHR);
-  // bf16 q, k, v: the state scans run on the matrix cores
-  // (dn_backward_mfma.hip); fp32 inputs keep the vector-ALU scans.
+  // bf16 q, k, v: the five kernels' products run on the matrix cores
+  // (dn_backward_mfma.hip); fp32 inputs keep the vector-ALU kernels below.
   constexpr bool kMatrixCores = sizeof(IT) == 2;
   if (nc > 0) {
-    DN_TRY(set_smem(&prep_kernel<DK, DV, IT>, PrepSmem<DK>::bytes));
     prof_mark(kSlotBwdPrep, false, a.stream);
-    hipLaunchKernelGGL((prep_kernel<DK, DV, IT>), chunks, blk, PrepSmem<DK>::bytes, a.stream, q, k,
-                       a.beta, a.L, ws);
-    DN_TRY(hipGetLastError());
+    if (kMatrixCores) {
+      DN_TRY(launch_prep_mfma(DK, DV, q, k, a.beta, a.L, nc, bh, ws, a.stream));
+    } else {
+      DN_TRY(set_smem(&prep_kernel<DK, DV, IT>, PrepSmem<DK>::bytes));
+      hipLaunchKernelGGL((prep_kernel<DK, DV, IT>), chunks, blk, PrepSmem<DK>::bytes, a.stream, q,
+                         k, a.beta, a.L, ws);
+      DN_TRY(hipGetLastError());
+    }
     prof_mark(kSlotBwdPrep, true, a.stream);
     prof_mark(kSlotBwdFwdScan, false, a.stream);
     if (kMatrixCores) {

@@ -28,6 +28,7 @@
 #include "dn_backward.h"
 #include "dn_common.h"
 #include "dn_mfma.h"
+#include "dn_valu_common.h"
 
 namespace dn {
 namespace bwd {
@@ -134,6 +135,69 @@ struct SqTile {
     }
   }
 };
+
+// ---- prep: X = (I + A)^{-1} and M = tril(Q K^T) ---------------------------
+// One 4-wave workgroup per (chunk, head).  Wave w forms row tile w of the
+// Gram products K K^T and Q K^T (exact bf16 products, fp32 sums); the
+// blocked fp32 inverse of I + A then runs on the vector ALUs.
+template <int DK>
+struct PrepLds {
+  static constexpr int PK = DK + 8;
+  static constexpr int PF = C + 1;
+  static constexpr size_t bytes =
+      2 * (size_t)C * PK * 2 + (2 * (size_t)C * PF + C) * sizeof(float);
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NTH) void prep_kernel(const bf16* __restrict__ q,
+                                                   const bf16* __restrict__ k,
+                                                   const float* __restrict__ beta, int L,
+                                                   float* __restrict__ ws) {
+  using LD = PrepLds<DK>;
+  constexpr int PK = LD::PK, PF = LD::PF;
+  constexpr Ws W{DK, DV};
+  extern __shared__ uint4 lds_u4[];
+  uint16_t* Kb = reinterpret_cast<uint16_t*>(lds_u4);  // K rows [C][PK]
+  uint16_t* Qb = Kb + C * PK;                           // Q rows [C][PK]
+  float* As = reinterpret_cast<float*>(Qb + C * PK);    // A      [C][PF]
+  float* Xs = As + C * PF;                              // X      [C][PF]
+  float* bs = Xs + C * PF;
+  const int c = blockIdx.x, bh = blockIdx.y, nc = gridDim.x;
+  const int valid = min(C, L - c * C);
+  const size_t tok0 = (size_t)bh * L + (size_t)c * C;
+  float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
+  const int r0 = 16 * w;
+  {
+    RowTile<DK> tq, tk;
+    tq.load(q + tok0 * DK, valid);
+    tk.load(k + tok0 * DK, valid);
+    tq.put_rows(Qb);
+    tk.put_rows(Kb);
+    if (t < C) bs[t] = t < valid ? beta[tok0 + t] : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    f32x4 gk = zero4(), gq = zero4();
+    if (ct <= w) {
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        const bf16x8 bk = frag(Kb, PK, 16 * ct, 32 * ks);
+        gk = mfma16(frag(Kb, PK, r0, 32 * ks), bk, gk);
+        gq = mfma16(frag(Qb, PK, r0, 32 * ks), bk, gq);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = r0 + 4 * g + e, i = 16 * ct + n;
+      As[r * PF + i] = i < r ? bs[r] * gk[e] : 0.f;
+      blk[W.M() + r * C + i] = i <= r ? gq[e] : 0.f;
+    }
+  }
+  valu::unit_lower_inverse<C>(As, PF, Xs, PF);
+  for (int e = t; e < C * C; e += NTH) blk[W.X() + e] = Xs[(e / C) * PF + e % C];
+}
 
 // ---- forward state pass -----------------------------------------------------
 template <int DK>
@@ -847,6 +911,17 @@ hipError_t cc_t(const void* k, const float* beta, const float* dO, float* dbeta,
   return hipGetLastError();
 }
 
+template <int DK, int DV>
+hipError_t prep_t(const void* q, const void* k, const float* beta, int L, int nc, int bh,
+                  float* ws, hipStream_t s) {
+  auto* kern = &prep_kernel<DK, DV>;
+  hipError_t e = set_lds(kern, PrepLds<DK>::bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(nc, bh), dim3(NTH), PrepLds<DK>::bytes, s,
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k), beta, L, ws);
+  return hipGetLastError();
+}
+
 }  // namespace mf
 
 hipError_t launch_fwd_scan_mfma(int d_k, int d_v, const void* k, const void* v,
@@ -887,6 +962,14 @@ hipError_t launch_cc_grad_mfma(int d_k, int d_v, const void* k, const float* bet
   if (d_k == 64 && d_v == 128) return mf::cc_t<64, 128>(k, beta, dO, dbeta, L, nc, bh, ws, stream);
   if (d_k == 128 && d_v == 64) return mf::cc_t<128, 64>(k, beta, dO, dbeta, L, nc, bh, ws, stream);
   return mf::cc_t<128, 128>(k, beta, dO, dbeta, L, nc, bh, ws, stream);
+}
+
+hipError_t launch_prep_mfma(int d_k, int d_v, const void* q, const void* k, const float* beta,
+                            int L, int nc, int bh, float* ws, hipStream_t stream) {
+  if (d_k == 64 && d_v == 64) return mf::prep_t<64, 64>(q, k, beta, L, nc, bh, ws, stream);
+  if (d_k == 64 && d_v == 128) return mf::prep_t<64, 128>(q, k, beta, L, nc, bh, ws, stream);
+  if (d_k == 128 && d_v == 64) return mf::prep_t<128, 64>(q, k, beta, L, nc, bh, ws, stream);
+  return mf::prep_t<128, 128>(q, k, beta, L, nc, bh, ws, stream);
 }
 
 }  // namespace bwd
