@@ -53,6 +53,24 @@ __device__ __forceinline__ void put_split_t(uint16_t* hi, uint16_t* lo, int P, i
   *reinterpret_cast<uint2*>(lo + off) = o;
 }
 
+// Transposed copies ([column][chunk row], 8 chunks of 8 rows per line) have
+// their 16-byte chunks XOR-swizzled by a function of the line, so that the
+// deposits below (lanes along the source rows) hit distinct banks:
+//   lines from a C x DK tile: chunk ^ ((line >> 3) & 7)   (SH = 3)
+//   lines from a C x C block: chunk ^ ((line >> 2) & 7)   (SH = 2)
+template <int SH>
+__device__ __forceinline__ int tpos(int line, int row) {
+  return line * PC + ((((row >> 3) ^ (line >> SH)) & 7) << 3) + (row & 7);
+}
+
+// frag() for a swizzled transposed copy.
+template <int SH>
+__device__ __forceinline__ bf16x8 fragT(const uint16_t* a, int r0, int kb) {
+  const int l = threadIdx.x & 63, line = r0 + (l & 15);
+  const int ch = (((kb >> 3) + (l >> 4)) ^ (line >> SH)) & 7;
+  return as_bf16x8(*reinterpret_cast<const uint4*>(a + line * PC + (ch << 3)));
+}
+
 // bf16 element e (0..7) of 16 bytes.
 __device__ __forceinline__ uint16_t elem8(const uint4& x, int e) {
   const uint32_t w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
@@ -60,8 +78,8 @@ __device__ __forceinline__ uint16_t elem8(const uint4& x, int e) {
 }
 
 // Loads of one chunk's C x DK bf16 tile (q or k): 16 bytes per thread per
-// step, the chunk row fastest across lanes; rows at or past `valid` read as
-// zero (the load itself is clamped to a valid row).
+// step, consecutive lanes along a row; rows at or past `valid` read as zero
+// (the load itself is clamped to a valid row).
 template <int DK, int NTHR = NTH>
 struct RowTile {
   static constexpr int N = C * DK / 8 / NTHR;
@@ -70,7 +88,7 @@ struct RowTile {
     const uint4* s = reinterpret_cast<const uint4*>(src);
 #pragma unroll
     for (int p = 0; p < N; ++p) {
-      const int f = threadIdx.x + p * NTHR, r = f % C, c8 = f / C;
+      const int f = threadIdx.x + p * NTHR, r = f / (DK / 8), c8 = f % (DK / 8);
       const uint4 v = s[min(r, valid - 1) * (DK / 8) + c8];
       x[p] = r < valid ? v : make_uint4(0u, 0u, 0u, 0u);
     }
@@ -79,59 +97,57 @@ struct RowTile {
   __device__ __forceinline__ void put_rows(uint16_t* dst) const {
 #pragma unroll
     for (int p = 0; p < N; ++p) {
-      const int f = threadIdx.x + p * NTHR, r = f % C, c8 = f / C;
+      const int f = threadIdx.x + p * NTHR, r = f / (DK / 8), c8 = f % (DK / 8);
       *reinterpret_cast<uint4*>(dst + r * (DK + 8) + 8 * c8) = x[p];
     }
   }
-  // Transposed copy [DK][PC].
+  // Transposed copy [DK][PC], swizzled (SH = 3).
   __device__ __forceinline__ void put_cols(uint16_t* dst) const {
 #pragma unroll
     for (int p = 0; p < N; ++p) {
-      const int f = threadIdx.x + p * NTHR, r = f % C, c8 = f / C;
+      const int f = threadIdx.x + p * NTHR, r = f / (DK / 8), c8 = f % (DK / 8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dst[(8 * c8 + e) * PC + r] = elem8(x[p], e);
+      for (int e = 0; e < 8; ++e) dst[tpos<3>(8 * c8 + e, r)] = elem8(x[p], e);
     }
   }
 };
 
-// Loads of one chunk's C x C fp32 block of the workspace (X or M).
+// Loads of one chunk's C x C fp32 block of the workspace (X or M),
+// contiguous across the workgroup.
 struct SqTile {
   static constexpr int N = C * C / 4 / NTH;
   float4 x[N];
   __device__ __forceinline__ void load(const float* src) {
     const float4* s = reinterpret_cast<const float4*>(src);
 #pragma unroll
-    for (int p = 0; p < N; ++p) {
-      const int f = threadIdx.x + p * NTH, r = f % C, c4 = f / C;
-      x[p] = s[r * (C / 4) + c4];
-    }
+    for (int p = 0; p < N; ++p) x[p] = s[threadIdx.x + p * NTH];
   }
   // Split, row-major [C][PC].
   __device__ __forceinline__ void put_rows(uint16_t* hi, uint16_t* lo) const {
 #pragma unroll
     for (int p = 0; p < N; ++p) {
-      const int f = threadIdx.x + p * NTH, r = f % C, c4 = f / C;
+      const int f = threadIdx.x + p * NTH, r = f / (C / 4), c4 = f % (C / 4);
       uint2 h, o;
       split4(x[p], h, o);
       *reinterpret_cast<uint2*>(hi + r * PC + 4 * c4) = h;
       *reinterpret_cast<uint2*>(lo + r * PC + 4 * c4) = o;
     }
   }
-  // Split, transposed [C][PC]: hi[column * PC + row].
+  // Split, transposed [C][PC] and swizzled (SH = 2).
   __device__ __forceinline__ void put_cols(uint16_t* hi, uint16_t* lo) const {
 #pragma unroll
     for (int p = 0; p < N; ++p) {
-      const int f = threadIdx.x + p * NTH, r = f % C, c4 = f / C;
+      const int f = threadIdx.x + p * NTH, r = f / (C / 4), c4 = f % (C / 4);
       uint2 h, o;
       split4(x[p], h, o);
-      hi[(4 * c4 + 0) * PC + r] = static_cast<uint16_t>(h.x);
-      hi[(4 * c4 + 1) * PC + r] = static_cast<uint16_t>(h.x >> 16);
-      hi[(4 * c4 + 2) * PC + r] = static_cast<uint16_t>(h.y);
-      hi[(4 * c4 + 3) * PC + r] = static_cast<uint16_t>(h.y >> 16);
-      lo[(4 * c4 + 0) * PC + r] = static_cast<uint16_t>(o.x);
-      lo[(4 * c4 + 1) * PC + r] = static_cast<uint16_t>(o.x >> 16);
-      lo[(4 * c4 + 2) * PC + r] = static_cast<uint16_t>(o.y);
-      lo[(4 * c4 + 3) * PC + r] = static_cast<uint16_t>(o.y >> 16);
+      hi[tpos<2>(4 * c4 + 0, r)] = static_cast<uint16_t>(h.x);
+      hi[tpos<2>(4 * c4 + 1, r)] = static_cast<uint16_t>(h.x >> 16);
+      hi[tpos<2>(4 * c4 + 2, r)] = static_cast<uint16_t>(h.y);
+      hi[tpos<2>(4 * c4 + 3, r)] = static_cast<uint16_t>(h.y >> 16);
+      lo[tpos<2>(4 * c4 + 0, r)] = static_cast<uint16_t>(o.x);
+      lo[tpos<2>(4 * c4 + 1, r)] = static_cast<uint16_t>(o.x >> 16);
+      lo[tpos<2>(4 * c4 + 2, r)] = static_cast<uint16_t>(o.y);
+      lo[tpos<2>(4 * c4 + 3, r)] = static_cast<uint16_t>(o.y >> 16);
     }
   }
 };
@@ -319,7 +335,7 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
     for (int i = 0; i < TPW; ++i)
 #pragma unroll
       for (int ks = 0; ks < C / 32; ++ks)
-        S[i] = mfma_split2(frag(Kt, PC, 16 * (w * TPW + i), 32 * ks), frag(Dh, PC, 0, 32 * ks),
+        S[i] = mfma_split2(fragT<3>(Kt, 16 * (w * TPW + i), 32 * ks), frag(Dh, PC, 0, 32 * ks),
                            frag(Dl, PC, 0, 32 * ks), S[i]);
     __syncthreads();
   }
@@ -432,7 +448,7 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
     f32x4 acc = zero4();
 #pragma unroll
     for (int ks = w / 2; ks < C / 32; ++ks)
-      acc = mfma_split3(frag(Mh, PC, r0, 32 * ks), frag(Ml, PC, r0, 32 * ks), frag(Oh, PC, 0, 32 * ks),
+      acc = mfma_split3(fragT<2>(Mh, r0, 32 * ks), fragT<2>(Ml, r0, 32 * ks), frag(Oh, PC, 0, 32 * ks),
                         frag(Ol, PC, 0, 32 * ks), acc);
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks)
@@ -447,7 +463,7 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
     acc = zero4();
 #pragma unroll
     for (int ks = w / 2; ks < C / 32; ++ks)
-      acc = mfma_split3(frag(Xh, PC, r0, 32 * ks), frag(Xl, PC, r0, 32 * ks), frag(Eh, PC, 0, 32 * ks),
+      acc = mfma_split3(fragT<2>(Xh, r0, 32 * ks), fragT<2>(Xl, r0, 32 * ks), frag(Eh, PC, 0, 32 * ks),
                         frag(El, PC, 0, 32 * ks), acc);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -464,9 +480,9 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
       const int d0 = 16 * (w * TPW + i);
 #pragma unroll
       for (int ks = 0; ks < C / 32; ++ks) {
-        G[i] = mfma_split2(frag(Qt, PC, d0, 32 * ks), frag(Oh, PC, 0, 32 * ks), frag(Ol, PC, 0, 32 * ks),
+        G[i] = mfma_split2(fragT<3>(Qt, d0, 32 * ks), frag(Oh, PC, 0, 32 * ks), frag(Ol, PC, 0, 32 * ks),
                            G[i]);
-        G[i] = mfma_split2(frag(Kt, PC, d0, 32 * ks), frag(Fh, PC, 0, 32 * ks), frag(Fl, PC, 0, 32 * ks),
+        G[i] = mfma_split2(fragT<3>(Kt, d0, 32 * ks), frag(Fh, PC, 0, 32 * ks), frag(Fl, PC, 0, 32 * ks),
                            G[i]);
       }
     }
@@ -638,7 +654,7 @@ __global__ __launch_bounds__(DK * 4) void qk_grad_kernel(
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
           const int d0 = 16 * (w * TPW + i);
-          const bf16x8 bk = frag(Kt, PC, d0, 32 * ks), bq = frag(Qt, PC, d0, 32 * ks);
+          const bf16x8 bk = fragT<3>(Kt, d0, 32 * ks), bq = fragT<3>(Qt, d0, 32 * ks);
           aq[rt][i] = mfma16(mh, bk, aq[rt][i]);
           aq[rt][i] = mfma16(ml, bk, aq[rt][i]);
           ak[rt][i] = mfma16(th, bq, ak[rt][i]);
