@@ -439,7 +439,7 @@ def main(argv=None) -> int:
             "workload": w.name + "_kda", "steps": a.steps, "ms_per_step": ms_k,
             "tokens_per_s": w.B * w.L / (ms_k * 1e-3),
             "kernels_ms": {name: tot / n for name, (tot, n) in kprof.items()},
-            "path": "fp32 vector ALU, 64-token chunks",
+            "path": "64-token chunks; prep fp32 vector ALU, scan on bf16 MFMA (split-precision operands)",
             "alpha": "sigmoid(N(3, 1)) per token and key dimension (seeded stream of its own)",
         }
         del kws, kalpha

@@ -27,6 +27,7 @@
 
 #include "dn_backward.h"
 #include "dn_common.h"
+#include "dn_lds64.h"
 #include "dn_mfma.h"
 #include "dn_valu_common.h"
 
@@ -34,42 +35,8 @@ namespace dn {
 namespace bwd {
 namespace mf {
 
-constexpr int NTH = 256;   // 4 waves
-constexpr int PC = C + 8;  // pitch (bf16) of arrays whose contraction runs over chunk rows
-
-__device__ __forceinline__ bf16x8 frag(const uint16_t* a, int P, int r0, int kb) {
-  const int l = threadIdx.x & 63;
-  return as_bf16x8(*reinterpret_cast<const uint4*>(a + (r0 + (l & 15)) * P + kb + 8 * (l >> 4)));
-}
-
-// A D tile (lane: column l % 16, rows r0 + 4 (l / 16) + e) split into hi and
-// lo and stored transposed, hi[column * P + row].
-__device__ __forceinline__ void put_split_t(uint16_t* hi, uint16_t* lo, int P, int r0, f32x4 v) {
-  const int l = threadIdx.x & 63;
-  uint2 h, o;
-  split4(v, h, o);
-  const int off = (l & 15) * P + r0 + 4 * (l >> 4);
-  *reinterpret_cast<uint2*>(hi + off) = h;
-  *reinterpret_cast<uint2*>(lo + off) = o;
-}
-
-// Transposed copies ([column][chunk row], 8 chunks of 8 rows per line) have
-// their 16-byte chunks XOR-swizzled by a function of the line, so that the
-// deposits below (lanes along the source rows) hit distinct banks:
-//   lines from a C x DK tile: chunk ^ ((line >> 3) & 7)   (SH = 3)
-//   lines from a C x C block: chunk ^ ((line >> 2) & 7)   (SH = 2)
-template <int SH>
-__device__ __forceinline__ int tpos(int line, int row) {
-  return line * PC + ((((row >> 3) ^ (line >> SH)) & 7) << 3) + (row & 7);
-}
-
-// frag() for a swizzled transposed copy.
-template <int SH>
-__device__ __forceinline__ bf16x8 fragT(const uint16_t* a, int r0, int kb) {
-  const int l = threadIdx.x & 63, line = r0 + (l & 15);
-  const int ch = (((kb >> 3) + (l >> 4)) ^ (line >> SH)) & 7;
-  return as_bf16x8(*reinterpret_cast<const uint4*>(a + line * PC + (ch << 3)));
-}
+constexpr int NTH = 256;  // 4 waves
+using namespace lds64;
 
 // bf16 element e (0..7) of 16 bytes.
 __device__ __forceinline__ uint16_t elem8(const uint4& x, int e) {
@@ -516,15 +483,6 @@ struct QkLds {
   static constexpr size_t b_bytes = 2 * (size_t)DK * PC * 2 + 2 * (size_t)C * PF * sizeof(float);
   static constexpr size_t bytes = a_bytes > b_bytes ? a_bytes : b_bytes;
 };
-
-// 8 fp32 values -> split bf16x8 pair.
-__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
-  uint2 h0, l0, h1, l1;
-  split4(make_float4(x[0], x[1], x[2], x[3]), h0, l0);
-  split4(make_float4(x[4], x[5], x[6], x[7]), h1, l1);
-  hi = as_bf16x8(h0, h1);
-  lo = as_bf16x8(l0, l1);
-}
 
 template <int DK, int DV>
 __global__ __launch_bounds__(DK * 4) void qk_grad_kernel(

@@ -1,0 +1,31 @@
+// dn_kda.h -- what the per-dimension-decay (KDA) kernels share: the chunk
+// size, the column slice of the scan and the per-chunk workspace layout, and
+// the launch of the matrix-core scan (dn_kda_mfma.hip) that replaces the
+// vector-ALU scan for bf16 v.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace dn {
+namespace kda {
+
+constexpr int C = 64;   // chunk rows
+constexpr int NT = 16;  // d_v columns per scan workgroup
+
+// Workspace per (head, chunk), in floats, each block row-major: T, P
+// (C x C each), K o e^g, Q o e^g, K o e^{g_C - g} (C x d_k each), e^{g_C}
+// (d_k).
+__host__ __device__ constexpr size_t chunk_floats(int dk) {
+  return 2 * (size_t)C * C + 3 * (size_t)C * dk + dk;
+}
+
+// The scan over chunks on the matrix cores, from the workspace the prep
+// kernel has filled: o (out_dtype 0 = fp32, 1 = bf16) and S_final (when not
+// null).  v is bf16.  nc = ceil(L / C) >= 0; bh = B * H.
+hipError_t launch_scan_mfma(int d_k, int d_v, int out_dtype, const void* v, const float* S0,
+                            void* o, float* S_final, int L, int nc, int bh, const float* ws,
+                            hipStream_t stream);
+
+}  // namespace kda
+}  // namespace dn

@@ -33,6 +33,7 @@
 //        independently), staging each chunk's operands into LDS first.
 
 #include "dn_common.h"
+#include "dn_kda.h"
 #include "dn_launch.h"
 #include "dn_valu_common.h"
 
@@ -40,17 +41,9 @@ namespace dn {
 namespace kda {
 
 using valu::load_rows;
-constexpr int C = 64;      // chunk rows
-constexpr int NT = 16;     // d_v columns per scan workgroup
 constexpr int NTHR = 1024; // threads per workgroup: the LDS a chunk needs
                            // allows one workgroup per CU, so it brings 16
                            // waves to hide LDS and memory latency
-
-// Workspace per (head, chunk), in floats: T, P (C x C each), K o e^g,
-// Q o e^g, K o e^{g_C - g} (C x d_k each), e^{g_C} (d_k).
-__host__ __device__ constexpr size_t chunk_floats(int dk) {
-  return 2 * (size_t)C * C + 3 * (size_t)C * dk + dk;
-}
 
 template <int DK>
 struct PrepSmem {
@@ -288,6 +281,13 @@ hipError_t launch_t(const ChunkArgs& a) {
     e = hipGetLastError();
     prof_mark(kSlotChunkPrep, true, a.stream);
     if (e != hipSuccess) return e;
+  }
+  if constexpr (sizeof(IT) == 2) {  // bf16 v: the scan runs on the matrix cores
+    prof_mark(kSlotChunkScan, false, a.stream);
+    const hipError_t e = launch_scan_mfma(DK, DV, a.out_dtype, a.v, a.S0, a.o, a.S_final, a.L, nc,
+                                          bh, ws, a.stream);
+    prof_mark(kSlotChunkScan, true, a.stream);
+    return e;
   }
   constexpr size_t sm2 = ScanSmem<DK>::bytes;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<DK, DV, IT, OT>),

@@ -1,0 +1,274 @@
+// dn_kda_mfma.hip -- the per-dimension-decay (KDA) scan on the gfx950 matrix
+// cores, for bf16 v.
+//
+// Same products as the vector-ALU scan in dn_kda.hip, chunk by chunk from
+// the prep kernel's workspace (T, P, K o e^g, Q o e^g, K o e^{g_C - g},
+// e^{g_C}):
+//     R  = V - (K o e^g) S,        Delta = T R,
+//     O  = (Q o e^g) S + P Delta,  S' = diag(e^{g_C}) S + (K o e^{g_C - g})^T Delta.
+// Every operand is fp32, so each product is taken as three 16 x 16 x 32
+// bf16 MFMAs on split (hi, lo) pairs (dn_mfma.h), accumulated in fp32.
+//
+// One 4-wave workgroup per (head, 16 columns of d_v); the slice of the state
+// lives in MFMA accumulators (wave w holds row tiles w d_k / 64 ...).  Wave w
+// owns chunk rows 16 w .. 16 w + 15 of R, Delta and O, so the row operands of
+// those products (rows of K o e^g, Q o e^g, T and P) are private to it: each
+// wave loads them from the workspace straight into fragment registers, a
+// chunk ahead.  Only K o e^{g_C - g}, which the state update contracts over
+// chunk rows, goes through LDS (transposed, split), together with the split
+// state and the R and Delta columns that pass between the waves.  Four
+// barriers per chunk: deposit, R (and (Q o e^g) S), Delta, O and S'.
+
+#include "dn_common.h"
+#include "dn_kda.h"
+#include "dn_lds64.h"
+#include "dn_mfma.h"
+
+namespace dn {
+namespace kda {
+namespace mf {
+
+using lds64::frag;
+using lds64::fragT;
+using lds64::PC;
+using lds64::put_split_t;
+using lds64::tpos;
+
+constexpr int NTH = 256;  // 4 waves
+
+template <int DK>
+struct ScanLds {
+  static constexpr int PK = DK + 8;
+  static constexpr int PV = NT + 1;
+  static constexpr size_t halves =
+      2 * (size_t)DK * PC + 2 * (size_t)NT * PK + 4 * (size_t)NT * PC;
+  static constexpr size_t bytes = halves * 2 + ((size_t)C * PV + DK) * sizeof(float);
+};
+
+// 8 fp32 values (two float4) -> split bf16x8 pair.
+__device__ __forceinline__ void split_f8(const float4& a, const float4& b, bf16x8& hi, bf16x8& lo) {
+  uint2 h0, l0, h1, l1;
+  split4(a, h0, l0);
+  split4(b, h1, l1);
+  hi = as_bf16x8(h0, h1);
+  lo = as_bf16x8(l0, l1);
+}
+
+template <typename OT> __device__ __forceinline__ void put_out(OT* p, float x);
+template <> __device__ __forceinline__ void put_out<float>(float* p, float x) { *p = x; }
+template <> __device__ __forceinline__ void put_out<bf16>(bf16* p, float x) { *p = from_f32<bf16>(x); }
+
+template <int DK, int DV, typename OT>
+__global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
+                                                   const float* __restrict__ S0,
+                                                   OT* __restrict__ o,
+                                                   float* __restrict__ S_final, int L, int nc,
+                                                   const float* __restrict__ ws) {
+  using LD = ScanLds<DK>;
+  constexpr int PK = LD::PK, PV = LD::PV;
+  constexpr int TPW = DK / 64;              // state row tiles per wave
+  constexpr int KS = DK / 32;               // contraction steps over d_k
+  constexpr int NKU = C * DK / 4 / NTH;     // float4 of K o e^{g_C - g} per thread
+  constexpr size_t CF = chunk_floats(DK);
+  constexpr size_t OFF_P = (size_t)C * C, OFF_KD = 2 * (size_t)C * C;
+  constexpr size_t OFF_QD = OFF_KD + (size_t)C * DK, OFF_KU = OFF_QD + (size_t)C * DK;
+  constexpr size_t OFF_GAM = OFF_KU + (size_t)C * DK;
+  extern __shared__ uint4 lds_u4[];
+  uint16_t* Uh = reinterpret_cast<uint16_t*>(lds_u4);  // (K o e^{g_C-g})^T, swizzled [DK][PC]
+  uint16_t* Ul = Uh + DK * PC;
+  uint16_t* Sh = Ul + DK * PC;                          // -S^T        [NT][PK]
+  uint16_t* Sl = Sh + NT * PK;
+  uint16_t* Rh = Sl + NT * PK;                          // R^T         [NT][PC]
+  uint16_t* Rl = Rh + NT * PC;
+  uint16_t* Dh = Rl + NT * PC;                          // Delta^T     [NT][PC]
+  uint16_t* Dl = Dh + NT * PC;
+  float* Vs = reinterpret_cast<float*>(Dl + NT * PC);   // V slice     [C][PV]
+  float* gs = Vs + C * PV;                              // e^{g_C}     [DK]
+
+  const int j0 = blockIdx.x * NT, bh = blockIdx.y;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
+  const int r0 = 16 * w;
+
+  f32x4 S[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int d0 = 16 * (w * TPW + i) + 4 * g;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      S[i][e] = S0 ? S0[((size_t)bh * DK + d0 + e) * DV + j0 + n] : 0.f;
+  }
+
+  // Next chunk's operands, in registers.
+  float4 kd[KS][2], qd[KS][2], tt[2][2], pp[2][2], ku[NKU];
+  uint2 pv = make_uint2(0u, 0u);
+  float pg = 0.f;
+  auto fetch = [&](int cc) {
+    const int vc = min(C, L - cc * C);
+    const size_t t0 = (size_t)bh * L + (size_t)cc * C;
+    const float* b = ws + ((size_t)bh * nc + cc) * CF;
+    const int row = r0 + n;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const size_t off = (size_t)row * DK + 32 * ks + 8 * g;
+      kd[ks][0] = *reinterpret_cast<const float4*>(b + OFF_KD + off);
+      kd[ks][1] = *reinterpret_cast<const float4*>(b + OFF_KD + off + 4);
+      qd[ks][0] = *reinterpret_cast<const float4*>(b + OFF_QD + off);
+      qd[ks][1] = *reinterpret_cast<const float4*>(b + OFF_QD + off + 4);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const size_t off = (size_t)row * C + 32 * ks + 8 * g;
+      tt[ks][0] = *reinterpret_cast<const float4*>(b + off);
+      tt[ks][1] = *reinterpret_cast<const float4*>(b + off + 4);
+      pp[ks][0] = *reinterpret_cast<const float4*>(b + OFF_P + off);
+      pp[ks][1] = *reinterpret_cast<const float4*>(b + OFF_P + off + 4);
+    }
+#pragma unroll
+    for (int p = 0; p < NKU; ++p) {  // 8 lanes per 128-byte line, 8 rows per wave
+      const int f = t + p * NTH, c4 = (f >> 9) * 8 + (f & 7), r = (f >> 3) & 63;
+      ku[p] = *reinterpret_cast<const float4*>(b + OFF_KU + (size_t)r * DK + 4 * c4);
+    }
+    {
+      const int r = t % C, c4 = t / C;
+      const uint2 x =
+          *reinterpret_cast<const uint2*>(v + (t0 + min(r, vc - 1)) * DV + j0 + 4 * c4);
+      pv = r < vc ? x : make_uint2(0u, 0u);
+    }
+    if (t < DK) pg = b[OFF_GAM + t];
+  };
+
+  if (nc > 0) fetch(0);
+  for (int c = 0; c < nc; ++c) {
+    const int valid = min(C, L - c * C);
+    const size_t tok0 = (size_t)bh * L + (size_t)c * C;
+    // Phase 0: this chunk's operands from the registers into split
+    // fragments and LDS; the state into LDS.
+    bf16x8 kdh[KS], kdl[KS], qdh[KS], qdl[KS], tth[2], ttl[2], pph[2], ppl[2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      split_f8(kd[ks][0], kd[ks][1], kdh[ks], kdl[ks]);
+      split_f8(qd[ks][0], qd[ks][1], qdh[ks], qdl[ks]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      split_f8(tt[ks][0], tt[ks][1], tth[ks], ttl[ks]);
+      split_f8(pp[ks][0], pp[ks][1], pph[ks], ppl[ks]);
+    }
+#pragma unroll
+    for (int p = 0; p < NKU; ++p) {
+      const int f = t + p * NTH, c4 = (f >> 9) * 8 + (f & 7), r = (f >> 3) & 63;
+      uint2 h, lo;
+      split4(ku[p], h, lo);
+      Uh[tpos<2>(4 * c4 + 0, r)] = static_cast<uint16_t>(h.x);
+      Uh[tpos<2>(4 * c4 + 1, r)] = static_cast<uint16_t>(h.x >> 16);
+      Uh[tpos<2>(4 * c4 + 2, r)] = static_cast<uint16_t>(h.y);
+      Uh[tpos<2>(4 * c4 + 3, r)] = static_cast<uint16_t>(h.y >> 16);
+      Ul[tpos<2>(4 * c4 + 0, r)] = static_cast<uint16_t>(lo.x);
+      Ul[tpos<2>(4 * c4 + 1, r)] = static_cast<uint16_t>(lo.x >> 16);
+      Ul[tpos<2>(4 * c4 + 2, r)] = static_cast<uint16_t>(lo.y);
+      Ul[tpos<2>(4 * c4 + 3, r)] = static_cast<uint16_t>(lo.y >> 16);
+    }
+    {
+      const int r = t % C, c4 = t / C;
+      Vs[r * PV + 4 * c4 + 0] = __uint_as_float(pv.x << 16);
+      Vs[r * PV + 4 * c4 + 1] = __uint_as_float(pv.x & 0xffff0000u);
+      Vs[r * PV + 4 * c4 + 2] = __uint_as_float(pv.y << 16);
+      Vs[r * PV + 4 * c4 + 3] = __uint_as_float(pv.y & 0xffff0000u);
+    }
+    if (t < DK) gs[t] = pg;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) put_split_t(Sh, Sl, PK, 16 * (w * TPW + i), -S[i]);
+    __syncthreads();
+    if (c + 1 < nc) fetch(c + 1);
+
+    // Phase 1: R = V - (K o e^g) S and (Q o e^g)(-S), row tile w.
+    f32x4 ar, aq = zero4();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ar[e] = Vs[(r0 + 4 * g + e) * PV + n];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 sh = frag(Sh, PK, 0, 32 * ks), sl = frag(Sl, PK, 0, 32 * ks);
+      ar = mfma_split3(kdh[ks], kdl[ks], sh, sl, ar);
+      aq = mfma_split3(qdh[ks], qdl[ks], sh, sl, aq);
+    }
+    put_split_t(Rh, Rl, PC, r0, ar);
+    __syncthreads();
+
+    // Phase 2: Delta = T R, row tile w (T is lower triangular).
+    f32x4 ad = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      if (ks <= w / 2)
+        ad = mfma_split3(tth[ks], ttl[ks], frag(Rh, PC, 0, 32 * ks), frag(Rl, PC, 0, 32 * ks), ad);
+    put_split_t(Dh, Dl, PC, r0, ad);
+    __syncthreads();
+
+    // Phase 3: O = (Q o e^g) S + P Delta (row tile w), and
+    // S' = diag(e^{g_C}) S + (K o e^{g_C - g})^T Delta.
+    f32x4 ao = -aq;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      if (ks <= w / 2)
+        ao = mfma_split3(pph[ks], ppl[ks], frag(Dh, PC, 0, 32 * ks), frag(Dl, PC, 0, 32 * ks), ao);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = r0 + 4 * g + e;
+      if (r < valid) put_out<OT>(o + (tok0 + r) * DV + j0 + n, ao[e]);
+    }
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int d0 = 16 * (w * TPW + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[i][e] *= gs[d0 + 4 * g + e];
+#pragma unroll
+      for (int ks = 0; ks < C / 32; ++ks)
+        S[i] = mfma_split3(fragT<2>(Uh, d0, 32 * ks), fragT<2>(Ul, d0, 32 * ks),
+                           frag(Dh, PC, 0, 32 * ks), frag(Dl, PC, 0, 32 * ks), S[i]);
+    }
+    __syncthreads();
+  }
+  if (S_final)
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int d0 = 16 * (w * TPW + i) + 4 * g;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S_final[((size_t)bh * DK + d0 + e) * DV + j0 + n] = S[i][e];
+    }
+}
+
+template <int DK, int DV, typename OT>
+hipError_t scan_t(const void* v, const float* S0, void* o, float* S_final, int L, int nc, int bh,
+                  const float* ws, hipStream_t s) {
+  auto* kern = &scan_kernel<DK, DV, OT>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)ScanLds<DK>::bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(DV / NT, bh), dim3(NTH), ScanLds<DK>::bytes, s,
+                     static_cast<const bf16*>(v), S0, static_cast<OT*>(o), S_final, L, nc, ws);
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t scan_types(int out_dtype, const void* v, const float* S0, void* o, float* S_final, int L,
+                      int nc, int bh, const float* ws, hipStream_t s) {
+  return out_dtype == 1 ? scan_t<DK, DV, bf16>(v, S0, o, S_final, L, nc, bh, ws, s)
+                        : scan_t<DK, DV, float>(v, S0, o, S_final, L, nc, bh, ws, s);
+}
+
+}  // namespace mf
+
+hipError_t launch_scan_mfma(int d_k, int d_v, int out_dtype, const void* v, const float* S0,
+                            void* o, float* S_final, int L, int nc, int bh, const float* ws,
+                            hipStream_t stream) {
+  if (d_k == 64 && d_v == 64)
+    return mf::scan_types<64, 64>(out_dtype, v, S0, o, S_final, L, nc, bh, ws, stream);
+  if (d_k == 64 && d_v == 128)
+    return mf::scan_types<64, 128>(out_dtype, v, S0, o, S_final, L, nc, bh, ws, stream);
+  if (d_k == 128 && d_v == 64)
+    return mf::scan_types<128, 64>(out_dtype, v, S0, o, S_final, L, nc, bh, ws, stream);
+  return mf::scan_types<128, 128>(out_dtype, v, S0, o, S_final, L, nc, bh, ws, stream);
+}
+
+}  // namespace kda
+}  // namespace dn
