@@ -439,7 +439,7 @@ def main(argv=None) -> int:
             "workload": w.name + "_kda", "steps": a.steps, "ms_per_step": ms_k,
             "tokens_per_s": w.B * w.L / (ms_k * 1e-3),
             "kernels_ms": {name: tot / n for name, (tot, n) in kprof.items()},
-            "path": "64-token chunks; prep fp32 vector ALU, scan on bf16 MFMA (split-precision operands)",
+            "path": "64-token chunks; bf16 MFMA with split-precision operands for the scan and the prep tiles below the 16-row block diagonal, fp32 vector ALU for the diagonal tiles and the triangular inverse",
             "alpha": "sigmoid(N(3, 1)) per token and key dimension (seeded stream of its own)",
         }
         del kws, kalpha

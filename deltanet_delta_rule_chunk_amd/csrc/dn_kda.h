@@ -1,7 +1,7 @@
 // dn_kda.h -- what the per-dimension-decay (KDA) kernels share: the chunk
 // size, the column slice of the scan and the per-chunk workspace layout, and
-// the launch of the matrix-core scan (dn_kda_mfma.hip) that replaces the
-// vector-ALU scan for bf16 v.
+// the launches of the matrix-core prep and scan (dn_kda_mfma.hip) that
+// replace the vector-ALU kernels for bf16 q, k, v.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,6 +19,12 @@ constexpr int NT = 16;  // d_v columns per scan workgroup
 __host__ __device__ constexpr size_t chunk_floats(int dk) {
   return 2 * (size_t)C * C + 3 * (size_t)C * dk + dk;
 }
+
+// The prep on the matrix cores for bf16 q, k (the tiles of A and P below
+// the 16-row block diagonal): fills the workspace of every chunk.  nc >= 1.
+hipError_t launch_prep_mfma(int d_k, const void* q, const void* k, const float* alpha,
+                            const float* beta, int L, int nc, int bh, float* ws,
+                            hipStream_t stream);
 
 // The scan over chunks on the matrix cores, from the workspace the prep
 // kernel has filled: o (out_dtype 0 = fp32, 1 = bf16) and S_final (when not

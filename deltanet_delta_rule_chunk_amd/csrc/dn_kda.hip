@@ -81,12 +81,17 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const IT* __restrict__ q,
   load_rows(Ks, LD, k + tok0 * DK, valid, C, DK);
   load_rows(Qs, LD, q + tok0 * DK, valid, C, DK);
   for (int r = threadIdx.x; r < C; r += blockDim.x) bs[r] = r < valid ? beta[tok0 + r] : 0.f;
-  // g: one thread per dimension walks the rows (reads of alpha coalesce
-  // across the threads of a row).
+  // g: the log-decays of the whole tile at once (coalesced), then a prefix
+  // sum down each dimension's column in LDS (rows past L add zero).
+  for (int e = threadIdx.x; e < C * DK; e += blockDim.x) {
+    const int r = e / DK, j = e % DK;
+    Gs[r * LD + j] = r < valid ? log_decay(alpha[(tok0 + r) * DK + j]) : 0.f;
+  }
+  __syncthreads();
   for (int j = threadIdx.x; j < DK; j += blockDim.x) {
     float acc = 0.f;
     for (int r = 0; r < C; ++r) {
-      if (r < valid) acc += log_decay(alpha[(tok0 + r) * DK + j]);
+      acc += Gs[r * LD + j];
       Gs[r * LD + j] = acc;
     }
   }
@@ -269,7 +274,12 @@ hipError_t launch_t(const ChunkArgs& a) {
   const int nc = cdiv(a.L, C);
   const int bh = a.B * a.H;
   float* ws = static_cast<float*>(a.workspace);
-  if (nc > 0) {
+  if (nc > 0 && sizeof(IT) == 2) {  // bf16 q, k: the prep's products on the matrix cores
+    prof_mark(kSlotChunkPrep, false, a.stream);
+    const hipError_t e = launch_prep_mfma(DK, a.q, a.k, a.alpha, a.beta, a.L, nc, bh, ws, a.stream);
+    prof_mark(kSlotChunkPrep, true, a.stream);
+    if (e != hipSuccess) return e;
+  } else if (nc > 0) {
     constexpr size_t sm = PrepSmem<DK>::bytes;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<DK, IT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);

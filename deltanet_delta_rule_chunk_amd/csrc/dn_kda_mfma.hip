@@ -23,18 +23,161 @@
 #include "dn_kda.h"
 #include "dn_lds64.h"
 #include "dn_mfma.h"
+#include "dn_valu_common.h"
 
 namespace dn {
 namespace kda {
 namespace mf {
 
 using lds64::frag;
+using lds64::split8;
 using lds64::fragT;
 using lds64::PC;
 using lds64::put_split_t;
 using lds64::tpos;
 
 constexpr int NTH = 256;  // 4 waves
+
+// ---- prep ------------------------------------------------------------------
+// The pair factors of A and P, e^{g_r - g_i} per dimension, are bounded
+// (every exponent <= 0) but do not factor into matrix-core operands over a
+// whole chunk.  Between 16-row blocks they do: for row r in block b > b' and
+// row i in block b', with m = 16 b the first row of r's block,
+//     e^{g_r - g_i} = e^{g_r - g_m} e^{g_m - g_i},
+// and both exponents are <= 0 (g only decreases along the chunk).  So each
+// of the six tiles below the block diagonal is a product of two bounded fp32
+// operands, K o e^{g - g_m} (or Q o e^{g - g_m}) against K o e^{g_m - g},
+// taken on the matrix cores with split operands (one wave per tile).  The
+// four diagonal tiles keep the factor per (pair, dimension) on the vector
+// ALUs (one thread per pair, on the other ten waves).  Then the blocked fp32
+// inverse of I + A, as in the vector-ALU prep.
+constexpr int PNTHR = 1024;
+
+template <int DK>
+struct PrepLds {
+  static constexpr int LD = DK + 1;  // row pitch of the C x d_k tiles
+  static constexpr int LDA = C + 1;  // row pitch of A
+  static constexpr size_t bytes = (3 * (size_t)C * LD + (size_t)C * LDA + C) * sizeof(float);
+};
+
+template <int DK>
+__global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
+                                                     const bf16* __restrict__ k,
+                                                     const float* __restrict__ alpha,
+                                                     const float* __restrict__ beta, int L,
+                                                     float* __restrict__ ws) {
+  constexpr int LD = PrepLds<DK>::LD, LDA = PrepLds<DK>::LDA;
+  constexpr int KS = DK / 32;
+  constexpr size_t CF = chunk_floats(DK);
+  extern __shared__ float smem_f[];
+  float* Ks = smem_f;          // K, later X = (I + A)^{-1}
+  float* Qs = Ks + C * LD;     // Q
+  float* Gs = Qs + C * LD;     // g (cumulative log-decays)
+  float* As = Gs + C * LD;     // A
+  float* bs = As + C * LDA;    // beta
+
+  const int c = blockIdx.x, bh = blockIdx.y, nc = gridDim.x;
+  const int valid = min(C, L - c * C);
+  const size_t tok0 = (size_t)bh * L + (size_t)c * C;
+  float* Tc = ws + ((size_t)bh * nc + c) * CF;
+  float* Pc = Tc + C * C;
+  float* Kd = Pc + C * C;    // K o e^g
+  float* Qd = Kd + C * DK;   // Q o e^g
+  float* Ku = Qd + C * DK;   // K o e^{g_C - g}
+  float* gam = Ku + C * DK;  // e^{g_C}
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
+
+  valu::load_rows(Ks, LD, k + tok0 * DK, valid, C, DK);
+  valu::load_rows(Qs, LD, q + tok0 * DK, valid, C, DK);
+  if (t < C) bs[t] = t < valid ? beta[tok0 + t] : 0.f;
+  // g: the log-decays of the whole tile at once (coalesced), then a prefix
+  // sum down each dimension's column in LDS.
+  for (int e = t; e < C * DK; e += PNTHR) {
+    const int r = e / DK, j = e % DK;
+    Gs[r * LD + j] = r < valid ? log_decay(alpha[(tok0 + r) * DK + j]) : 0.f;
+  }
+  __syncthreads();
+  for (int j = t; j < DK; j += PNTHR) {
+    float acc = 0.f;
+    for (int r = 0; r < C; ++r) {
+      acc += Gs[r * LD + j];
+      Gs[r * LD + j] = acc;
+    }
+  }
+  __syncthreads();
+
+  for (int e = t; e < C * DK; e += PNTHR) {  // the decayed operands of the scan
+    const int r = e / DK, j = e % DK;
+    const float gv = Gs[r * LD + j], gC = Gs[(C - 1) * LD + j];
+    const float kv = Ks[r * LD + j];
+    Kd[e] = kv * __expf(gv);
+    Qd[e] = Qs[r * LD + j] * __expf(gv);
+    Ku[e] = kv * __expf(gC - gv);
+  }
+  for (int j = t; j < DK; j += PNTHR) gam[j] = __expf(Gs[(C - 1) * LD + j]);
+  for (int e = t; e < C * C; e += PNTHR)  // P above the diagonal
+    if (e % C > e / C) Pc[e] = 0.f;
+
+  if (w < 6) {
+    // Tile (br, bi) below the block diagonal; wave w takes tile w of
+    // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
+    const int br = w < 1 ? 1 : w < 3 ? 2 : 3;
+    const int bi = w - (br * (br - 1)) / 2;
+    const int m = 16 * br, ra = 16 * br + n, ib = 16 * bi + n;
+    f32x4 aa = zero4(), ap = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float kt[8], qt[8], kh[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = 32 * ks + 8 * g + e;
+        const float gm = Gs[m * LD + j];
+        const float fr = __expf(Gs[ra * LD + j] - gm);
+        kt[e] = Ks[ra * LD + j] * fr;
+        qt[e] = Qs[ra * LD + j] * fr;
+        kh[e] = Ks[ib * LD + j] * __expf(gm - Gs[ib * LD + j]);
+      }
+      bf16x8 kth, ktl, qth, qtl, khh, khl;
+      split8(kt, kth, ktl);
+      split8(qt, qth, qtl);
+      split8(kh, khh, khl);
+      aa = mfma_split3(kth, ktl, khh, khl, aa);
+      ap = mfma_split3(qth, qtl, khh, khl, ap);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * br + 4 * g + e, i = 16 * bi + n;
+      As[r * LDA + i] = bs[r] * aa[e];
+      Pc[r * C + i] = ap[e];
+    }
+  } else {
+    // Pairs (r, i), i <= r, inside the diagonal tiles: 4 x 136 of them.
+    const int pidx = t - 6 * 64;
+    if (pidx < 4 * 136) {
+      const int b = pidx / 136, qi = pidx % 136;
+      int rr = 0;
+      while ((rr + 1) * (rr + 2) / 2 <= qi) ++rr;
+      const int r = 16 * b + rr, i = 16 * b + qi - rr * (rr + 1) / 2;
+      const float *kr = Ks + r * LD, *ki = Ks + i * LD, *qr = Qs + r * LD;
+      const float *gr = Gs + r * LD, *gi = Gs + i * LD;
+      float a = 0.f, pv = 0.f;
+      for (int j = 0; j < DK; ++j) {
+        const float f = __expf(gr[j] - gi[j]) * ki[j];
+        a += kr[j] * f;
+        pv += qr[j] * f;
+      }
+      As[r * LDA + i] = i < r ? a * bs[r] : 0.f;
+      Pc[r * C + i] = pv;
+    }
+  }
+
+  // X = (I + A)^{-1} over the K tile (no longer needed), then T = X diag(beta).
+  valu::unit_lower_inverse<C>(As, LDA, Ks, LD);
+  for (int e = t; e < C * C; e += PNTHR) {
+    const int r = e / C, i = e % C;
+    Tc[e] = Ks[r * LD + i] * bs[i];
+  }
+}
 
 template <int DK>
 struct ScanLds {
@@ -268,6 +411,22 @@ hipError_t launch_scan_mfma(int d_k, int d_v, int out_dtype, const void* v, cons
   if (d_k == 128 && d_v == 64)
     return mf::scan_types<128, 64>(out_dtype, v, S0, o, S_final, L, nc, bh, ws, stream);
   return mf::scan_types<128, 128>(out_dtype, v, S0, o, S_final, L, nc, bh, ws, stream);
+}
+
+hipError_t launch_prep_mfma(int d_k, const void* q, const void* k, const float* alpha,
+                            const float* beta, int L, int nc, int bh, float* ws,
+                            hipStream_t stream) {
+  auto run = [&](auto* kern, size_t bytes) -> hipError_t {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(nc, bh), dim3(mf::PNTHR), bytes, stream,
+                       static_cast<const bf16*>(q), static_cast<const bf16*>(k), alpha, beta, L,
+                       ws);
+    return hipGetLastError();
+  };
+  if (d_k == 64) return run(&mf::prep_kernel<64>, mf::PrepLds<64>::bytes);
+  return run(&mf::prep_kernel<128>, mf::PrepLds<128>::bytes);
 }
 
 }  // namespace kda
