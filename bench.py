@@ -47,9 +47,11 @@ KERNEL_SOURCES.update({"gated_" + k: v for k, v in list(KERNEL_SOURCES.items()) 
 KERNEL_SOURCES["features_decode"] = KERNEL_SOURCES["decode"]
 KERNEL_SOURCES["kda_decode"] = KERNEL_SOURCES["decode"]
 KERNEL_SOURCES["kda_chunk_prep"] = KERNEL_SOURCES["kda_chunk_scan"] = [
-    "dn_kda.hip", "dn_valu_common.h", "dn_common.h"]
+    "dn_kda.hip", "dn_kda.h", "dn_kda_mfma.hip", "dn_lds64.h", "dn_mfma.h", "dn_valu_common.h",
+    "dn_common.h"]
 for _k in ("bwd_prep", "bwd_fwd_scan", "bwd_scan", "bwd_cc", "bwd_qk"):
-    KERNEL_SOURCES[_k] = ["dn_backward.hip", "dn_valu_common.h", "dn_common.h"]
+    KERNEL_SOURCES[_k] = ["dn_backward.hip", "dn_backward.h", "dn_backward_mfma.hip", "dn_lds64.h",
+                          "dn_mfma.h", "dn_valu_common.h", "dn_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters.json")
 
@@ -413,8 +415,8 @@ def main(argv=None) -> int:
         del bws, dO, grads
 
     if not a.no_kda:
-        # Per-dimension decay (KDA): fp32 vector-ALU chunk kernels, and the
-        # decode step with a d_k-vector gate per (b, h).
+        # Per-dimension decay (KDA): the chunked forward, and the decode step
+        # with a d_k-vector gate per (b, h).
         print(f"[bench] kda forward {w.name}: {a.steps} steps", file=sys.stderr, flush=True)
         kalpha = inputs.make_chunk_kda_alpha(w, seed=a.seed).to(dev)
         kws = torch.empty(binding.kda_workspace_bytes(w.B, w.H, w.L, w.d_k, w.d_v, w.C),

@@ -151,8 +151,9 @@ int deltanet_gated_decode_step(const void* q, const void* k, const void* v, cons
  *   dbeta  : [B, H, L] fp32;       dS0 : [B, H, d_k, d_v] fp32 or NULL (not
  *            written)
  * The forward is recomputed inside (nothing from a previous forward call is
- * needed).  fp32 vector-ALU kernels for either input dtype, 64-token chunks
- * whatever C names (C must still be 64 or 128).  Outputs may not overlap
+ * needed).  64-token chunks whatever C names (C must still be 64 or 128).
+ * bf16 inputs run every product on bf16 matrix cores with each fp32 operand
+ * split into a (hi, lo) bf16 pair; fp32 inputs run fp32 vector-ALU kernels.  Outputs may not overlap
  * inputs or one another.  The workspace holds, per 64-token chunk, the
  * entering state and the exit gradient (2 d_k d_v floats) besides per-chunk
  * matrices: query deltanet_chunk_bwd_workspace_bytes().
@@ -182,9 +183,10 @@ size_t deltanet_chunk_bwd_workspace_bytes(int B, int H, int L, int d_k, int d_v,
  * dimension: [B, H, L, d_k] for the chunked forward, [B, H, d_k] for the
  * decode step.  alpha must be 16-byte aligned and may not overlap an output;
  * zeros are floored inside a chunk as for the scalar gate.  The chunked
- * forward runs fp32 vector-ALU kernels for either input dtype, in 64-token
- * chunks whatever C names (the result does not depend on the chunk size; C
- * must still be 64 or 128).  Its workspace is larger than the other forms':
+ * forward runs in 64-token chunks whatever C names (the result does not
+ * depend on the chunk size; C must still be 64 or 128): for bf16 inputs its
+ * scan and most of its prep on bf16 matrix cores with split operands, for
+ * fp32 inputs on fp32 vector-ALU kernels.  Its workspace is larger than the other forms':
  * query deltanet_kda_chunk_fwd_workspace_bytes().  With L = 0, alpha may be
  * NULL.
  */
