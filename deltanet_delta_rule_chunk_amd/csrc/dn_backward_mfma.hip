@@ -44,77 +44,94 @@ __device__ __forceinline__ uint16_t elem8(const uint4& x, int e) {
   return static_cast<uint16_t>(w >> (16 * (e & 1)));
 }
 
-// Loads of one chunk's C x DK bf16 tile (q or k): 16 bytes per thread per
-// step, consecutive lanes along a row; rows at or past `valid` read as zero
-// (the load itself is clamped to a valid row).
+// Loads of one chunk's C x DK bf16 tile (q or k): each thread takes N
+// consecutive rows of one 16-byte column chunk (consecutive lanes along a
+// row, so a wave's load covers whole cache lines); rows at or past `valid`
+// read as zero (the load itself is clamped to a valid row).  Holding N rows
+// of a column lets the transposed copy store N rows per LDS write.
 template <int DK, int NTHR = NTH>
 struct RowTile {
-  static constexpr int N = C * DK / 8 / NTHR;
+  static constexpr int CPR = DK / 8;              // 16-byte chunks per row
+  static constexpr int N = C * CPR / NTHR;        // rows per thread
+  static_assert(N == 2 || N == 4, "rows per thread");
   uint4 x[N];
+  __device__ __forceinline__ int row0() const { return N * (threadIdx.x / CPR); }
+  __device__ __forceinline__ int chunk() const { return threadIdx.x % CPR; }
   __device__ __forceinline__ void load(const bf16* src, int valid) {
     const uint4* s = reinterpret_cast<const uint4*>(src);
 #pragma unroll
     for (int p = 0; p < N; ++p) {
-      const int f = threadIdx.x + p * NTHR, r = f / (DK / 8), c8 = f % (DK / 8);
-      const uint4 v = s[min(r, valid - 1) * (DK / 8) + c8];
+      const int r = row0() + p;
+      const uint4 v = s[min(r, valid - 1) * CPR + chunk()];
       x[p] = r < valid ? v : make_uint4(0u, 0u, 0u, 0u);
     }
   }
   // Row-major copy [C][DK + 8].
   __device__ __forceinline__ void put_rows(uint16_t* dst) const {
 #pragma unroll
-    for (int p = 0; p < N; ++p) {
-      const int f = threadIdx.x + p * NTHR, r = f / (DK / 8), c8 = f % (DK / 8);
-      *reinterpret_cast<uint4*>(dst + r * (DK + 8) + 8 * c8) = x[p];
-    }
+    for (int p = 0; p < N; ++p)
+      *reinterpret_cast<uint4*>(dst + (row0() + p) * (DK + 8) + 8 * chunk()) = x[p];
   }
-  // Transposed copy [DK][PC], swizzled (SH = 3).
+  // Transposed copy [DK][PC], swizzled (SH = 3): one N-row write per column.
   __device__ __forceinline__ void put_cols(uint16_t* dst) const {
+    const int r0 = row0();
 #pragma unroll
-    for (int p = 0; p < N; ++p) {
-      const int f = threadIdx.x + p * NTHR, r = f / (DK / 8), c8 = f % (DK / 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dst[tpos<3>(8 * c8 + e, r)] = elem8(x[p], e);
+    for (int e = 0; e < 8; ++e) {
+      uint16_t* d = dst + tpos<3>(8 * chunk() + e, r0);
+      if constexpr (N == 4) {
+        *reinterpret_cast<uint2*>(d) =
+            make_uint2(elem8(x[0], e) | (uint32_t)elem8(x[1], e) << 16,
+                       elem8(x[2], e) | (uint32_t)elem8(x[3], e) << 16);
+      } else {
+        *reinterpret_cast<uint32_t*>(d) = elem8(x[0], e) | (uint32_t)elem8(x[1], e) << 16;
+      }
     }
   }
 };
 
-// Loads of one chunk's C x C fp32 block of the workspace (X or M),
-// contiguous across the workgroup.
+// bf16 element e (0..3) of 4 packed in 8 bytes.
+__device__ __forceinline__ uint32_t elem4(const uint2& h, int e) {
+  return ((e < 2 ? h.x : h.y) >> (16 * (e & 1))) & 0xffffu;
+}
+
+// Loads of one chunk's C x C fp32 block of the workspace (X or M): each
+// thread takes 4 consecutive rows of one 16-byte column chunk.
 struct SqTile {
-  static constexpr int N = C * C / 4 / NTH;
+  static constexpr int CPR = C / 4;
+  static constexpr int N = C * CPR / NTH;  // 4
   float4 x[N];
+  __device__ __forceinline__ int row0() const { return N * (threadIdx.x / CPR); }
+  __device__ __forceinline__ int chunk() const { return threadIdx.x % CPR; }
   __device__ __forceinline__ void load(const float* src) {
     const float4* s = reinterpret_cast<const float4*>(src);
 #pragma unroll
-    for (int p = 0; p < N; ++p) x[p] = s[threadIdx.x + p * NTH];
+    for (int p = 0; p < N; ++p) x[p] = s[(row0() + p) * CPR + chunk()];
   }
   // Split, row-major [C][PC].
   __device__ __forceinline__ void put_rows(uint16_t* hi, uint16_t* lo) const {
 #pragma unroll
     for (int p = 0; p < N; ++p) {
-      const int f = threadIdx.x + p * NTH, r = f / (C / 4), c4 = f % (C / 4);
       uint2 h, o;
       split4(x[p], h, o);
-      *reinterpret_cast<uint2*>(hi + r * PC + 4 * c4) = h;
-      *reinterpret_cast<uint2*>(lo + r * PC + 4 * c4) = o;
+      const int off = (row0() + p) * PC + 4 * chunk();
+      *reinterpret_cast<uint2*>(hi + off) = h;
+      *reinterpret_cast<uint2*>(lo + off) = o;
     }
   }
-  // Split, transposed [C][PC] and swizzled (SH = 2).
+  // Split, transposed [C][PC] and swizzled (SH = 2): one 4-row write per
+  // column and half.
   __device__ __forceinline__ void put_cols(uint16_t* hi, uint16_t* lo) const {
+    uint2 h[N], o[N];
 #pragma unroll
-    for (int p = 0; p < N; ++p) {
-      const int f = threadIdx.x + p * NTH, r = f / (C / 4), c4 = f % (C / 4);
-      uint2 h, o;
-      split4(x[p], h, o);
-      hi[tpos<2>(4 * c4 + 0, r)] = static_cast<uint16_t>(h.x);
-      hi[tpos<2>(4 * c4 + 1, r)] = static_cast<uint16_t>(h.x >> 16);
-      hi[tpos<2>(4 * c4 + 2, r)] = static_cast<uint16_t>(h.y);
-      hi[tpos<2>(4 * c4 + 3, r)] = static_cast<uint16_t>(h.y >> 16);
-      lo[tpos<2>(4 * c4 + 0, r)] = static_cast<uint16_t>(o.x);
-      lo[tpos<2>(4 * c4 + 1, r)] = static_cast<uint16_t>(o.x >> 16);
-      lo[tpos<2>(4 * c4 + 2, r)] = static_cast<uint16_t>(o.y);
-      lo[tpos<2>(4 * c4 + 3, r)] = static_cast<uint16_t>(o.y >> 16);
+    for (int p = 0; p < N; ++p) split4(x[p], h[p], o[p]);
+    const int r0 = row0();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int off = tpos<2>(4 * chunk() + e, r0);
+      *reinterpret_cast<uint2*>(hi + off) = make_uint2(elem4(h[0], e) | elem4(h[1], e) << 16,
+                                                       elem4(h[2], e) | elem4(h[3], e) << 16);
+      *reinterpret_cast<uint2*>(lo + off) = make_uint2(elem4(o[0], e) | elem4(o[1], e) << 16,
+                                                       elem4(o[2], e) | elem4(o[3], e) << 16);
     }
   }
 };

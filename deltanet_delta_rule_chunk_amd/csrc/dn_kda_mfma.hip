@@ -212,6 +212,7 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
   constexpr int TPW = DK / 64;              // state row tiles per wave
   constexpr int KS = DK / 32;               // contraction steps over d_k
   constexpr int NKU = C * DK / 4 / NTH;     // float4 of K o e^{g_C - g} per thread
+  static_assert(NKU == 4 || NKU == 8, "rows per thread");
   constexpr size_t CF = chunk_floats(DK);
   constexpr size_t OFF_P = (size_t)C * C, OFF_KD = 2 * (size_t)C * C;
   constexpr size_t OFF_QD = OFF_KD + (size_t)C * DK, OFF_KU = OFF_QD + (size_t)C * DK;
@@ -231,6 +232,7 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
   const int j0 = blockIdx.x * NT, bh = blockIdx.y;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
   const int r0 = 16 * w;
+  const int ku_c4 = t % (DK / 4), ku_r0 = NKU * (t / (DK / 4));
 
   f32x4 S[TPW];
 #pragma unroll
@@ -267,10 +269,8 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
       pp[ks][1] = *reinterpret_cast<const float4*>(b + OFF_P + off + 4);
     }
 #pragma unroll
-    for (int p = 0; p < NKU; ++p) {  // 8 lanes per 128-byte line, 8 rows per wave
-      const int f = t + p * NTH, c4 = (f >> 9) * 8 + (f & 7), r = (f >> 3) & 63;
-      ku[p] = *reinterpret_cast<const float4*>(b + OFF_KU + (size_t)r * DK + 4 * c4);
-    }
+    for (int p = 0; p < NKU; ++p)  // NKU consecutive rows of one 16-byte column chunk
+      ku[p] = *reinterpret_cast<const float4*>(b + OFF_KU + (size_t)(ku_r0 + p) * DK + 4 * ku_c4);
     {
       const int r = t % C, c4 = t / C;
       const uint2 x =
@@ -297,19 +297,32 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
       split_f8(tt[ks][0], tt[ks][1], tth[ks], ttl[ks]);
       split_f8(pp[ks][0], pp[ks][1], pph[ks], ppl[ks]);
     }
+    {  // (K o e^{g_C - g})^T: one NKU-row write per column and half
+      uint32_t h[NKU][2], lo[NKU][2];
 #pragma unroll
-    for (int p = 0; p < NKU; ++p) {
-      const int f = t + p * NTH, c4 = (f >> 9) * 8 + (f & 7), r = (f >> 3) & 63;
-      uint2 h, lo;
-      split4(ku[p], h, lo);
-      Uh[tpos<2>(4 * c4 + 0, r)] = static_cast<uint16_t>(h.x);
-      Uh[tpos<2>(4 * c4 + 1, r)] = static_cast<uint16_t>(h.x >> 16);
-      Uh[tpos<2>(4 * c4 + 2, r)] = static_cast<uint16_t>(h.y);
-      Uh[tpos<2>(4 * c4 + 3, r)] = static_cast<uint16_t>(h.y >> 16);
-      Ul[tpos<2>(4 * c4 + 0, r)] = static_cast<uint16_t>(lo.x);
-      Ul[tpos<2>(4 * c4 + 1, r)] = static_cast<uint16_t>(lo.x >> 16);
-      Ul[tpos<2>(4 * c4 + 2, r)] = static_cast<uint16_t>(lo.y);
-      Ul[tpos<2>(4 * c4 + 3, r)] = static_cast<uint16_t>(lo.y >> 16);
+      for (int p = 0; p < NKU; ++p) {
+        uint2 hh, ll;
+        split4(ku[p], hh, ll);
+        h[p][0] = hh.x, h[p][1] = hh.y, lo[p][0] = ll.x, lo[p][1] = ll.y;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t ph[NKU / 2], pl[NKU / 2];
+#pragma unroll
+        for (int q = 0; q < NKU / 2; ++q) {
+          const int sh = 16 * (e & 1);
+          ph[q] = ((h[2 * q][e >> 1] >> sh) & 0xffffu) | ((h[2 * q + 1][e >> 1] >> sh) << 16);
+          pl[q] = ((lo[2 * q][e >> 1] >> sh) & 0xffffu) | ((lo[2 * q + 1][e >> 1] >> sh) << 16);
+        }
+        const int off = tpos<2>(4 * ku_c4 + e, ku_r0);
+        if constexpr (NKU == 8) {
+          *reinterpret_cast<uint4*>(Uh + off) = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+          *reinterpret_cast<uint4*>(Ul + off) = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+        } else {
+          *reinterpret_cast<uint2*>(Uh + off) = make_uint2(ph[0], ph[1]);
+          *reinterpret_cast<uint2*>(Ul + off) = make_uint2(pl[0], pl[1]);
+        }
+      }
     }
     {
       const int r = t % C, c4 = t / C;
