@@ -199,6 +199,20 @@ __global__ __launch_bounds__(NTH) void prep_kernel(const bf16* __restrict__ q,
   for (int e = t; e < C * C; e += NTH) blk[W.X() + e] = Xs[(e / C) * PF + e % C];
 }
 
+// The state passes' workgroups: a 1-D grid of 8 * ns * ceil(nbh / 8), where
+// ns = d_v / 16 column slices per head.  Workgroups go to the 8 XCDs
+// round-robin by flat id; all slices of a head get the same flat id mod 8,
+// so they run on one XCD and its L2 serves their common q, k, X, M reads.
+// Returns false for the padding workgroups past the last head.
+__device__ __forceinline__ bool slice_of(int ns, int nbh, int& j0, int& bh) {
+  const int flat = blockIdx.x, xcd = flat & 7, sl = flat >> 3;
+  j0 = (sl % ns) * NT;
+  bh = (sl / ns) * 8 + xcd;
+  return bh < nbh;
+}
+
+inline dim3 slice_grid(int ns, int nbh) { return dim3(8 * ns * ((nbh + 7) / 8)); }
+
 // ---- forward state pass -----------------------------------------------------
 template <int DK>
 struct FwdLds {
@@ -214,7 +228,7 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
                                                        const bf16* __restrict__ v,
                                                        const float* __restrict__ beta,
                                                        const float* __restrict__ S0, int L,
-                                                       int nc, float* __restrict__ ws) {
+                                                       int nc, int nbh, float* __restrict__ ws) {
   using LD = FwdLds<DK>;
   constexpr int PK = LD::PK, PV = LD::PV;
   constexpr Ws W{DK, DV};
@@ -233,7 +247,8 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
   float* Vs = reinterpret_cast<float*>(Dl + NT * PC);   // V slice    [C][PV]
   float* bs = Vs + C * PV;
 
-  const int j0 = blockIdx.x * NT, bh = blockIdx.y;
+  int j0, bh;
+  if (!slice_of(DV / NT, nbh, j0, bh)) return;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
 
   f32x4 S[TPW];
@@ -338,7 +353,7 @@ template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ beta,
     const float* __restrict__ dO, const float* __restrict__ dS_final, float* __restrict__ dv,
-    float* __restrict__ dS0, int L, int nc, float* __restrict__ ws) {
+    float* __restrict__ dS0, int L, int nc, int nbh, float* __restrict__ ws) {
   using LD = BwdLds<DK>;
   constexpr int PK = LD::PK;
   constexpr Ws W{DK, DV};
@@ -361,7 +376,8 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
   uint16_t* Fl = Fh + NT * PC;
   float* bs = reinterpret_cast<float*>(Fl + NT * PC);
 
-  const int j0 = blockIdx.x * NT, bh = blockIdx.y;
+  int j0, bh;
+  if (!slice_of(DV / NT, nbh, j0, bh)) return;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
 
   f32x4 G[TPW];
@@ -861,8 +877,9 @@ hipError_t fwd_t(const void* k, const void* v, const float* beta, const float* S
   auto* kern = &fwd_scan_kernel<DK, DV>;
   hipError_t e = set_lds(kern, FwdLds<DK>::bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(DV / NT, bh), dim3(NTH), FwdLds<DK>::bytes, s,
-                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), beta, S0, L, nc, ws);
+  hipLaunchKernelGGL(kern, slice_grid(DV / NT, bh), dim3(NTH), FwdLds<DK>::bytes, s,
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), beta, S0, L, nc, bh,
+                     ws);
   return hipGetLastError();
 }
 
@@ -873,9 +890,9 @@ hipError_t bwd_t(const void* q, const void* k, const float* beta, const float* d
   auto* kern = &bwd_scan_kernel<DK, DV>;
   hipError_t e = set_lds(kern, BwdLds<DK>::bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(DV / NT, bh), dim3(NTH), BwdLds<DK>::bytes, s,
+  hipLaunchKernelGGL(kern, slice_grid(DV / NT, bh), dim3(NTH), BwdLds<DK>::bytes, s,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k), beta, dO, dS_final,
-                     dv, dS0, L, nc, ws);
+                     dv, dS0, L, nc, bh, ws);
   return hipGetLastError();
 }
 

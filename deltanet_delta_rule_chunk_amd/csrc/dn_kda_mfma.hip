@@ -206,7 +206,7 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
                                                    const float* __restrict__ S0,
                                                    OT* __restrict__ o,
                                                    float* __restrict__ S_final, int L, int nc,
-                                                   const float* __restrict__ ws) {
+                                                   int nbh, const float* __restrict__ ws) {
   using LD = ScanLds<DK>;
   constexpr int PK = LD::PK, PV = LD::PV;
   constexpr int TPW = DK / 64;              // state row tiles per wave
@@ -229,7 +229,12 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
   float* Vs = reinterpret_cast<float*>(Dl + NT * PC);   // V slice     [C][PV]
   float* gs = Vs + C * PV;                              // e^{g_C}     [DK]
 
-  const int j0 = blockIdx.x * NT, bh = blockIdx.y;
+  // 1-D grid of 8 * (d_v / 16) * ceil(nbh / 8): all column slices of a head
+  // get the same flat id mod 8, so they share an XCD and its L2 (the
+  // workspace block of a chunk is read by every slice).
+  const int flat = blockIdx.x, xcd = flat & 7, sl = flat >> 3;
+  const int j0 = (sl % (DV / NT)) * NT, bh = (sl / (DV / NT)) * 8 + xcd;
+  if (bh >= nbh) return;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
   const int r0 = 16 * w;
   const int ku_c4 = t % (DK / 4), ku_r0 = NKU * (t / (DK / 4));
@@ -400,8 +405,8 @@ hipError_t scan_t(const void* v, const float* S0, void* o, float* S_final, int L
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)ScanLds<DK>::bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(DV / NT, bh), dim3(NTH), ScanLds<DK>::bytes, s,
-                     static_cast<const bf16*>(v), S0, static_cast<OT*>(o), S_final, L, nc, ws);
+  hipLaunchKernelGGL(kern, dim3(8 * (DV / NT) * ((bh + 7) / 8)), dim3(NTH), ScanLds<DK>::bytes, s,
+                     static_cast<const bf16*>(v), S0, static_cast<OT*>(o), S_final, L, nc, bh, ws);
   return hipGetLastError();
 }
 
