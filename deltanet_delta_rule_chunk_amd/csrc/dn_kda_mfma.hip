@@ -285,10 +285,41 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
     if (t < DK) pg = b[OFF_GAM + t];
   };
 
+  // L2 prefetch of chunk c + 2: the 128-byte lines of its workspace block
+  // and v rows are split over the head's column-slice workgroups (which
+  // share an XCD); thread t touches line slice + NS t with one dword load.
+  // The value is folded in a chunk later, so the load never stalls anything,
+  // and the fold is only ever stored under a condition that is false.
+  constexpr int NS = DV / NT;
+  constexpr int WL = (int)(CF * 4 / 128), VL = C * DV * 2 / 128;
+  constexpr int NPF = ((WL + VL + NS - 1) / NS + NTH - 1) / NTH;
+  const int sidx = sl % NS;
+  uint32_t pf_acc = 0, pf_val[NPF];
+#pragma unroll
+  for (int j = 0; j < NPF; ++j) pf_val[j] = 0;
+  auto prefetch = [&](int cc) {
+    const int vc = min(C, L - cc * C);
+    const size_t t0 = (size_t)bh * L + (size_t)cc * C;
+#pragma unroll
+    for (int j = 0; j < NPF; ++j) {
+      const int ln = min(sidx + NS * (t + NTH * j), WL + VL - 1);
+      const uint32_t* src;
+      if (ln < WL) {
+        src = reinterpret_cast<const uint32_t*>(ws + ((size_t)bh * nc + cc) * CF) + 32 * ln;
+      } else {
+        const int e = (ln - WL) * 64, row = min(e / DV, vc - 1);
+        src = reinterpret_cast<const uint32_t*>(v + (t0 + row) * DV + e % DV);
+      }
+      pf_val[j] = *src;
+    }
+  };
+
   if (nc > 0) fetch(0);
   for (int c = 0; c < nc; ++c) {
     const int valid = min(C, L - c * C);
     const size_t tok0 = (size_t)bh * L + (size_t)c * C;
+#pragma unroll
+    for (int j = 0; j < NPF; ++j) pf_acc ^= pf_val[j];
     // Phase 0: this chunk's operands from the registers into split
     // fragments and LDS; the state into LDS.
     bf16x8 kdh[KS], kdl[KS], qdh[KS], qdl[KS], tth[2], ttl[2], pph[2], ppl[2];
@@ -341,6 +372,7 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
     for (int i = 0; i < TPW; ++i) put_split_t(Sh, Sl, PK, 16 * (w * TPW + i), -S[i]);
     __syncthreads();
     if (c + 1 < nc) fetch(c + 1);
+    prefetch(min(c + 2, nc - 1));
 
     // Phase 1: R = V - (K o e^g) S and (Q o e^g)(-S), row tile w.
     f32x4 ar, aq = zero4();
@@ -395,6 +427,9 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
 #pragma unroll
       for (int e = 0; e < 4; ++e) S_final[((size_t)bh * DK + d0 + e) * DV + j0 + n] = S[i][e];
     }
+#pragma unroll
+  for (int j = 0; j < NPF; ++j) pf_acc ^= pf_val[j];
+  if (nc < 0) S_final[0] = __uint_as_float(pf_acc);
 }
 
 template <int DK, int DV, typename OT>
