@@ -58,6 +58,8 @@ SMALL = [
     ("bf16_d64_ragged", "bf16", 2, 2, 64 * 5 + 7, 64, 64, 64, True, True),
     ("bf16_d128_states", "bf16", 1, 2, 640, 128, 128, 128, True, True),
     ("bf16_L_below_chunk", "bf16", 1, 2, 37, 128, 128, 64, True, True),
+    ("bf16_dk64_dv128_ragged", "bf16", 3, 3, 64 * 3 + 19, 64, 128, 64, True, True),
+    ("bf16_dk128_dv64_nine_heads", "bf16", 1, 9, 64 * 4, 128, 64, 128, False, True),
 ]
 
 

@@ -39,6 +39,8 @@ SMALL = [
     ("bf16_d64_ragged", "bf16", 2, 2, 64 * 5 + 7, 64, 64, 64, False),
     ("bf16_d128_S0", "bf16", 1, 2, 640, 128, 128, 64, True),
     ("bf16_L_below_chunk", "bf16", 1, 2, 37, 128, 128, 128, True),
+    ("bf16_dk64_dv128_ragged", "bf16", 3, 3, 64 * 4 + 50, 64, 128, 64, True),
+    ("bf16_d128_nine_heads", "bf16", 1, 9, 64 * 3, 128, 128, 128, False),
 ]
 
 
@@ -56,6 +58,25 @@ def test_kda_small_parity(gpu_lib, case):
     e = assert_parity(o.cpu(), o_ref, dt, f"{name} o")
     assert_parity(S.cpu(), S_ref, dt, f"{name} S_final")
     _note(f"  o err = {e:.3e}")
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128)])
+def test_kda_bf16_output_is_rounded_fp32_output(gpu_lib, dk, dv):
+    """The bf16 output of the same forward is the fp32 output rounded to
+    nearest even (only the final store differs), and it meets the bf16 bar."""
+    w = I.ChunkWorkload("kda_bf16_out", 2, 3, 64 * 3 + 5, dk, dv, 64, "bf16", s0_std=0.1)
+    x = I.make_chunk_inputs(w, seed=12)
+    alpha = I.make_chunk_kda_alpha(w, seed=12)
+    g = {k: t.to(DEV) for k, t in x.items()}
+    o32, S32 = kda_chunk_fwd(g["q"], g["k"], g["v"], alpha.to(DEV), g["beta"], g["S0"], 64)
+    o16, S16 = kda_chunk_fwd(g["q"], g["k"], g["v"], alpha.to(DEV), g["beta"], g["S0"], 64,
+                             out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o16.cpu(), o32.cpu().to(torch.bfloat16))
+    assert torch.equal(S16.cpu(), S32.cpu())
+    o_ref, _ = _oracle(x, alpha)
+    assert_parity(o16.cpu().float(), o_ref, "bf16", "kda bf16 o")
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
