@@ -27,6 +27,7 @@
 
 #include "dn_backward.h"
 #include "dn_common.h"
+#include "dn_inv64.h"
 #include "dn_lds64.h"
 #include "dn_mfma.h"
 #include "dn_valu_common.h"
@@ -138,14 +139,14 @@ struct SqTile {
 
 // ---- prep: X = (I + A)^{-1} and M = tril(Q K^T) ---------------------------
 // One 4-wave workgroup per (chunk, head).  Wave w forms row tile w of the
-// Gram products K K^T and Q K^T (exact bf16 products, fp32 sums); the
-// blocked fp32 inverse of I + A then runs on the vector ALUs.
+// Gram products K K^T and Q K^T (exact bf16 products, fp32 sums); then the
+// blocked fp32 inverse of I + A (dn_inv64.h).
 template <int DK>
 struct PrepLds {
   static constexpr int PK = DK + 8;
   static constexpr int PF = C + 1;
   static constexpr size_t bytes =
-      2 * (size_t)C * PK * 2 + (2 * (size_t)C * PF + C) * sizeof(float);
+      2 * (size_t)C * PK * 2 + (2 * (size_t)C * PF + C + inv64::SCRATCH_FLOATS) * sizeof(float);
 };
 
 template <int DK, int DV>
@@ -162,6 +163,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(const bf16* __restrict__ q,
   float* As = reinterpret_cast<float*>(Qb + C * PK);    // A      [C][PF]
   float* Xs = As + C * PF;                              // X      [C][PF]
   float* bs = Xs + C * PF;
+  float* scratch = bs + C;
   const int c = blockIdx.x, bh = blockIdx.y, nc = gridDim.x;
   const int valid = min(C, L - c * C);
   const size_t tok0 = (size_t)bh * L + (size_t)c * C;
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(const bf16* __restrict__ q,
       blk[W.M() + r * C + i] = i <= r ? gq[e] : 0.f;
     }
   }
-  valu::unit_lower_inverse<C>(As, PF, Xs, PF);
+  inv64::inverse<PF, PF>(As, Xs, scratch);
   for (int e = t; e < C * C; e += NTH) blk[W.X() + e] = Xs[(e / C) * PF + e % C];
 }
 

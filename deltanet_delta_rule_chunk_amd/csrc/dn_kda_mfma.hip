@@ -20,6 +20,7 @@
 // barriers per chunk: deposit, R (and (Q o e^g) S), Delta, O and S'.
 
 #include "dn_common.h"
+#include "dn_inv64.h"
 #include "dn_kda.h"
 #include "dn_lds64.h"
 #include "dn_mfma.h"
@@ -50,14 +51,15 @@ constexpr int NTH = 256;  // 4 waves
 // taken on the matrix cores with split operands (one wave per tile).  The
 // four diagonal tiles keep the factor per (pair, dimension) on the vector
 // ALUs (one thread per pair, on the other ten waves).  Then the blocked fp32
-// inverse of I + A, as in the vector-ALU prep.
+// inverse of I + A (dn_inv64.h).
 constexpr int PNTHR = 1024;
 
 template <int DK>
 struct PrepLds {
   static constexpr int LD = DK + 1;  // row pitch of the C x d_k tiles
   static constexpr int LDA = C + 1;  // row pitch of A
-  static constexpr size_t bytes = (3 * (size_t)C * LD + (size_t)C * LDA + C) * sizeof(float);
+  static constexpr size_t bytes =
+      (3 * (size_t)C * LD + (size_t)C * LDA + C + inv64::SCRATCH_FLOATS) * sizeof(float);
 };
 
 template <int DK>
@@ -75,6 +77,7 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
   float* Gs = Qs + C * LD;     // g (cumulative log-decays)
   float* As = Gs + C * LD;     // A
   float* bs = As + C * LDA;    // beta
+  float* scratch = bs + C;     // the inverse's per-wave tiles
 
   const int c = blockIdx.x, bh = blockIdx.y, nc = gridDim.x;
   const int valid = min(C, L - c * C);
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
   }
 
   // X = (I + A)^{-1} over the K tile (no longer needed), then T = X diag(beta).
-  valu::unit_lower_inverse<C>(As, LDA, Ks, LD);
+  inv64::inverse<LDA, LD>(As, Ks, scratch);
   for (int e = t; e < C * C; e += PNTHR) {
     const int r = e / C, i = e % C;
     Tc[e] = Ks[r * LD + i] * bs[i];
