@@ -15,7 +15,9 @@ constexpr int NT = 16;  // d_v columns per scan workgroup
 
 // Workspace per (head, chunk), in floats, each block row-major: T, P
 // (C x C each), K o e^g, Q o e^g, K o e^{g_C - g} (C x d_k each), e^{g_C}
-// (d_k).
+// (d_k).  The vector-ALU prep stores the matrix blocks in fp32; the
+// matrix-core prep stores each as its split pair, a bf16 plane of hi =
+// bf16(x) followed by one of lo = bf16(x - hi), in the same bytes.
 __host__ __device__ constexpr size_t chunk_floats(int dk) {
   return 2 * (size_t)C * C + 3 * (size_t)C * dk + dk;
 }

@@ -6,8 +6,10 @@
 // e^{g_C}):
 //     R  = V - (K o e^g) S,        Delta = T R,
 //     O  = (Q o e^g) S + P Delta,  S' = diag(e^{g_C}) S + (K o e^{g_C - g})^T Delta.
-// Every operand is fp32, so each product is taken as three 16 x 16 x 32
-// bf16 MFMAs on split (hi, lo) pairs (dn_mfma.h), accumulated in fp32.
+// Every operand is an fp32 value, which the prep stores as a split (hi, lo)
+// bf16 pair (two planes per matrix block, in the bytes of the fp32 block), so
+// each product is taken as three 16 x 16 x 32 bf16 MFMAs (dn_mfma.h),
+// accumulated in fp32.
 //
 // One 4-wave workgroup per (head, 16 columns of d_v); the slice of the state
 // lives in MFMA accumulators (wave w holds row tiles w d_k / 64 ...).  Wave w
@@ -54,6 +56,13 @@ constexpr int NTH = 256;  // 4 waves
 // inverse of I + A (dn_inv64.h).
 constexpr int PNTHR = 1024;
 
+// x as a split pair: hi[i] = bf16(x), hi[plane + i] = bf16(x - hi[i]).
+__device__ __forceinline__ void put_split(uint16_t* hi, int plane, int i, float x) {
+  const __bf16 h = static_cast<__bf16>(x);
+  hi[i] = __builtin_bit_cast(uint16_t, h);
+  hi[plane + i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x - static_cast<float>(h)));
+}
+
 template <int DK>
 struct PrepLds {
   static constexpr int LD = DK + 1;  // row pitch of the C x d_k tiles
@@ -82,12 +91,14 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
   const int c = blockIdx.x, bh = blockIdx.y, nc = gridDim.x;
   const int valid = min(C, L - c * C);
   const size_t tok0 = (size_t)bh * L + (size_t)c * C;
-  float* Tc = ws + ((size_t)bh * nc + c) * CF;
-  float* Pc = Tc + C * C;
-  float* Kd = Pc + C * C;    // K o e^g
-  float* Qd = Kd + C * DK;   // Q o e^g
-  float* Ku = Qd + C * DK;   // K o e^{g_C - g}
-  float* gam = Ku + C * DK;  // e^{g_C}
+  // Each matrix block holds its split pair as two bf16 planes, hi then lo.
+  float* blk = ws + ((size_t)bh * nc + c) * CF;
+  uint16_t* Tc = reinterpret_cast<uint16_t*>(blk);
+  uint16_t* Pc = Tc + 2 * C * C;
+  uint16_t* Kd = Pc + 2 * C * C;   // K o e^g
+  uint16_t* Qd = Kd + 2 * C * DK;  // Q o e^g
+  uint16_t* Ku = Qd + 2 * C * DK;  // K o e^{g_C - g}
+  float* gam = reinterpret_cast<float*>(Ku + 2 * C * DK);  // e^{g_C}
   const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
 
   valu::load_rows(Ks, LD, k + tok0 * DK, valid, C, DK);
@@ -113,13 +124,13 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
     const int r = e / DK, j = e % DK;
     const float gv = Gs[r * LD + j], gC = Gs[(C - 1) * LD + j];
     const float kv = Ks[r * LD + j];
-    Kd[e] = kv * __expf(gv);
-    Qd[e] = Qs[r * LD + j] * __expf(gv);
-    Ku[e] = kv * __expf(gC - gv);
+    put_split(Kd, C * DK, e, kv * __expf(gv));
+    put_split(Qd, C * DK, e, Qs[r * LD + j] * __expf(gv));
+    put_split(Ku, C * DK, e, kv * __expf(gC - gv));
   }
   for (int j = t; j < DK; j += PNTHR) gam[j] = __expf(Gs[(C - 1) * LD + j]);
   for (int e = t; e < C * C; e += PNTHR)  // P above the diagonal
-    if (e % C > e / C) Pc[e] = 0.f;
+    if (e % C > e / C) put_split(Pc, C * C, e, 0.f);
 
   if (w < 6) {
     // Tile (br, bi) below the block diagonal; wave w takes tile w of
@@ -151,7 +162,7 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * br + 4 * g + e, i = 16 * bi + n;
       As[r * LDA + i] = bs[r] * aa[e];
-      Pc[r * C + i] = ap[e];
+      put_split(Pc, C * C, r * C + i, ap[e]);
     }
   } else {
     // Pairs (r, i), i <= r, inside the diagonal tiles: 4 x 136 of them.
@@ -170,7 +181,7 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
         pv += qr[j] * f;
       }
       As[r * LDA + i] = i < r ? a * bs[r] : 0.f;
-      Pc[r * C + i] = pv;
+      put_split(Pc, C * C, r * C + i, pv);
     }
   }
 
@@ -178,7 +189,7 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
   inv64::inverse<LDA, LD>(As, Ks, scratch);
   for (int e = t; e < C * C; e += PNTHR) {
     const int r = e / C, i = e % C;
-    Tc[e] = Ks[r * LD + i] * bs[i];
+    put_split(Tc, C * C, e, Ks[r * LD + i] * bs[i]);
   }
 }
 
@@ -190,15 +201,6 @@ struct ScanLds {
       2 * (size_t)DK * PC + 2 * (size_t)NT * PK + 4 * (size_t)NT * PC;
   static constexpr size_t bytes = halves * 2 + ((size_t)C * PV + DK) * sizeof(float);
 };
-
-// 8 fp32 values (two float4) -> split bf16x8 pair.
-__device__ __forceinline__ void split_f8(const float4& a, const float4& b, bf16x8& hi, bf16x8& lo) {
-  uint2 h0, l0, h1, l1;
-  split4(a, h0, l0);
-  split4(b, h1, l1);
-  hi = as_bf16x8(h0, h1);
-  lo = as_bf16x8(l0, l1);
-}
 
 template <typename OT> __device__ __forceinline__ void put_out(OT* p, float x);
 template <> __device__ __forceinline__ void put_out<float>(float* p, float x) { *p = x; }
@@ -216,10 +218,8 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
   constexpr int KS = DK / 32;               // contraction steps over d_k
   constexpr int NKU = C * DK / 4 / NTH;     // float4 of K o e^{g_C - g} per thread
   static_assert(NKU == 4 || NKU == 8, "rows per thread");
+  static_assert(NKU == 8 || DK == 64, "rows per thread");
   constexpr size_t CF = chunk_floats(DK);
-  constexpr size_t OFF_P = (size_t)C * C, OFF_KD = 2 * (size_t)C * C;
-  constexpr size_t OFF_QD = OFF_KD + (size_t)C * DK, OFF_KU = OFF_QD + (size_t)C * DK;
-  constexpr size_t OFF_GAM = OFF_KU + (size_t)C * DK;
   extern __shared__ uint4 lds_u4[];
   uint16_t* Uh = reinterpret_cast<uint16_t*>(lds_u4);  // (K o e^{g_C-g})^T, swizzled [DK][PC]
   uint16_t* Ul = Uh + DK * PC;
@@ -251,41 +251,50 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
       S[i][e] = S0 ? S0[((size_t)bh * DK + d0 + e) * DV + j0 + n] : 0.f;
   }
 
-  // Next chunk's operands, in registers.
-  float4 kd[KS][2], qd[KS][2], tt[2][2], pp[2][2], ku[NKU];
+  // Next chunk's operands, in registers: (hi, lo) bf16 fragments straight
+  // from the split planes of the workspace; phase 0 moves them into the
+  // current chunk's set.
+  bf16x8 nkdh[KS], nkdl[KS], nqdh[KS], nqdl[KS], ntth[2], nttl[2], npph[2], nppl[2];
+  uint2 kuh[NKU], kul[NKU];
   uint2 pv = make_uint2(0u, 0u);
   float pg = 0.f;
   auto fetch = [&](int cc) {
     const int vc = min(C, L - cc * C);
     const size_t t0 = (size_t)bh * L + (size_t)cc * C;
-    const float* b = ws + ((size_t)bh * nc + cc) * CF;
+    const uint16_t* b = reinterpret_cast<const uint16_t*>(ws + ((size_t)bh * nc + cc) * CF);
+    const uint16_t *bt = b, *bp = b + 2 * C * C, *bk = bp + 2 * C * C;
+    const uint16_t *bq = bk + 2 * C * DK, *bu = bq + 2 * C * DK;
     const int row = r0 + n;
+    auto ld16 = [](const uint16_t* p) { return as_bf16x8(*reinterpret_cast<const uint4*>(p)); };
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const size_t off = (size_t)row * DK + 32 * ks + 8 * g;
-      kd[ks][0] = *reinterpret_cast<const float4*>(b + OFF_KD + off);
-      kd[ks][1] = *reinterpret_cast<const float4*>(b + OFF_KD + off + 4);
-      qd[ks][0] = *reinterpret_cast<const float4*>(b + OFF_QD + off);
-      qd[ks][1] = *reinterpret_cast<const float4*>(b + OFF_QD + off + 4);
+      const int off = row * DK + 32 * ks + 8 * g;
+      nkdh[ks] = ld16(bk + off);
+      nkdl[ks] = ld16(bk + C * DK + off);
+      nqdh[ks] = ld16(bq + off);
+      nqdl[ks] = ld16(bq + C * DK + off);
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const size_t off = (size_t)row * C + 32 * ks + 8 * g;
-      tt[ks][0] = *reinterpret_cast<const float4*>(b + off);
-      tt[ks][1] = *reinterpret_cast<const float4*>(b + off + 4);
-      pp[ks][0] = *reinterpret_cast<const float4*>(b + OFF_P + off);
-      pp[ks][1] = *reinterpret_cast<const float4*>(b + OFF_P + off + 4);
+      const int off = row * C + 32 * ks + 8 * g;
+      ntth[ks] = ld16(bt + off);
+      nttl[ks] = ld16(bt + C * C + off);
+      npph[ks] = ld16(bp + off);
+      nppl[ks] = ld16(bp + C * C + off);
     }
 #pragma unroll
-    for (int p = 0; p < NKU; ++p)  // NKU consecutive rows of one 16-byte column chunk
-      ku[p] = *reinterpret_cast<const float4*>(b + OFF_KU + (size_t)(ku_r0 + p) * DK + 4 * ku_c4);
+    for (int p = 0; p < NKU; ++p) {  // NKU consecutive rows of one 4-column group
+      const int off = (ku_r0 + p) * DK + 4 * ku_c4;
+      kuh[p] = *reinterpret_cast<const uint2*>(bu + off);
+      kul[p] = *reinterpret_cast<const uint2*>(bu + C * DK + off);
+    }
     {
       const int r = t % C, c4 = t / C;
       const uint2 x =
           *reinterpret_cast<const uint2*>(v + (t0 + min(r, vc - 1)) * DV + j0 + 4 * c4);
       pv = r < vc ? x : make_uint2(0u, 0u);
     }
-    if (t < DK) pg = b[OFF_GAM + t];
+    if (t < DK) pg = reinterpret_cast<const float*>(bu + 2 * C * DK)[t];
   };
 
   // L2 prefetch of chunk c + 2: the 128-byte lines of its workspace block
@@ -327,23 +336,14 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
     // fragments and LDS; the state into LDS.
     bf16x8 kdh[KS], kdl[KS], qdh[KS], qdl[KS], tth[2], ttl[2], pph[2], ppl[2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      split_f8(kd[ks][0], kd[ks][1], kdh[ks], kdl[ks]);
-      split_f8(qd[ks][0], qd[ks][1], qdh[ks], qdl[ks]);
-    }
+    for (int ks = 0; ks < KS; ++ks) kdh[ks] = nkdh[ks], kdl[ks] = nkdl[ks], qdh[ks] = nqdh[ks], qdl[ks] = nqdl[ks];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      split_f8(tt[ks][0], tt[ks][1], tth[ks], ttl[ks]);
-      split_f8(pp[ks][0], pp[ks][1], pph[ks], ppl[ks]);
-    }
+    for (int ks = 0; ks < 2; ++ks) tth[ks] = ntth[ks], ttl[ks] = nttl[ks], pph[ks] = npph[ks], ppl[ks] = nppl[ks];
     {  // (K o e^{g_C - g})^T: one NKU-row write per column and half
       uint32_t h[NKU][2], lo[NKU][2];
 #pragma unroll
-      for (int p = 0; p < NKU; ++p) {
-        uint2 hh, ll;
-        split4(ku[p], hh, ll);
-        h[p][0] = hh.x, h[p][1] = hh.y, lo[p][0] = ll.x, lo[p][1] = ll.y;
-      }
+      for (int p = 0; p < NKU; ++p)
+        h[p][0] = kuh[p].x, h[p][1] = kuh[p].y, lo[p][0] = kul[p].x, lo[p][1] = kul[p].y;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         uint32_t ph[NKU / 2], pl[NKU / 2];
