@@ -96,6 +96,17 @@ def measured_mfma(kernel):
     return rec
 
 
+def hbm_rate(kernel, ms):
+    """HBM rate of one launch of `kernel` taking `ms`: the counter-measured
+    bytes per launch (workspace traffic included) over the time, or None
+    when the committed counters are missing or stale."""
+    b = measured_traffic(kernel)
+    if b is None:
+        return None
+    gbs = b / (ms * 1e-3) / 1e9
+    return {"bytes": b, "gbs": gbs, "pct_hbm_peak": 100.0 * gbs / PEAK_HBM_GBS}
+
+
 def chunk_bytes(w, in_bytes=2, out_bytes=4, s0=False):
     """Algorithmic bytes of one chunked forward: q, k, v, beta read once, o and
     S_final written once (S0 read once if given)."""
@@ -405,11 +416,13 @@ def main(argv=None) -> int:
         bprof = binding.profile_stop()
         assert all(torch.isfinite(t).all() for t in grads if t is not None)
         ms_b = ev0.elapsed_time(ev1) / a.steps
+        bms = {name: tot / n for name, (tot, n) in bprof.items()}
         result["backward"] = {
             "workload": w.name + "_backward", "steps": a.steps, "ms_per_step": ms_b,
             "tokens_per_s": w.B * w.L / (ms_b * 1e-3),
-            "kernels_ms": {name: tot / n for name, (tot, n) in bprof.items()},
-            "path": "64-token chunks, forward recomputed inside; every product on bf16 MFMA (split-precision operands), the 64 x 64 triangular inverse fp32 vector ALU",
+            "kernels_ms": bms,
+            "kernels_hbm": {name: hbm_rate(name, t) for name, t in bms.items()},
+            "path": "64-token chunks, forward recomputed inside; every product on bf16 MFMA (split-precision operands), the 64 x 64 triangular inverse's diagonal blocks fp32 vector ALU",
             "grads_in": "dO ~ N(0, 1) (torch generator seeded), no dS_final",
         }
         del bws, dO, grads
@@ -437,11 +450,13 @@ def main(argv=None) -> int:
         kprof = binding.profile_stop()
         assert torch.isfinite(o).all() and torch.isfinite(S_final).all()
         ms_k = ev0.elapsed_time(ev1) / a.steps
+        kms = {name: tot / n for name, (tot, n) in kprof.items()}
         result["kda"] = {
             "workload": w.name + "_kda", "steps": a.steps, "ms_per_step": ms_k,
             "tokens_per_s": w.B * w.L / (ms_k * 1e-3),
-            "kernels_ms": {name: tot / n for name, (tot, n) in kprof.items()},
-            "path": "64-token chunks; bf16 MFMA with split-precision operands for the scan and the prep tiles below the 16-row block diagonal, fp32 vector ALU for the diagonal tiles and the triangular inverse",
+            "kernels_ms": kms,
+            "kernels_hbm": {name: hbm_rate("kda_" + name, t) for name, t in kms.items()},
+            "path": "64-token chunks; bf16 MFMA with split-precision operands for the scan, the prep tiles below the 16-row block diagonal and the inverse's off-diagonal blocks; fp32 vector ALU for the diagonal tiles",
             "alpha": "sigmoid(N(3, 1)) per token and key dimension (seeded stream of its own)",
         }
         del kws, kalpha
