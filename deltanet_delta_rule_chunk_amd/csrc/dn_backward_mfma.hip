@@ -220,11 +220,14 @@ template <int DK>
 struct FwdLds {
   static constexpr int PK = DK + 8;
   static constexpr int PV = NT + 1;
-  static constexpr size_t halves = (size_t)C * PK + (size_t)DK * PC + 2 * (size_t)C * PC +
+  static constexpr size_t halves = (size_t)C * PK + 2 * (size_t)DK * PC + 2 * (size_t)C * PC +
                                    2 * (size_t)NT * PK + 4 * (size_t)NT * PC;
   static constexpr size_t bytes = halves * 2 + ((size_t)C * PV + C) * sizeof(float);
 };
 
+// Three barriers per chunk: phase 1 (R) | phase 2 (Delta) | phase 3 (state
+// update).  The next chunk's operands are deposited during phase 3: by then
+// only K^T (double buffered) and Delta are still being read.
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ k,
                                                        const bf16* __restrict__ v,
@@ -237,8 +240,8 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
   constexpr int TPW = DK / 64;  // state row tiles per wave
   extern __shared__ uint4 lds_u4[];
   uint16_t* Kb = reinterpret_cast<uint16_t*>(lds_u4);  // K rows     [C][PK]
-  uint16_t* Kt = Kb + C * PK;                           // K^T        [DK][PC]
-  uint16_t* Xh = Kt + DK * PC;                          // X          [C][PC]
+  uint16_t* Kt = Kb + C * PK;                           // K^T        [2][DK][PC]
+  uint16_t* Xh = Kt + 2 * DK * PC;                      // X          [C][PC]
   uint16_t* Xl = Xh + C * PC;
   uint16_t* Sh = Xl + C * PC;                           // -S^T       [NT][PK]
   uint16_t* Sl = Sh + NT * PK;
@@ -275,22 +278,24 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
     pv = r < vc ? x : make_uint2(0u, 0u);
     if (t < C) pb = t < vc ? beta[t0 + t] : 0.f;
   };
+  // The fetched chunk into LDS (its K^T into buffer kb).
+  auto deposit = [&](int kb) {
+    tk.put_rows(Kb);
+    tk.put_cols(Kt + kb * DK * PC);
+    tx.put_rows(Xh, Xl);
+    const int r = t % C, c4 = t / C;
+    Vs[r * PV + 4 * c4 + 0] = __uint_as_float(pv.x << 16);
+    Vs[r * PV + 4 * c4 + 1] = __uint_as_float(pv.x & 0xffff0000u);
+    Vs[r * PV + 4 * c4 + 2] = __uint_as_float(pv.y << 16);
+    Vs[r * PV + 4 * c4 + 3] = __uint_as_float(pv.y & 0xffff0000u);
+    if (t < C) bs[t] = pb;
+  };
 
   fetch(0);
+  deposit(0);
   for (int c = 0; c < nc; ++c) {
     float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
-    // Phase 0: operands into LDS; the entering state out and into LDS.
-    tk.put_rows(Kb);
-    tk.put_cols(Kt);
-    tx.put_rows(Xh, Xl);
-    {
-      const int r = t % C, c4 = t / C;
-      Vs[r * PV + 4 * c4 + 0] = __uint_as_float(pv.x << 16);
-      Vs[r * PV + 4 * c4 + 1] = __uint_as_float(pv.x & 0xffff0000u);
-      Vs[r * PV + 4 * c4 + 2] = __uint_as_float(pv.y << 16);
-      Vs[r * PV + 4 * c4 + 3] = __uint_as_float(pv.y & 0xffff0000u);
-    }
-    if (t < C) bs[t] = pb;
+    // The entering state: out to the workspace and into LDS.
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int d0 = 16 * (w * TPW + i);
@@ -331,14 +336,16 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
     put_split_t(Dh, Dl, PC, r0, acc);
     __syncthreads();
 
-    // Phase 3: S += K^T Delta.
+    // Phase 3: S += K^T Delta; meanwhile the next chunk goes into LDS (K
+    // rows, X, V and beta were last read in phases 1 and 2).
+    const uint16_t* Kc = Kt + (c & 1) * DK * PC;
 #pragma unroll
     for (int i = 0; i < TPW; ++i)
 #pragma unroll
       for (int ks = 0; ks < C / 32; ++ks)
-        S[i] = mfma_split2(fragT<3>(Kt, 16 * (w * TPW + i), 32 * ks), frag(Dh, PC, 0, 32 * ks),
+        S[i] = mfma_split2(fragT<3>(Kc, 16 * (w * TPW + i), 32 * ks), frag(Dh, PC, 0, 32 * ks),
                            frag(Dl, PC, 0, 32 * ks), S[i]);
-    __syncthreads();
+    if (c + 1 < nc) deposit((c + 1) & 1);
   }
 }
 
