@@ -353,10 +353,15 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
 template <int DK>
 struct BwdLds {
   static constexpr int PK = DK + 8;
-  static constexpr size_t halves = (size_t)C * PK + 2 * (size_t)DK * PC + 4 * (size_t)C * PC +
-                                   2 * (size_t)NT * PK + 6 * (size_t)NT * PC;
+  static constexpr size_t halves = (size_t)C * PK + 4 * (size_t)DK * PC + 4 * (size_t)C * PC +
+                                   2 * (size_t)NT * PK + 8 * (size_t)NT * PC;
   static constexpr size_t bytes = halves * 2 + (size_t)C * sizeof(float);
+  static_assert(bytes <= 160 * 1024, "LDS budget");
 };
+
+// Three barriers per chunk, as in the forward pass: the next chunk (in
+// reverse order) is deposited during phase 3, with Q^T, K^T and dO^T, which
+// phase 3 still reads, double buffered.
 
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
@@ -369,17 +374,16 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
   constexpr int TPW = DK / 64;
   extern __shared__ uint4 lds_u4[];
   uint16_t* Kb = reinterpret_cast<uint16_t*>(lds_u4);  // K rows        [C][PK]
-  uint16_t* Kt = Kb + C * PK;                           // K^T           [DK][PC]
-  uint16_t* Qt = Kt + DK * PC;                          // Q^T           [DK][PC]
-  uint16_t* Mh = Qt + DK * PC;                          // M^T           [C][PC]
+  uint16_t* Kt = Kb + C * PK;                           // K^T           [2][DK][PC]
+  uint16_t* Qt = Kt + 2 * DK * PC;                      // Q^T           [2][DK][PC]
+  uint16_t* Mh = Qt + 2 * DK * PC;                      // M^T           [C][PC]
   uint16_t* Ml = Mh + C * PC;
   uint16_t* Xh = Ml + C * PC;                           // X^T           [C][PC]
   uint16_t* Xl = Xh + C * PC;
   uint16_t* Gh = Xl + C * PC;                           // G'^T          [NT][PK]
   uint16_t* Gl = Gh + NT * PK;
-  uint16_t* Oh = Gl + NT * PK;                          // dO^T          [NT][PC]
-  uint16_t* Ol = Oh + NT * PC;
-  uint16_t* Eh = Ol + NT * PC;                          // dDelta^T      [NT][PC]
+  uint16_t* Oh = Gl + NT * PK;                          // dO^T          [2][hi, lo][NT][PC]
+  uint16_t* Eh = Oh + 4 * NT * PC;                      // dDelta^T      [NT][PC]
   uint16_t* El = Eh + NT * PC;
   uint16_t* Fh = El + NT * PC;                          // -dR^T         [NT][PC]
   uint16_t* Fl = Fh + NT * PC;
@@ -416,31 +420,41 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
     if (t < C) pb = t < vc ? beta[t0 + t] : 0.f;
   };
 
+  // The fetched chunk into LDS (its Q^T, K^T, dO^T into buffer bb).
+  auto deposit = [&](int bb) {
+    tk.put_rows(Kb);
+    tk.put_cols(Kt + bb * DK * PC);
+    tq.put_cols(Qt + bb * DK * PC);
+    tm.put_cols(Mh, Ml);
+    tx.put_cols(Xh, Xl);
+    uint16_t* oh = Oh + bb * 2 * NT * PC;
+    uint16_t* ol = oh + NT * PC;
+    const int r = t % C, c4 = t / C;
+    uint2 h, o;
+    split4(pd, h, o);
+    oh[(4 * c4 + 0) * PC + r] = static_cast<uint16_t>(h.x);
+    oh[(4 * c4 + 1) * PC + r] = static_cast<uint16_t>(h.x >> 16);
+    oh[(4 * c4 + 2) * PC + r] = static_cast<uint16_t>(h.y);
+    oh[(4 * c4 + 3) * PC + r] = static_cast<uint16_t>(h.y >> 16);
+    ol[(4 * c4 + 0) * PC + r] = static_cast<uint16_t>(o.x);
+    ol[(4 * c4 + 1) * PC + r] = static_cast<uint16_t>(o.x >> 16);
+    ol[(4 * c4 + 2) * PC + r] = static_cast<uint16_t>(o.y);
+    ol[(4 * c4 + 3) * PC + r] = static_cast<uint16_t>(o.y >> 16);
+    if (t < C) bs[t] = pb;
+  };
+
   fetch(nc - 1);
+  deposit((nc - 1) & 1);
   for (int c = nc - 1; c >= 0; --c) {
     const int valid = min(C, L - c * C);
     const size_t tok0 = (size_t)bh * L + (size_t)c * C;
     float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
-    // Phase 0.
-    tk.put_rows(Kb);
-    tk.put_cols(Kt);
-    tq.put_cols(Qt);
-    tm.put_cols(Mh, Ml);
-    tx.put_cols(Xh, Xl);
-    {
-      const int r = t % C, c4 = t / C;
-      uint2 h, o;
-      split4(pd, h, o);
-      Oh[(4 * c4 + 0) * PC + r] = static_cast<uint16_t>(h.x);
-      Oh[(4 * c4 + 1) * PC + r] = static_cast<uint16_t>(h.x >> 16);
-      Oh[(4 * c4 + 2) * PC + r] = static_cast<uint16_t>(h.y);
-      Oh[(4 * c4 + 3) * PC + r] = static_cast<uint16_t>(h.y >> 16);
-      Ol[(4 * c4 + 0) * PC + r] = static_cast<uint16_t>(o.x);
-      Ol[(4 * c4 + 1) * PC + r] = static_cast<uint16_t>(o.x >> 16);
-      Ol[(4 * c4 + 2) * PC + r] = static_cast<uint16_t>(o.y);
-      Ol[(4 * c4 + 3) * PC + r] = static_cast<uint16_t>(o.y >> 16);
-    }
-    if (t < C) bs[t] = pb;
+    const int bb = c & 1;
+    const uint16_t* Kc = Kt + bb * DK * PC;
+    const uint16_t* Qc = Qt + bb * DK * PC;
+    const uint16_t* Oc = Oh + bb * 2 * NT * PC;
+    const uint16_t* Ocl = Oc + NT * PC;
+    // The exit gradient: out to the workspace and into LDS.
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int d0 = 16 * (w * TPW + i);
@@ -457,8 +471,8 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
     f32x4 acc = zero4();
 #pragma unroll
     for (int ks = w / 2; ks < C / 32; ++ks)
-      acc = mfma_split3(fragT<2>(Mh, r0, 32 * ks), fragT<2>(Ml, r0, 32 * ks), frag(Oh, PC, 0, 32 * ks),
-                        frag(Ol, PC, 0, 32 * ks), acc);
+      acc = mfma_split3(fragT<2>(Mh, r0, 32 * ks), fragT<2>(Ml, r0, 32 * ks), frag(Oc, PC, 0, 32 * ks),
+                        frag(Ocl, PC, 0, 32 * ks), acc);
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks)
       acc = mfma_split2(frag(Kb, PK, r0, 32 * ks), frag(Gh, PK, 0, 32 * ks), frag(Gl, PK, 0, 32 * ks),
@@ -483,19 +497,20 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
     put_split_t(Fh, Fl, PC, r0, -acc);
     __syncthreads();
 
-    // Phase 3: G = G' + Q^T dO - K^T dR.
+    // Phase 3: G = G' + Q^T dO - K^T dR; meanwhile the next chunk goes into
+    // LDS (K rows, M^T, X^T and beta were last read in phases 1 and 2).
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int d0 = 16 * (w * TPW + i);
 #pragma unroll
       for (int ks = 0; ks < C / 32; ++ks) {
-        G[i] = mfma_split2(fragT<3>(Qt, d0, 32 * ks), frag(Oh, PC, 0, 32 * ks), frag(Ol, PC, 0, 32 * ks),
+        G[i] = mfma_split2(fragT<3>(Qc, d0, 32 * ks), frag(Oc, PC, 0, 32 * ks), frag(Ocl, PC, 0, 32 * ks),
                            G[i]);
-        G[i] = mfma_split2(fragT<3>(Kt, d0, 32 * ks), frag(Fh, PC, 0, 32 * ks), frag(Fl, PC, 0, 32 * ks),
+        G[i] = mfma_split2(fragT<3>(Kc, d0, 32 * ks), frag(Fh, PC, 0, 32 * ks), frag(Fl, PC, 0, 32 * ks),
                            G[i]);
       }
     }
-    __syncthreads();
+    if (c > 0) deposit((c - 1) & 1);
   }
   if (dS0)
 #pragma unroll
