@@ -141,3 +141,16 @@ def test_backward_long_context_identities(gpu_lib):
     _note(f"  <dq,q> {q_side:.6e} vs <dO,o> {lo:.6e}; <dv,v>+<dS0,S0> {v_side:.6e} vs {lo + ls:.6e}")
     assert abs(q_side - lo) <= 1e-4 * scale_q
     assert abs(v_side - (lo + ls)) <= 1e-4 * scale_v
+
+
+def test_backward_bitwise_determinism(gpu_lib):
+    """Two runs of the same gradient give identical bits (no atomics or
+    order-dependent reductions anywhere in the backward)."""
+    w = I.ChunkWorkload("det", 2, 5, 64 * 6 + 21, 128, 128, 64, "bf16", s0_std=0.1)
+    x = I.make_chunk_inputs(w, seed=8)
+    dO, dSf = _grads_in(w, 8)
+    a = _run(x, dO, dSf, 64)
+    b = _run(x, dO, dSf, 64)
+    for n, ga, gb in zip(NAMES, a, b):
+        assert torch.equal(ga, gb), n
+

@@ -205,3 +205,16 @@ def test_kda_decode_matches_chunk(gpu_lib):
     torch.cuda.synchronize()
     assert_parity(torch.stack(outs, dim=2).cpu(), to64(o_c.cpu()), "bf16", "decode vs chunk o")
     assert_parity(S.cpu(), to64(S_c.cpu()), "bf16", "decode vs chunk S")
+
+
+def test_kda_bitwise_determinism(gpu_lib):
+    """Two runs of the same per-dimension-decay forward give identical bits."""
+    w = I.ChunkWorkload("kda_det", 2, 5, 64 * 5 + 9, 128, 128, 64, "bf16", s0_std=0.1)
+    x = I.make_chunk_inputs(w, seed=6)
+    alpha = I.make_chunk_kda_alpha(w, seed=6).to(DEV)
+    g = {k: t.to(DEV) for k, t in x.items()}
+    o1, S1 = kda_chunk_fwd(g["q"], g["k"], g["v"], alpha, g["beta"], g["S0"], 64)
+    o2, S2 = kda_chunk_fwd(g["q"], g["k"], g["v"], alpha, g["beta"], g["S0"], 64)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
