@@ -535,7 +535,7 @@ hipError_t launch_t(const BwdArgs& a) {
   constexpr bool kMatrixCores = sizeof(IT) == 2;
   if (nc > 0) {
     prof_mark(kSlotBwdPrep, false, a.stream);
-    if (kMatrixCores) {
+    if constexpr (kMatrixCores) {
       DN_TRY(launch_prep_mfma(DK, DV, q, k, a.beta, a.L, nc, bh, ws, a.stream));
     } else {
       DN_TRY(set_smem(&prep_kernel<DK, DV, IT>, PrepSmem<DK>::bytes));
@@ -545,7 +545,7 @@ hipError_t launch_t(const BwdArgs& a) {
     }
     prof_mark(kSlotBwdPrep, true, a.stream);
     prof_mark(kSlotBwdFwdScan, false, a.stream);
-    if (kMatrixCores) {
+    if constexpr (kMatrixCores) {
       DN_TRY(launch_fwd_scan_mfma(DK, DV, k, v, a.beta, a.S0, a.L, nc, bh, ws, a.stream));
     } else {
       DN_TRY(set_smem(&fwd_scan_kernel<DK, DV, IT>, FwdSmem<DK>::bytes));
@@ -568,7 +568,7 @@ hipError_t launch_t(const BwdArgs& a) {
   prof_mark(kSlotBwdScan, true, a.stream);
   if (nc > 0) {
     prof_mark(kSlotBwdCc, false, a.stream);
-    if (kMatrixCores) {
+    if constexpr (kMatrixCores) {
       DN_TRY(launch_cc_grad_mfma(DK, DV, k, a.beta, a.dO, a.dbeta, a.L, nc, bh, ws, a.stream));
     } else {
       DN_TRY(set_smem(&cc_grad_kernel<DK, DV, IT>, CcSmem<DK>::bytes));
@@ -578,7 +578,7 @@ hipError_t launch_t(const BwdArgs& a) {
     }
     prof_mark(kSlotBwdCc, true, a.stream);
     prof_mark(kSlotBwdQk, false, a.stream);
-    if (kMatrixCores) {
+    if constexpr (kMatrixCores) {
       DN_TRY(launch_qk_grad_mfma(DK, DV, q, k, a.dO, a.dv, a.dq, a.dk, a.L, nc, bh, ws, a.stream));
     } else {
       DN_TRY(set_smem(&qk_grad_kernel<DK, DV, IT>, QkSmem<DK>::bytes));

@@ -274,11 +274,14 @@ hipError_t launch_t(const ChunkArgs& a) {
   const int nc = cdiv(a.L, C);
   const int bh = a.B * a.H;
   float* ws = static_cast<float*>(a.workspace);
-  if (nc > 0 && sizeof(IT) == 2) {  // bf16 q, k: the prep's products on the matrix cores
-    prof_mark(kSlotChunkPrep, false, a.stream);
-    const hipError_t e = launch_prep_mfma(DK, a.q, a.k, a.alpha, a.beta, a.L, nc, bh, ws, a.stream);
-    prof_mark(kSlotChunkPrep, true, a.stream);
-    if (e != hipSuccess) return e;
+  if constexpr (sizeof(IT) == 2) {  // bf16 q, k: the prep's products on the matrix cores
+    if (nc > 0) {
+      prof_mark(kSlotChunkPrep, false, a.stream);
+      const hipError_t e =
+          launch_prep_mfma(DK, a.q, a.k, a.alpha, a.beta, a.L, nc, bh, ws, a.stream);
+      prof_mark(kSlotChunkPrep, true, a.stream);
+      if (e != hipSuccess) return e;
+    }
   } else if (nc > 0) {
     constexpr size_t sm = PrepSmem<DK>::bytes;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<DK, IT>),
@@ -298,18 +301,19 @@ hipError_t launch_t(const ChunkArgs& a) {
                                           bh, ws, a.stream);
     prof_mark(kSlotChunkScan, true, a.stream);
     return e;
+  } else {
+    constexpr size_t sm2 = ScanSmem<DK>::bytes;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<DK, DV, IT, OT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm2);
+    if (e != hipSuccess) return e;
+    prof_mark(kSlotChunkScan, false, a.stream);
+    hipLaunchKernelGGL((scan_kernel<DK, DV, IT, OT>), dim3(DV / NT, bh), dim3(NTHR), sm2,
+                       a.stream, static_cast<const IT*>(a.v), a.S0, static_cast<OT*>(a.o),
+                       a.S_final, a.L, nc, ws);
+    e = hipGetLastError();
+    prof_mark(kSlotChunkScan, true, a.stream);
+    return e;
   }
-  constexpr size_t sm2 = ScanSmem<DK>::bytes;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<DK, DV, IT, OT>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm2);
-  if (e != hipSuccess) return e;
-  prof_mark(kSlotChunkScan, false, a.stream);
-  hipLaunchKernelGGL((scan_kernel<DK, DV, IT, OT>), dim3(DV / NT, bh), dim3(NTHR), sm2, a.stream,
-                     static_cast<const IT*>(a.v), a.S0, static_cast<OT*>(a.o), a.S_final, a.L, nc,
-                     ws);
-  e = hipGetLastError();
-  prof_mark(kSlotChunkScan, true, a.stream);
-  return e;
 }
 
 template <int DK, int DV>
