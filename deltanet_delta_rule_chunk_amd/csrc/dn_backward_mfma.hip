@@ -145,8 +145,13 @@ template <int DK>
 struct PrepLds {
   static constexpr int PK = DK + 8;
   static constexpr int PF = C + 1;
-  static constexpr size_t bytes =
-      2 * (size_t)C * PK * 2 + (2 * (size_t)C * PF + C + inv64::SCRATCH_FLOATS) * sizeof(float);
+  // K and Q rows, later X and the inverse's scratch (the rows are dead once
+  // the Gram tiles are formed); then A and beta.  ~52 KB at d_k = 128, so
+  // three workgroups share a CU.
+  static constexpr size_t rows_bytes = 2 * (size_t)C * PK * 2;
+  static constexpr size_t x_bytes = ((size_t)C * PF + inv64::SCRATCH_FLOATS) * sizeof(float);
+  static constexpr size_t region0 = rows_bytes > x_bytes ? rows_bytes : x_bytes;
+  static constexpr size_t bytes = region0 + ((size_t)C * PF + C) * sizeof(float);
 };
 
 template <int DK, int DV>
@@ -160,10 +165,10 @@ __global__ __launch_bounds__(NTH) void prep_kernel(const bf16* __restrict__ q,
   extern __shared__ uint4 lds_u4[];
   uint16_t* Kb = reinterpret_cast<uint16_t*>(lds_u4);  // K rows [C][PK]
   uint16_t* Qb = Kb + C * PK;                           // Q rows [C][PK]
-  float* As = reinterpret_cast<float*>(Qb + C * PK);    // A      [C][PF]
-  float* Xs = As + C * PF;                              // X      [C][PF]
-  float* bs = Xs + C * PF;
-  float* scratch = bs + C;
+  float* Xs = reinterpret_cast<float*>(lds_u4);         // X      [C][PF], over the rows
+  float* scratch = Xs + C * PF;
+  float* As = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(lds_u4) + LD::region0);
+  float* bs = As + C * PF;                              // A      [C][PF], beta
   const int c = blockIdx.x, bh = blockIdx.y, nc = gridDim.x;
   const int valid = min(C, L - c * C);
   const size_t tok0 = (size_t)bh * L + (size_t)c * C;
