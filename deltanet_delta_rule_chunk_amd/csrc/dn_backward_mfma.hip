@@ -702,7 +702,7 @@ __global__ __launch_bounds__(DK * 4) void qk_grad_kernel(
 // ---- the C x C gradients: dM, dT, dA, W and dbeta -------------------------
 // One 4-wave workgroup per (chunk, head); wave w owns row tile w of every
 // C x C product.
-//   phase 1, over d_v in passes of 64 columns: dM = tril(dO Delta^T) and
+//   phase 1, over d_v in passes of 32 columns: dM = tril(dO Delta^T) and
 //            dT = tril(dDelta R^T), all four operands staged split in LDS
 //            (the Delta and R rows are the B operands as stored);
 //   phase 2: dbeta_i = sum_a X_ai dT_ai; Y = X^T dX with dX = dT diag(beta)
@@ -712,13 +712,14 @@ __global__ __launch_bounds__(DK * 4) void qk_grad_kernel(
 //            dbeta_r += sum_{i<r} dA_ri (k_r . k_i).
 template <int DK>
 struct CcLds {
-  static constexpr int HJ = 64;
+  static constexpr int HJ = 32;  // d_v columns per phase-1 pass
   static constexpr int PJ = HJ + 8;
   static constexpr int PF = C + 4;
   static constexpr int PK = DK + 8;
   static constexpr size_t p1 = 8 * (size_t)C * PJ * 2;
-  static constexpr size_t p2 = 3 * (size_t)C * PF * sizeof(float) + (size_t)C * PK * 2 +
+  static constexpr size_t p2 = 2 * (size_t)C * PF * sizeof(float) + (size_t)C * PK * 2 +
                                2 * (size_t)C * sizeof(float);
+  // ~52 KB at d_k = 128: three workgroups share a CU.
   static constexpr size_t bytes = p1 > p2 ? p1 : p2;
 };
 
@@ -795,9 +796,9 @@ __global__ __launch_bounds__(NTH) void cc_grad_kernel(const bf16* __restrict__ k
   }
   __syncthreads();
   float* Xs = reinterpret_cast<float*>(lds_u4);  // X    [C][PF]
-  float* Ts = Xs + C * PF;                        // dT   [C][PF]
-  float* Ys = Ts + C * PF;                        // Y    [C][PF]
-  float* bs = Ys + C * PF;
+  float* Ts = Xs + C * PF;                        // dT   [C][PF], then Y
+  float* Ys = Ts;
+  float* bs = Ts + C * PF;
   float* dbs = bs + C;
   uint16_t* Kb = reinterpret_cast<uint16_t*>(dbs + C);  // K rows [C][PK]
   {
@@ -827,10 +828,13 @@ __global__ __launch_bounds__(NTH) void cc_grad_kernel(const bf16* __restrict__ k
     for (int a = t; a < C; ++a) s += Xs[a * PF + t] * Ts[a * PF + t];
     dbs[t] = s;
   }
-  // Y = X^T dX, row tile w: Y_ab = sum_{r >= a} X_ra dT_rb beta_b.
+  // Y = X^T dX, row tile w: Y_ab = sum_{r >= a} X_ra dT_rb beta_b (held in
+  // registers until every wave is done reading dT, then written over it).
+  f32x4 yt[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    f32x4 y = zero4();
+    f32x4& y = yt[ct];
+    y = zero4();
     const int a = r0 + n, b = 16 * ct + n;
     const float bb = bs[b];
 #pragma unroll
@@ -847,9 +851,12 @@ __global__ __launch_bounds__(NTH) void cc_grad_kernel(const bf16* __restrict__ k
       split8(xb, bh_, bl);
       y = mfma_split3(ah, al, bh_, bl, y);
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Ys[(r0 + 4 * g + e) * PF + 16 * ct + n] = y[e];
   }
+  __syncthreads();
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Ys[(r0 + 4 * g + e) * PF + 16 * ct + n] = yt[ct][e];
   __syncthreads();
   // dA = -Y X^T (strictly lower), W = diag(beta) dA, and the dbeta row sums
   // against the Gram tiles.
