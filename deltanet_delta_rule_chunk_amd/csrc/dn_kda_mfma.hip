@@ -65,7 +65,7 @@ __device__ __forceinline__ void put_split(uint16_t* hi, int plane, int i, float 
 
 template <int DK>
 struct PrepLds {
-  static constexpr int LD = DK + 1;  // row pitch of the C x d_k tiles
+  static constexpr int LD = DK + 4;  // row pitch of the C x d_k tiles (16-byte rows)
   static constexpr int LDA = C + 1;  // row pitch of A
   static constexpr size_t bytes =
       (3 * (size_t)C * LD + (size_t)C * LDA + C + inv64::SCRATCH_FLOATS) * sizeof(float);
@@ -172,13 +172,23 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
       int rr = 0;
       while ((rr + 1) * (rr + 2) / 2 <= qi) ++rr;
       const int r = 16 * b + rr, i = 16 * b + qi - rr * (rr + 1) / 2;
-      const float *kr = Ks + r * LD, *ki = Ks + i * LD, *qr = Qs + r * LD;
-      const float *gr = Gs + r * LD, *gi = Gs + i * LD;
+      const float4 *kr = reinterpret_cast<const float4*>(Ks + r * LD);
+      const float4 *ki = reinterpret_cast<const float4*>(Ks + i * LD);
+      const float4 *qr = reinterpret_cast<const float4*>(Qs + r * LD);
+      const float4 *gr = reinterpret_cast<const float4*>(Gs + r * LD);
+      const float4 *gi = reinterpret_cast<const float4*>(Gs + i * LD);
       float a = 0.f, pv = 0.f;
-      for (int j = 0; j < DK; ++j) {
-        const float f = __expf(gr[j] - gi[j]) * ki[j];
-        a += kr[j] * f;
-        pv += qr[j] * f;
+#pragma unroll 4
+      for (int j4 = 0; j4 < DK / 4; ++j4) {  // 16-byte reads, the sum in order of j
+        const float4 gr4 = gr[j4], gi4 = gi[j4], ki4 = ki[j4], kr4 = kr[j4], qr4 = qr[j4];
+        float f = __expf(gr4.x - gi4.x) * ki4.x;
+        a += kr4.x * f, pv += qr4.x * f;
+        f = __expf(gr4.y - gi4.y) * ki4.y;
+        a += kr4.y * f, pv += qr4.y * f;
+        f = __expf(gr4.z - gi4.z) * ki4.z;
+        a += kr4.z * f, pv += qr4.z * f;
+        f = __expf(gr4.w - gi4.w) * ki4.w;
+        a += kr4.w * f, pv += qr4.w * f;
       }
       As[r * LDA + i] = i < r ? a * bs[r] : 0.f;
       put_split(Pc, C * C, r * C + i, pv);
