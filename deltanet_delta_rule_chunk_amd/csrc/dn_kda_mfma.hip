@@ -101,21 +101,52 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
   float* gam = reinterpret_cast<float*>(Ku + 2 * C * DK);  // e^{g_C}
   const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
 
-  valu::load_rows(Ks, LD, k + tok0 * DK, valid, C, DK);
-  valu::load_rows(Qs, LD, q + tok0 * DK, valid, C, DK);
+  {  // q and k rows, 16 bytes per load, into fp32 tiles
+    const uint4* kg = reinterpret_cast<const uint4*>(k + tok0 * DK);
+    const uint4* qg = reinterpret_cast<const uint4*>(q + tok0 * DK);
+    for (int e8 = t; e8 < C * DK / 8; e8 += PNTHR) {
+      const int r = e8 / (DK / 8), c8 = e8 % (DK / 8), rc = min(r, valid - 1);
+      uint4 xk = kg[rc * (DK / 8) + c8], xq = qg[rc * (DK / 8) + c8];
+      if (r >= valid) xk = xq = make_uint4(0u, 0u, 0u, 0u);
+      float4* dk = reinterpret_cast<float4*>(Ks + r * LD + 8 * c8);
+      float4* dq = reinterpret_cast<float4*>(Qs + r * LD + 8 * c8);
+      dk[0] = make_float4(__uint_as_float(xk.x << 16), __uint_as_float(xk.x & 0xffff0000u),
+                          __uint_as_float(xk.y << 16), __uint_as_float(xk.y & 0xffff0000u));
+      dk[1] = make_float4(__uint_as_float(xk.z << 16), __uint_as_float(xk.z & 0xffff0000u),
+                          __uint_as_float(xk.w << 16), __uint_as_float(xk.w & 0xffff0000u));
+      dq[0] = make_float4(__uint_as_float(xq.x << 16), __uint_as_float(xq.x & 0xffff0000u),
+                          __uint_as_float(xq.y << 16), __uint_as_float(xq.y & 0xffff0000u));
+      dq[1] = make_float4(__uint_as_float(xq.z << 16), __uint_as_float(xq.z & 0xffff0000u),
+                          __uint_as_float(xq.w << 16), __uint_as_float(xq.w & 0xffff0000u));
+    }
+  }
   if (t < C) bs[t] = t < valid ? beta[tok0 + t] : 0.f;
   // g: the log-decays of the whole tile at once (coalesced), then a prefix
-  // sum down each dimension's column in LDS.
+  // sum down each dimension's column: 8 segments of 8 rows per column, each
+  // summed in registers, then offset by the totals of the segments above it
+  // (parked in the A tile, which is written only later).
   for (int e = t; e < C * DK; e += PNTHR) {
     const int r = e / DK, j = e % DK;
     Gs[r * LD + j] = r < valid ? log_decay(alpha[(tok0 + r) * DK + j]) : 0.f;
   }
   __syncthreads();
-  for (int j = t; j < DK; j += PNTHR) {
-    float acc = 0.f;
-    for (int r = 0; r < C; ++r) {
-      acc += Gs[r * LD + j];
-      Gs[r * LD + j] = acc;
+  {
+    static_assert(8 * DK <= PNTHR && 8 * DK <= C * LDA, "prefix layout");
+    const int j = t % DK, seg = t / DK;
+    float v[8];
+    if (seg < 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = Gs[(8 * seg + i) * LD + j];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) v[i] += v[i - 1];
+      As[seg * DK + j] = v[7];
+    }
+    __syncthreads();
+    if (seg < 8) {
+      float off = 0.f;
+      for (int s2 = 0; s2 < seg; ++s2) off += As[s2 * DK + j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Gs[(8 * seg + i) * LD + j] = v[i] + off;
     }
   }
   __syncthreads();
