@@ -56,6 +56,15 @@ constexpr int NTH = 256;  // 4 waves
 // inverse of I + A (dn_inv64.h).
 constexpr int PNTHR = 1024;
 
+// 8 consecutive values as split pairs, one 16-byte store per plane (i is a
+// multiple of 8).
+__device__ __forceinline__ void put_split8(uint16_t* hi, int plane, int i, const float* x) {
+  bf16x8 h, o;
+  lds64::split8(x, h, o);
+  *reinterpret_cast<bf16x8*>(hi + i) = h;
+  *reinterpret_cast<bf16x8*>(hi + plane + i) = o;
+}
+
 // x as a split pair: hi[i] = bf16(x), hi[plane + i] = bf16(x - hi[i]).
 __device__ __forceinline__ void put_split(uint16_t* hi, int plane, int i, float x) {
   const __bf16 h = static_cast<__bf16>(x);
@@ -151,13 +160,20 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
   }
   __syncthreads();
 
-  for (int e = t; e < C * DK; e += PNTHR) {  // the decayed operands of the scan
-    const int r = e / DK, j = e % DK;
-    const float gv = Gs[r * LD + j], gC = Gs[(C - 1) * LD + j];
-    const float kv = Ks[r * LD + j];
-    put_split(Kd, C * DK, e, kv * __expf(gv));
-    put_split(Qd, C * DK, e, Qs[r * LD + j] * __expf(gv));
-    put_split(Ku, C * DK, e, kv * __expf(gC - gv));
+  for (int e8 = t; e8 < C * DK / 8; e8 += PNTHR) {  // the decayed operands of the scan
+    const int r = e8 / (DK / 8), j0 = 8 * (e8 % (DK / 8));
+    float kd[8], qd[8], ku[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float gv = Gs[r * LD + j0 + i], gC = Gs[(C - 1) * LD + j0 + i];
+      const float kv = Ks[r * LD + j0 + i];
+      kd[i] = kv * __expf(gv);
+      qd[i] = Qs[r * LD + j0 + i] * __expf(gv);
+      ku[i] = kv * __expf(gC - gv);
+    }
+    put_split8(Kd, C * DK, 8 * e8, kd);
+    put_split8(Qd, C * DK, 8 * e8, qd);
+    put_split8(Ku, C * DK, 8 * e8, ku);
   }
   for (int j = t; j < DK; j += PNTHR) gam[j] = __expf(Gs[(C - 1) * LD + j]);
   for (int e = t; e < C * C; e += PNTHR)  // P above the diagonal
@@ -228,9 +244,12 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
 
   // X = (I + A)^{-1} over the K tile (no longer needed), then T = X diag(beta).
   inv64::inverse<LDA, LD>(As, Ks, scratch);
-  for (int e = t; e < C * C; e += PNTHR) {
-    const int r = e / C, i = e % C;
-    put_split(Tc, C * C, e, Ks[r * LD + i] * bs[i]);
+  for (int e8 = t; e8 < C * C / 8; e8 += PNTHR) {
+    const int r = e8 / (C / 8), i0 = 8 * (e8 % (C / 8));
+    float tv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tv[i] = Ks[r * LD + i0 + i] * bs[i0 + i];
+    put_split8(Tc, C * C, 8 * e8, tv);
   }
 }
 
