@@ -227,7 +227,8 @@ struct FwdLds {
   static constexpr int PV = NT + 1;
   static constexpr size_t halves = (size_t)C * PK + 2 * (size_t)DK * PC + 2 * (size_t)C * PC +
                                    2 * (size_t)NT * PK + 4 * (size_t)NT * PC;
-  static constexpr size_t bytes = halves * 2 + ((size_t)C * PV + C) * sizeof(float);
+  static constexpr size_t bytes =
+      halves * 2 + ((size_t)C * PV + C + 4 * 16 * 16) * sizeof(float);
 };
 
 // Three barriers per chunk: phase 1 (R) | phase 2 (Delta) | phase 3 (state
@@ -260,6 +261,7 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
   int j0, bh;
   if (!slice_of(DV / NT, nbh, j0, bh)) return;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
+  float* ot = bs + C + w * 256;                         // this wave's store tile
 
   f32x4 S[TPW];
 #pragma unroll
@@ -304,8 +306,7 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int d0 = 16 * (w * TPW + i);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) blk[W.S() + (size_t)(d0 + 4 * g + e) * DV + j0 + n] = S[i][e];
+      store_rows16(ot, S[i], blk + W.S() + (size_t)d0 * DV + j0, DV);
       put_split_t(Sh, Sl, PK, d0, -S[i]);
     }
     __syncthreads();
@@ -322,10 +323,8 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
                         acc);
     f32x4 rb;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      blk[W.R() + (size_t)(r0 + 4 * g + e) * DV + j0 + n] = acc[e];
-      rb[e] = acc[e] * bs[r0 + 4 * g + e];
-    }
+    for (int e = 0; e < 4; ++e) rb[e] = acc[e] * bs[r0 + 4 * g + e];
+    store_rows16(ot, acc, blk + W.R() + (size_t)r0 * DV + j0, DV);
     put_split_t(Rh, Rl, PC, r0, rb);
     __syncthreads();
 
@@ -336,8 +335,7 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
     for (int ks = 0; ks <= w / 2; ++ks)
       acc = mfma_split3(frag(Xh, PC, r0, 32 * ks), frag(Xl, PC, r0, 32 * ks), frag(Rh, PC, 0, 32 * ks),
                         frag(Rl, PC, 0, 32 * ks), acc);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) blk[W.D() + (size_t)(r0 + 4 * g + e) * DV + j0 + n] = acc[e];
+    store_rows16(ot, acc, blk + W.D() + (size_t)r0 * DV + j0, DV);
     put_split_t(Dh, Dl, PC, r0, acc);
     __syncthreads();
 
@@ -360,7 +358,7 @@ struct BwdLds {
   static constexpr int PK = DK + 8;
   static constexpr size_t halves = (size_t)C * PK + 4 * (size_t)DK * PC + 4 * (size_t)C * PC +
                                    2 * (size_t)NT * PK + 8 * (size_t)NT * PC;
-  static constexpr size_t bytes = halves * 2 + (size_t)C * sizeof(float);
+  static constexpr size_t bytes = halves * 2 + ((size_t)C + 4 * 16 * 16) * sizeof(float);
   static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
@@ -397,6 +395,7 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
   int j0, bh;
   if (!slice_of(DV / NT, nbh, j0, bh)) return;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
+  float* ot = bs + C + w * 256;                         // this wave's store tile
 
   f32x4 G[TPW];
 #pragma unroll
@@ -463,8 +462,7 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int d0 = 16 * (w * TPW + i);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) blk[W.G() + (size_t)(d0 + 4 * g + e) * DV + j0 + n] = G[i][e];
+      store_rows16(ot, G[i], blk + W.G() + (size_t)d0 * DV + j0, DV);
       put_split_t(Gh, Gl, PK, d0, G[i]);
     }
     __syncthreads();
@@ -482,8 +480,7 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
     for (int ks = 0; ks < DK / 32; ++ks)
       acc = mfma_split2(frag(Kb, PK, r0, 32 * ks), frag(Gh, PK, 0, 32 * ks), frag(Gl, PK, 0, 32 * ks),
                         acc);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) blk[W.dD() + (size_t)(r0 + 4 * g + e) * DV + j0 + n] = acc[e];
+    store_rows16(ot, acc, blk + W.dD() + (size_t)r0 * DV + j0, DV);
     put_split_t(Eh, El, PC, r0, acc);
     __syncthreads();
 
@@ -494,11 +491,8 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
       acc = mfma_split3(fragT<2>(Xh, r0, 32 * ks), fragT<2>(Xl, r0, 32 * ks), frag(Eh, PC, 0, 32 * ks),
                         frag(El, PC, 0, 32 * ks), acc);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = r0 + 4 * g + e;
-      acc[e] *= bs[r];
-      if (r < valid) dv[(tok0 + r) * DV + j0 + n] = acc[e];
-    }
+    for (int e = 0; e < 4; ++e) acc[e] *= bs[r0 + 4 * g + e];
+    store_rows16(ot, acc, dv + (tok0 + r0) * DV + j0, DV, valid - r0);
     put_split_t(Fh, Fl, PC, r0, -acc);
     __syncthreads();
 

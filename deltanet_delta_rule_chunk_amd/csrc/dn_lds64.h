@@ -51,6 +51,25 @@ __device__ __forceinline__ bf16x8 fragT(const uint16_t* a, int r0, int kb) {
   return as_bf16x8(*reinterpret_cast<const uint4*>(a + line * PC + (ch << 3)));
 }
 
+// Stores a D tile (lane: column l % 16, rows 4 (l / 16) + e) into a
+// row-major fp32 matrix (dst = the tile's top-left element, row pitch ld) as
+// 16-byte row pieces, passing it through the wave's own 16 x 16 fp32 LDS tile
+// `ot` (1 KB; 16-byte groups XOR-swizzled by row).  A wave's LDS operations
+// complete in order, so the tile needs no barrier.  Rows at or past `rows`
+// are not stored.
+__device__ __forceinline__ void store_rows16(float* ot, f32x4 v, float* dst, size_t ld,
+                                             int rows = 16) {
+  const int l = threadIdx.x & 63, n = l & 15, g = l >> 4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int row = 4 * g + e;
+    ot[row * 16 + ((((n >> 2) ^ (row >> 2)) & 3) << 2) + (n & 3)] = v[e];
+  }
+  const int row = l >> 2, cg = l & 3;
+  const f32x4 val = *reinterpret_cast<const f32x4*>(ot + row * 16 + (((cg ^ (row >> 2)) & 3) << 2));
+  if (row < rows) *reinterpret_cast<f32x4*>(dst + row * ld + 4 * cg) = val;
+}
+
 // 8 fp32 values -> split bf16x8 pair.
 __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
   uint2 h0, l0, h1, l1;
