@@ -1,27 +1,29 @@
-// dn_backward_mfma.hip -- the backward's two state scans on the gfx950
-// matrix cores, for bf16 q, k, v.
+// dn_backward_mfma.hip -- the backward's five kernels on the gfx950 matrix
+// cores, for bf16 q, k, v.
 //
-// The products are those of the vector-ALU scans in dn_backward.hip (the
+// The products are those of the vector-ALU kernels in dn_backward.hip (the
 // chunk algebra is derived there), taken as 16 x 16 x 32 bf16 MFMAs with
 // fp32 accumulation.  q and k are exact in bf16; every fp32 operand (the
-// state S, its gradient G', X, M, dO, R, Delta, dDelta, dR) is carried as a
-// split (hi, lo) bf16 pair (dn_mfma.h), so each product keeps roughly fp32
-// accuracy.
+// state S, its gradient G', X, M, dO, R, Delta, dDelta, dR, dT, Y, W) is
+// carried as a split (hi, lo) bf16 pair (dn_mfma.h), so each product keeps
+// roughly fp32 accuracy.  The 64 x 64 triangular inverse is dn_inv64.h.
 //
-// One 4-wave workgroup per (head, 16 columns of d_v).  The slice of the
-// state lives in MFMA accumulators: wave w holds the d_k / 64 row tiles
-// w * d_k / 64 ...  Each chunk step is four phases separated by barriers:
-//   0  the staged operands of the chunk go into LDS (transposed copies where
-//      a product contracts over chunk rows), the state is written out and
-//      published to LDS as a split B operand;
+// The two state passes run one 4-wave workgroup per (head, 16 columns of
+// d_v), all column slices of a head on one XCD.  The slice of the state
+// lives in MFMA accumulators: wave w holds the d_k / 64 row tiles
+// w * d_k / 64 ...  Each chunk step is three phases separated by barriers:
 //   1  wave w forms row tile w (16 chunk rows) of the first product;
 //   2  wave w forms row tile w of the second;
-//   3  every wave advances its state tiles.
-// The next chunk's operands are loaded into registers right after phase 0,
-// so their latency hides behind phases 1-3.
+//   3  every wave advances its state tiles, and the next chunk's operands go
+//      into LDS (row-major and, where a product contracts over chunk rows,
+//      transposed copies); the ones phase 3 itself reads are double
+//      buffered.
+// Each step starts by writing the state out and publishing it to LDS as a
+// split B operand; the following chunk's operands are loaded into registers
+// right after the first barrier, so their latency hides behind the phases.
 //
-// LDS operand arrays are bf16 with rows padded by 16 bytes.  A fragment
-// read `frag(a, P, r0, kb)` gives lane l the 8 contraction slots
+// LDS operand arrays are bf16 with rows padded by 16 bytes (dn_lds64.h).  A
+// fragment read `frag(a, P, r0, kb)` gives lane l the 8 contraction slots
 // kb + 8 (l / 16) ... of row r0 + l % 16, which is the A layout of the MFMA
 // and, for an array stored [column][contraction], also its B layout.
 
