@@ -95,13 +95,19 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
 
   int bh = blockIdx.x;
   if (bh >= BH) return;
-  vf4 s[RPT], sn[RPT];
+  // The states of this head and of the next two, in flight meanwhile.
+  auto next_of = [&](int h) {  // no int overflow near BH = 2^31
+    const long long nl = (long long)h + gridDim.x;
+    return nl < BH ? (int)nl : h;
+  };
+  vf4 s[RPT], sn[RPT], snn[RPT];
   load_state(bh, s);
+  int nb = next_of(bh);
+  load_state(nb, sn);
   for (;;) {
-    const long long nbl = (long long)bh + gridDim.x;  // no int overflow near BH = 2^31
-    const bool more = nbl < BH;
-    const int nb = more ? (int)nbl : bh;
-    load_state(nb, sn);  // next head's state, in flight meanwhile
+    const bool more = nb != bh;
+    const int nnb = next_of(nb);
+    load_state(nnb, snn);
     if (FEAT) {
       static_assert(DK % 64 == 0, "one wave per feature row");
       if (tid < 64)
@@ -169,7 +175,8 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
     __syncthreads();  // the LDS vectors are rewritten for the next head
     if (!more) break;
     bh = nb;
-    for (int i = 0; i < RPT; ++i) s[i] = sn[i];
+    nb = nnb;
+    for (int i = 0; i < RPT; ++i) s[i] = sn[i], sn[i] = snn[i];
   }
 }
 
