@@ -7,8 +7,8 @@ import pytest
 import torch
 
 from deltanet_delta_rule_chunk_amd import inputs as I
-from deltanet_delta_rule_chunk_amd.binding import decode_step
-from oracle import delta_rule_decode_step
+from deltanet_delta_rule_chunk_amd.binding import decode_step, gated_decode_step, kda_decode_step
+from oracle import delta_rule_decode_step, gated_delta_rule_decode_step, kda_delta_rule_decode_step
 from parity import assert_parity, to64
 
 pytestmark = pytest.mark.gpu
@@ -90,3 +90,35 @@ def test_decode_workload_1000_steps_head_subset(gpu_lib):
             _note(f"  step {step} worst err/RMS {worst:.3e}")
     S_sub = Sg[torch.as_tensor(bi, device=DEV), torch.as_tensor(hi, device=DEV)].cpu()[None]
     assert_parity(S_sub, S_ref, "bf16", "S after 1000 steps")
+
+
+@pytest.mark.parametrize("form", ["plain", "gated", "kda"])
+def test_decode_ragged_heads_per_workgroup(gpu_lib, form):
+    """B * H = 805 heads: the persistent workgroups (one per CU) walk three or
+    four heads each, with the next two heads' state loads in flight, so the
+    end of every walk is exercised; three successive steps against the
+    oracle on every head."""
+    _note(f"[decode] ragged heads, {form}")
+    w = I.DecodeWorkload("ragged", 35, 23, 128, 128, 3, "bf16", 0.1)
+    S = I.make_decode_state(w, seed=9)
+    S_ref = to64(S)
+    Sg = S.to(DEV)
+    for step in range(w.steps):
+        x = I.make_decode_step_inputs(w, step, seed=9)
+        args = [x[n].to(DEV) for n in ("q", "k", "v")]
+        ref_args = [to64(x[n]) for n in ("q", "k", "v")]
+        if form == "plain":
+            o = decode_step(*args, x["beta"].to(DEV), Sg)
+            o_ref, S_ref = delta_rule_decode_step(*ref_args, to64(x["beta"]), S_ref)
+        elif form == "gated":
+            a = I.make_decode_alpha(w, step, seed=9)
+            o = gated_decode_step(*args, a.to(DEV), x["beta"].to(DEV), Sg)
+            o_ref, S_ref = gated_delta_rule_decode_step(*ref_args, to64(a), to64(x["beta"]), S_ref)
+        else:
+            a = I.make_decode_kda_alpha(w, step, seed=9)
+            o = kda_decode_step(*args, a.to(DEV), x["beta"].to(DEV), Sg)
+            o_ref, S_ref = kda_delta_rule_decode_step(*ref_args, to64(a), to64(x["beta"]), S_ref)
+        torch.cuda.synchronize()
+        assert_parity(o.cpu(), o_ref, "bf16", f"{form} o step {step}")
+    assert_parity(Sg.cpu(), S_ref, "bf16", f"{form} S")
+
