@@ -278,7 +278,6 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
   constexpr int KS = DK / 32;               // contraction steps over d_k
   constexpr int NKU = C * DK / 4 / NTH;     // float4 of K o e^{g_C - g} per thread
   static_assert(NKU == 4 || NKU == 8, "rows per thread");
-  static_assert(NKU == 8 || DK == 64, "rows per thread");
   constexpr size_t CF = chunk_floats(DK);
   extern __shared__ uint4 lds_u4[];
   uint16_t* Uh = reinterpret_cast<uint16_t*>(lds_u4);  // (K o e^{g_C-g})^T, swizzled [DK][PC]
