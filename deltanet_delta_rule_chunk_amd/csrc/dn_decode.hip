@@ -34,7 +34,7 @@
 //
 // With FEAT the step also applies the layer's feature maps to its inputs
 // (same page and section: q, k = normalise(silu(.)), beta = sigmoid(logit);
-// dn_features.h): waves 0 and 1 map k and q while the others stage v, and
+// dn_features.h): waves 0 and 1 map k and q while waves 2 and 3 stage v, and
 // the mapped q, k are held in the input dtype, as the streaming feature
 // kernel stores them for the chunked path.  It adds no memory traffic.
 
@@ -110,11 +110,13 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
     load_state(nnb, snn);
     if (FEAT) {
       static_assert(DK % 64 == 0, "one wave per feature row");
+      static_assert(128 + DV <= NT, "v staged by the waves that do not map");
       if (tid < 64)
         map_row_to_lds<DK>(k + (size_t)bh * DK, ks, tid);
       else if (tid < 128)
         map_row_to_lds<DK>(q + (size_t)bh * DK, qs, tid - 64);
-      for (int i = tid; i < DV; i += NT) vs[i] = to_f32(v[(size_t)bh * DV + i]);
+      else if (tid < 128 + DV)  // waves 2.. stage v, so its load overlaps the maps
+        vs[tid - 128] = to_f32(v[(size_t)bh * DV + tid - 128]);
     } else {
       for (int i = tid; i < DK; i += NT) {
         ks[i] = to_f32(k[(size_t)bh * DK + i]);
