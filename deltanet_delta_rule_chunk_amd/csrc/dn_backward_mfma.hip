@@ -449,9 +449,45 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
     if (t < C) bs[t] = pb;
   };
 
+  // L2 prefetch of chunk c - 2: the 128-byte lines of its q, k, M, X rows and
+  // dO rows are split over the head's column-slice workgroups (which share an
+  // XCD); thread t touches line slice + ns t with one dword load, folded in a
+  // chunk later and only ever stored under a condition that is false.
+  constexpr int NS = DV / NT;
+  constexpr int QL = C * DK * 2 / 128, ML = C * C * 4 / 128, OL = C * DV * 4 / 128;
+  constexpr int NLINES = 2 * QL + 2 * ML + OL;
+  constexpr int NPF = ((NLINES + NS - 1) / NS + NTH - 1) / NTH;
+  const int sidx = (j0 / NT);
+  uint32_t pf_acc = 0, pf_val[NPF];
+#pragma unroll
+  for (int i = 0; i < NPF; ++i) pf_val[i] = 0;
+  auto prefetch = [&](int cc) {
+    const int vc = min(C, L - cc * C);
+    const size_t t0 = (size_t)bh * L + (size_t)cc * C;
+    const float* b = ws + ((size_t)bh * nc + cc) * W.per_chunk();
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int ln = min(sidx + NS * (t + NTH * i), NLINES - 1);
+      const uint32_t* src;
+      if (ln < 2 * QL) {
+        const int e = (ln % QL) * 64, row = min(e / DK, vc - 1);
+        src = reinterpret_cast<const uint32_t*>((ln < QL ? q : k) + (t0 + row) * DK + e % DK);
+      } else if (ln < 2 * QL + 2 * ML) {
+        const int m = ln - 2 * QL;
+        src = reinterpret_cast<const uint32_t*>(b + (m < ML ? W.M() : W.X())) + 32 * (m % ML);
+      } else {
+        const int e = (ln - 2 * QL - 2 * ML) * 32, row = min(e / DV, vc - 1);
+        src = reinterpret_cast<const uint32_t*>(dO + (t0 + row) * DV + e % DV);
+      }
+      pf_val[i] = *src;
+    }
+  };
+
   fetch(nc - 1);
   deposit((nc - 1) & 1);
   for (int c = nc - 1; c >= 0; --c) {
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) pf_acc ^= pf_val[i];
     const int valid = min(C, L - c * C);
     const size_t tok0 = (size_t)bh * L + (size_t)c * C;
     float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
@@ -469,6 +505,7 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
     }
     __syncthreads();
     if (c > 0) fetch(c - 1);
+    prefetch(max(c - 2, 0));
 
     // Phase 1: dDelta = M^T dO + K G', row tile w (M^T is upper triangular,
     // so the first product starts at the tile's first row).
@@ -520,6 +557,9 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) dS0[((size_t)bh * DK + d0 + e) * DV + j0 + n] = G[i][e];
     }
+#pragma unroll
+  for (int i = 0; i < NPF; ++i) pf_acc ^= pf_val[i];
+  if (nc < 0) dv[0] = __uint_as_float(pf_acc);
 }
 
 // ---- dQ and dK -------------------------------------------------------------
