@@ -300,10 +300,45 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
     if (t < C) bs[t] = pb;
   };
 
+  // L2 prefetch of chunk c + 2: the 128-byte lines of its k, X and v rows
+  // are split over the head's column-slice workgroups (which share an XCD);
+  // thread t touches line slice + ns t with one dword load, folded in a chunk
+  // later and only ever stored under a condition that is false.
+  constexpr int NS = DV / NT;
+  constexpr int KL = C * DK * 2 / 128, XL = C * C * 4 / 128, VL = C * DV * 2 / 128;
+  constexpr int NLINES = KL + XL + VL;
+  constexpr int NPF = ((NLINES + NS - 1) / NS + NTH - 1) / NTH;
+  const int sidx = j0 / NT;
+  uint32_t pf_acc = 0, pf_val[NPF];
+#pragma unroll
+  for (int i = 0; i < NPF; ++i) pf_val[i] = 0;
+  auto prefetch = [&](int cc) {
+    const int vc = min(C, L - cc * C);
+    const size_t t0 = (size_t)bh * L + (size_t)cc * C;
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int ln = min(sidx + NS * (t + NTH * i), NLINES - 1);
+      const uint32_t* src;
+      if (ln < KL) {
+        const int e = ln * 64, row = min(e / DK, vc - 1);
+        src = reinterpret_cast<const uint32_t*>(k + (t0 + row) * DK + e % DK);
+      } else if (ln < KL + XL) {
+        src = reinterpret_cast<const uint32_t*>(ws + ((size_t)bh * nc + cc) * W.per_chunk() + W.X()) +
+              32 * (ln - KL);
+      } else {
+        const int e = (ln - KL - XL) * 64, row = min(e / DV, vc - 1);
+        src = reinterpret_cast<const uint32_t*>(v + (t0 + row) * DV + e % DV);
+      }
+      pf_val[i] = *src;
+    }
+  };
+
   fetch(0);
   deposit(0);
   for (int c = 0; c < nc; ++c) {
     float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) pf_acc ^= pf_val[i];
     // The entering state: out to the workspace and into LDS.
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
@@ -313,6 +348,7 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
     }
     __syncthreads();
     if (c + 1 < nc) fetch(c + 1);
+    prefetch(min(c + 2, nc - 1));
 
     // Phase 1: R = V - K S, row tile w.
     const int r0 = 16 * w;
@@ -352,6 +388,9 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
                            frag(Dl, PC, 0, 32 * ks), S[i]);
     if (c + 1 < nc) deposit((c + 1) & 1);
   }
+#pragma unroll
+  for (int i = 0; i < NPF; ++i) pf_acc ^= pf_val[i];
+  if (nc < 0) ws[0] = __uint_as_float(pf_acc);
 }
 
 // ---- reverse state pass -----------------------------------------------------
