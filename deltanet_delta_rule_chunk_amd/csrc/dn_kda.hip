@@ -82,17 +82,31 @@ __global__ __launch_bounds__(NTHR) void prep_kernel(const IT* __restrict__ q,
   load_rows(Qs, LD, q + tok0 * DK, valid, C, DK);
   for (int r = threadIdx.x; r < C; r += blockDim.x) bs[r] = r < valid ? beta[tok0 + r] : 0.f;
   // g: the log-decays of the whole tile at once (coalesced), then a prefix
-  // sum down each dimension's column in LDS (rows past L add zero).
+  // sum down each dimension's column (rows past L add zero): 8 segments of 8
+  // rows per column, each summed in registers, then offset by the totals of
+  // the segments above it (parked in the A tile, which is written only later).
   for (int e = threadIdx.x; e < C * DK; e += blockDim.x) {
     const int r = e / DK, j = e % DK;
     Gs[r * LD + j] = r < valid ? log_decay(alpha[(tok0 + r) * DK + j]) : 0.f;
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < DK; j += blockDim.x) {
-    float acc = 0.f;
-    for (int r = 0; r < C; ++r) {
-      acc += Gs[r * LD + j];
-      Gs[r * LD + j] = acc;
+  {
+    static_assert(8 * DK <= NTHR && 8 * DK <= C * LDA && C == 64, "prefix layout");
+    const int j = threadIdx.x % DK, seg = threadIdx.x / DK;
+    float v[8];
+    if (seg < 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = Gs[(8 * seg + i) * LD + j];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) v[i] += v[i - 1];
+      As[seg * DK + j] = v[7];
+    }
+    __syncthreads();
+    if (seg < 8) {
+      float off = 0.f;
+      for (int s2 = 0; s2 < seg; ++s2) off += As[s2 * DK + j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Gs[(8 * seg + i) * LD + j] = v[i] + off;
     }
   }
   __syncthreads();
