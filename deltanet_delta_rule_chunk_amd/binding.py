@@ -32,7 +32,7 @@ EXPORTS = ("deltanet_chunk_fwd", "deltanet_chunk_fwd_workspace_bytes", "deltanet
            "deltanet_kda_chunk_fwd", "deltanet_kda_chunk_fwd_workspace_bytes",
            "deltanet_kda_decode_step", "deltanet_chunk_bwd", "deltanet_chunk_bwd_workspace_bytes",
            "deltanet_status_string", "deltanet_last_hip_error", "deltanet_version",
-           "deltanet_profile_start", "deltanet_profile_stop")
+           "deltanet_profile_start", "deltanet_profile_stop", "deltanet_chunk_fwd_noalloc")
 PROFILE_SLOTS = ("chunk_prep", "chunk_scan", "decode", "features", "bwd_prep", "bwd_fwd_scan",
                  "bwd_scan", "bwd_cc", "bwd_qk")
 
@@ -58,6 +58,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.deltanet_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
     lib.deltanet_chunk_fwd.restype = i
+    lib.deltanet_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                               vp]
+    lib.deltanet_chunk_fwd_noalloc.restype = i
     lib.deltanet_chunk_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.deltanet_chunk_fwd_workspace_bytes.restype = sz
     lib.deltanet_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]

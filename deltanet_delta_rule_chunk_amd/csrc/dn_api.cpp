@@ -116,7 +116,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alp
                    const float* beta, const float* S0, void* o, float* S_final, int B, int H,
                    int L, int d_k, int d_v, int C, int in_dtype, int out_dtype, void* workspace,
                    size_t workspace_bytes, hipStream_t stream, bool features = false,
-                   bool per_dim = false) {
+                   bool per_dim = false, bool fixed_scratch = false) {
   ChunkSizes s;
   int st = check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, out_dtype, &s);
   if (st != DN_OK) return st;
@@ -141,8 +141,13 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alp
   for (Span x : {sq, sk, sv, sa, sb, ss0, so, ssf})
     if (overlap(sw, x)) return DN_ERR_ALIASING;
   if (workspace && workspace_bytes < need) return DN_ERR_WORKSPACE;
+  if (fixed_scratch && need > dn::kNoallocScratchBytes) return DN_ERR_WORKSPACE;
 
   void* ws = workspace;
+  if (fixed_scratch && need > 0) {
+    hipError_t e = dn::noalloc_scratch(stream, &ws);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   const bool own_ws = (ws == nullptr && need > 0);
   if (own_ws) {
     hipError_t e = hipMallocAsync(&ws, need, stream);
@@ -432,6 +437,14 @@ int deltanet_chunk_fwd(const void* q, const void* k, const void* v, const float*
                        size_t workspace_bytes, hipStream_t stream) {
   return chunk_fwd_impl(q, k, v, nullptr, beta, S0, o, S_final, B, H, L, d_k, d_v, C, in_dtype,
                         out_dtype, workspace, workspace_bytes, stream);
+}
+
+int deltanet_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* beta,
+                               const float* S0, void* o, float* S_final, int B, int H, int L,
+                               int d_k, int d_v, int C, int in_dtype, int out_dtype,
+                               hipStream_t stream) {
+  return chunk_fwd_impl(q, k, v, nullptr, beta, S0, o, S_final, B, H, L, d_k, d_v, C, in_dtype,
+                        out_dtype, nullptr, 0, stream, false, false, true);
 }
 
 int deltanet_gated_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,

@@ -100,4 +100,10 @@ hipError_t launch_kda_chunk_fwd(const ChunkArgs& a);
 // the workspace, after the kernels' other scratch.
 size_t gated_log_decay_bytes(int B, int H, int L, int C);
 
+// The fixed per-GPU scratch area of the allocation-free forward
+// (dn_noalloc.hip): its size, and its address on the device `stream` belongs
+// to (looked up on the first call for that device, then cached).
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(hipStream_t stream, void** out);
+
 }  // namespace dn

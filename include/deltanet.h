@@ -84,6 +84,32 @@ size_t deltanet_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v,
                                           int in_dtype);
 
 /*
+ * deltanet_chunk_fwd that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, layouts and result as
+ * deltanet_chunk_fwd, without the workspace arguments: the scratch comes from
+ * a fixed area of DN_NOALLOC_SCRATCH_BYTES compiled into the library, one per
+ * GPU, held from the library's load until the process ends.  No call makes
+ * hipMalloc, hipFree or any other allocation.
+ *
+ *  - Sizes whose workspace (deltanet_chunk_fwd_workspace_bytes) exceeds
+ *    DN_NOALLOC_SCRATCH_BYTES return DN_ERR_WORKSPACE and launch nothing
+ *    (64 MiB holds e.g. B*H = 32 heads of L = 8192 at C = 64 with bf16
+ *    inputs, not the L = 65536, 32-head long-context shape).
+ *  - The area is found on the device `stream` belongs to; its address is
+ *    looked up (hipGetSymbolAddress) on the first call for each device, so
+ *    make one call per device before capturing a graph.
+ *  - All calls on one GPU share its area and it keeps the previous call's
+ *    contents (nothing in it has to start cleared).  Calls that overlap in
+ *    time on one GPU (other streams, other threads) race on it: serialise them.
+ */
+#define DN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int deltanet_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* beta,
+                               const float* S0, void* o, float* S_final,
+                               int B, int H, int L, int d_k, int d_v, int C,
+                               int in_dtype, int out_dtype, hipStream_t stream);
+
+/*
  * One decode step for B sequences x H heads (the recurrence at one token),
  * updating the state in place.
  *
