@@ -24,7 +24,8 @@ from deltanet_delta_rule_chunk_amd import inputs as I
 from deltanet_delta_rule_chunk_amd.binding import chunk_fwd, decode_step, feature_prep
 from oracle import (delta_rule_decode_step, delta_rule_forward, feature_maps,
                     gated_delta_rule_decode_step, gated_delta_rule_forward, round_to_bf16)
-from parity import assert_parity, to64
+from oracle_pool import features_forward, oracle_heads
+from parity import assert_parity, check_bf16_out, record, to64, worst_head
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -188,22 +189,36 @@ def test_chunk_fwd_features_empty_sequence(gpu_lib):
 
 
 def test_chunk_fwd_features_long_context(gpu_lib):
-    """L = 65536, 32 heads of d = 128, C = 128 at full size; the oracle on two
-    sampled heads over the whole sequence."""
+    """L = 65536, 32 heads of d = 128, C = 128 at full size from raw
+    projections, o stored in fp32 and in bf16; every head against the oracle
+    (the oracle's feature maps, then its forward)."""
     w = I.WORKLOADS[3]
     _note(f"[features] chunk {w.name}")
     x = I.make_chunk_raw_inputs(w, seed=0)
     g = {k: (None if t is None else t.to(DEV)) for k, t in x.items()}
-    o, S = chunk_fwd(g["q_raw"], g["k_raw"], g["v"], g["beta_logit"], None, w.C,
-                     out_dtype=torch.bfloat16, features=True)
-    torch.cuda.synchronize()
-    assert torch.isfinite(o).all() and torch.isfinite(S).all()
+    outs = []
+    for od in (torch.float32, torch.bfloat16):
+        o, S = chunk_fwd(g["q_raw"], g["k_raw"], g["v"], g["beta_logit"], None, w.C,
+                         out_dtype=od, features=True)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o).all() and torch.isfinite(S).all()
+        outs.append((o.cpu(), S.cpu()))
     del g
-    heads = [(0, 5), (0, 26)]
-    o_ref, S_ref = _fwd_oracle(x, "bf16", heads=heads)
-    e = assert_parity(o[0, [5, 26]][None].cpu(), o_ref, "bf16", "o")
-    assert_parity(S[0, [5, 26]][None].cpu(), S_ref, "bf16", "S_final")
-    _note(f"  o err/RMS = {e:.3e}")
+    (o32, S), (o16, S16) = outs
+    assert torch.equal(S, S16)
+    _note(f"  oracle on all {w.B * w.H} heads")
+    o_ref, S_ref = oracle_heads(features_forward,
+                                (x["q_raw"], x["k_raw"], x["v"], x["beta_logit"], x["S0"], None),
+                                dtype="bf16")
+    e = assert_parity(o32, o_ref, "bf16", "o")
+    eS = assert_parity(S, S_ref, "bf16", "S_final")
+    e16, floor = check_bf16_out(o16, o32, o_ref, e)
+    wh = worst_head(o32, o_ref)
+    _note(f"  o err/RMS = {e:.3e} (worst head {wh}), bf16 out {e16:.3e} (rounding floor "
+          f"{floor:.3e}), S_final {eS:.3e}")
+    record("features_workload3", workload=w.name + "_features", heads=w.B * w.H,
+           o_f32_out=e, o_bf16_out=e16, bf16_rounding_floor=floor, S_final=eS,
+           worst_head_f32_out=wh)
 
 
 @pytest.mark.parametrize("dt,dk,dv,gated", [("bf16", 128, 128, False), ("bf16", 64, 128, True),
