@@ -2,9 +2,10 @@
 
 Every step of the computation runs in the library's HIP kernels; this module
 checks tensors (device, dtype, contiguity, shape), allocates outputs and the
-workspace through PyTorch's caching allocator, and passes raw device pointers
-and the current HIP stream to the C ABI.  If the library is missing it raises:
-there is no fallback.
+workspace through PyTorch's caching allocator (recorded on the launch stream
+when that is not the current one), and passes raw device pointers and the HIP
+stream (the current one unless ``stream=`` names another) to the C ABI.  If
+the library is missing it raises: there is no fallback.
 """
 
 from __future__ import annotations
@@ -146,6 +147,17 @@ def _stream(device: torch.device, stream) -> int:
     return s.cuda_stream
 
 
+def _alloc(shape, dtype: torch.dtype, device: torch.device, stream) -> torch.Tensor:
+    """A new tensor from PyTorch's caching allocator.  The allocator ties a
+    block to the stream current at allocation; when the kernels run on another
+    stream, the block is also recorded on that stream, so that it is not
+    handed out again while those kernels may still use it."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        t.record_stream(stream)
+    return t
+
+
 def workspace_bytes(B: int, H: int, L: int, d_k: int, d_v: int, C: int,
                     in_dtype: torch.dtype = torch.bfloat16, gated: bool = False,
                     features: bool = False) -> int:
@@ -182,13 +194,13 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     for t, n in ((S0, "S0"), (dS_final, "dS_final")):
         if t is not None:
             _check(t, n, (B, H, d_k, d_v), torch.float32, dev)
-    f32 = dict(dtype=torch.float32, device=dev)
-    dq, dk = torch.empty((B, H, L, d_k), **f32), torch.empty((B, H, L, d_k), **f32)
-    dv, db = torch.empty((B, H, L, d_v), **f32), torch.empty((B, H, L), **f32)
-    dS0 = torch.empty((B, H, d_k, d_v), **f32) if want_dS0 else None
+    f32 = dict(dtype=torch.float32, device=dev, stream=stream)
+    dq, dk = _alloc((B, H, L, d_k), **f32), _alloc((B, H, L, d_k), **f32)
+    dv, db = _alloc((B, H, L, d_v), **f32), _alloc((B, H, L), **f32)
+    dS0 = _alloc((B, H, d_k, d_v), **f32) if want_dS0 else None
     need = bwd_workspace_bytes(B, H, L, d_k, d_v, C, q.dtype)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _alloc(need, torch.uint8, dev, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.deltanet_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(dO),
                                 _ptr(dS_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(dS0),
@@ -225,15 +237,15 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torc
     if S0 is not None:
         _check(S0, "S0", (B, H, d_k, d_v), torch.float32, dev)
     if o is None:
-        o = torch.empty((B, H, L, d_v), dtype=out_dtype, device=dev)
+        o = _alloc((B, H, L, d_v), out_dtype, dev, stream)
     _check(o, "o", (B, H, L, d_v), out_dtype, dev)
     if S_final is None and want_state:
-        S_final = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=dev)
+        S_final = _alloc((B, H, d_k, d_v), torch.float32, dev, stream)
     if S_final is not None:
         _check(S_final, "S_final", (B, H, d_k, d_v), torch.float32, dev)
     need = kda_workspace_bytes(B, H, L, d_k, d_v, C, q.dtype)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _alloc(need, torch.uint8, dev, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.deltanet_kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),
                                     _ptr(o), _ptr(S_final), B, H, L, d_k, d_v, C, _code(q.dtype),
@@ -260,7 +272,7 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: to
     _check(beta, "beta", (B, H), torch.float32, dev)
     _check(S, "S", (B, H, d_k, d_v), torch.float32, dev)
     if o is None:
-        o = torch.empty((B, H, d_v), dtype=out_dtype, device=dev)
+        o = _alloc((B, H, d_v), out_dtype, dev, stream)
     _check(o, "o", (B, H, d_v), out_dtype, dev)
     st = lib.deltanet_kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S),
                                       _ptr(o), B, H, d_k, d_v, _code(q.dtype), _code(out_dtype),
@@ -286,7 +298,9 @@ def feature_prep(q_raw: torch.Tensor, k_raw: torch.Tensor, beta_logit: torch.Ten
     if in_place:
         qh, kh, b = q_raw, k_raw, beta_logit
     else:
-        qh, kh, b = torch.empty_like(q_raw), torch.empty_like(k_raw), torch.empty_like(beta_logit)
+        qh = _alloc(q_raw.shape, q_raw.dtype, dev, stream)
+        kh = _alloc(k_raw.shape, k_raw.dtype, dev, stream)
+        b = _alloc(beta_logit.shape, beta_logit.dtype, dev, stream)
     st = lib.deltanet_feature_prep(_ptr(q_raw), _ptr(k_raw), _ptr(beta_logit), _ptr(qh), _ptr(kh),
                                    _ptr(b), B, H, L, d_k, _code(q_raw.dtype), _stream(dev, stream))
     if st != DN_OK:
@@ -321,17 +335,17 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     if S0 is not None:
         _check(S0, "S0", (B, H, d_k, d_v), torch.float32, dev)
     if o is None:
-        o = torch.empty((B, H, L, d_v), dtype=out_dtype, device=dev)
+        o = _alloc((B, H, L, d_v), out_dtype, dev, stream)
     _check(o, "o", (B, H, L, d_v), out_dtype, dev)
     if S_final is None and want_state:
-        S_final = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=dev)
+        S_final = _alloc((B, H, d_k, d_v), torch.float32, dev, stream)
     if S_final is not None:
         _check(S_final, "S_final", (B, H, d_k, d_v), torch.float32, dev)
     in_code = _code(q.dtype)
     need = workspace_bytes(B, H, L, d_k, d_v, C, q.dtype, gated=alpha is not None,
                            features=features)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _alloc(need, torch.uint8, dev, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if features:
         st = lib.deltanet_chunk_fwd_features(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
@@ -384,7 +398,7 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.T
     _check(beta, "beta", (B, H), torch.float32, dev)
     _check(S, "S", (B, H, d_k, d_v), torch.float32, dev)
     if o is None:
-        o = torch.empty((B, H, d_v), dtype=out_dtype, device=dev)
+        o = _alloc((B, H, d_v), out_dtype, dev, stream)
     _check(o, "o", (B, H, d_v), out_dtype, dev)
     if alpha is not None:
         _check(alpha, "alpha", (B, H), torch.float32, dev)
