@@ -38,9 +38,18 @@
 // (hi = bf16(x), lo = bf16(x - hi)); the states inside a chunk are stored as
 // fp32 and split by their reader.  q and k are exact in bf16, so every
 // product keeps roughly fp32 accuracy.
-// A ragged last chunk loads clamped rows and zeroes them at first use
-// (k, v rows and beta = 0 make those rows of R, Delta and T zero: no-ops);
-// outputs past L are not stored.
+// Global reads go through buffer descriptors made per chunk (base address in
+// scalar registers, a fixed byte offset per lane), so a chunk step spends no
+// vector instructions on addresses, and the descriptor's range check returns
+// zero for rows past L: a ragged last chunk reads k and v rows of zero (with
+// beta = 0 those rows of R, Delta and T are zero: no-ops); outputs past L
+// are not stored.
+//
+// Each split product accumulates all of its passes (hi*hi, hi*lo, lo*hi) in
+// one fp32 accumulator, and the outputs are formed as transposed tiles,
+// (Q S + P Delta)^T = S^T Q^T + Delta^T P^T: the same operand registers with
+// A and B swapped, which leaves each lane holding 4 consecutive columns of
+// one output row, stored to HBM as one 16-byte write.
 //
 // Gated form (GATED; Gated DeltaNet, article "How a Baseten Engineer Traced 7
 // Years of Attention Mechanism Evolution", Gated DeltaNet section: the state
@@ -93,8 +102,7 @@ struct Cfg {
   static constexpr int OFF_R = OFF_FSNAP + NFSNAP * 2 * SPLANE;
   static constexpr int OFF_D = OFF_R + 2 * RPLANE;
   static constexpr int OFF_V = OFF_D + 2 * 2 * RPLANE;   // [2][C][16] bf16 v slice
-  static constexpr int OFF_O = OFF_V + 2 * C * 16;       // [4 waves][32][16] fp32 out tile
-  static constexpr int OFF_DT = OFF_O + 4 * 32 * 16 * 2;  // decayed Delta planes (gated form)
+  static constexpr int OFF_DT = OFF_V + 2 * C * 16;       // decayed Delta planes (gated form)
   // Gated form: per slot (chunk parity), 4 rows of C fp32: g, e^{g},
   // e^{G_{b+1} - g}, e^{g - G_b} (b = the row's sub-block).
   static constexpr int OFF_G = OFF_DT + 2 * RPLANE;
@@ -134,6 +142,24 @@ __device__ __forceinline__ void put_split(uint16_t* base, int plane, int off, f3
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
 
+// Buffer descriptor over `bytes` bytes from `base` (raw access, stride 0): a
+// read at byte offset >= bytes returns zero.  Both arguments are the same in
+// every lane; reading them from the first lane keeps the descriptor in
+// scalar registers.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // (readfirstlane returns a signed int: each half goes through uint32_t so
+  // that widening it never sign-extends into the other half.)
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((hi << 32) | lo), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 template <int C, int DK, int DV, typename OT, bool GATED>
 __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -167,7 +193,10 @@ __global__ __launch_bounds__(512) void scan_kernel(
   const int ct = sl % NCT, bh = (sl / NCT) * 8 + xcd;
   if (bh >= BH) return;
   const int j0 = ct * 16;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, i16 = lane & 15;
+  // (The wave index is the same in every lane: read from the first lane it
+  // lives in a scalar register, and so does everything derived from it.)
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool chain = w < CF::NCW;
   const size_t sbase = (size_t)bh * DK * DV;
   const size_t tokh = (size_t)bh * L;
@@ -188,37 +217,33 @@ __global__ __launch_bounds__(512) void scan_kernel(
   }
 
   auto valid_of = [&](int cc) { return min(C, L - cc * C); };
+  // Descriptors over chunk cc's rows of q, k (d_k wide) and v (d_v wide): rows
+  // past L read as zero.
+  auto rows_rsrc = [&](const uint16_t* base, int width, int cc) {
+    const size_t t0 = tokh + (size_t)cc * C;
+    return make_rsrc(base + t0 * width, (uint32_t)valid_of(cc) * width * 2);
+  };
 
   // Staging of a chunk's k tile into LDS, shared by all 512 threads.  The
   // global loads of the next chunk are issued early and consumed by the
-  // store one or two phases later; rows past L are zeroed at the store.
+  // store one or two phases later.
   uint4 kst[SPT];
+  uint32_t kvoff[SPT];
+  int kdst[SPT];
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int e = i * CF::NTHR + tid, row = e / (DK / 8), ch = e % (DK / 8);
+    kvoff[i] = (uint32_t)(row * DK + ch * 8) * 2;
+    kdst[i] = koff<DK>(row, ch);
+  }
   auto stage_load = [&](int cc) {
-    const int valid = valid_of(cc);
-    const size_t t0 = tokh + (size_t)cc * C;
+    const rsrc_t rk = rows_rsrc(k, DK, cc);
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int e = i * CF::NTHR + tid, row = e / (DK / 8), ch = e % (DK / 8);
-      kst[i] = *reinterpret_cast<const uint4*>(k + (t0 + min(row, valid - 1)) * DK + ch * 8);
-    }
+    for (int i = 0; i < SPT; ++i) kst[i] = bload16(rk, kvoff[i], 0);
   };
-  auto stage_store = [&](int cc, uint16_t* dst) {
-    const int valid = valid_of(cc);
-    if (valid == C) {
+  auto stage_store = [&](uint16_t* dst) {
 #pragma unroll
-      for (int i = 0; i < SPT; ++i) {
-        const int e = i * CF::NTHR + tid, row = e / (DK / 8), ch = e % (DK / 8);
-        *reinterpret_cast<uint4*>(dst + koff<DK>(row, ch)) = kst[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < SPT; ++i) {
-        const int e = i * CF::NTHR + tid, row = e / (DK / 8), ch = e % (DK / 8);
-        const uint32_t m = row < valid ? 0xffffffffu : 0u;
-        *reinterpret_cast<uint4*>(dst + koff<DK>(row, ch)) =
-            make_uint4(kst[i].x & m, kst[i].y & m, kst[i].z & m, kst[i].w & m);
-      }
-    }
+    for (int i = 0; i < SPT; ++i) *reinterpret_cast<uint4*>(dst + kdst[i]) = kst[i];
   };
 
   // Each role runs its own loop with the same three barriers per chunk, and
@@ -229,7 +254,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     // ======================= chain waves =====================================
     __builtin_amdgcn_s_setprio(2);
     const int rt0 = w, rt1 = NRT - 1 - w;  // row tiles (rt1 only if RPW == 2)
-    f32x4 sa[DPW], sb[DPW];
+    f32x4 st[DPW];
     // T fragments of one chunk for this wave's row tiles, loaded at the very
     // start of the chunk's step (ahead of every other wave's loads of that
     // step) and used in its Delta phase.
@@ -237,33 +262,38 @@ __global__ __launch_bounds__(512) void scan_kernel(
       uint4 h[NTS], l[NTS];
     };
     TRegs tA;
+    // Byte offset of slot sl's block within a chunk's fragments (wave-uniform).
+    int tsoff[NTS];
+#pragma unroll
+    for (int sl = 0; sl < NTS; ++sl) {
+      // (RPW == 1: a slot past the tile's last block re-reads block 0, unused.)
+      const bool first = RPW == 1 || sl <= rt0 / 2;
+      const int blk = RPW == 1 ? (sl <= rt0 / 2 ? sl : 0) : (first ? sl : NTS - 1 - sl);
+      tsoff[sl] = (Frag<C>::base(first ? rt0 : rt1) + blk) * 128 * 16;
+    }
     auto t_load = [&](int cc, TRegs& t) {
-      const uint4* tb = Tfrag + ((size_t)bh * nc + cc) * Frag<C>::chunk_u4 + lane;
+      const rsrc_t rt = make_rsrc(Tfrag + ((size_t)bh * nc + cc) * Frag<C>::chunk_u4,
+                                  (uint32_t)(Frag<C>::chunk_u4 * 16));
 #pragma unroll
       for (int sl = 0; sl < NTS; ++sl) {
-        // (RPW == 1: a slot past the tile's last block re-reads block 0, unused.)
-        const bool first = RPW == 1 || sl <= rt0 / 2;
-        const int blk = RPW == 1 ? (sl <= rt0 / 2 ? sl : 0) : (first ? sl : NTS - 1 - sl);
-        const uint4* p = tb + (size_t)Frag<C>::base(first ? rt0 : rt1) * 128 + (size_t)blk * 128;
-        t.h[sl] = p[0];
-        t.l[sl] = p[64];
+        t.h[sl] = bload16(rt, lane * 16, tsoff[sl]);
+        t.l[sl] = bload16(rt, lane * 16, tsoff[sl] + 64 * 16);
       }
     };
 
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int dt = DPW * w + i;
-      sa[i] = zero4();
-      sb[i] = zero4();
+      st[i] = zero4();
       if (S0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          sa[i][r] = S0[sbase + (size_t)(16 * dt + 4 * g + r) * DV + j0 + i16];
+          st[i][r] = S0[sbase + (size_t)(16 * dt + 4 * g + r) * DV + j0 + i16];
       }
-      put_split(Snap, SPLANE, fo_d(dt, g, i16), sa[i]);
+      put_split(Snap, SPLANE, fo_d(dt, g, i16), st[i]);
     }
     stage_load(0);
-    stage_store(0, Kbuf);
+    stage_store(Kbuf);
     __syncthreads();
 
     const int m = i16 >> 2, ap = i16 & 3;
@@ -293,16 +323,13 @@ __global__ __launch_bounds__(512) void scan_kernel(
           for (int i = 0; i < RPW; ++i)
             Ka[i][kb] = lds16(Kc + koff<DK>(16 * (i == 0 ? rt0 : rt1) + i16, 4 * kb + g));
         }
-        f32x4 rh[RPW], rl[RPW];
+        f32x4 ks[RPW];
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) { rh[i] = zero4(); rl[i] = zero4(); }
+        for (int i = 0; i < RPW; ++i) ks[i] = zero4();
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-          for (int i = 0; i < RPW; ++i) {
-            rh[i] = mfma16(Ka[i][kb], Sh[kb], rh[i]);
-            rl[i] = mfma16(Ka[i][kb], Sl[kb], rl[i]);
-          }
+          for (int i = 0; i < RPW; ++i) ks[i] = mfma_split2(Ka[i][kb], Sh[kb], Sl[kb], ks[i]);
         }
         // v in the D layout straight from the staged row-major slice: the
         // transposing read gives lane (i16, g) rows 16 rt + 4 g .. + 3 of
@@ -317,9 +344,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
           f32x4 R;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float ks = rh[i][r] + rl[i][r];
-            if constexpr (GATED) ks *= Gs[(c & 1) * 4 * C + C + 16 * rt + 4 * g + r];
-            R[r] = v4[r] - ks;
+            float kv = ks[i][r];
+            if constexpr (GATED) kv *= Gs[(c & 1) * 4 * C + C + 16 * rt + 4 * g + r];
+            R[r] = v4[r] - kv;
           }
           put_split(Rb, RPLANE, fo_d(rt, g, i16), R);
         }
@@ -339,30 +366,25 @@ __global__ __launch_bounds__(512) void scan_kernel(
                                lds8(Rb + RPLANE + fo_d(2 * cb + 1, g, i16)));
           }
         }
-        f32x4 d0 = zero4(), d1 = zero4(), d2 = zero4();
+        f32x4 d0 = zero4();
 #pragma unroll
         for (int cb = 0; cb < TB0; ++cb) {
-          if (cb <= rt0 / 2) {
-            d0 = mfma16(as_bf16x8(tc.h[cb]), Rh[cb], d0);
-            d1 = mfma16(as_bf16x8(tc.h[cb]), Rl[cb], d1);
-            d2 = mfma16(as_bf16x8(tc.l[cb]), Rh[cb], d2);
-          }
+          if (cb <= rt0 / 2)
+            d0 = mfma_split3(as_bf16x8(tc.h[cb]), as_bf16x8(tc.l[cb]), Rh[cb], Rl[cb], d0);
         }
         if constexpr (RPW == 2) {
-          f32x4 e0 = zero4(), e1 = zero4(), e2 = zero4();
+          f32x4 e0 = zero4();
 #pragma unroll
           for (int cb = 0; cb < TB1; ++cb) {
-            if (cb <= rt1 / 2) {
-              e0 = mfma16(as_bf16x8(tc.h[NTS - 1 - cb]), Rh[cb], e0);
-              e1 = mfma16(as_bf16x8(tc.h[NTS - 1 - cb]), Rl[cb], e1);
-              e2 = mfma16(as_bf16x8(tc.l[NTS - 1 - cb]), Rh[cb], e2);
-            }
+            if (cb <= rt1 / 2)
+              e0 = mfma_split3(as_bf16x8(tc.h[NTS - 1 - cb]), as_bf16x8(tc.l[NTS - 1 - cb]), Rh[cb],
+                               Rl[cb], e0);
           }
-          put_split(Dc, RPLANE, fo_d(rt1, g, i16), e0 + e1 + e2);
-          if constexpr (GATED) put_split(DTb, RPLANE, fo_d(rt1, g, i16), decay_rows(rt1, e0 + e1 + e2, c));
+          put_split(Dc, RPLANE, fo_d(rt1, g, i16), e0);
+          if constexpr (GATED) put_split(DTb, RPLANE, fo_d(rt1, g, i16), decay_rows(rt1, e0, c));
         }
-        put_split(Dc, RPLANE, fo_d(rt0, g, i16), d0 + d1 + d2);
-        if constexpr (GATED) put_split(DTb, RPLANE, fo_d(rt0, g, i16), decay_rows(rt0, d0 + d1 + d2, c));
+        put_split(Dc, RPLANE, fo_d(rt0, g, i16), d0);
+        if constexpr (GATED) put_split(DTb, RPLANE, fo_d(rt0, g, i16), decay_rows(rt0, d0, c));
       }
       __syncthreads();
 
@@ -387,29 +409,23 @@ __global__ __launch_bounds__(512) void scan_kernel(
           if constexpr (GATED) {  // S_b -> e^{G_{b+1} - G_b} S_b  (= e^{g - G_b} at the block's last row)
             const float f = Gs[(c & 1) * 4 * C + 3 * C + 32 * b + 31];
 #pragma unroll
-            for (int i = 0; i < DPW; ++i) { sa[i] *= f; sb[i] *= f; }
+            for (int i = 0; i < DPW; ++i) st[i] *= f;
           }
 #pragma unroll
-          for (int i = 0; i < DPW; ++i) {
-            sa[i] = mfma16(Kt[b][i], Dh[b], sa[i]);
-            sb[i] = mfma16(Kt[b][i], Dl[b], sb[i]);
-          }
+          for (int i = 0; i < DPW; ++i) st[i] = mfma_split2(Kt[b][i], Dh[b], Dl[b], st[i]);
           if (b + 1 < NSB) {
             float* dst = Fsnap + b * DK * 16;
 #pragma unroll
             for (int i = 0; i < DPW; ++i)
-              *reinterpret_cast<f32x4*>(dst + fo_d(DPW * w + i, g, i16)) = sa[i] + sb[i];
+              *reinterpret_cast<f32x4*>(dst + fo_d(DPW * w + i, g, i16)) = st[i];
           } else {
             uint16_t* dst = Snap + ((c + 1) & 1) * 2 * SPLANE;
 #pragma unroll
-            for (int i = 0; i < DPW; ++i)
-              put_split(dst, SPLANE, fo_d(DPW * w + i, g, i16), sa[i] + sb[i]);
+            for (int i = 0; i < DPW; ++i) put_split(dst, SPLANE, fo_d(DPW * w + i, g, i16), st[i]);
           }
         }
       }
-#pragma unroll
-      for (int i = 0; i < DPW; ++i) { sa[i] = sa[i] + sb[i]; sb[i] = zero4(); }
-      stage_store(cn, Kbuf + ((c + 1) & 1) * KELEMS);
+      stage_store(Kbuf + ((c + 1) & 1) * KELEMS);
       __syncthreads();
     };
     for (int c = 0; c < nc; ++c) step(c, tA);
@@ -420,7 +436,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
         const int dt = DPW * w + i;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          S_final[sbase + (size_t)(16 * dt + 4 * g + r) * DV + j0 + i16] = sa[i][r];
+          S_final[sbase + (size_t)(16 * dt + 4 * g + r) * DV + j0 + i16] = st[i][r];
       }
     }
   } else {
@@ -432,11 +448,15 @@ __global__ __launch_bounds__(512) void scan_kernel(
     const bool outw = a < NSB;
     const int aq = outw ? a : 0;
     uint4 qreg[2][NKB];
+    uint32_t qvoff[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) qvoff[h] = (uint32_t)((32 * aq + 16 * h + i16) * DK + 8 * g) * 2;
     // The chunk's 16-column v slice is staged row-major into LDS by the
     // output waves' 256 threads (16 bytes each: row tl / 2, half tl % 2);
-    // rows past L are stored as zero.
+    // rows past L read as zero.
     const int tl = tid - CF::NCW * 64;  // 0 .. 255
     const int vrow = min(tl >> 1, C - 1), vhalf = tl & 1;
+    const uint32_t vvoff = (uint32_t)(vrow * DV + j0 + 8 * vhalf) * 2;
     // (Gated form: the chunk's C log-decays ride along, 16 bytes per thread,
     // into slot `gslot` of Gs, the parity of the chunk step that uses them.)
     uint4 vst;
@@ -444,9 +464,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     float gb0, gb1;  // G_b and G_{b+1} of the sub-block of this thread's 4 rows
     const int grow4 = 4 * (tl % (C / 4)), gblk = grow4 >> 5;
     auto v_stage_load = [&](int cc) {
-      const int valid = valid_of(cc);
-      const size_t t0 = tokh + (size_t)cc * C;
-      vst = *reinterpret_cast<const uint4*>(v + (t0 + min(vrow, valid - 1)) * DV + j0 + 8 * vhalf);
+      vst = bload16(rows_rsrc(v, DV, cc), vvoff, 0);
       if constexpr (GATED) {
         const float* gsrc = Gws + ((size_t)bh * nc + cc) * C;
         gst = *reinterpret_cast<const float4*>(gsrc + grow4);
@@ -454,13 +472,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
         gb1 = gsrc[32 * gblk + 31];
       }
     };
-    auto v_stage_store = [&](int cc, uint16_t* dst, int gslot) {
-      const int valid = valid_of(cc);
-      if (tl < 2 * C) {
-        const uint32_t msk = vrow < valid ? 0xffffffffu : 0u;
-        *reinterpret_cast<uint4*>(dst + vrow * 16 + 8 * vhalf) =
-            make_uint4(vst.x & msk, vst.y & msk, vst.z & msk, vst.w & msk);
-      }
+    auto v_stage_store = [&](uint16_t* dst, int gslot) {
+      if (tl < 2 * C) *reinterpret_cast<uint4*>(dst + vrow * 16 + 8 * vhalf) = vst;
       if constexpr (GATED) {
         if (tl < C / 4) {
           const float G0 = gblk > 0 ? gb0 : 0.f;
@@ -477,18 +490,15 @@ __global__ __launch_bounds__(512) void scan_kernel(
       }
     };
     auto q_load = [&](int cc) {
-      const int valid = valid_of(cc);
-      const size_t t0 = tokh + (size_t)cc * C;
+      const rsrc_t rq = rows_rsrc(q, DK, cc);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int row = min(32 * aq + 16 * h + i16, valid - 1);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          qreg[h][kb] = *reinterpret_cast<const uint4*>(q + (t0 + row) * DK + 32 * kb + 8 * g);
+        for (int kb = 0; kb < NKB; ++kb) qreg[h][kb] = bload16(rq, qvoff[h] + 64 * kb, 0);
       }
     };
     // Diagonal 32 x 32 block of Q K^T of chunk cc for sub-block a, as split
-    // A operands of the P Delta product.  Computed as transposed 16 x 16
+    // operands of the P Delta product.  Computed as transposed 16 x 16
     // tiles: lane (i16, g) register r holds P[q = i16][k = 4 g + r] of its
     // tile; the two diagonal tiles keep k <= q, the tile above the diagonal is
     // not needed.  "d4" slot map: slots (g, 0..3) <-> k tile 2a rows
@@ -534,8 +544,10 @@ __global__ __launch_bounds__(512) void scan_kernel(
       ph1 = make_uint4(h01.x, h01.y, h11.x, h11.y);
       pl1 = make_uint4(l01.x, l01.y, l11.x, l11.y);
     };
-    // Outputs of chunk cc for sub-block a: Q_a S_a + tril(Q_a K_a^T) Delta_a,
-    // with chunk cc's q rows in qreg and its diagonal Q K^T block in ph/pl.
+    // Outputs of chunk cc for sub-block a, (Q_a S_a + tril(Q_a K_a^T) Delta_a)^T
+    // = S_a^T Q_a^T + Delta_a^T P^T, with chunk cc's q rows in qreg and its
+    // diagonal Q K^T block in ph/pl: lane (i16, g) ends with row 32 a + 16 h +
+    // i16 of o, columns 4 g .. 4 g + 3 of the slice.
     auto outputs = [&](int cc) {
       const int valid = valid_of(cc);
       const size_t t0 = tokh + (size_t)cc * C;
@@ -564,47 +576,25 @@ __global__ __launch_bounds__(512) void scan_kernel(
       const bf16x8 Dh = as_bf16x8(lds8(Dc + fo_d(2 * a, g, i16)), lds8(Dc + fo_d(2 * a + 1, g, i16)));
       const bf16x8 Dl = as_bf16x8(lds8(Dc + RPLANE + fo_d(2 * a, g, i16)),
                                   lds8(Dc + RPLANE + fo_d(2 * a + 1, g, i16)));
-      f32x4 o0h = zero4(), o0l = zero4(), o1h = zero4(), o1l = zero4();
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 Q0 = as_bf16x8(qreg[0][kb]), Q1 = as_bf16x8(qreg[1][kb]);
-        o0h = mfma16(Q0, Sh[kb], o0h);
-        o0l = mfma16(Q0, Sl[kb], o0l);
-        o1h = mfma16(Q1, Sh[kb], o1h);
-        o1l = mfma16(Q1, Sl[kb], o1l);
-      }
-      f32x4 x0 = mfma16(as_bf16x8(ph0), Dh, zero4());
-      f32x4 x1 = mfma16(as_bf16x8(ph1), Dh, zero4());
-      x0 = mfma16(as_bf16x8(ph0), Dl, x0);
-      x1 = mfma16(as_bf16x8(ph1), Dl, x1);
-      x0 = mfma16(as_bf16x8(pl0), Dh, x0);
-      x1 = mfma16(as_bf16x8(pl1), Dh, x1);
-      // Transpose the 32 x 16 output tile through this wave's LDS tile so
-      // each lane stores 4 consecutive columns of one row (16-byte groups of
-      // a row XOR-swizzled by row / 4 to keep both accesses conflict-free).
-      float* Ot = reinterpret_cast<float*>(lds + CF::OFF_O) + a * 32 * 16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row0 = 4 * g + r, row1 = row0 + 16;
-        float s0 = o0h[r] + o0l[r], s1 = o1h[r] + o1l[r];
-        if constexpr (GATED) {  // rows of Q_a S_a decayed by e^{g_row - G_a}
-          const float* f3 = Gs + (cc & 1) * 4 * C + 3 * C + 32 * a;
-          s0 *= f3[row0];
-          s1 *= f3[row1];
-        }
-        Ot[row0 * 16 + ((((i16 >> 2) ^ (row0 >> 2)) & 3) << 2) + (i16 & 3)] = s0 + x0[r];
-        Ot[row1 * 16 + ((((i16 >> 2) ^ (row1 >> 2)) & 3) << 2) + (i16 & 3)] = s1 + x1[r];
-      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int row = 16 * h + (lane >> 2), cg = lane & 3;
-        const f32x4 val = *reinterpret_cast<const f32x4*>(Ot + row * 16 + (((cg ^ (row >> 2)) & 3) << 2));
-        if (32 * a + row < valid) {
-          OT* dst = o + (t0 + 32 * a + row) * DV + j0 + 4 * cg;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const bf16x8 Qh = as_bf16x8(qreg[h][kb]);
+          acc = mfma16(Sh[kb], Qh, acc);
+          acc = mfma16(Sl[kb], Qh, acc);
+        }
+        const int row = 32 * a + 16 * h + i16;
+        if constexpr (GATED)  // row of Q_a S_a decayed by e^{g_row - G_a}
+          acc *= Gs[(cc & 1) * 4 * C + 3 * C + row];
+        acc = mfma_split3(Dh, Dl, as_bf16x8(h == 0 ? ph0 : ph1), as_bf16x8(h == 0 ? pl0 : pl1), acc);
+        if (row < valid) {
+          OT* dst = o + (t0 + row) * DV + j0 + 4 * g;
           if constexpr (sizeof(OT) == 4) {
-            *reinterpret_cast<f32x4*>(dst) = val;
+            *reinterpret_cast<f32x4*>(dst) = acc;
           } else {
-            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16(val[0], val[1]), pack_bf16(val[2], val[3]));
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
           }
         }
       }
@@ -612,47 +602,51 @@ __global__ __launch_bounds__(512) void scan_kernel(
 
     // L2 prefetch: the 128-byte lines of chunk cc's k, q, v and T data are
     // split over the head's column-slice workgroups (which share an XCD and
-    // its L2); output-wave thread t touches lines ct + NCT (t + 256 j) with
-    // one dword load each.  The values are folded into pf_acc one chunk later,
-    // so the loads never stall anything, and pf_acc is only ever stored under
-    // a condition that is false.  (Whole lines rather than 64-byte sectors:
-    // the kernel runs power-limited, and touching half as many lines was
-    // measured to save ~3.5% of its cycles at the same clock.)
+    // its L2); output-wave thread tl touches line ct + NCT tl of the list
+    // [k lines | q lines | v lines | T lines] with one dword load.  The values
+    // are folded into pf_acc one chunk later, so the loads never stall
+    // anything, and pf_acc is only ever stored under a condition that is
+    // false.  (Whole lines rather than 64-byte sectors: the kernel runs
+    // power-limited, and touching half as many lines was measured to save
+    // ~3.5% of its cycles at the same clock.)  Each thread's line keeps its
+    // place within the chunk, so its address is a fixed base plus the chunk
+    // index times a fixed stride; on a ragged last chunk the row is clamped.
     constexpr int PFL = 128;                 // line bytes
-    constexpr int EPL = PFL / 2;             // bf16 elements per line
-    constexpr int LK = C * DK / EPL, LV = C * DV / EPL;
+    constexpr int LK = C * DK * 2 / PFL, LV = C * DV * 2 / PFL;
     constexpr int LT = (int)(Frag<C>::chunk_u4 * 16 / PFL);
     constexpr int NLINES = 2 * LK + LV + LT;
-    constexpr int NPF = (NLINES / NCT + 255) / 256;
-    uint32_t pf_acc = 0, pf_val[NPF];
-#pragma unroll
-    for (int j = 0; j < NPF; ++j) pf_val[j] = 0;
+    static_assert(NLINES <= 256 * NCT, "one prefetch line per output-wave thread");
+    const int pn = min(ct + NCT * tl, NLINES - 1);
+    const char* pbase;
+    size_t pstride;
+    uint32_t poff, prow_bytes;
+    if (pn < 2 * LK) {
+      pbase = reinterpret_cast<const char*>((pn < LK ? k : q) + tokh * DK);
+      pstride = (size_t)C * DK * 2;
+      poff = (uint32_t)(pn % LK) * PFL;
+      prow_bytes = DK * 2;
+    } else if (pn < 2 * LK + LV) {
+      pbase = reinterpret_cast<const char*>(v + tokh * DV);
+      pstride = (size_t)C * DV * 2;
+      poff = (uint32_t)(pn - 2 * LK) * PFL;
+      prow_bytes = DV * 2;
+    } else {
+      pbase = reinterpret_cast<const char*>(Tfrag + (size_t)bh * nc * Frag<C>::chunk_u4);
+      pstride = Frag<C>::chunk_u4 * 16;
+      poff = (uint32_t)(pn - 2 * LK - LV) * PFL;
+      prow_bytes = 0;  // T is never ragged
+    }
+    uint32_t pf_acc = 0, pf_val = 0;
     auto prefetch = [&](int cc) {
-      const int valid = valid_of(cc);
-      const size_t t0 = tokh + (size_t)cc * C;
-#pragma unroll
-      for (int j = 0; j < NPF; ++j) {
-        const int n = min(ct + NCT * (tl + 256 * j), NLINES - 1);
-        const uint32_t* src;
-        if (n < 2 * LK) {
-          const int e = (n % LK) * EPL, row = min(e / DK, valid - 1);
-          const uint16_t* base = n < LK ? k : q;
-          src = reinterpret_cast<const uint32_t*>(base + (t0 + row) * DK + e % DK);
-        } else if (n < 2 * LK + LV) {
-          const int e = (n - 2 * LK) * EPL, row = min(e / DV, valid - 1);
-          src = reinterpret_cast<const uint32_t*>(v + (t0 + row) * DV + e % DV);
-        } else {
-          src = reinterpret_cast<const uint32_t*>(Tfrag + ((size_t)bh * nc + cc) * Frag<C>::chunk_u4 +
-                                                  (PFL / 16) * (n - 2 * LK - LV));
-        }
-        pf_val[j] = *src;
-      }
+      uint32_t off = poff;
+      if (prow_bytes && L - cc * C < C) off = min(off, (uint32_t)(L - cc * C - 1) * prow_bytes);
+      pf_val = *reinterpret_cast<const uint32_t*>(pbase + (size_t)cc * pstride + off);
     };
 
     v_stage_load(0);
     stage_load(0);
-    v_stage_store(0, Vbuf, 0);
-    stage_store(0, Kbuf);
+    v_stage_store(Vbuf, 0);
+    stage_store(Kbuf);
     __syncthreads();
     for (int c = 0; c < nc; ++c) {
       const int cn = min(c + 1, nc - 1);
@@ -663,19 +657,17 @@ __global__ __launch_bounds__(512) void scan_kernel(
       q_load(c);
       __syncthreads();
       // ---- phase B: L2 prefetch of chunk c+2 ------------------------------------
-#pragma unroll
-      for (int j = 0; j < NPF; ++j) pf_acc ^= pf_val[j];
+      pf_acc ^= pf_val;
       prefetch(min(c + 2, nc - 1));
       __syncthreads();
       // ---- phase C: diagonal Q K^T block of chunk c ------------------------------
       if (outw) diag_qk(c);
-      v_stage_store(cn, Vbuf + ((c + 1) & 1) * C * 16, (c + 1) & 1);
-      stage_store(cn, Kbuf + ((c + 1) & 1) * KELEMS);
+      v_stage_store(Vbuf + ((c + 1) & 1) * C * 16, (c + 1) & 1);
+      stage_store(Kbuf + ((c + 1) & 1) * KELEMS);
       __syncthreads();
     }
     if (outw) outputs(nc - 1);
-#pragma unroll
-    for (int j = 0; j < NPF; ++j) pf_acc ^= pf_val[j];
+    pf_acc ^= pf_val;
     if (nc < 0) S_final[0] = __uint_as_float(pf_acc);
   }
 }
