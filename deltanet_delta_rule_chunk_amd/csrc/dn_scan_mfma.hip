@@ -36,8 +36,8 @@
 // conflicts), the state snapshots, R and Delta (Delta double buffered).  The
 // entering state, R and Delta are stored as split-bf16 operand planes
 // (hi = bf16(x), lo = bf16(x - hi)); the states inside a chunk are stored as
-// fp32 and split by their reader.  q and k are exact in bf16, so every
-// product keeps roughly fp32 accuracy.
+// fp32 (in 4-row groups, see fo_f) and split by their reader.  q and k are
+// exact in bf16, so every product keeps roughly fp32 accuracy.
 // Global reads go through buffer descriptors made per chunk (base address in
 // scalar registers, a fixed byte offset per lane), so a chunk step spends no
 // vector instructions on addresses, and the descriptor's range check returns
@@ -120,6 +120,12 @@ __device__ __forceinline__ int fo_b(int blk, int g, int j) { return ((4 * blk + 
 __device__ __forceinline__ int fo_d(int t, int g, int j) {
   return ((2 * t + (g >> 1)) * 16 + j) * 8 + 4 * (g & 1);
 }
+
+// fp32 state snapshot [DK x 16]: the 4-row group q (rows 4 q .. 4 q + 3) of
+// column j as 16 contiguous bytes at float offset (q * 16 + j) * 4, so that a
+// 16-lane group reading or writing one 4-row group touches 256 contiguous
+// bytes (no LDS bank conflict).
+__device__ __forceinline__ int fo_f(int q, int j) { return (q * 16 + j) * 4; }
 
 __device__ __forceinline__ bf16x8 lds16(const uint16_t* p) {
   return as_bf16x8(*reinterpret_cast<const uint4*>(p));
@@ -417,7 +423,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
             float* dst = Fsnap + b * DK * 16;
 #pragma unroll
             for (int i = 0; i < DPW; ++i)
-              *reinterpret_cast<f32x4*>(dst + fo_d(DPW * w + i, g, i16)) = st[i];
+              *reinterpret_cast<f32x4*>(dst + fo_f(4 * (DPW * w + i) + g, i16)) = st[i];
           } else {
             uint16_t* dst = Snap + ((c + 1) & 1) * 2 * SPLANE;
 #pragma unroll
@@ -564,8 +570,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
         const float* Sn = Fsnap + (a - 1) * DK * 16;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          const f32x4 x0 = *reinterpret_cast<const f32x4*>(Sn + fo_b(kb, g, i16));
-          const f32x4 x1 = *reinterpret_cast<const f32x4*>(Sn + fo_b(kb, g, i16) + 4);
+          // rows 32 kb + 8 g .. + 7: the 4-row groups 8 kb + 2 g and 8 kb + 2 g + 1
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(Sn + fo_f(8 * kb + 2 * g, i16));
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(Sn + fo_f(8 * kb + 2 * g + 1, i16));
           uint2 h0, l0, h1, l1;
           split4(x0, h0, l0);
           split4(x1, h1, l1);
