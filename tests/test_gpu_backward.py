@@ -12,7 +12,8 @@ import torch
 from deltanet_delta_rule_chunk_amd import inputs as I
 from deltanet_delta_rule_chunk_amd.binding import chunk_bwd, chunk_fwd
 from oracle import delta_rule_backward
-from parity import assert_parity, to64
+from oracle_pool import oracle_heads
+from parity import assert_parity, record, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -141,6 +142,27 @@ def test_backward_long_context_identities(gpu_lib):
     _note(f"  <dq,q> {q_side:.6e} vs <dO,o> {lo:.6e}; <dv,v>+<dS0,S0> {v_side:.6e} vs {lo + ls:.6e}")
     assert abs(q_side - lo) <= 1e-4 * scale_q
     assert abs(v_side - (lo + ls)) <= 1e-4 * scale_v
+
+
+def test_backward_long_context_elementwise(gpu_lib):
+    """L = 65536, 32 heads of d = 128 at full size on the GPU, every gradient
+    element-wise against the fp64 backward oracle on four heads spread over
+    the head range (the oracle keeps all L + 1 states of a head in fp64,
+    8.6 GB each, so it runs one head per worker process)."""
+    w = I.WORKLOADS[3]
+    _note(f"[bwd] {w.name} element-wise, four heads")
+    x = I.make_chunk_inputs(w, seed=0)
+    dO, dSf = _grads_in(w, 0)
+    got = _run(x, dO, dSf, w.C)
+    heads = [(0, 0), (0, 9), (0, 21), (0, 31)]
+    ref = oracle_heads(delta_rule_backward, (x["q"], x["k"], x["v"], x["beta"], x["S0"], dO, dSf),
+                       heads)
+    bi, hi = [b for b, _ in heads], [h for _, h in heads]
+    errs = {}
+    for n, a, b in zip(NAMES, got, ref):
+        errs[n] = assert_parity(a[bi, hi][None], b, "bf16", n)
+    _note("  " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    record("backward_workload3", workload=w.name + "_backward", heads=heads, **errs)
 
 
 def test_backward_bitwise_determinism(gpu_lib):
