@@ -126,3 +126,117 @@ def test_orthonormal_overwrite_on_gpu(gpu_lib):
     o, S = chunk_fwd(t(Q), t(K), t(V), torch.ones(1, H, d, device=DEV), None, 64)
     torch.cuda.synchronize()
     assert_parity(o.cpu(), want, "f32", "retrieval")
+
+
+# The same properties on bf16 inputs, which run the matrix-core WY prep and
+# state scan (the kernels the long-context benchmark times) instead of the
+# fp32 vector-ALU pair.
+
+
+def _rms(t):
+    return float(t.double().pow(2).mean().sqrt())
+
+
+@pytest.mark.parametrize("C", [64, 128])
+def test_split_invariance_bf16(gpu_lib, C):
+    """State passing through S_final -> S0 on the matrix-core path.  At a chunk
+    boundary the second call starts from the same fp32 state the single call
+    holds in its accumulators, so the results are the same bits; off a
+    boundary the chunking differs and they agree to rounding."""
+    _note(f"[inv] split bf16 C={C}")
+    w = I.ChunkWorkload("splitb", 2, 3, 5 * C + 17, 128, 128, C, "bf16", s0_std=0.1)
+    g = _dev(I.make_chunk_inputs(w, seed=32))
+    o, S = chunk_fwd(g["q"], g["k"], g["v"], g["beta"], g["S0"], C)
+    for cut in (2 * C, 2 * C + 37):
+        a = {k: g[k][:, :, :cut].contiguous() for k in ("q", "k", "v", "beta")}
+        b = {k: g[k][:, :, cut:].contiguous() for k in ("q", "k", "v", "beta")}
+        o1, S1 = chunk_fwd(a["q"], a["k"], a["v"], a["beta"], g["S0"], C)
+        o2, S2 = chunk_fwd(b["q"], b["k"], b["v"], b["beta"], S1, C)
+        torch.cuda.synchronize()
+        oc = torch.cat([o1, o2], 2)
+        if cut % C == 0:
+            assert torch.equal(oc, o) and torch.equal(S2, S), cut
+        else:
+            assert float((oc - o).abs().max()) <= 2e-4 * _rms(o), cut
+            assert float((S2 - S).abs().max()) <= 2e-4 * _rms(S), cut
+
+
+def test_decode_equals_chunk_bf16(gpu_lib):
+    """L decode steps (fp32 arithmetic on the bf16 inputs) against one
+    matrix-core chunked forward: two different computations of the same
+    recurrence, each within ~6e-5 RMS of the oracle, checked at 2e-4."""
+    _note("[inv] decode vs chunk bf16")
+    w = I.ChunkWorkload("dvcb", 2, 3, 150, 128, 128, 64, "bf16", s0_std=0.1)
+    g = _dev(I.make_chunk_inputs(w, seed=33))
+    o, S = chunk_fwd(g["q"], g["k"], g["v"], g["beta"], g["S0"], 64)
+    Sd = g["S0"].clone()
+    outs = []
+    for t in range(w.L):
+        outs.append(decode_step(*(g[n][:, :, t].contiguous() for n in ("q", "k", "v", "beta")), Sd))
+    torch.cuda.synchronize()
+    od = torch.stack(outs, 2)
+    assert float((od - o).abs().max()) <= 2e-4 * _rms(o)
+    assert float((Sd - S).abs().max()) <= 2e-4 * _rms(S)
+
+
+def test_homogeneity_and_affinity_bf16(gpu_lib):
+    """For fixed q, k, beta: (V, S0) -> (O, S_final) is linear.  Doubling V and
+    S0 is exact in every number type the kernels use (bf16 values, split
+    pairs, fp32 sums), so the result doubles bit for bit; and an affine
+    combination of two initial states (weights summing to 1, V fixed) gives
+    the same combination of the outputs to rounding."""
+    _note("[inv] homogeneity bf16")
+    w = I.ChunkWorkload("homb", 1, 2, 300, 128, 128, 128, "bf16", s0_std=0.1)
+    g1 = _dev(I.make_chunk_inputs(w, seed=34))
+    g2 = _dev(I.make_chunk_inputs(w, seed=35))
+    o1, S1 = chunk_fwd(g1["q"], g1["k"], g1["v"], g1["beta"], g1["S0"], 128)
+    o2x, S2x = chunk_fwd(g1["q"], g1["k"], (2 * g1["v"]).contiguous(), g1["beta"],
+                         (2 * g1["S0"]).contiguous(), 128)
+    torch.cuda.synchronize()
+    assert torch.equal(o2x, 2 * o1) and torch.equal(S2x, 2 * S1)
+    a, b = 0.75, 0.25
+    oa, Sa = chunk_fwd(g1["q"], g1["k"], g1["v"], g1["beta"], g2["S0"], 128)
+    om, Sm = chunk_fwd(g1["q"], g1["k"], g1["v"], g1["beta"], (a * g1["S0"] + b * g2["S0"]).contiguous(),
+                       128)
+    torch.cuda.synchronize()
+    assert float((a * o1 + b * oa - om).abs().max()) <= 2e-4 * _rms(om)
+    assert float((a * S1 + b * Sa - Sm).abs().max()) <= 2e-4 * _rms(Sm)
+
+
+def test_beta_zero_bf16(gpu_lib):
+    """beta = 0 on the matrix-core path: T = 0, so Delta = 0 and the state is
+    S0 bit for bit; o = q S0 through split-precision products (fp32 bar)."""
+    _note("[inv] beta zero bf16")
+    w = I.ChunkWorkload("b0b", 1, 2, 300, 128, 128, 128, "bf16", s0_std=0.1)
+    g = _dev(I.make_chunk_inputs(w, seed=36))
+    beta = torch.zeros_like(g["beta"])
+    o, S = chunk_fwd(g["q"], g["k"], g["v"], beta, g["S0"], 128)
+    torch.cuda.synchronize()
+    assert torch.equal(S, g["S0"])
+    assert_parity(o.cpu(), to64(g["q"]) @ to64(g["S0"]), "f32", "o")
+
+
+def test_orthonormal_overwrite_bf16(gpu_lib):
+    """beta = 1 and keys that are orthonormal before the bf16 cast: queries
+    equal to earlier keys read back (nearly) those keys' values; exactly
+    the oracle's on the rounded inputs, to the bf16 bar."""
+    _note("[inv] overwrite bf16")
+    rng = np.random.default_rng(38)
+    d, H = 128, 2
+    Q = np.zeros((1, H, d, d)); K = np.zeros((1, H, d, d)); V = rng.standard_normal((1, H, d, d))
+    want = np.zeros_like(V)
+    for h in range(H):
+        m, r = np.linalg.qr(rng.standard_normal((d, d)))
+        K[0, h] = (m * np.sign(np.diag(r))).T
+        pick = np.array([rng.integers(0, t + 1) for t in range(d)])
+        Q[0, h] = K[0, h][pick]
+        want[0, h] = V[0, h][pick]
+    t = lambda a: torch.from_numpy(a).to(DEV, torch.bfloat16).contiguous()
+    q, k, v = t(Q), t(K), t(V)
+    beta = torch.ones(1, H, d, device=DEV)
+    o, S = chunk_fwd(q, k, v, beta, None, 128)
+    torch.cuda.synchronize()
+    o_ref, _ = delta_rule_forward(to64(q), to64(k), to64(v), to64(beta), None)
+    assert_parity(o.cpu(), o_ref, "bf16", "o against the oracle")
+    # the rounding of k, q, v to bf16 keeps the readback within a few percent
+    assert float(np.abs(to64(o) - want).max()) <= 0.1 * float(np.sqrt(np.mean(want * want)))
