@@ -59,7 +59,14 @@ typedef enum { DN_F32 = 0, DN_BF16 = 1 } dn_dtype;
  *   v      : [B, H, L, d_v]   in_dtype
  *   beta   : [B, H, L]        fp32, per-token write strength
  *   S0     : [B, H, d_k, d_v] fp32 initial state, or NULL for the zero state
- *   o      : [B, H, L, d_v]   out_dtype, written (o_t read after token t's write)
+ *   o      : [B, H, L, d_v]   out_dtype, written (o_t read after token t's write).
+ *            The kernels compute o in fp32; out_dtype = DN_BF16 stores it
+ *            rounded to nearest even, which alone moves an element by up to
+ *            2^-9 |o| (measured against the exact result: 1.2e-2 RMS(o) at
+ *            B=4 H=12 L=2048 d=64, 2.5e-2 at B=2 H=16 L=8192 d=128 with beta
+ *            = 1 heads, 1.7e-2 at B=1 H=32 L=65536 d=128, the largest errors
+ *            being the roundings of the largest outputs).  Where an error
+ *            bound of 2e-2 RMS(o) has to hold at such sizes, take DN_F32.
  *   S_final: [B, H, d_k, d_v] fp32 state after the last token, or NULL to skip.
  *            S_final may be the same buffer as S0 (in-place state update);
  *            any other overlap with an input is rejected.
