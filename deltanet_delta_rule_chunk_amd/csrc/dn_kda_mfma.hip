@@ -74,28 +74,51 @@ __device__ __forceinline__ void put_split(uint16_t* hi, int plane, int i, float 
 
 template <int DK>
 struct PrepLds {
-  static constexpr int LD = DK + 4;  // row pitch of the C x d_k tiles (16-byte rows)
-  static constexpr int LDA = C + 1;  // row pitch of A
-  static constexpr size_t bytes =
-      (3 * (size_t)C * LD + (size_t)C * LDA + C + inv64::SCRATCH_FLOATS) * sizeof(float);
+  // K and Q stay in LDS as bf16 (exact: they are bf16 inputs); g, and later
+  // X = (I + A)^{-1}, in fp32; A takes the bytes of K and Q once their last
+  // reader is done.  About 72 KB at d_k = 128, so two workgroups share a CU
+  // and one chunk's loads and stores overlap another's arithmetic.
+  static constexpr int LDH = DK + 8;  // row pitch of the bf16 K and Q tiles (elements)
+  static constexpr int LD = DK + 4;   // row pitch of the fp32 g tile and of X
+  static constexpr int LDA = C + 1;   // row pitch of A
+  static constexpr size_t kq_bytes = 2 * (size_t)C * LDH * 2;
+  static_assert((size_t)C * LDA * 4 <= kq_bytes, "A over K and Q");
+  static_assert(LD >= C, "X over g");
+  static_assert(8 * DK <= inv64::SCRATCH_FLOATS, "prefix totals in the inverse's scratch");
+  static constexpr size_t bytes = kq_bytes + ((size_t)C * LD + C + inv64::SCRATCH_FLOATS) * 4;
 };
 
+// 8 consecutive bf16 (16 bytes, aligned) as fp32.
+__device__ __forceinline__ void bf8(const uint16_t* p, float* x) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t h[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(h[i] << 16);
+    x[2 * i + 1] = __uint_as_float(h[i] & 0xffff0000u);
+  }
+}
+// 4 consecutive bf16 (8 bytes, aligned) as fp32.
+__device__ __forceinline__ float4 bf4(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
 template <int DK>
-__global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
-                                                     const bf16* __restrict__ k,
-                                                     const float* __restrict__ alpha,
-                                                     const float* __restrict__ beta, int L,
-                                                     float* __restrict__ ws) {
-  constexpr int LD = PrepLds<DK>::LD, LDA = PrepLds<DK>::LDA;
+__global__ __launch_bounds__(PNTHR) __attribute__((amdgpu_waves_per_eu(8))) void prep_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ alpha,
+    const float* __restrict__ beta, int L, float* __restrict__ ws) {
+  constexpr int LDH = PrepLds<DK>::LDH, LD = PrepLds<DK>::LD, LDA = PrepLds<DK>::LDA;
   constexpr int KS = DK / 32;
   constexpr size_t CF = chunk_floats(DK);
   extern __shared__ float smem_f[];
-  float* Ks = smem_f;          // K, later X = (I + A)^{-1}
-  float* Qs = Ks + C * LD;     // Q
-  float* Gs = Qs + C * LD;     // g (cumulative log-decays)
-  float* As = Gs + C * LD;     // A
-  float* bs = As + C * LDA;    // beta
-  float* scratch = bs + C;     // the inverse's per-wave tiles
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem_f);  // K (bf16)
+  uint16_t* Qs = Ks + C * LDH;                           // Q (bf16)
+  float* As = smem_f;                                    // A, over K and Q after their last read
+  float* Gs = smem_f + PrepLds<DK>::kq_bytes / 4;        // g (cumulative log-decays), later X
+  float* bs = Gs + C * LD;                               // beta
+  float* scratch = bs + C;                               // the inverse's per-wave tiles
 
   const int c = blockIdx.x, bh = blockIdx.y, nc = gridDim.x;
   const int valid = min(C, L - c * C);
@@ -110,37 +133,29 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
   float* gam = reinterpret_cast<float*>(Ku + 2 * C * DK);  // e^{g_C}
   const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
 
-  {  // q and k rows, 16 bytes per load, into fp32 tiles
+  {  // q and k rows, 16 bytes per load, into the bf16 tiles as they are
     const uint4* kg = reinterpret_cast<const uint4*>(k + tok0 * DK);
     const uint4* qg = reinterpret_cast<const uint4*>(q + tok0 * DK);
     for (int e8 = t; e8 < C * DK / 8; e8 += PNTHR) {
       const int r = e8 / (DK / 8), c8 = e8 % (DK / 8), rc = min(r, valid - 1);
       uint4 xk = kg[rc * (DK / 8) + c8], xq = qg[rc * (DK / 8) + c8];
       if (r >= valid) xk = xq = make_uint4(0u, 0u, 0u, 0u);
-      float4* dk = reinterpret_cast<float4*>(Ks + r * LD + 8 * c8);
-      float4* dq = reinterpret_cast<float4*>(Qs + r * LD + 8 * c8);
-      dk[0] = make_float4(__uint_as_float(xk.x << 16), __uint_as_float(xk.x & 0xffff0000u),
-                          __uint_as_float(xk.y << 16), __uint_as_float(xk.y & 0xffff0000u));
-      dk[1] = make_float4(__uint_as_float(xk.z << 16), __uint_as_float(xk.z & 0xffff0000u),
-                          __uint_as_float(xk.w << 16), __uint_as_float(xk.w & 0xffff0000u));
-      dq[0] = make_float4(__uint_as_float(xq.x << 16), __uint_as_float(xq.x & 0xffff0000u),
-                          __uint_as_float(xq.y << 16), __uint_as_float(xq.y & 0xffff0000u));
-      dq[1] = make_float4(__uint_as_float(xq.z << 16), __uint_as_float(xq.z & 0xffff0000u),
-                          __uint_as_float(xq.w << 16), __uint_as_float(xq.w & 0xffff0000u));
+      *reinterpret_cast<uint4*>(Ks + r * LDH + 8 * c8) = xk;
+      *reinterpret_cast<uint4*>(Qs + r * LDH + 8 * c8) = xq;
     }
   }
   if (t < C) bs[t] = t < valid ? beta[tok0 + t] : 0.f;
   // g: the log-decays of the whole tile at once (coalesced), then a prefix
   // sum down each dimension's column: 8 segments of 8 rows per column, each
   // summed in registers, then offset by the totals of the segments above it
-  // (parked in the A tile, which is written only later).
+  // (parked in the inverse's scratch, which is used only later).
   for (int e = t; e < C * DK; e += PNTHR) {
     const int r = e / DK, j = e % DK;
     Gs[r * LD + j] = r < valid ? log_decay(alpha[(tok0 + r) * DK + j]) : 0.f;
   }
   __syncthreads();
   {
-    static_assert(8 * DK <= PNTHR && 8 * DK <= C * LDA, "prefix layout");
+    static_assert(8 * DK <= PNTHR, "prefix layout");
     const int j = t % DK, seg = t / DK;
     float v[8];
     if (seg < 8) {
@@ -148,12 +163,12 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
       for (int i = 0; i < 8; ++i) v[i] = Gs[(8 * seg + i) * LD + j];
 #pragma unroll
       for (int i = 1; i < 8; ++i) v[i] += v[i - 1];
-      As[seg * DK + j] = v[7];
+      scratch[seg * DK + j] = v[7];
     }
     __syncthreads();
     if (seg < 8) {
       float off = 0.f;
-      for (int s2 = 0; s2 < seg; ++s2) off += As[s2 * DK + j];
+      for (int s2 = 0; s2 < seg; ++s2) off += scratch[s2 * DK + j];
 #pragma unroll
       for (int i = 0; i < 8; ++i) Gs[(8 * seg + i) * LD + j] = v[i] + off;
     }
@@ -162,14 +177,15 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
 
   for (int e8 = t; e8 < C * DK / 8; e8 += PNTHR) {  // the decayed operands of the scan
     const int r = e8 / (DK / 8), j0 = 8 * (e8 % (DK / 8));
-    float kd[8], qd[8], ku[8];
+    float kv[8], qv[8], kd[8], qd[8], ku[8];
+    bf8(Ks + r * LDH + j0, kv);
+    bf8(Qs + r * LDH + j0, qv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float gv = Gs[r * LD + j0 + i], gC = Gs[(C - 1) * LD + j0 + i];
-      const float kv = Ks[r * LD + j0 + i];
-      kd[i] = kv * __expf(gv);
-      qd[i] = Qs[r * LD + j0 + i] * __expf(gv);
-      ku[i] = kv * __expf(gC - gv);
+      kd[i] = kv[i] * __expf(gv);
+      qd[i] = qv[i] * __expf(gv);
+      ku[i] = kv[i] * __expf(gC - gv);
     }
     put_split8(Kd, C * DK, 8 * e8, kd);
     put_split8(Qd, C * DK, 8 * e8, qd);
@@ -179,24 +195,32 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
   for (int e = t; e < C * C; e += PNTHR)  // P above the diagonal
     if (e % C > e / C) put_split(Pc, C * C, e, 0.f);
 
+  // The entries of A below the diagonal, held in registers until K and Q
+  // have no reader left, then written over them.
+  f32x4 aa = zero4();
+  float a = 0.f;
+  int ar = 0, ai = 0;  // the vector-ALU pair's (row, column), a valid zero entry by default
   if (w < 6) {
     // Tile (br, bi) below the block diagonal; wave w takes tile w of
     // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
     const int br = w < 1 ? 1 : w < 3 ? 2 : 3;
     const int bi = w - (br * (br - 1)) / 2;
     const int m = 16 * br, ra = 16 * br + n, ib = 16 * bi + n;
-    f32x4 aa = zero4(), ap = zero4();
+    f32x4 ap = zero4();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      const int j = 32 * ks + 8 * g;
       float kt[8], qt[8], kh[8];
+      bf8(Ks + ra * LDH + j, kt);
+      bf8(Qs + ra * LDH + j, qt);
+      bf8(Ks + ib * LDH + j, kh);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int j = 32 * ks + 8 * g + e;
-        const float gm = Gs[m * LD + j];
-        const float fr = __expf(Gs[ra * LD + j] - gm);
-        kt[e] = Ks[ra * LD + j] * fr;
-        qt[e] = Qs[ra * LD + j] * fr;
-        kh[e] = Ks[ib * LD + j] * __expf(gm - Gs[ib * LD + j]);
+        const float gm = Gs[m * LD + j + e];
+        const float fr = __expf(Gs[ra * LD + j + e] - gm);
+        kt[e] *= fr;
+        qt[e] *= fr;
+        kh[e] *= __expf(gm - Gs[ib * LD + j + e]);
       }
       bf16x8 kth, ktl, qth, qtl, khh, khl;
       split8(kt, kth, ktl);
@@ -206,11 +230,8 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
       ap = mfma_split3(qth, qtl, khh, khl, ap);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * br + 4 * g + e, i = 16 * bi + n;
-      As[r * LDA + i] = bs[r] * aa[e];
-      put_split(Pc, C * C, r * C + i, ap[e]);
-    }
+    for (int e = 0; e < 4; ++e)
+      put_split(Pc, C * C, (16 * br + 4 * g + e) * C + 16 * bi + n, ap[e]);
   } else {
     // Pairs (r, i), i <= r, inside the diagonal tiles: 4 x 136 of them.
     const int pidx = t - 6 * 64;
@@ -219,15 +240,14 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
       int rr = 0;
       while ((rr + 1) * (rr + 2) / 2 <= qi) ++rr;
       const int r = 16 * b + rr, i = 16 * b + qi - rr * (rr + 1) / 2;
-      const float4 *kr = reinterpret_cast<const float4*>(Ks + r * LD);
-      const float4 *ki = reinterpret_cast<const float4*>(Ks + i * LD);
-      const float4 *qr = reinterpret_cast<const float4*>(Qs + r * LD);
+      const uint16_t *kr = Ks + r * LDH, *ki = Ks + i * LDH, *qr = Qs + r * LDH;
       const float4 *gr = reinterpret_cast<const float4*>(Gs + r * LD);
       const float4 *gi = reinterpret_cast<const float4*>(Gs + i * LD);
-      float a = 0.f, pv = 0.f;
-#pragma unroll 4
-      for (int j4 = 0; j4 < DK / 4; ++j4) {  // 16-byte reads, the sum in order of j
-        const float4 gr4 = gr[j4], gi4 = gi[j4], ki4 = ki[j4], kr4 = kr[j4], qr4 = qr[j4];
+      float pv = 0.f;
+#pragma unroll 2
+      for (int j4 = 0; j4 < DK / 4; ++j4) {  // the sum in order of j
+        const float4 gr4 = gr[j4], gi4 = gi[j4];
+        const float4 ki4 = bf4(ki + 4 * j4), kr4 = bf4(kr + 4 * j4), qr4 = bf4(qr + 4 * j4);
         float f = __expf(gr4.x - gi4.x) * ki4.x;
         a += kr4.x * f, pv += qr4.x * f;
         f = __expf(gr4.y - gi4.y) * ki4.y;
@@ -237,18 +257,32 @@ __global__ __launch_bounds__(PNTHR) void prep_kernel(const bf16* __restrict__ q,
         f = __expf(gr4.w - gi4.w) * ki4.w;
         a += kr4.w * f, pv += qr4.w * f;
       }
-      As[r * LDA + i] = i < r ? a * bs[r] : 0.f;
       put_split(Pc, C * C, r * C + i, pv);
+      ar = r, ai = i;
+      a = i < r ? a * bs[r] : 0.f;
     }
   }
+  __syncthreads();  // K and Q are dead from here: A goes over them
+  if (w < 6) {
+    const int br = w < 1 ? 1 : w < 3 ? 2 : 3;
+    const int bi = w - (br * (br - 1)) / 2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * br + 4 * g + e;
+      As[r * LDA + 16 * bi + n] = bs[r] * aa[e];
+    }
+  } else if (t - 6 * 64 < 4 * 136) {
+    As[ar * LDA + ai] = a;
+  }
 
-  // X = (I + A)^{-1} over the K tile (no longer needed), then T = X diag(beta).
-  inv64::inverse<LDA, LD>(As, Ks, scratch);
+  // X = (I + A)^{-1} over the g tile (no longer needed), then T = X diag(beta).
+  float* Xs = Gs;
+  inv64::inverse<LDA, LD>(As, Xs, scratch);
   for (int e8 = t; e8 < C * C / 8; e8 += PNTHR) {
     const int r = e8 / (C / 8), i0 = 8 * (e8 % (C / 8));
     float tv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tv[i] = Ks[r * LD + i0 + i] * bs[i0 + i];
+    for (int i = 0; i < 8; ++i) tv[i] = Xs[r * LD + i0 + i] * bs[i0 + i];
     put_split8(Tc, C * C, 8 * e8, tv);
   }
 }
