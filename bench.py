@@ -213,6 +213,36 @@ def stage_steps(make, steps, dev):
     return out
 
 
+def timed_steps(step, warmup, steps):
+    """``warmup`` untimed calls of ``step()`` straight before ``steps`` timed
+    ones, with nothing but a device synchronisation between the two: after
+    an idle stretch the GPU's clocks take some milliseconds of load to
+    settle, so a host-side pause (an allocation, a check that reads the
+    result back) between warmup and timing would put that transient in the
+    timed region.  Returns (ms per step from events around the timed calls,
+    the library's per-kernel profile of them, wall seconds)."""
+    import torch
+
+    from deltanet_delta_rule_chunk_amd import binding
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    binding.profile_start()
+    binding.profile_stop()  # creates the profiling events outside the timed region
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    binding.profile_start()
+    t_wall = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    prof = binding.profile_stop()
+    return ev0.elapsed_time(ev1) / steps, prof, t_wall
+
+
 def graph_ms_per_step(launch, steps, reset, check):
     """Captures ``launch(0) .. launch(steps-1)`` into one HIP graph and replays
     it three times, each from the same starting state (``reset()`` runs
@@ -245,7 +275,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -300,25 +330,11 @@ def main(argv=None) -> int:
         binding.chunk_fwd(g["q"], g["k"], g["v"], g["beta"], None, w.C, o=o, S_final=S_final,
                           workspace=ws)
 
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
+    print(f"[bench] {a.warmup} warmup + {a.steps} timed chunked-forward steps", file=sys.stderr,
+          flush=True)
+    ms_step, prof, t_wall = timed_steps(step, a.warmup, a.steps)
     assert torch.isfinite(o).all() and torch.isfinite(S_final).all()
-
-    print(f"[bench] timing {a.steps} chunked-forward steps", file=sys.stderr, flush=True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    binding.profile_start()
-    t_wall = time.perf_counter()
-    ev0.record()
-    for _ in range(a.steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    prof = binding.profile_stop()
-    ms_step = ev0.elapsed_time(ev1) / a.steps
 
     tokens_s = w.B * w.L / (ms_step * 1e-3)
     flops = model_flops(w)
@@ -384,18 +400,8 @@ def main(argv=None) -> int:
         binding.chunk_fwd(g["q"], g["k"], g["v"], g["beta"], None, w.C, o=o16, S_final=S_final,
                           workspace=ws, out_dtype=torch.bfloat16)
 
-    for _ in range(a.warmup):
-        step16()
-    torch.cuda.synchronize()
-    binding.profile_start()
-    ev0.record()
-    for _ in range(a.steps):
-        step16()
-    ev1.record()
-    torch.cuda.synchronize()
-    prof16 = binding.profile_stop()
+    ms16, prof16, _ = timed_steps(step16, a.warmup, a.steps)
     assert torch.isfinite(o16).all()
-    ms16 = ev0.elapsed_time(ev1) / a.steps
     kern16 = {name: tot / n for name, (tot, n) in prof16.items()}
     b16 = scan_kernel_bytes(w, out_bytes=2)
     result["bf16_out"] = {
@@ -481,18 +487,8 @@ def main(argv=None) -> int:
             binding.chunk_fwd(g["q"], g["k"], g["v"], g["beta"], None, w.C, o=o, S_final=S_final,
                               workspace=gws, alpha=alpha)
 
-        for _ in range(a.warmup):
-            gstep()
-        torch.cuda.synchronize()
-        binding.profile_start()
-        ev0.record()
-        for _ in range(a.steps):
-            gstep()
-        ev1.record()
-        torch.cuda.synchronize()
-        gprof = binding.profile_stop()
+        ms_g, gprof, _ = timed_steps(gstep, a.warmup, a.steps)
         assert torch.isfinite(o).all() and torch.isfinite(S_final).all()
-        ms_g = ev0.elapsed_time(ev1) / a.steps
         result["gated"] = {
             "workload": w.name + "_gated", "steps": a.steps, "ms_per_step": ms_g,
             "tokens_per_s": w.B * w.L / (ms_g * 1e-3),
@@ -534,21 +530,14 @@ def main(argv=None) -> int:
         bws = torch.empty(binding.bwd_workspace_bytes(w.B, w.H, w.L, w.d_k, w.d_v, w.C),
                           dtype=torch.uint8, device=dev)
 
-        def bstep():
-            return binding.chunk_bwd(g["q"], g["k"], g["v"], g["beta"], None, dO, None, w.C,
-                                     workspace=bws)
+        grads = []
 
-        bstep()
-        torch.cuda.synchronize()
-        binding.profile_start()
-        ev0.record()
-        for _ in range(a.steps):
-            grads = bstep()
-        ev1.record()
-        torch.cuda.synchronize()
-        bprof = binding.profile_stop()
+        def bstep():
+            grads[:] = binding.chunk_bwd(g["q"], g["k"], g["v"], g["beta"], None, dO, None, w.C,
+                                         workspace=bws)
+
+        ms_b, bprof, _ = timed_steps(bstep, a.warmup, a.steps)
         assert all(torch.isfinite(t).all() for t in grads if t is not None)
-        ms_b = ev0.elapsed_time(ev1) / a.steps
         bms = {name: tot / n for name, (tot, n) in bprof.items()}
         result["backward"] = {
             "workload": w.name + "_backward", "steps": a.steps, "ms_per_step": ms_b,
@@ -572,17 +561,8 @@ def main(argv=None) -> int:
             binding.kda_chunk_fwd(g["q"], g["k"], g["v"], kalpha, g["beta"], None, w.C, o=o,
                                   S_final=S_final, workspace=kws)
 
-        kstep()
-        torch.cuda.synchronize()
-        binding.profile_start()
-        ev0.record()
-        for _ in range(a.steps):
-            kstep()
-        ev1.record()
-        torch.cuda.synchronize()
-        kprof = binding.profile_stop()
+        ms_k, kprof, _ = timed_steps(kstep, a.warmup, a.steps)
         assert torch.isfinite(o).all() and torch.isfinite(S_final).all()
-        ms_k = ev0.elapsed_time(ev1) / a.steps
         kms = {name: tot / n for name, (tot, n) in kprof.items()}
         result["kda"] = {
             "workload": w.name + "_kda", "steps": a.steps, "ms_per_step": ms_k,
@@ -636,18 +616,8 @@ def main(argv=None) -> int:
             binding.chunk_fwd(r["q_raw"], r["k_raw"], r["v"], r["beta_logit"], None, w.C, o=o,
                               S_final=S_final, workspace=fws, features=True)
 
-        for _ in range(a.warmup):
-            fstep()
-        torch.cuda.synchronize()
-        binding.profile_start()
-        ev0.record()
-        for _ in range(a.steps):
-            fstep()
-        ev1.record()
-        torch.cuda.synchronize()
-        fprof = binding.profile_stop()
+        ms_f, fprof, _ = timed_steps(fstep, a.warmup, a.steps)
         assert torch.isfinite(o).all() and torch.isfinite(S_final).all()
-        ms_f = ev0.elapsed_time(ev1) / a.steps
         fk = {name: tot / n for name, (tot, n) in fprof.items()}
         fb = feature_bytes(w)
         result["features"] = {
@@ -703,16 +673,9 @@ def main(argv=None) -> int:
                 binding.chunk_fwd(xo["q"], xo["k"], xo["v"], xo["beta"], xo["S0"], wo.C, o=oo, S_final=So,
                                   workspace=wso)
 
-            for _ in range(a.warmup):
-                ostep()
-            torch.cuda.synchronize()
-            ev0.record()
-            for _ in range(a.steps):
-                ostep()
-            ev1.record()
-            torch.cuda.synchronize()
+            # Short steps: enough warmup calls for about 20 ms of load.
+            mso, _, _ = timed_steps(ostep, max(a.warmup, 200), a.steps)
             assert torch.isfinite(oo).all()
-            mso = ev0.elapsed_time(ev1) / a.steps
             fo = model_flops(wo)
             others.append({"workload": wo.name, "ms_per_step": mso, "tokens_per_s": wo.B * wo.L / (mso * 1e-3),
                            "model_tflops": fo / (mso * 1e-3) / 1e12,

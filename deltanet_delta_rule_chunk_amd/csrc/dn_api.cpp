@@ -77,6 +77,8 @@ struct ProfState {
   hipError_t error = hipSuccess;
 };
 thread_local ProfState g_prof;
+// Events kept ready by deltanet_profile_start (two per bracketed launch).
+constexpr size_t kProfPoolEvents = 4096;
 
 hipEvent_t prof_event() {
   if (!g_prof.pool.empty()) {
@@ -240,6 +242,15 @@ int deltanet_profile_start(void) {
   g_prof.recs.clear();
   g_prof.pending = nullptr;
   g_prof.error = hipSuccess;
+  // Create the events up front: creating one between a kernel's launch and
+  // its closing record can leave the GPU waiting on the host, and that wait
+  // would be counted as the kernel's time.
+  while (g_prof.pool.size() < kProfPoolEvents) {
+    hipEvent_t e = nullptr;
+    const hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) return hip_fail(r);
+    g_prof.pool.push_back(e);
+  }
   g_prof.on = true;
   return DN_OK;
 }
