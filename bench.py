@@ -41,7 +41,8 @@ CSRC = os.path.join(ROOT, "deltanet_delta_rule_chunk_amd", "csrc")
 # committed counter measurement stale).
 KERNEL_SOURCES = {
     "chunk_scan": ["dn_scan_mfma.hip", "dn_ktile.h", "dn_tfrag.h", "dn_mfma.h", "dn_common.h"],
-    "chunk_prep": ["dn_chunk_mfma.hip", "dn_ktile.h", "dn_tfrag.h", "dn_mfma.h", "dn_common.h"],
+    "chunk_prep": ["dn_chunk_mfma.hip", "dn_features.h", "dn_ktile.h", "dn_tfrag.h", "dn_mfma.h",
+                   "dn_common.h"],
     "decode": ["dn_decode.hip", "dn_features.h", "dn_common.h"],
     "features": ["dn_features.hip", "dn_features.h", "dn_common.h"],
 }
@@ -49,6 +50,8 @@ KERNEL_SOURCES = {
 # maps in-kernel, come from the same sources.
 KERNEL_SOURCES.update({"gated_" + k: v for k, v in list(KERNEL_SOURCES.items()) if k != "features"})
 KERNEL_SOURCES["features_decode"] = KERNEL_SOURCES["decode"]
+# The WY-prep kernel that applies the feature maps as it loads q and k.
+KERNEL_SOURCES["features_chunk_prep"] = KERNEL_SOURCES["chunk_prep"]
 KERNEL_SOURCES["kda_decode"] = KERNEL_SOURCES["decode"]
 KERNEL_SOURCES["kda_chunk_prep"] = KERNEL_SOURCES["kda_chunk_scan"] = [
     "dn_kda.hip", "dn_kda.h", "dn_kda_mfma.hip", "dn_lds64.h", "dn_inv64.h", "dn_mfma.h",
@@ -144,8 +147,11 @@ def t_workspace_bytes(w):
 
 
 def feature_bytes(w, in_bytes=2):
-    """Algorithmic bytes of the feature-map kernel: q, k read and written once
-    in the storage dtype, the beta logits read and beta written once (fp32)."""
+    """Algorithmic bytes of the feature maps: raw q, k read and mapped q, k
+    written once in the storage dtype, the beta logits read and beta written
+    once (fp32).  The same figure serves the streaming feature kernel and the
+    WY-prep kernel that applies the maps (which also writes T, counted
+    apart)."""
     tok_heads = w.B * w.H * w.L
     return tok_heads * (4 * w.d_k * in_bytes + 8)
 
@@ -620,17 +626,43 @@ def main(argv=None) -> int:
         assert torch.isfinite(o).all() and torch.isfinite(S_final).all()
         fk = {name: tot / n for name, (tot, n) in fprof.items()}
         fb = feature_bytes(w)
+        fpb = fb + t_workspace_bytes(w)
         result["features"] = {
             "workload": w.name + "_features", "steps": a.steps, "ms_per_step": ms_f,
             "tokens_per_s": w.B * w.L / (ms_f * 1e-3), "kernels_ms": fk,
-            "roofline": {"bound": "hbm", "kernel": "features",
-                         "achieved": fb / (fk["features"] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s",
-                         "frac": fb / (fk["features"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                         "traffic": measured_traffic("features")},
+            "path": "feature maps applied inside the WY-prep kernel (raw q, k, beta logits in; "
+                    "mapped q, k, beta and T out), then the scan",
+            "roofline": {"bound": "hbm", "kernel": "features_chunk_prep",
+                         "achieved": fpb / (fk["chunk_prep"] * 1e-3) / 1e9,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": fpb / (fk["chunk_prep"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "bytes": "feature maps' bytes + T written",
+                         "traffic": measured_traffic("features_chunk_prep")},
             "inputs": "q_raw, k_raw, v ~ N(0,1) bf16; beta logits ~ N(0,1) fp32 (own seeded stream)",
         }
-        del r, fws
+        # The streaming feature kernel alone (deltanet_feature_prep), which the
+        # fp32 path runs in front of its forward.
+        fo = [torch.empty_like(r["q_raw"]), torch.empty_like(r["k_raw"]),
+              torch.empty_like(r["beta_logit"])]
+
+        def mstep():
+            lib = binding.load()
+            st = lib.deltanet_feature_prep(r["q_raw"].data_ptr(), r["k_raw"].data_ptr(),
+                                           r["beta_logit"].data_ptr(), fo[0].data_ptr(),
+                                           fo[1].data_ptr(), fo[2].data_ptr(), w.B, w.H, w.L,
+                                           w.d_k, 1, torch.cuda.current_stream().cuda_stream)
+            assert st == 0, st
+
+        ms_m, mprof, _ = timed_steps(mstep, a.warmup, a.steps)
+        km = mprof["features"][0] / mprof["features"][1]
+        result["features"]["feature_kernel"] = {
+            "ms": km,
+            "roofline": {"bound": "hbm", "kernel": "features", "achieved": fb / (km * 1e-3) / 1e9,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": fb / (km * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "traffic": measured_traffic("features")},
+        }
+        del r, fws, fo
         if not a.no_decode:
             nd = max(1, a.decode_steps // 4)
             print(f"[bench] decode with feature maps {wd.name}: {nd} steps", file=sys.stderr,

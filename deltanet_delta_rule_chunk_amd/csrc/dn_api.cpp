@@ -156,12 +156,16 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alp
     if (e != hipSuccess) return hip_fail(e);
   }
   hipError_t e = hipSuccess;
+  dn::FeatureArgs f{};
+  // The bf16 matrix-core path maps q, k and beta inside its WY-prep kernel;
+  // the other paths run the streaming feature kernel first.
+  const bool fused_maps = features && L > 0 && in_dtype == DN_BF16 && !per_dim;
   if (features && L > 0) {
     char* base = static_cast<char*>(ws) + wl.core;
     void *qh = base, *kh = base + wl.qk;
     float* bh = reinterpret_cast<float*>(base + 2 * wl.qk);
-    dn::FeatureArgs f{q, k, beta, qh, kh, bh, (long long)B * H * L, d_k, in_dtype, stream};
-    e = dn::launch_features(f);
+    f = dn::FeatureArgs{q, k, beta, qh, kh, bh, (long long)B * H * L, d_k, in_dtype, stream};
+    if (!fused_maps) e = dn::launch_features(f);
     q = qh;
     k = kh;
     beta = bh;
@@ -169,6 +173,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alp
   if (e == hipSuccess) {
     dn::ChunkArgs a{q, k, v, alpha, beta, S0, o, S_final, B, H, L, d_k, d_v, C, in_dtype,
                     out_dtype, ws, stream, per_dim};
+    if (fused_maps) a.feat = &f;
     e = dn::launch_chunk_fwd(a);
   }
   if (own_ws) {

@@ -43,6 +43,7 @@
 // of the chunk (rows past L: alpha = 1) for the scan.
 
 #include "dn_common.h"
+#include "dn_features.h"
 #include "dn_ktile.h"
 #include "dn_launch.h"
 #include "dn_mfma.h"
@@ -245,12 +246,21 @@ __device__ __forceinline__ void cols_wave(const uint2* Atl, const float* Lrow, c
   }
 }
 
-template <int C, int DK, bool GATED>
+// FEAT: k and beta are the raw k projection and the beta logits; the
+// layer's feature maps are applied as the rows arrive (the same arithmetic
+// as the streaming feature kernel, so the same bits), and the mapped q, k
+// and beta are written out for the scan.  q_raw, q_hat, k_hat and beta_out
+// are used only then.
+template <int C, int DK, bool GATED, bool FEAT>
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ k,
                                                    const float* __restrict__ alpha,
                                                    const float* __restrict__ beta, int L,
                                                    int nc, uint4* __restrict__ Tfrag,
-                                                   float* __restrict__ Gws) {
+                                                   float* __restrict__ Gws,
+                                                   const uint16_t* __restrict__ q_raw,
+                                                   uint16_t* __restrict__ q_hat,
+                                                   uint16_t* __restrict__ k_hat,
+                                                   float* __restrict__ beta_out) {
   using CF = Cfg<C, DK>;
   constexpr int NT = CF::NT;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -269,25 +279,78 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   // ---- 1-2. k tile (64 columns at a time) and Gram tiles -------------------
   // The next slice's loads are in flight while the current one is used.
   constexpr int KW = CF::KW, NH = CF::NH, SPT = CF::SPT;
-  uint4 kv[SPT];
+  // With the feature maps the rows come whole (a row's norm needs all of
+  // it): PPR adjacent lanes hold a row, 16 bytes each, FPT pieces per
+  // thread; piece p of a row lies in staging slice p / (KW / 8).
+  constexpr int PPR = DK / 8, FPT = C * DK / (8 * 256);
+  static_assert(256 % PPR == 0 && FPT >= 1, "row pieces");
+  uint4 kv[FEAT ? FPT : SPT];
   auto kload = [&](int h) {
+    if constexpr (!FEAT) {
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int e = i * 256 + tid, row = e / (KW / 8), ch = e % (KW / 8);
-      kv[i] = *reinterpret_cast<const uint4*>(k + (tok0 + min(row, valid - 1)) * DK + h * KW + ch * 8);
+      for (int i = 0; i < SPT; ++i) {
+        const int e = i * 256 + tid, row = e / (KW / 8), ch = e % (KW / 8);
+        kv[i] = *reinterpret_cast<const uint4*>(k + (tok0 + min(row, valid - 1)) * DK + h * KW + ch * 8);
+      }
     }
   };
-  auto kstore = [&]() {
+  auto kstore = [&](int h) {
+    if constexpr (FEAT) {
+      const int p = tid % PPR;
+      if (p / (KW / 8) == h) {
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int e = i * 256 + tid, row = e / (KW / 8), ch = e % (KW / 8);
-      const uint32_t m = row < valid ? 0xffffffffu : 0u;
-      *reinterpret_cast<uint4*>(Ks + koff<KW>(row, ch)) =
-          make_uint4(kv[i].x & m, kv[i].y & m, kv[i].z & m, kv[i].w & m);
+        for (int i = 0; i < FPT; ++i)
+          *reinterpret_cast<uint4*>(Ks + koff<KW>((i * 256 + tid) / PPR, p % (KW / 8))) = kv[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < SPT; ++i) {
+        const int e = i * 256 + tid, row = e / (KW / 8), ch = e % (KW / 8);
+        const uint32_t m = row < valid ? 0xffffffffu : 0u;
+        *reinterpret_cast<uint4*>(Ks + koff<KW>(row, ch)) =
+            make_uint4(kv[i].x & m, kv[i].y & m, kv[i].z & m, kv[i].w & m);
+      }
     }
   };
-  kload(0);
-  if (tid < C) bs[tid] = tid < valid ? beta[tok0 + tid] : 0.f;
+  if constexpr (FEAT) {
+    // Raw q and k rows (rows past L as zeros, which map to zeros), mapped;
+    // the mapped rows of the sequence go to the workspace.
+    using feat::u32x4;
+    const int p = tid % PPR;
+    uint4 qv[FPT];
+#pragma unroll
+    for (int i = 0; i < FPT; ++i) {
+      const int row = (i * 256 + tid) / PPR;
+      const size_t off = (tok0 + min(row, valid - 1)) * DK + 8 * p;
+      const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off));
+      const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q_raw + off));
+      const bool in = row < valid;
+      kv[i] = in ? make_uint4(a.x, a.y, a.z, a.w) : make_uint4(0u, 0u, 0u, 0u);
+      qv[i] = in ? make_uint4(b.x, b.y, b.z, b.w) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const float bl = tid < valid && tid < C ? beta[tok0 + tid] : 0.f;
+#pragma unroll
+    for (int i = 0; i < FPT; ++i) {
+      const int row = (i * 256 + tid) / PPR;
+      kv[i] = feat::map_piece<PPR, 8>(kv[i]);
+      const uint4 qm = feat::map_piece<PPR, 8>(qv[i]);
+      if (row < valid) {
+        const size_t off = (tok0 + row) * DK + 8 * p;
+        __builtin_nontemporal_store(u32x4{kv[i].x, kv[i].y, kv[i].z, kv[i].w},
+                                    reinterpret_cast<u32x4*>(k_hat + off));
+        __builtin_nontemporal_store(u32x4{qm.x, qm.y, qm.z, qm.w},
+                                    reinterpret_cast<u32x4*>(q_hat + off));
+      }
+    }
+    if (tid < C) {
+      const float b = tid < valid ? fast_sigmoid(bl) : 0.f;
+      bs[tid] = b;
+      if (tid < valid) beta_out[tok0 + tid] = b;
+    }
+  } else {
+    kload(0);
+    if (tid < C) bs[tid] = tid < valid ? beta[tok0 + tid] : 0.f;
+  }
   // Gated form: g_r by an inclusive scan over each wave (every wave keeps its
   // own copy in registers); wave 0 also writes the chunk's g to the workspace.
   GRegs<C> gr_;
@@ -315,7 +378,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
       for (int e = 0; e < E; ++e) gout[E * lane + e] = gr_.v[e];
     }
   }
-  kstore();
+  kstore(0);
   f32x4 acc[2][NT];
 #pragma unroll
   for (int gc = 0; gc < 2; ++gc)
@@ -340,7 +403,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
     if (h + 1 < NH) {
       gram(std::integral_constant<bool, false>{});
       __syncthreads();
-      kstore();
+      kstore(h + 1);
     } else {
       gram(std::integral_constant<bool, true>{});
     }
@@ -387,17 +450,23 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   }
 }
 
-template <int C, int DK, bool GATED>
+template <int C, int DK, bool GATED, bool FEAT>
 hipError_t launch_g(const ChunkArgs& a, uint4* Tfrag, float* Gws) {
   const int nc = cdiv(a.L, C);
   const int BH = a.B * a.H;
   constexpr size_t sm = Cfg<C, DK>::bytes;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<C, DK, GATED>),
+  auto* kern = &prep_kernel<C, DK, GATED, FEAT>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
+  const FeatureArgs* f = a.feat;
   prof_mark(kSlotChunkPrep, false, a.stream);
-  hipLaunchKernelGGL((prep_kernel<C, DK, GATED>), dim3(nc, BH), dim3(256), sm, a.stream,
-                     static_cast<const uint16_t*>(a.k), a.alpha, a.beta, a.L, nc, Tfrag, Gws);
+  hipLaunchKernelGGL(kern, dim3(nc, BH), dim3(256), sm, a.stream,
+                     static_cast<const uint16_t*>(FEAT ? f->k_raw : a.k), a.alpha,
+                     FEAT ? f->beta_logit : a.beta, a.L, nc, Tfrag, Gws,
+                     static_cast<const uint16_t*>(FEAT ? f->q_raw : nullptr),
+                     static_cast<uint16_t*>(FEAT ? f->q_hat : nullptr),
+                     static_cast<uint16_t*>(FEAT ? f->k_hat : nullptr), FEAT ? f->beta : nullptr);
   e = hipGetLastError();
   prof_mark(kSlotChunkPrep, true, a.stream);
   return e;
@@ -410,7 +479,11 @@ hipError_t launch_c(const ChunkArgs& a) {
   // The gated form's log-decay table follows the T fragments.
   float* Gws = reinterpret_cast<float*>(Tfrag + (size_t)a.B * a.H * nc * Frag<C>::chunk_u4);
   if (nc > 0) {
-    hipError_t e = a.alpha ? launch_g<C, DK, true>(a, Tfrag, Gws) : launch_g<C, DK, false>(a, Tfrag, Gws);
+    hipError_t e =
+        a.feat ? (a.alpha ? launch_g<C, DK, true, true>(a, Tfrag, Gws)
+                          : launch_g<C, DK, false, true>(a, Tfrag, Gws))
+               : (a.alpha ? launch_g<C, DK, true, false>(a, Tfrag, Gws)
+                          : launch_g<C, DK, false, false>(a, Tfrag, Gws));
     if (e != hipSuccess) return e;
   }
   return launch_scan_mfma(a, Tfrag, a.alpha ? Gws : nullptr);

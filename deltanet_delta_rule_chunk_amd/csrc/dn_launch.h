@@ -24,6 +24,8 @@ struct DecodeArgs {
   bool per_dim_alpha;
 };
 
+struct FeatureArgs;
+
 struct ChunkArgs {
   const void *q, *k, *v;
   const float* alpha;  // per-token decay of the gated form, or null (plain delta rule);
@@ -36,6 +38,10 @@ struct ChunkArgs {
   void* workspace;  // at least chunk_workspace_bytes(...) bytes (kda_workspace_bytes)
   hipStream_t stream;
   bool per_dim_alpha;  // one decay per key dimension (KDA, dn_kda.hip)
+  // bf16 matrix-core path only: apply the layer's feature maps inside the
+  // WY-prep kernel, from feat's raw inputs into its outputs, which q, k and
+  // beta above must then point at (the scan reads them).
+  const FeatureArgs* feat = nullptr;
 };
 
 hipError_t launch_decode(const DecodeArgs& a);

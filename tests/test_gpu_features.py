@@ -163,18 +163,23 @@ def test_chunk_fwd_features_parity(gpu_lib, case):
     _note(f"  o err = {e:.3e}")
 
 
-@pytest.mark.parametrize("dt,gated", [("bf16", False), ("bf16", True), ("f32", False)])
-def test_chunk_fwd_features_is_maps_then_core(gpu_lib, dt, gated):
-    """The fused call runs the same kernels as the feature prep followed by
-    the core on its outputs: bit for bit the same result."""
-    w = I.ChunkWorkload("two", 1, 2, 2 * 128 + 9, 128, 128, 128, dt, s0_std=0.1)
+@pytest.mark.parametrize("dt,gated,dk,dv,C,L", [
+    ("bf16", False, 128, 128, 128, 2 * 128 + 9), ("bf16", True, 128, 128, 128, 2 * 128 + 9),
+    ("bf16", False, 64, 64, 64, 3 * 64 + 1), ("bf16", True, 64, 128, 128, 100),
+    ("bf16", False, 128, 64, 64, 5 * 64), ("f32", False, 128, 128, 128, 2 * 128 + 9)])
+def test_chunk_fwd_features_is_maps_then_core(gpu_lib, dt, gated, dk, dv, C, L):
+    """The fused call gives bit for bit what the feature prep followed by the
+    core on its outputs gives: the bf16 path applies the maps inside its
+    WY-prep kernel with the streaming kernel's arithmetic, the fp32 path runs
+    the streaming kernel itself."""
+    w = I.ChunkWorkload("two", 1, 2, L, dk, dv, C, dt, s0_std=0.1)
     x = I.make_chunk_raw_inputs(w, seed=2)
     g = {k: t.to(DEV) for k, t in x.items()}
     alpha = I.make_chunk_alpha(w, seed=2).to(DEV) if gated else None
-    o1, S1 = chunk_fwd(g["q_raw"], g["k_raw"], g["v"], g["beta_logit"], g["S0"], 128,
+    o1, S1 = chunk_fwd(g["q_raw"], g["k_raw"], g["v"], g["beta_logit"], g["S0"], C,
                        alpha=alpha, features=True)
     qh, kh, b = feature_prep(g["q_raw"], g["k_raw"], g["beta_logit"])
-    o2, S2 = chunk_fwd(qh, kh, g["v"], b, g["S0"], 128, alpha=alpha)
+    o2, S2 = chunk_fwd(qh, kh, g["v"], b, g["S0"], C, alpha=alpha)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
