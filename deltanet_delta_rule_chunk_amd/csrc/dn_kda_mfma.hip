@@ -39,7 +39,8 @@ using lds64::PC;
 using lds64::put_split_t;
 using lds64::tpos;
 
-constexpr int NTH = 256;  // 4 waves
+constexpr int NTH = 256;   // 4 waves: one role of the scan
+constexpr int SNTH = 512;  // the scan's workgroup: 4 chain + 4 output waves
 
 // ---- prep ------------------------------------------------------------------
 // The pair factors of A and P, e^{g_r - g_i} per dimension, are bounded
@@ -301,16 +302,16 @@ template <> __device__ __forceinline__ void put_out<float>(float* p, float x) { 
 template <> __device__ __forceinline__ void put_out<bf16>(bf16* p, float x) { *p = from_f32<bf16>(x); }
 
 template <int DK, int DV, typename OT>
-__global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
-                                                   const float* __restrict__ S0,
-                                                   OT* __restrict__ o,
-                                                   float* __restrict__ S_final, int L, int nc,
-                                                   int nbh, const float* __restrict__ ws) {
+__global__ __launch_bounds__(SNTH) void scan_kernel(const bf16* __restrict__ v,
+                                                    const float* __restrict__ S0,
+                                                    OT* __restrict__ o,
+                                                    float* __restrict__ S_final, int L, int nc,
+                                                    int nbh, const float* __restrict__ ws) {
   using LD = ScanLds<DK>;
   constexpr int PK = LD::PK, PV = LD::PV;
-  constexpr int TPW = DK / 64;              // state row tiles per wave
+  constexpr int TPW = DK / 64;              // state row tiles per chain wave
   constexpr int KS = DK / 32;               // contraction steps over d_k
-  constexpr int NKU = C * DK / 4 / NTH;     // float4 of K o e^{g_C - g} per thread
+  constexpr int NKU = C * DK / 4 / NTH;     // float4 of K o e^{g_C - g} per chain thread
   static_assert(NKU == 4 || NKU == 8, "rows per thread");
   constexpr size_t CF = chunk_floats(DK);
   extern __shared__ uint4 lds_u4[];
@@ -332,22 +333,27 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
   const int j0 = (sl % (DV / NT)) * NT, bh = (sl / (DV / NT)) * 8 + xcd;
   if (bh >= nbh) return;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
-  const int r0 = 16 * w;
-  const int ku_c4 = t % (DK / 4), ku_r0 = NKU * (t / (DK / 4));
+  // Waves 0-3 carry the chain (R, Delta, the state); waves 4-7 form the
+  // outputs.  Wave w of either kind owns chunk rows 16 (w & 3) .. + 15.
+  const bool chain = w < 4;
+  const int ct = t & (NTH - 1), r0 = 16 * (w & 3);
+  const int ku_c4 = ct % (DK / 4), ku_r0 = NKU * (ct / (DK / 4));
 
   f32x4 S[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
-    const int d0 = 16 * (w * TPW + i) + 4 * g;
+    const int d0 = 16 * ((w & 3) * TPW + i) + 4 * g;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      S[i][e] = S0 ? S0[((size_t)bh * DK + d0 + e) * DV + j0 + n] : 0.f;
+      S[i][e] = S0 && chain ? S0[((size_t)bh * DK + d0 + e) * DV + j0 + n] : 0.f;
   }
 
   // Next chunk's operands, in registers: (hi, lo) bf16 fragments straight
   // from the split planes of the workspace; phase 0 moves them into the
-  // current chunk's set.
-  bf16x8 nkdh[KS], nkdl[KS], nqdh[KS], nqdl[KS], ntth[2], nttl[2], npph[2], nppl[2];
+  // current chunk's set.  A chain wave holds rows of K o e^g and T (and its
+  // share of K o e^{g_C - g}, v and e^{g_C}), an output wave rows of Q o e^g
+  // and P, in the same registers.
+  bf16x8 nah[KS], nal[KS], nbh_[2], nbl[2];
   uint2 kuh[NKU], kul[NKU];
   uint2 pv = make_uint2(0u, 0u);
   float pg = 0.f;
@@ -359,35 +365,33 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
     const uint16_t *bq = bk + 2 * C * DK, *bu = bq + 2 * C * DK;
     const int row = r0 + n;
     auto ld16 = [](const uint16_t* p) { return as_bf16x8(*reinterpret_cast<const uint4*>(p)); };
+    const uint16_t* ba = chain ? bk : bq;  // K o e^g or Q o e^g
+    const uint16_t* bb = chain ? bt : bp;  // T or P
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int off = row * DK + 32 * ks + 8 * g;
-      nkdh[ks] = ld16(bk + off);
-      nkdl[ks] = ld16(bk + C * DK + off);
-      nqdh[ks] = ld16(bq + off);
-      nqdl[ks] = ld16(bq + C * DK + off);
+      nah[ks] = ld16(ba + off);
+      nal[ks] = ld16(ba + C * DK + off);
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int off = row * C + 32 * ks + 8 * g;
-      ntth[ks] = ld16(bt + off);
-      nttl[ks] = ld16(bt + C * C + off);
-      npph[ks] = ld16(bp + off);
-      nppl[ks] = ld16(bp + C * C + off);
+      nbh_[ks] = ld16(bb + off);
+      nbl[ks] = ld16(bb + C * C + off);
     }
+    if (chain) {
 #pragma unroll
-    for (int p = 0; p < NKU; ++p) {  // NKU consecutive rows of one 4-column group
-      const int off = (ku_r0 + p) * DK + 4 * ku_c4;
-      kuh[p] = *reinterpret_cast<const uint2*>(bu + off);
-      kul[p] = *reinterpret_cast<const uint2*>(bu + C * DK + off);
-    }
-    {
-      const int r = t % C, c4 = t / C;
+      for (int p = 0; p < NKU; ++p) {  // NKU consecutive rows of one 4-column group
+        const int off = (ku_r0 + p) * DK + 4 * ku_c4;
+        kuh[p] = *reinterpret_cast<const uint2*>(bu + off);
+        kul[p] = *reinterpret_cast<const uint2*>(bu + C * DK + off);
+      }
+      const int r = ct % C, c4 = ct / C;
       const uint2 x =
           *reinterpret_cast<const uint2*>(v + (t0 + min(r, vc - 1)) * DV + j0 + 4 * c4);
       pv = r < vc ? x : make_uint2(0u, 0u);
+      if (ct < DK) pg = reinterpret_cast<const float*>(bu + 2 * C * DK)[ct];
     }
-    if (t < DK) pg = reinterpret_cast<const float*>(bu + 2 * C * DK)[t];
   };
 
   // L2 prefetch of chunk c + 2: the 128-byte lines of its workspace block
@@ -397,7 +401,7 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
   // and the fold is only ever stored under a condition that is false.
   constexpr int NS = DV / NT;
   constexpr int WL = (int)(CF * 4 / 128), VL = C * DV * 2 / 128;
-  constexpr int NPF = ((WL + VL + NS - 1) / NS + NTH - 1) / NTH;
+  constexpr int NPF = ((WL + VL + NS - 1) / NS + SNTH - 1) / SNTH;
   const int sidx = sl % NS;
   uint32_t pf_acc = 0, pf_val[NPF];
 #pragma unroll
@@ -407,7 +411,7 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
     const size_t t0 = (size_t)bh * L + (size_t)cc * C;
 #pragma unroll
     for (int j = 0; j < NPF; ++j) {
-      const int ln = min(sidx + NS * (t + NTH * j), WL + VL - 1);
+      const int ln = min(sidx + NS * (t + SNTH * j), WL + VL - 1);
       const uint32_t* src;
       if (ln < WL) {
         src = reinterpret_cast<const uint32_t*>(ws + ((size_t)bh * nc + cc) * CF) + 32 * ln;
@@ -426,100 +430,108 @@ __global__ __launch_bounds__(NTH) void scan_kernel(const bf16* __restrict__ v,
 #pragma unroll
     for (int j = 0; j < NPF; ++j) pf_acc ^= pf_val[j];
     // Phase 0: this chunk's operands from the registers into split
-    // fragments and LDS; the state into LDS.
-    bf16x8 kdh[KS], kdl[KS], qdh[KS], qdl[KS], tth[2], ttl[2], pph[2], ppl[2];
+    // fragments; the chain waves also stage K o e^{g_C - g} (transposed), the
+    // v slice, e^{g_C} and the entering state in LDS.
+    bf16x8 ah[KS], al[KS], bh2[2], bl2[2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kdh[ks] = nkdh[ks], kdl[ks] = nkdl[ks], qdh[ks] = nqdh[ks], qdl[ks] = nqdl[ks];
+    for (int ks = 0; ks < KS; ++ks) ah[ks] = nah[ks], al[ks] = nal[ks];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) tth[ks] = ntth[ks], ttl[ks] = nttl[ks], pph[ks] = npph[ks], ppl[ks] = nppl[ks];
-    {  // (K o e^{g_C - g})^T: one NKU-row write per column and half
-      uint32_t h[NKU][2], lo[NKU][2];
+    for (int ks = 0; ks < 2; ++ks) bh2[ks] = nbh_[ks], bl2[ks] = nbl[ks];
+    if (chain) {
+      {  // (K o e^{g_C - g})^T: one NKU-row write per column and half
+        uint32_t h[NKU][2], lo[NKU][2];
 #pragma unroll
-      for (int p = 0; p < NKU; ++p)
-        h[p][0] = kuh[p].x, h[p][1] = kuh[p].y, lo[p][0] = kul[p].x, lo[p][1] = kul[p].y;
+        for (int p = 0; p < NKU; ++p)
+          h[p][0] = kuh[p].x, h[p][1] = kuh[p].y, lo[p][0] = kul[p].x, lo[p][1] = kul[p].y;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint32_t ph[NKU / 2], pl[NKU / 2];
+        for (int e = 0; e < 4; ++e) {
+          uint32_t ph[NKU / 2], pl[NKU / 2];
 #pragma unroll
-        for (int q = 0; q < NKU / 2; ++q) {
-          const int sh = 16 * (e & 1);
-          ph[q] = ((h[2 * q][e >> 1] >> sh) & 0xffffu) | ((h[2 * q + 1][e >> 1] >> sh) << 16);
-          pl[q] = ((lo[2 * q][e >> 1] >> sh) & 0xffffu) | ((lo[2 * q + 1][e >> 1] >> sh) << 16);
-        }
-        const int off = tpos<2>(4 * ku_c4 + e, ku_r0);
-        if constexpr (NKU == 8) {
-          *reinterpret_cast<uint4*>(Uh + off) = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-          *reinterpret_cast<uint4*>(Ul + off) = make_uint4(pl[0], pl[1], pl[2], pl[3]);
-        } else {
-          *reinterpret_cast<uint2*>(Uh + off) = make_uint2(ph[0], ph[1]);
-          *reinterpret_cast<uint2*>(Ul + off) = make_uint2(pl[0], pl[1]);
+          for (int q = 0; q < NKU / 2; ++q) {
+            const int sh = 16 * (e & 1);
+            ph[q] = ((h[2 * q][e >> 1] >> sh) & 0xffffu) | ((h[2 * q + 1][e >> 1] >> sh) << 16);
+            pl[q] = ((lo[2 * q][e >> 1] >> sh) & 0xffffu) | ((lo[2 * q + 1][e >> 1] >> sh) << 16);
+          }
+          const int off = tpos<2>(4 * ku_c4 + e, ku_r0);
+          if constexpr (NKU == 8) {
+            *reinterpret_cast<uint4*>(Uh + off) = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+            *reinterpret_cast<uint4*>(Ul + off) = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+          } else {
+            *reinterpret_cast<uint2*>(Uh + off) = make_uint2(ph[0], ph[1]);
+            *reinterpret_cast<uint2*>(Ul + off) = make_uint2(pl[0], pl[1]);
+          }
         }
       }
-    }
-    {
-      const int r = t % C, c4 = t / C;
-      Vs[r * PV + 4 * c4 + 0] = __uint_as_float(pv.x << 16);
-      Vs[r * PV + 4 * c4 + 1] = __uint_as_float(pv.x & 0xffff0000u);
-      Vs[r * PV + 4 * c4 + 2] = __uint_as_float(pv.y << 16);
-      Vs[r * PV + 4 * c4 + 3] = __uint_as_float(pv.y & 0xffff0000u);
-    }
-    if (t < DK) gs[t] = pg;
+      {
+        const int r = ct % C, c4 = ct / C;
+        Vs[r * PV + 4 * c4 + 0] = __uint_as_float(pv.x << 16);
+        Vs[r * PV + 4 * c4 + 1] = __uint_as_float(pv.x & 0xffff0000u);
+        Vs[r * PV + 4 * c4 + 2] = __uint_as_float(pv.y << 16);
+        Vs[r * PV + 4 * c4 + 3] = __uint_as_float(pv.y & 0xffff0000u);
+      }
+      if (ct < DK) gs[ct] = pg;
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) put_split_t(Sh, Sl, PK, 16 * (w * TPW + i), -S[i]);
+      for (int i = 0; i < TPW; ++i) put_split_t(Sh, Sl, PK, 16 * ((w & 3) * TPW + i), -S[i]);
+    }
     __syncthreads();
     if (c + 1 < nc) fetch(c + 1);
     prefetch(min(c + 2, nc - 1));
 
-    // Phase 1: R = V - (K o e^g) S and (Q o e^g)(-S), row tile w.
-    f32x4 ar, aq = zero4();
+    // Phase 1: chain waves R = V - (K o e^g) S, output waves (Q o e^g)(-S);
+    // row tile w & 3 each.
+    f32x4 acc = zero4();
+    if (chain) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ar[e] = Vs[(r0 + 4 * g + e) * PV + n];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 sh = frag(Sh, PK, 0, 32 * ks), sl = frag(Sl, PK, 0, 32 * ks);
-      ar = mfma_split3(kdh[ks], kdl[ks], sh, sl, ar);
-      aq = mfma_split3(qdh[ks], qdl[ks], sh, sl, aq);
+      for (int e = 0; e < 4; ++e) acc[e] = Vs[(r0 + 4 * g + e) * PV + n];
     }
-    put_split_t(Rh, Rl, PC, r0, ar);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      acc = mfma_split3(ah[ks], al[ks], frag(Sh, PK, 0, 32 * ks), frag(Sl, PK, 0, 32 * ks), acc);
+    if (chain) put_split_t(Rh, Rl, PC, r0, acc);
     __syncthreads();
 
     // Phase 2: Delta = T R, row tile w (T is lower triangular).
-    f32x4 ad = zero4();
+    if (chain) {
+      f32x4 ad = zero4();
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      if (ks <= w / 2)
-        ad = mfma_split3(tth[ks], ttl[ks], frag(Rh, PC, 0, 32 * ks), frag(Rl, PC, 0, 32 * ks), ad);
-    put_split_t(Dh, Dl, PC, r0, ad);
+      for (int ks = 0; ks < 2; ++ks)
+        if (ks <= (w & 3) / 2)
+          ad = mfma_split3(bh2[ks], bl2[ks], frag(Rh, PC, 0, 32 * ks), frag(Rl, PC, 0, 32 * ks), ad);
+      put_split_t(Dh, Dl, PC, r0, ad);
+    }
     __syncthreads();
 
-    // Phase 3: O = (Q o e^g) S + P Delta (row tile w), and
-    // S' = diag(e^{g_C}) S + (K o e^{g_C - g})^T Delta.
-    f32x4 ao = -aq;
+    // Phase 3: output waves O = (Q o e^g) S + P Delta (row tile w & 3); chain
+    // waves S' = diag(e^{g_C}) S + (K o e^{g_C - g})^T Delta.
+    if (!chain) {
+      f32x4 ao = -acc;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      if (ks <= w / 2)
-        ao = mfma_split3(pph[ks], ppl[ks], frag(Dh, PC, 0, 32 * ks), frag(Dl, PC, 0, 32 * ks), ao);
+      for (int ks = 0; ks < 2; ++ks)
+        if (ks <= (w & 3) / 2)
+          ao = mfma_split3(bh2[ks], bl2[ks], frag(Dh, PC, 0, 32 * ks), frag(Dl, PC, 0, 32 * ks), ao);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = r0 + 4 * g + e;
-      if (r < valid) put_out<OT>(o + (tok0 + r) * DV + j0 + n, ao[e]);
-    }
+      for (int e = 0; e < 4; ++e) {
+        const int r = r0 + 4 * g + e;
+        if (r < valid) put_out<OT>(o + (tok0 + r) * DV + j0 + n, ao[e]);
+      }
+    } else {
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int d0 = 16 * (w * TPW + i);
+      for (int i = 0; i < TPW; ++i) {
+        const int d0 = 16 * ((w & 3) * TPW + i);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[i][e] *= gs[d0 + 4 * g + e];
+        for (int e = 0; e < 4; ++e) S[i][e] *= gs[d0 + 4 * g + e];
 #pragma unroll
-      for (int ks = 0; ks < C / 32; ++ks)
-        S[i] = mfma_split3(fragT<2>(Uh, d0, 32 * ks), fragT<2>(Ul, d0, 32 * ks),
-                           frag(Dh, PC, 0, 32 * ks), frag(Dl, PC, 0, 32 * ks), S[i]);
+        for (int ks = 0; ks < C / 32; ++ks)
+          S[i] = mfma_split3(fragT<2>(Uh, d0, 32 * ks), fragT<2>(Ul, d0, 32 * ks),
+                             frag(Dh, PC, 0, 32 * ks), frag(Dl, PC, 0, 32 * ks), S[i]);
+      }
     }
     __syncthreads();
   }
-  if (S_final)
+  if (S_final && chain)
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const int d0 = 16 * (w * TPW + i) + 4 * g;
+      const int d0 = 16 * ((w & 3) * TPW + i) + 4 * g;
 #pragma unroll
       for (int e = 0; e < 4; ++e) S_final[((size_t)bh * DK + d0 + e) * DV + j0 + n] = S[i][e];
     }
@@ -536,7 +548,7 @@ hipError_t scan_t(const void* v, const float* S0, void* o, float* S_final, int L
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)ScanLds<DK>::bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(8 * (DV / NT) * ((bh + 7) / 8)), dim3(NTH), ScanLds<DK>::bytes, s,
+  hipLaunchKernelGGL(kern, dim3(8 * (DV / NT) * ((bh + 7) / 8)), dim3(SNTH), ScanLds<DK>::bytes, s,
                      static_cast<const bf16*>(v), S0, static_cast<OT*>(o), S_final, L, nc, bh, ws);
   return hipGetLastError();
 }
