@@ -332,7 +332,8 @@ __global__ __launch_bounds__(SNTH) void scan_kernel(const bf16* __restrict__ v,
   const int flat = blockIdx.x, xcd = flat & 7, sl = flat >> 3;
   const int j0 = (sl % (DV / NT)) * NT, bh = (sl / (DV / NT)) * 8 + xcd;
   if (bh >= nbh) return;
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
+  const int t = threadIdx.x, l = t & 63, n = l & 15, g = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   // Waves 0-3 carry the chain (R, Delta, the state); waves 4-7 form the
   // outputs.  Wave w of either kind owns chunk rows 16 (w & 3) .. + 15.
   const bool chain = w < 4;
@@ -375,6 +376,7 @@ __global__ __launch_bounds__(SNTH) void scan_kernel(const bf16* __restrict__ v,
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      if (ks > (w & 3) / 2) continue;  // T and P are lower triangular
       const int off = row * C + 32 * ks + 8 * g;
       nbh_[ks] = ld16(bb + off);
       nbl[ks] = ld16(bb + C * C + off);

@@ -66,6 +66,7 @@
 // once per chunk by the output waves while they stage the chunk, and kept in
 // LDS next to g, so the chain waves only multiply.
 
+#include "dn_buffer.h"
 #include "dn_common.h"
 #include "dn_launch.h"
 #include "dn_mfma.h"
@@ -147,24 +148,6 @@ __device__ __forceinline__ void put_split(uint16_t* base, int plane, int off, f3
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
-
-// Buffer descriptor over `bytes` bytes from `base` (raw access, stride 0): a
-// read at byte offset >= bytes returns zero.  Both arguments are the same in
-// every lane; reading them from the first lane keeps the descriptor in
-// scalar registers.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // (readfirstlane returns a signed int: each half goes through uint32_t so
-  // that widening it never sign-extends into the other half.)
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((hi << 32) | lo), (short)0,
-                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
-}
-__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
 
 template <int C, int DK, int DV, typename OT, bool GATED>
 __global__ __launch_bounds__(512) void scan_kernel(
