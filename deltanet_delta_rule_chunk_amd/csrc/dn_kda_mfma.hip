@@ -59,11 +59,14 @@ constexpr int PNTHR = 1024;
 
 // 8 consecutive values as split pairs, one 16-byte store per plane (i is a
 // multiple of 8).
+// The stores are non-temporal: the workspace is read back only by the scan,
+// a whole kernel later.
 __device__ __forceinline__ void put_split8(uint16_t* hi, int plane, int i, const float* x) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   bf16x8 h, o;
   lds64::split8(x, h, o);
-  *reinterpret_cast<bf16x8*>(hi + i) = h;
-  *reinterpret_cast<bf16x8*>(hi + plane + i) = o;
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, h), reinterpret_cast<u32x4*>(hi + i));
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, o), reinterpret_cast<u32x4*>(hi + plane + i));
 }
 
 // x as a split pair: hi[i] = bf16(x), hi[plane + i] = bf16(x - hi[i]).
@@ -134,25 +137,49 @@ __global__ __launch_bounds__(PNTHR) __attribute__((amdgpu_waves_per_eu(8))) void
   float* gam = reinterpret_cast<float*>(Ku + 2 * C * DK);  // e^{g_C}
   const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
 
-  {  // q and k rows, 16 bytes per load, into the bf16 tiles as they are
+  // Every global read of the chunk (q and k rows, 16 bytes per load, the
+  // decays, beta) is issued before the first of them is waited on.
+  constexpr int NKQ = (C * DK / 8 + PNTHR - 1) / PNTHR, NA = C * DK / PNTHR;
+  static_assert(C * DK % PNTHR == 0 && (C * DK / 8) % 64 == 0, "load shape");
+  uint4 xk[NKQ], xq[NKQ];
+  float av[NA];
+  {
     const uint4* kg = reinterpret_cast<const uint4*>(k + tok0 * DK);
     const uint4* qg = reinterpret_cast<const uint4*>(q + tok0 * DK);
-    for (int e8 = t; e8 < C * DK / 8; e8 += PNTHR) {
-      const int r = e8 / (DK / 8), c8 = e8 % (DK / 8), rc = min(r, valid - 1);
-      uint4 xk = kg[rc * (DK / 8) + c8], xq = qg[rc * (DK / 8) + c8];
-      if (r >= valid) xk = xq = make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(Ks + r * LDH + 8 * c8) = xk;
-      *reinterpret_cast<uint4*>(Qs + r * LDH + 8 * c8) = xq;
+#pragma unroll
+    for (int it = 0; it < NKQ; ++it) {
+      const int e8 = t + PNTHR * it, r = e8 / (DK / 8), c8 = e8 % (DK / 8);
+      const int rc = min(r, valid - 1);
+      if (e8 < C * DK / 8) {
+        xk[it] = kg[rc * (DK / 8) + c8];
+        xq[it] = qg[rc * (DK / 8) + c8];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NA; ++it) {
+      const int e = t + PNTHR * it, r = e / DK, j = e % DK;
+      av[it] = alpha[(tok0 + min(r, valid - 1)) * DK + j];
     }
   }
-  if (t < C) bs[t] = t < valid ? beta[tok0 + t] : 0.f;
+  const float bt = t < C && t < valid ? beta[tok0 + t] : 0.f;
+#pragma unroll
+  for (int it = 0; it < NKQ; ++it) {  // into the bf16 tiles as they are (rows past L: zeros)
+    const int e8 = t + PNTHR * it, r = e8 / (DK / 8), c8 = e8 % (DK / 8);
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    if (e8 < C * DK / 8) {
+      *reinterpret_cast<uint4*>(Ks + r * LDH + 8 * c8) = r < valid ? xk[it] : z;
+      *reinterpret_cast<uint4*>(Qs + r * LDH + 8 * c8) = r < valid ? xq[it] : z;
+    }
+  }
+  if (t < C) bs[t] = bt;
   // g: the log-decays of the whole tile at once (coalesced), then a prefix
   // sum down each dimension's column: 8 segments of 8 rows per column, each
   // summed in registers, then offset by the totals of the segments above it
   // (parked in the inverse's scratch, which is used only later).
-  for (int e = t; e < C * DK; e += PNTHR) {
-    const int r = e / DK, j = e % DK;
-    Gs[r * LD + j] = r < valid ? log_decay(alpha[(tok0 + r) * DK + j]) : 0.f;
+#pragma unroll
+  for (int it = 0; it < NA; ++it) {
+    const int e = t + PNTHR * it, r = e / DK, j = e % DK;
+    Gs[r * LD + j] = r < valid ? log_decay(av[it]) : 0.f;
   }
   __syncthreads();
   {
