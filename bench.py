@@ -40,7 +40,8 @@ CSRC = os.path.join(ROOT, "deltanet_delta_rule_chunk_amd", "csrc")
 # Source files each kernel is built from (a change to any of them makes the
 # committed counter measurement stale).
 KERNEL_SOURCES = {
-    "chunk_scan": ["dn_scan_mfma.hip", "dn_ktile.h", "dn_tfrag.h", "dn_mfma.h", "dn_common.h"],
+    "chunk_scan": ["dn_scan_mfma.hip", "dn_buffer.h", "dn_ktile.h", "dn_tfrag.h", "dn_mfma.h",
+                   "dn_common.h"],
     "chunk_prep": ["dn_chunk_mfma.hip", "dn_features.h", "dn_ktile.h", "dn_tfrag.h", "dn_mfma.h",
                    "dn_common.h"],
     "decode": ["dn_decode.hip", "dn_features.h", "dn_common.h"],
