@@ -58,8 +58,9 @@ struct RowTile {
   static constexpr int N = C * CPR / NTHR;        // rows per thread
   static_assert(N == 2 || N == 4, "rows per thread");
   uint4 x[N];
-  __device__ __forceinline__ int row0() const { return N * (threadIdx.x / CPR); }
-  __device__ __forceinline__ int chunk() const { return threadIdx.x % CPR; }
+  int tid = threadIdx.x;  // the thread's index among the NTHR that share the tile
+  __device__ __forceinline__ int row0() const { return N * (tid / CPR); }
+  __device__ __forceinline__ int chunk() const { return tid % CPR; }
   __device__ __forceinline__ void load(const bf16* src, int valid) {
     const uint4* s = reinterpret_cast<const uint4*>(src);
 #pragma unroll
@@ -103,8 +104,9 @@ struct SqTile {
   static constexpr int CPR = C / 4;
   static constexpr int N = C * CPR / NTH;  // 4
   float4 x[N];
-  __device__ __forceinline__ int row0() const { return N * (threadIdx.x / CPR); }
-  __device__ __forceinline__ int chunk() const { return threadIdx.x % CPR; }
+  int tid = threadIdx.x;  // the thread's index among the NTH that share the tile
+  __device__ __forceinline__ int row0() const { return N * (tid / CPR); }
+  __device__ __forceinline__ int chunk() const { return tid % CPR; }
   __device__ __forceinline__ void load(const float* src) {
     const float4* s = reinterpret_cast<const float4*>(src);
 #pragma unroll
@@ -405,10 +407,14 @@ struct BwdLds {
 
 // Three barriers per chunk, as in the forward pass: the next chunk (in
 // reverse order) is deposited during phase 3, with Q^T, K^T and dO^T, which
-// phase 3 still reads, double buffered.
+// phase 3 still reads, double buffered.  Eight waves: waves 0-3 carry the
+// chain (the three phases' products, the exit gradient and the stores);
+// waves 4-7 load the next chunk, prefetch the one after into L2 and deposit
+// the next chunk into LDS, off the chain's path.
+constexpr int BNTH = 2 * NTH;
 
 template <int DK, int DV>
-__global__ __launch_bounds__(NTH) void bwd_scan_kernel(
+__global__ __launch_bounds__(BNTH) void bwd_scan_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ beta,
     const float* __restrict__ dO, const float* __restrict__ dS_final, float* __restrict__ dv,
     float* __restrict__ dS0, int L, int nc, int nbh, float* __restrict__ ws) {
@@ -435,8 +441,12 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
 
   int j0, bh;
   if (!slice_of(DV / NT, nbh, j0, bh)) return;
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
-  float* ot = bs + C + w * 256;                         // this wave's store tile
+  const int l = threadIdx.x & 63, n = l & 15, g = l >> 4;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool chain = wid < 4;
+  const int w = wid & 3;                 // a chain wave's row tile and state tiles
+  const int t = threadIdx.x & (NTH - 1);  // index within the role (loads, deposits)
+  float* ot = bs + C + w * 256;          // a chain wave's store tile
 
   f32x4 G[TPW];
 #pragma unroll
@@ -444,11 +454,12 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
     const int d0 = 16 * (w * TPW + i) + 4 * g;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      G[i][e] = dS_final ? dS_final[((size_t)bh * DK + d0 + e) * DV + j0 + n] : 0.f;
+      G[i][e] = dS_final && chain ? dS_final[((size_t)bh * DK + d0 + e) * DV + j0 + n] : 0.f;
   }
 
   RowTile<DK> tq, tk;
   SqTile tm, tx;
+  tq.tid = tk.tid = tm.tid = tx.tid = t;
   float4 pd;
   float pb = 0.f;
   auto fetch = [&](int cc) {
@@ -522,8 +533,10 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
     }
   };
 
-  fetch(nc - 1);
-  deposit((nc - 1) & 1);
+  if (!chain) {
+    fetch(nc - 1);
+    deposit((nc - 1) & 1);
+  }
   for (int c = nc - 1; c >= 0; --c) {
 #pragma unroll
     for (int i = 0; i < NPF; ++i) pf_acc ^= pf_val[i];
@@ -536,20 +549,25 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
     const uint16_t* Oc = Oh + bb * 2 * NT * PC;
     const uint16_t* Ocl = Oc + NT * PC;
     // The exit gradient: out to the workspace and into LDS.
+    if (chain) {
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int d0 = 16 * (w * TPW + i);
-      store_rows16(ot, G[i], blk + W.G() + (size_t)d0 * DV + j0, DV);
-      put_split_t(Gh, Gl, PK, d0, G[i]);
+      for (int i = 0; i < TPW; ++i) {
+        const int d0 = 16 * (w * TPW + i);
+        store_rows16(ot, G[i], blk + W.G() + (size_t)d0 * DV + j0, DV);
+        put_split_t(Gh, Gl, PK, d0, G[i]);
+      }
     }
     __syncthreads();
-    if (c > 0) fetch(c - 1);
-    prefetch(max(c - 2, 0));
+    if (!chain) {
+      if (c > 0) fetch(c - 1);
+      prefetch(max(c - 2, 0));
+    }
 
     // Phase 1: dDelta = M^T dO + K G', row tile w (M^T is upper triangular,
     // so the first product starts at the tile's first row).
     const int r0 = 16 * w;
     f32x4 acc = zero4();
+    if (chain) {
 #pragma unroll
     for (int ks = w / 2; ks < C / 32; ++ks)
       acc = mfma_split3(fragT<2>(Mh, r0, 32 * ks), fragT<2>(Ml, r0, 32 * ks), frag(Oc, PC, 0, 32 * ks),
@@ -560,9 +578,11 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
                         acc);
     store_rows16(ot, acc, blk + W.dD() + (size_t)r0 * DV + j0, DV);
     put_split_t(Eh, El, PC, r0, acc);
+    }
     __syncthreads();
 
     // Phase 2: dR = diag(beta) X^T dDelta, row tile w; dv = dR.
+    if (chain) {
     acc = zero4();
 #pragma unroll
     for (int ks = w / 2; ks < C / 32; ++ks)
@@ -572,10 +592,12 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
     for (int e = 0; e < 4; ++e) acc[e] *= bs[r0 + 4 * g + e];
     store_rows16(ot, acc, dv + (tok0 + r0) * DV + j0, DV, valid - r0);
     put_split_t(Fh, Fl, PC, r0, -acc);
+    }
     __syncthreads();
 
     // Phase 3: G = G' + Q^T dO - K^T dR; meanwhile the next chunk goes into
     // LDS (K rows, M^T, X^T and beta were last read in phases 1 and 2).
+    if (chain) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int d0 = 16 * (w * TPW + i);
@@ -587,9 +609,11 @@ __global__ __launch_bounds__(NTH) void bwd_scan_kernel(
                            G[i]);
       }
     }
-    if (c > 0) deposit((c - 1) & 1);
+    } else if (c > 0) {
+      deposit((c - 1) & 1);
+    }
   }
-  if (dS0)
+  if (dS0 && chain)
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int d0 = 16 * (w * TPW + i) + 4 * g;
@@ -1001,7 +1025,7 @@ hipError_t bwd_t(const void* q, const void* k, const float* beta, const float* d
   auto* kern = &bwd_scan_kernel<DK, DV>;
   hipError_t e = set_lds(kern, BwdLds<DK>::bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, slice_grid(DV / NT, bh), dim3(NTH), BwdLds<DK>::bytes, s,
+  hipLaunchKernelGGL(kern, slice_grid(DV / NT, bh), dim3(BNTH), BwdLds<DK>::bytes, s,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k), beta, dO, dS_final,
                      dv, dS0, L, nc, bh, ws);
   return hipGetLastError();
