@@ -237,9 +237,14 @@ struct FwdLds {
 
 // Three barriers per chunk: phase 1 (R) | phase 2 (Delta) | phase 3 (state
 // update).  The next chunk's operands are deposited during phase 3: by then
-// only K^T (double buffered) and Delta are still being read.
+// only K^T (double buffered) and Delta are still being read.  Eight waves:
+// waves 0-3 carry the chain (the products, the entering state and the
+// stores), waves 4-7 load the next chunk, prefetch the one after into L2 and
+// deposit the next chunk into LDS.
+constexpr int FNTH = 2 * NTH;
+
 template <int DK, int DV>
-__global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ k,
+__global__ __launch_bounds__(FNTH) void fwd_scan_kernel(const bf16* __restrict__ k,
                                                        const bf16* __restrict__ v,
                                                        const float* __restrict__ beta,
                                                        const float* __restrict__ S0, int L,
@@ -264,19 +269,25 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
 
   int j0, bh;
   if (!slice_of(DV / NT, nbh, j0, bh)) return;
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
-  float* ot = bs + C + w * 256;                         // this wave's store tile
+  const int l = threadIdx.x & 63, n = l & 15, g = l >> 4;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool chain = wid < 4;
+  const int w = wid & 3;                 // a chain wave's row tile and state tiles
+  const int t = threadIdx.x & (NTH - 1);  // index within the role (loads, deposits)
+  float* ot = bs + C + w * 256;          // a chain wave's store tile
 
   f32x4 S[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int d0 = 16 * (w * TPW + i) + 4 * g;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) S[i][e] = S0 ? S0[((size_t)bh * DK + d0 + e) * DV + j0 + n] : 0.f;
+    for (int e = 0; e < 4; ++e)
+      S[i][e] = S0 && chain ? S0[((size_t)bh * DK + d0 + e) * DV + j0 + n] : 0.f;
   }
 
   RowTile<DK> tk;
   SqTile tx;
+  tk.tid = tx.tid = t;
   uint2 pv;
   float pb = 0.f;
   auto fetch = [&](int cc) {
@@ -335,26 +346,33 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
     }
   };
 
-  fetch(0);
-  deposit(0);
+  if (!chain) {
+    fetch(0);
+    deposit(0);
+  }
   for (int c = 0; c < nc; ++c) {
     float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
 #pragma unroll
     for (int i = 0; i < NPF; ++i) pf_acc ^= pf_val[i];
     // The entering state: out to the workspace and into LDS.
+    if (chain) {
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int d0 = 16 * (w * TPW + i);
-      store_rows16(ot, S[i], blk + W.S() + (size_t)d0 * DV + j0, DV);
-      put_split_t(Sh, Sl, PK, d0, -S[i]);
+      for (int i = 0; i < TPW; ++i) {
+        const int d0 = 16 * (w * TPW + i);
+        store_rows16(ot, S[i], blk + W.S() + (size_t)d0 * DV + j0, DV);
+        put_split_t(Sh, Sl, PK, d0, -S[i]);
+      }
     }
     __syncthreads();
-    if (c + 1 < nc) fetch(c + 1);
-    prefetch(min(c + 2, nc - 1));
+    if (!chain) {
+      if (c + 1 < nc) fetch(c + 1);
+      prefetch(min(c + 2, nc - 1));
+    }
 
     // Phase 1: R = V - K S, row tile w.
     const int r0 = 16 * w;
     f32x4 acc;
+    if (chain) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] = Vs[(r0 + 4 * g + e) * PV + n];
 #pragma unroll
@@ -366,10 +384,12 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
     for (int e = 0; e < 4; ++e) rb[e] = acc[e] * bs[r0 + 4 * g + e];
     store_rows16(ot, acc, blk + W.R() + (size_t)r0 * DV + j0, DV);
     put_split_t(Rh, Rl, PC, r0, rb);
+    }
     __syncthreads();
 
     // Phase 2: Delta = X diag(beta) R, row tile w (X is lower triangular, so
     // the contraction stops at the tile's last row).
+    if (chain) {
     acc = zero4();
 #pragma unroll
     for (int ks = 0; ks <= w / 2; ++ks)
@@ -377,18 +397,22 @@ __global__ __launch_bounds__(NTH) void fwd_scan_kernel(const bf16* __restrict__ 
                         frag(Rl, PC, 0, 32 * ks), acc);
     store_rows16(ot, acc, blk + W.D() + (size_t)r0 * DV + j0, DV);
     put_split_t(Dh, Dl, PC, r0, acc);
+    }
     __syncthreads();
 
     // Phase 3: S += K^T Delta; meanwhile the next chunk goes into LDS (K
     // rows, X, V and beta were last read in phases 1 and 2).
-    const uint16_t* Kc = Kt + (c & 1) * DK * PC;
+    if (chain) {
+      const uint16_t* Kc = Kt + (c & 1) * DK * PC;
 #pragma unroll
-    for (int i = 0; i < TPW; ++i)
+      for (int i = 0; i < TPW; ++i)
 #pragma unroll
-      for (int ks = 0; ks < C / 32; ++ks)
-        S[i] = mfma_split2(fragT<3>(Kc, 16 * (w * TPW + i), 32 * ks), frag(Dh, PC, 0, 32 * ks),
-                           frag(Dl, PC, 0, 32 * ks), S[i]);
-    if (c + 1 < nc) deposit((c + 1) & 1);
+        for (int ks = 0; ks < C / 32; ++ks)
+          S[i] = mfma_split2(fragT<3>(Kc, 16 * (w * TPW + i), 32 * ks), frag(Dh, PC, 0, 32 * ks),
+                             frag(Dl, PC, 0, 32 * ks), S[i]);
+    } else if (c + 1 < nc) {
+      deposit((c + 1) & 1);
+    }
   }
 #pragma unroll
   for (int i = 0; i < NPF; ++i) pf_acc ^= pf_val[i];
@@ -1012,7 +1036,7 @@ hipError_t fwd_t(const void* k, const void* v, const float* beta, const float* S
   auto* kern = &fwd_scan_kernel<DK, DV>;
   hipError_t e = set_lds(kern, FwdLds<DK>::bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, slice_grid(DV / NT, bh), dim3(NTH), FwdLds<DK>::bytes, s,
+  hipLaunchKernelGGL(kern, slice_grid(DV / NT, bh), dim3(FNTH), FwdLds<DK>::bytes, s,
                      static_cast<const bf16*>(k), static_cast<const bf16*>(v), beta, S0, L, nc, bh,
                      ws);
   return hipGetLastError();
