@@ -232,7 +232,7 @@ struct FwdLds {
   static constexpr size_t halves = (size_t)C * PK + 2 * (size_t)DK * PC + 2 * (size_t)C * PC +
                                    2 * (size_t)NT * PK + 4 * (size_t)NT * PC;
   static constexpr size_t bytes =
-      halves * 2 + ((size_t)C * PV + C + 4 * 16 * 16) * sizeof(float);
+      halves * 2 + ((size_t)C * PV + C) * sizeof(float);
 };
 
 // Three barriers per chunk: phase 1 (R) | phase 2 (Delta) | phase 3 (state
@@ -274,7 +274,6 @@ __global__ __launch_bounds__(FNTH) void fwd_scan_kernel(const bf16* __restrict__
   const bool chain = wid < 4;
   const int w = wid & 3;                 // a chain wave's row tile and state tiles
   const int t = threadIdx.x & (NTH - 1);  // index within the role (loads, deposits)
-  float* ot = bs + C + w * 256;          // a chain wave's store tile
 
   f32x4 S[TPW];
 #pragma unroll
@@ -359,7 +358,7 @@ __global__ __launch_bounds__(FNTH) void fwd_scan_kernel(const bf16* __restrict__
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
         const int d0 = 16 * (w * TPW + i);
-        store_rows16(ot, S[i], blk + W.S() + (size_t)d0 * DV + j0, DV);
+        store_tile16(S[i], blk + W.S() + (size_t)d0 * DV + j0, DV);
         put_split_t(Sh, Sl, PK, d0, -S[i]);
       }
     }
@@ -382,7 +381,7 @@ __global__ __launch_bounds__(FNTH) void fwd_scan_kernel(const bf16* __restrict__
     f32x4 rb;
 #pragma unroll
     for (int e = 0; e < 4; ++e) rb[e] = acc[e] * bs[r0 + 4 * g + e];
-    store_rows16(ot, acc, blk + W.R() + (size_t)r0 * DV + j0, DV);
+    store_tile16(acc, blk + W.R() + (size_t)r0 * DV + j0, DV);
     put_split_t(Rh, Rl, PC, r0, rb);
     }
     __syncthreads();
@@ -395,7 +394,7 @@ __global__ __launch_bounds__(FNTH) void fwd_scan_kernel(const bf16* __restrict__
     for (int ks = 0; ks <= w / 2; ++ks)
       acc = mfma_split3(frag(Xh, PC, r0, 32 * ks), frag(Xl, PC, r0, 32 * ks), frag(Rh, PC, 0, 32 * ks),
                         frag(Rl, PC, 0, 32 * ks), acc);
-    store_rows16(ot, acc, blk + W.D() + (size_t)r0 * DV + j0, DV);
+    store_tile16(acc, blk + W.D() + (size_t)r0 * DV + j0, DV);
     put_split_t(Dh, Dl, PC, r0, acc);
     }
     __syncthreads();
@@ -425,7 +424,7 @@ struct BwdLds {
   static constexpr int PK = DK + 8;
   static constexpr size_t halves = (size_t)C * PK + 4 * (size_t)DK * PC + 4 * (size_t)C * PC +
                                    2 * (size_t)NT * PK + 8 * (size_t)NT * PC;
-  static constexpr size_t bytes = halves * 2 + ((size_t)C + 4 * 16 * 16) * sizeof(float);
+  static constexpr size_t bytes = halves * 2 + (size_t)C * sizeof(float);
   static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
@@ -470,7 +469,6 @@ __global__ __launch_bounds__(BNTH) void bwd_scan_kernel(
   const bool chain = wid < 4;
   const int w = wid & 3;                 // a chain wave's row tile and state tiles
   const int t = threadIdx.x & (NTH - 1);  // index within the role (loads, deposits)
-  float* ot = bs + C + w * 256;          // a chain wave's store tile
 
   f32x4 G[TPW];
 #pragma unroll
@@ -577,7 +575,7 @@ __global__ __launch_bounds__(BNTH) void bwd_scan_kernel(
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
         const int d0 = 16 * (w * TPW + i);
-        store_rows16(ot, G[i], blk + W.G() + (size_t)d0 * DV + j0, DV);
+        store_tile16(G[i], blk + W.G() + (size_t)d0 * DV + j0, DV);
         put_split_t(Gh, Gl, PK, d0, G[i]);
       }
     }
@@ -600,7 +598,7 @@ __global__ __launch_bounds__(BNTH) void bwd_scan_kernel(
     for (int ks = 0; ks < DK / 32; ++ks)
       acc = mfma_split2(frag(Kb, PK, r0, 32 * ks), frag(Gh, PK, 0, 32 * ks), frag(Gl, PK, 0, 32 * ks),
                         acc);
-    store_rows16(ot, acc, blk + W.dD() + (size_t)r0 * DV + j0, DV);
+    store_tile16(acc, blk + W.dD() + (size_t)r0 * DV + j0, DV);
     put_split_t(Eh, El, PC, r0, acc);
     }
     __syncthreads();
@@ -614,7 +612,7 @@ __global__ __launch_bounds__(BNTH) void bwd_scan_kernel(
                         frag(El, PC, 0, 32 * ks), acc);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] *= bs[r0 + 4 * g + e];
-    store_rows16(ot, acc, dv + (tok0 + r0) * DV + j0, DV, valid - r0);
+    store_tile16(acc, dv + (tok0 + r0) * DV + j0, DV, valid - r0);
     put_split_t(Fh, Fl, PC, r0, -acc);
     }
     __syncthreads();

@@ -52,22 +52,18 @@ __device__ __forceinline__ bf16x8 fragT(const uint16_t* a, int r0, int kb) {
 }
 
 // Stores a D tile (lane: column l % 16, rows 4 (l / 16) + e) into a
-// row-major fp32 matrix (dst = the tile's top-left element, row pitch ld) as
-// 16-byte row pieces, passing it through the wave's own 16 x 16 fp32 LDS tile
-// `ot` (1 KB; 16-byte groups XOR-swizzled by row).  A wave's LDS operations
-// complete in order, so the tile needs no barrier.  Rows at or past `rows`
-// are not stored.
-__device__ __forceinline__ void store_rows16(float* ot, f32x4 v, float* dst, size_t ld,
-                                             int rows = 16) {
+// row-major fp32 matrix (dst = the tile's top-left element, row pitch ld)
+// straight from the accumulators: four 4-byte stores per lane, each covering
+// 64 contiguous bytes of four rows.  (Going through an LDS tile to store 16
+// bytes per lane instead put an LDS round trip on the caller's path and was
+// measured slower.)  Rows at or past `rows` are not stored.
+__device__ __forceinline__ void store_tile16(f32x4 v, float* dst, size_t ld, int rows = 16) {
   const int l = threadIdx.x & 63, n = l & 15, g = l >> 4;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int row = 4 * g + e;
-    ot[row * 16 + ((((n >> 2) ^ (row >> 2)) & 3) << 2) + (n & 3)] = v[e];
+    if (row < rows) dst[row * ld + n] = v[e];
   }
-  const int row = l >> 2, cg = l & 3;
-  const f32x4 val = *reinterpret_cast<const f32x4*>(ot + row * 16 + (((cg ^ (row >> 2)) & 3) << 2));
-  if (row < rows) *reinterpret_cast<f32x4*>(dst + row * ld + 4 * cg) = val;
 }
 
 // 8 fp32 values -> split bf16x8 pair.
