@@ -52,17 +52,12 @@ hipError_t launch_bwd_scan_mfma(int d_k, int d_v, const void* q, const void* k,
                                 float* dv, float* dS0, int L, int nc, int bh, float* ws,
                                 hipStream_t stream);
 
-// The C x C gradients (dM, W into the workspace; dbeta) on the matrix cores
-// (bf16 k), after the two state scans.  nc >= 1.
-hipError_t launch_cc_grad_mfma(int d_k, int d_v, const void* k, const float* beta,
-                               const float* dO, float* dbeta, int L, int nc, int bh, float* ws,
-                               hipStream_t stream);
-
-// dQ and dK on the matrix cores (bf16 q, k), from the workspace the scans and
-// the C x C gradient kernel have filled.  nc >= 1.
-hipError_t launch_qk_grad_mfma(int d_k, int d_v, const void* q, const void* k,
-                               const float* dO, const float* dv, float* dq, float* dk, int L,
-                               int nc, int bh, const float* ws, hipStream_t stream);
+// The C x C gradients (dbeta) and dQ, dK in one kernel on the matrix cores
+// (bf16 q, k), from the workspace the two state scans have filled.  nc >= 1.
+hipError_t launch_grad_mfma(int d_k, int d_v, const void* q, const void* k, const float* beta,
+                            const float* dO, const float* dv, float* dq, float* dk,
+                            float* dbeta, int L, int nc, int bh, const float* ws,
+                            hipStream_t stream);
 
 }  // namespace bwd
 }  // namespace dn

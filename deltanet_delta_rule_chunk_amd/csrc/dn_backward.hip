@@ -567,26 +567,26 @@ hipError_t launch_t(const BwdArgs& a) {
   }
   prof_mark(kSlotBwdScan, true, a.stream);
   if (nc > 0) {
-    prof_mark(kSlotBwdCc, false, a.stream);
     if constexpr (kMatrixCores) {
-      DN_TRY(launch_cc_grad_mfma(DK, DV, k, a.beta, a.dO, a.dbeta, a.L, nc, bh, ws, a.stream));
+      // One kernel for the C x C gradients and dQ, dK (profiled as the latter).
+      prof_mark(kSlotBwdQk, false, a.stream);
+      DN_TRY(launch_grad_mfma(DK, DV, q, k, a.beta, a.dO, a.dv, a.dq, a.dk, a.dbeta, a.L, nc, bh,
+                              ws, a.stream));
+      prof_mark(kSlotBwdQk, true, a.stream);
     } else {
+      prof_mark(kSlotBwdCc, false, a.stream);
       DN_TRY(set_smem(&cc_grad_kernel<DK, DV, IT>, CcSmem<DK>::bytes));
       hipLaunchKernelGGL((cc_grad_kernel<DK, DV, IT>), chunks, blk, CcSmem<DK>::bytes, a.stream, k,
                          a.beta, a.dO, a.dbeta, a.L, ws);
       DN_TRY(hipGetLastError());
-    }
-    prof_mark(kSlotBwdCc, true, a.stream);
-    prof_mark(kSlotBwdQk, false, a.stream);
-    if constexpr (kMatrixCores) {
-      DN_TRY(launch_qk_grad_mfma(DK, DV, q, k, a.dO, a.dv, a.dq, a.dk, a.L, nc, bh, ws, a.stream));
-    } else {
+      prof_mark(kSlotBwdCc, true, a.stream);
+      prof_mark(kSlotBwdQk, false, a.stream);
       DN_TRY(set_smem(&qk_grad_kernel<DK, DV, IT>, QkSmem<DK>::bytes));
       hipLaunchKernelGGL((qk_grad_kernel<DK, DV, IT>), chunks, blk, QkSmem<DK>::bytes, a.stream, q,
                          k, a.dO, a.dv, a.dq, a.dk, a.L, ws);
       DN_TRY(hipGetLastError());
+      prof_mark(kSlotBwdQk, true, a.stream);
     }
-    prof_mark(kSlotBwdQk, true, a.stream);
   }
   return hipSuccess;
 }

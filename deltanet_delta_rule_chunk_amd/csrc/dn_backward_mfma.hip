@@ -647,51 +647,262 @@ __global__ __launch_bounds__(BNTH) void bwd_scan_kernel(
   if (nc < 0) dv[0] = __uint_as_float(pf_acc);
 }
 
-// ---- dQ and dK -------------------------------------------------------------
-// One workgroup of d_k / 16 waves per (chunk, head); wave w owns column tile
-// w (16 columns of d_k) of both outputs, for all four 16-row tiles.
-//   phase A, over d_v in passes of HJ columns:  dQ += dO S^T,
-//            dK += Delta G'^T - dR S^T.  dO, Delta and -dR rows are staged
-//            split in LDS; the S and G' rows are each wave's own B operands,
-//            loaded from the workspace straight into registers.
-//   phase B, over chunk rows:  dQ += dM K,  dK += dM^T Q + (W + W^T) K,
-//            with dM and W staged in fp32 and split per fragment, K and Q
-//            staged transposed.
+// ---- the chunk's C x C gradients, then dQ and dK, in one kernel ------------
+// One workgroup of d_k / 16 waves per (chunk, head), so that dM and W, and
+// the chunk's dO and Delta rows, never make a round trip through HBM between
+// the two halves.
+//   1. waves 0-3, row tile w of every C x C product, over d_v in passes of
+//      32 columns: dM = tril(dO Delta^T) and dT = tril(dDelta R^T), all four
+//      operands staged split in LDS (the Delta and R rows are the B operands
+//      as stored);
+//   2. waves 0-3: dbeta_i = sum_a X_ai dT_ai; Y = X^T dX with dX = dT diag(beta)
+//      (both operands gathered from fp32 LDS columns and split);
+//      dA = -Y X^T (strictly lower) and W = diag(beta) dA; the Gram tiles
+//      K K^T (exact bf16 products) give dbeta_r += sum_{i<r} dA_ri (k_r . k_i);
+//      dM and W wait in registers, then go into LDS as fp32;
+//   3. every wave owns column tile w (16 columns of d_k) of both outputs, for
+//      all four 16-row tiles; over d_v in passes of 32 columns:
+//      dQ += dO S^T, dK += Delta G'^T - dR S^T, with dO, Delta and -dR rows
+//      staged split in LDS and the S and G' rows each wave's own B operands,
+//      loaded from the workspace straight into registers;
+//   4. over chunk rows: dQ += dM K,  dK += dM^T Q + (W + W^T) K, with dM and W
+//      split per fragment, K and Q staged transposed.
+// LDS: dM and W (fp32) at the start, from step 2's end; the other arrays of
+// steps 3 and 4 after them; steps 1 and 2 use the space from the start
+// (about 72 KB at d_k = 128, two workgroups per CU).
 template <int DK>
-struct QkLds {
-  static constexpr int HJ = 64;
+struct GradLds {
+  static constexpr int HJ = 32;  // d_v columns per pass (steps 1 and 3)
   static constexpr int PJ = HJ + 8;
   static constexpr int PF = C + 4;
-  static constexpr size_t a_bytes = 6 * (size_t)C * PJ * 2;
-  static constexpr size_t b_bytes = 2 * (size_t)DK * PC * 2 + 2 * (size_t)C * PF * sizeof(float);
-  static constexpr size_t bytes = a_bytes > b_bytes ? a_bytes : b_bytes;
+  static constexpr int PK = DK + 8;
+  static constexpr size_t mw = 2 * (size_t)C * PF * sizeof(float);         // dM, W
+  static constexpr size_t s1 = 8 * (size_t)C * PJ * 2;                     // step 1 staging
+  static constexpr size_t s2 = 2 * (size_t)C * PF * sizeof(float) + 2 * (size_t)C * sizeof(float) +
+                               (size_t)C * PK * 2;                         // X, dT/Y, beta, K rows
+  static constexpr size_t s3 = mw + 6 * (size_t)C * PJ * 2;               // + dO, Delta, -dR
+  static constexpr size_t s4 = mw + 2 * (size_t)DK * PC * 2;              // + K^T, Q^T
+  static constexpr size_t m12 = s1 > s2 ? s1 : s2, m34 = s3 > s4 ? s3 : s4;
+  static constexpr size_t bytes = m12 > m34 ? m12 : m34;
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(DK * 4) void qk_grad_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ dO,
-    const float* __restrict__ dv, float* __restrict__ dq, float* __restrict__ dk, int L,
-    const float* __restrict__ ws) {
-  using LD = QkLds<DK>;
-  constexpr int HJ = LD::HJ < DV ? LD::HJ : DV, PJ = LD::PJ, PF = LD::PF;
+__global__ __launch_bounds__(DK * 4) void grad_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ beta,
+    const float* __restrict__ dO, const float* __restrict__ dv, float* __restrict__ dq,
+    float* __restrict__ dk, float* __restrict__ dbeta, int L, const float* __restrict__ ws) {
+  using LD = GradLds<DK>;
+  constexpr int HJ = LD::HJ < DV ? LD::HJ : DV, PJ = LD::PJ, PF = LD::PF, PK = LD::PK;
   constexpr Ws W{DK, DV};
   constexpr int TPW = 1, NTQ = DK * 4;
-  constexpr int KS = HJ / 32;
+  static_assert(NTQ >= 4 * 64, "four waves for the C x C products");
   extern __shared__ uint4 lds_u4[];
   const int c = blockIdx.x, bh = blockIdx.y, nc = gridDim.x;
   const int valid = min(C, L - c * C);
   const size_t tok0 = (size_t)bh * L + (size_t)c * C;
   const float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
+  const int t = threadIdx.x, l = t & 63, n = l & 15, g = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const bool ccw = w < 4;  // the waves of steps 1 and 2
+  const int r0 = 16 * w;
+  float* Ms = reinterpret_cast<float*>(lds_u4);  // dM [C][PF], from step 2's end
+  float* Wm = Ms + C * PF;                        // W  [C][PF]
+  uint16_t* U = reinterpret_cast<uint16_t*>(Wm + C * PF);  // steps 3 and 4
 
+  // ---- step 1 -----------------------------------------------------------------
+  f32x4 am[4], at[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) am[ct] = at[ct] = zero4();
+  {
+    uint16_t* Oh = reinterpret_cast<uint16_t*>(lds_u4);
+    uint16_t* Ol = Oh + C * PJ;
+    uint16_t* Dh = Ol + C * PJ;
+    uint16_t* Dl = Dh + C * PJ;
+    uint16_t* Eh = Dl + C * PJ;
+    uint16_t* El = Eh + C * PJ;
+    uint16_t* Rh = El + C * PJ;
+    uint16_t* Rl = Rh + C * PJ;
+    for (int h = 0; h < DV; h += HJ) {
+      if (h > 0) __syncthreads();
+#pragma unroll
+      for (int p = 0; p < C * HJ / 4 / NTQ; ++p) {
+        const int f = t + p * NTQ, r = f / (HJ / 4), c4 = f % (HJ / 4);
+        const size_t wo = (size_t)r * DV + h + 4 * c4;
+        float4 xo = *reinterpret_cast<const float4*>(dO + (tok0 + min(r, valid - 1)) * DV + h + 4 * c4);
+        if (r >= valid) xo = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 xd = *reinterpret_cast<const float4*>(blk + W.D() + wo);
+        const float4 xe = *reinterpret_cast<const float4*>(blk + W.dD() + wo);
+        const float4 xr = *reinterpret_cast<const float4*>(blk + W.R() + wo);
+        const int o = r * PJ + 4 * c4;
+        uint2 hh, ll;
+        split4(xo, hh, ll);
+        *reinterpret_cast<uint2*>(Oh + o) = hh;
+        *reinterpret_cast<uint2*>(Ol + o) = ll;
+        split4(xd, hh, ll);
+        *reinterpret_cast<uint2*>(Dh + o) = hh;
+        *reinterpret_cast<uint2*>(Dl + o) = ll;
+        split4(xe, hh, ll);
+        *reinterpret_cast<uint2*>(Eh + o) = hh;
+        *reinterpret_cast<uint2*>(El + o) = ll;
+        split4(xr, hh, ll);
+        *reinterpret_cast<uint2*>(Rh + o) = hh;
+        *reinterpret_cast<uint2*>(Rl + o) = ll;
+      }
+      __syncthreads();
+      if (ccw) {
+#pragma unroll
+        for (int ks = 0; ks < HJ / 32; ++ks) {
+          const bf16x8 oh = frag(Oh, PJ, r0, 32 * ks), ol = frag(Ol, PJ, r0, 32 * ks);
+          const bf16x8 eh = frag(Eh, PJ, r0, 32 * ks), el = frag(El, PJ, r0, 32 * ks);
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            if (ct > w) continue;  // above the diagonal
+            am[ct] = mfma_split3(oh, ol, frag(Dh, PJ, 16 * ct, 32 * ks), frag(Dl, PJ, 16 * ct, 32 * ks),
+                                 am[ct]);
+            at[ct] = mfma_split3(eh, el, frag(Rh, PJ, 16 * ct, 32 * ks), frag(Rl, PJ, 16 * ct, 32 * ks),
+                                 at[ct]);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- step 2 -----------------------------------------------------------------
+  f32x4 wv[4];  // this wave's row tile of W (columns 16 ct .. 16 ct + 15)
+  {
+    float* Xs = reinterpret_cast<float*>(lds_u4);  // X    [C][PF]
+    float* Ts = Xs + C * PF;                        // dT   [C][PF], then Y
+    float* Ys = Ts;
+    float* bs = Ts + C * PF;
+    float* dbs = bs + C;
+    uint16_t* Kb = reinterpret_cast<uint16_t*>(dbs + C);  // K rows [C][PK]
+    {
+      RowTile<DK, NTQ> tk;
+      tk.load(k + tok0 * DK, valid);
+#pragma unroll
+      for (int p = 0; p < C * C / 4 / NTQ; ++p) {
+        const int f = t + p * NTQ, r = f / (C / 4), c4 = f % (C / 4);
+        *reinterpret_cast<float4*>(Xs + r * PF + 4 * c4) =
+            *reinterpret_cast<const float4*>(blk + W.X() + r * C + 4 * c4);
+      }
+      if (t < C) bs[t] = t < valid ? beta[tok0 + t] : 0.f;
+      tk.put_rows(Kb);
+    }
+    if (ccw) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = r0 + 4 * g + e, i = 16 * ct + n;
+          Ts[r * PF + i] = i <= r ? at[ct][e] : 0.f;
+        }
+    }
+    __syncthreads();
+    if (t < C) {  // dbeta_i from T = X diag(beta)
+      float s = 0.f;
+      for (int a = t; a < C; ++a) s += Xs[a * PF + t] * Ts[a * PF + t];
+      dbs[t] = s;
+    }
+    // Y = X^T dX, row tile w: Y_ab = sum_{r >= a} X_ra dT_rb beta_b (held in
+    // registers until every wave is done reading dT, then written over it).
+    f32x4 yt[4];
+    if (ccw) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        f32x4& y = yt[ct];
+        y = zero4();
+        const int a = r0 + n, b = 16 * ct + n;
+        const float bb = bs[b];
+#pragma unroll
+        for (int ks = w / 2; ks < C / 32; ++ks) {
+          float xa[8], xb[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 32 * ks + 8 * g + e;
+            xa[e] = Xs[r * PF + a];
+            xb[e] = Ts[r * PF + b] * bb;
+          }
+          bf16x8 ah, al, bh_, bl;
+          split8(xa, ah, al);
+          split8(xb, bh_, bl);
+          y = mfma_split3(ah, al, bh_, bl, y);
+        }
+      }
+    }
+    __syncthreads();
+    if (ccw) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Ys[(r0 + 4 * g + e) * PF + 16 * ct + n] = yt[ct][e];
+    }
+    __syncthreads();
+    // dA = -Y X^T (strictly lower), W = diag(beta) dA, and the dbeta row sums
+    // against the Gram tiles.
+    if (ccw) {
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        f32x4 acc = zero4(), gr = zero4();
+        if (ct <= w) {
+#pragma unroll
+          for (int ks = 0; ks <= ct / 2; ++ks) {
+            const float* ya = Ys + (r0 + n) * PF + 32 * ks + 8 * g;
+            const float* xb = Xs + (16 * ct + n) * PF + 32 * ks + 8 * g;
+            float va[8], vb[8];
+            *reinterpret_cast<float4*>(va) = *reinterpret_cast<const float4*>(ya);
+            *reinterpret_cast<float4*>(va + 4) = *reinterpret_cast<const float4*>(ya + 4);
+            *reinterpret_cast<float4*>(vb) = *reinterpret_cast<const float4*>(xb);
+            *reinterpret_cast<float4*>(vb + 4) = *reinterpret_cast<const float4*>(xb + 4);
+            bf16x8 ah, al, bh_, bl;
+            split8(va, ah, al);
+            split8(vb, bh_, bl);
+            acc = mfma_split3(ah, al, bh_, bl, acc);
+          }
+#pragma unroll
+          for (int ks = 0; ks < DK / 32; ++ks)
+            gr = mfma16(frag(Kb, PK, r0, 32 * ks), frag(Kb, PK, 16 * ct, 32 * ks), gr);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = r0 + 4 * g + e, i = 16 * ct + n;
+          const float da = i < r ? -acc[e] : 0.f;
+          wv[ct][e] = bs[r] * da;
+          rs[e] += da * gr[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = rs[e];
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+        const int r = r0 + 4 * g + e;
+        if (n == 0 && r < valid) dbeta[tok0 + r] = dbs[r] + v;
+      }
+    }
+  }
+  __syncthreads();  // X, dT/Y and the K rows are dead: dM and W go over them
+  if (ccw) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = r0 + 4 * g + e, i = 16 * ct + n;
+        Ms[r * PF + i] = i <= r ? am[ct][e] : 0.f;
+        Wm[r * PF + i] = wv[ct][e];
+      }
+  }
+
+  // ---- step 3 -----------------------------------------------------------------
+  constexpr int KS = HJ / 32;
   f32x4 aq[4][TPW], ak[4][TPW];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int i = 0; i < TPW; ++i) aq[rt][i] = ak[rt][i] = zero4();
-
-  {  // phase A
-    uint16_t* Oh = reinterpret_cast<uint16_t*>(lds_u4);
+  {
+    uint16_t* Oh = U;
     uint16_t* Ol = Oh + C * PJ;
     uint16_t* Dh = Ol + C * PJ;
     uint16_t* Dl = Dh + C * PJ;
@@ -709,7 +920,7 @@ __global__ __launch_bounds__(DK * 4) void qk_grad_kernel(
           gv[i][ks][0] = *reinterpret_cast<const float4*>(blk + W.G() + o);
           gv[i][ks][1] = *reinterpret_cast<const float4*>(blk + W.G() + o + 4);
         }
-      if (h > 0) __syncthreads();
+      __syncthreads();  // the previous pass (or step 2) is done with this space
 #pragma unroll
       for (int p = 0; p < C * HJ / 4 / NTQ; ++p) {
         const int f = t + p * NTQ, r = f / (HJ / 4), c4 = f % (HJ / 4);
@@ -755,23 +966,15 @@ __global__ __launch_bounds__(DK * 4) void qk_grad_kernel(
     }
   }
   __syncthreads();
-  {  // phase B
-    uint16_t* Kt = reinterpret_cast<uint16_t*>(lds_u4);
+
+  // ---- step 4 -----------------------------------------------------------------
+  {
+    uint16_t* Kt = U;
     uint16_t* Qt = Kt + DK * PC;
-    float* Ms = reinterpret_cast<float*>(Qt + DK * PC);
-    float* Wm = Ms + C * PF;
     {
       RowTile<DK, NTQ> tq, tk;
       tq.load(q + tok0 * DK, valid);
       tk.load(k + tok0 * DK, valid);
-#pragma unroll
-      for (int p = 0; p < C * C / 4 / NTQ; ++p) {
-        const int f = t + p * NTQ, r = f / (C / 4), c4 = f % (C / 4);
-        *reinterpret_cast<float4*>(Ms + r * PF + 4 * c4) =
-            *reinterpret_cast<const float4*>(blk + W.dM() + r * C + 4 * c4);
-        *reinterpret_cast<float4*>(Wm + r * PF + 4 * c4) =
-            *reinterpret_cast<const float4*>(blk + W.W() + r * C + 4 * c4);
-      }
       tq.put_cols(Qt);
       tk.put_cols(Kt);
     }
@@ -820,208 +1023,6 @@ __global__ __launch_bounds__(DK * 4) void qk_grad_kernel(
       }
 }
 
-// ---- the C x C gradients: dM, dT, dA, W and dbeta -------------------------
-// One 4-wave workgroup per (chunk, head); wave w owns row tile w of every
-// C x C product.
-//   phase 1, over d_v in passes of 32 columns: dM = tril(dO Delta^T) and
-//            dT = tril(dDelta R^T), all four operands staged split in LDS
-//            (the Delta and R rows are the B operands as stored);
-//   phase 2: dbeta_i = sum_a X_ai dT_ai; Y = X^T dX with dX = dT diag(beta)
-//            (both operands gathered from fp32 LDS columns and split);
-//            dA = -Y X^T (strictly lower) and W = diag(beta) dA; the Gram
-//            tiles K K^T (exact bf16 products) give
-//            dbeta_r += sum_{i<r} dA_ri (k_r . k_i).
-template <int DK>
-struct CcLds {
-  static constexpr int HJ = 32;  // d_v columns per phase-1 pass
-  static constexpr int PJ = HJ + 8;
-  static constexpr int PF = C + 4;
-  static constexpr int PK = DK + 8;
-  static constexpr size_t p1 = 8 * (size_t)C * PJ * 2;
-  static constexpr size_t p2 = 2 * (size_t)C * PF * sizeof(float) + (size_t)C * PK * 2 +
-                               2 * (size_t)C * sizeof(float);
-  // ~52 KB at d_k = 128: three workgroups share a CU.
-  static constexpr size_t bytes = p1 > p2 ? p1 : p2;
-};
-
-template <int DK, int DV>
-__global__ __launch_bounds__(NTH) void cc_grad_kernel(const bf16* __restrict__ k,
-                                                      const float* __restrict__ beta,
-                                                      const float* __restrict__ dO,
-                                                      float* __restrict__ dbeta, int L,
-                                                      float* __restrict__ ws) {
-  using LD = CcLds<DK>;
-  constexpr int HJ = LD::HJ < DV ? LD::HJ : DV, PJ = LD::PJ, PF = LD::PF, PK = LD::PK;
-  constexpr Ws W{DK, DV};
-  extern __shared__ uint4 lds_u4[];
-  const int c = blockIdx.x, bh = blockIdx.y, nc = gridDim.x;
-  const int valid = min(C, L - c * C);
-  const size_t tok0 = (size_t)bh * L + (size_t)c * C;
-  float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
-  const int r0 = 16 * w;
-
-  f32x4 am[4], at[4];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) am[ct] = at[ct] = zero4();
-  {  // phase 1
-    uint16_t* Oh = reinterpret_cast<uint16_t*>(lds_u4);
-    uint16_t* Ol = Oh + C * PJ;
-    uint16_t* Dh = Ol + C * PJ;
-    uint16_t* Dl = Dh + C * PJ;
-    uint16_t* Eh = Dl + C * PJ;
-    uint16_t* El = Eh + C * PJ;
-    uint16_t* Rh = El + C * PJ;
-    uint16_t* Rl = Rh + C * PJ;
-    for (int h = 0; h < DV; h += HJ) {
-      if (h > 0) __syncthreads();
-#pragma unroll
-      for (int p = 0; p < C * HJ / 4 / NTH; ++p) {
-        const int f = t + p * NTH, r = f / (HJ / 4), c4 = f % (HJ / 4);
-        const size_t wo = (size_t)r * DV + h + 4 * c4;
-        float4 xo = *reinterpret_cast<const float4*>(dO + (tok0 + min(r, valid - 1)) * DV + h + 4 * c4);
-        if (r >= valid) xo = make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 xd = *reinterpret_cast<const float4*>(blk + W.D() + wo);
-        const float4 xe = *reinterpret_cast<const float4*>(blk + W.dD() + wo);
-        const float4 xr = *reinterpret_cast<const float4*>(blk + W.R() + wo);
-        const int o = r * PJ + 4 * c4;
-        uint2 hh, ll;
-        split4(xo, hh, ll);
-        *reinterpret_cast<uint2*>(Oh + o) = hh;
-        *reinterpret_cast<uint2*>(Ol + o) = ll;
-        split4(xd, hh, ll);
-        *reinterpret_cast<uint2*>(Dh + o) = hh;
-        *reinterpret_cast<uint2*>(Dl + o) = ll;
-        split4(xe, hh, ll);
-        *reinterpret_cast<uint2*>(Eh + o) = hh;
-        *reinterpret_cast<uint2*>(El + o) = ll;
-        split4(xr, hh, ll);
-        *reinterpret_cast<uint2*>(Rh + o) = hh;
-        *reinterpret_cast<uint2*>(Rl + o) = ll;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int ks = 0; ks < HJ / 32; ++ks) {
-        const bf16x8 oh = frag(Oh, PJ, r0, 32 * ks), ol = frag(Ol, PJ, r0, 32 * ks);
-        const bf16x8 eh = frag(Eh, PJ, r0, 32 * ks), el = frag(El, PJ, r0, 32 * ks);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          if (ct > w) continue;  // above the diagonal
-          am[ct] = mfma_split3(oh, ol, frag(Dh, PJ, 16 * ct, 32 * ks), frag(Dl, PJ, 16 * ct, 32 * ks),
-                               am[ct]);
-          at[ct] = mfma_split3(eh, el, frag(Rh, PJ, 16 * ct, 32 * ks), frag(Rl, PJ, 16 * ct, 32 * ks),
-                               at[ct]);
-        }
-      }
-    }
-  }
-  __syncthreads();
-  float* Xs = reinterpret_cast<float*>(lds_u4);  // X    [C][PF]
-  float* Ts = Xs + C * PF;                        // dT   [C][PF], then Y
-  float* Ys = Ts;
-  float* bs = Ts + C * PF;
-  float* dbs = bs + C;
-  uint16_t* Kb = reinterpret_cast<uint16_t*>(dbs + C);  // K rows [C][PK]
-  {
-    RowTile<DK> tk;
-    tk.load(k + tok0 * DK, valid);
-#pragma unroll
-    for (int p = 0; p < C * C / 4 / NTH; ++p) {
-      const int f = t + p * NTH, r = f / (C / 4), c4 = f % (C / 4);
-      *reinterpret_cast<float4*>(Xs + r * PF + 4 * c4) =
-          *reinterpret_cast<const float4*>(blk + W.X() + r * C + 4 * c4);
-    }
-    if (t < C) bs[t] = t < valid ? beta[tok0 + t] : 0.f;
-    tk.put_rows(Kb);
-  }
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = r0 + 4 * g + e, i = 16 * ct + n;
-      const float m = i <= r ? am[ct][e] : 0.f, d = i <= r ? at[ct][e] : 0.f;
-      blk[W.dM() + r * C + i] = m;
-      Ts[r * PF + i] = d;
-    }
-  __syncthreads();
-  if (t < C) {  // dbeta_i from T = X diag(beta)
-    float s = 0.f;
-    for (int a = t; a < C; ++a) s += Xs[a * PF + t] * Ts[a * PF + t];
-    dbs[t] = s;
-  }
-  // Y = X^T dX, row tile w: Y_ab = sum_{r >= a} X_ra dT_rb beta_b (held in
-  // registers until every wave is done reading dT, then written over it).
-  f32x4 yt[4];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    f32x4& y = yt[ct];
-    y = zero4();
-    const int a = r0 + n, b = 16 * ct + n;
-    const float bb = bs[b];
-#pragma unroll
-    for (int ks = w / 2; ks < C / 32; ++ks) {
-      float xa[8], xb[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 32 * ks + 8 * g + e;
-        xa[e] = Xs[r * PF + a];
-        xb[e] = Ts[r * PF + b] * bb;
-      }
-      bf16x8 ah, al, bh_, bl;
-      split8(xa, ah, al);
-      split8(xb, bh_, bl);
-      y = mfma_split3(ah, al, bh_, bl, y);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Ys[(r0 + 4 * g + e) * PF + 16 * ct + n] = yt[ct][e];
-  __syncthreads();
-  // dA = -Y X^T (strictly lower), W = diag(beta) dA, and the dbeta row sums
-  // against the Gram tiles.
-  float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    f32x4 acc = zero4(), gr = zero4();
-    if (ct <= w) {
-#pragma unroll
-      for (int ks = 0; ks <= ct / 2; ++ks) {
-        const float* ya = Ys + (r0 + n) * PF + 32 * ks + 8 * g;
-        const float* xb = Xs + (16 * ct + n) * PF + 32 * ks + 8 * g;
-        float va[8], vb[8];
-        *reinterpret_cast<float4*>(va) = *reinterpret_cast<const float4*>(ya);
-        *reinterpret_cast<float4*>(va + 4) = *reinterpret_cast<const float4*>(ya + 4);
-        *reinterpret_cast<float4*>(vb) = *reinterpret_cast<const float4*>(xb);
-        *reinterpret_cast<float4*>(vb + 4) = *reinterpret_cast<const float4*>(xb + 4);
-        bf16x8 ah, al, bh_, bl;
-        split8(va, ah, al);
-        split8(vb, bh_, bl);
-        acc = mfma_split3(ah, al, bh_, bl, acc);
-      }
-#pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks)
-        gr = mfma16(frag(Kb, PK, r0, 32 * ks), frag(Kb, PK, 16 * ct, 32 * ks), gr);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = r0 + 4 * g + e, i = 16 * ct + n;
-      const float da = i < r ? -acc[e] : 0.f;
-      blk[W.W() + r * C + i] = bs[r] * da;
-      rs[e] += da * gr[e];
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float v = rs[e];
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    const int r = r0 + 4 * g + e;
-    if (n == 0 && r < valid) dbeta[tok0 + r] = dbs[r] + v;
-  }
-}
-
 template <typename K>
 static hipError_t set_lds(K* kernel, size_t bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -1054,25 +1055,15 @@ hipError_t bwd_t(const void* q, const void* k, const float* beta, const float* d
 }
 
 template <int DK, int DV>
-hipError_t qk_t(const void* q, const void* k, const float* dO, const float* dv, float* dq,
-                float* dk, int L, int nc, int bh, const float* ws, hipStream_t s) {
-  auto* kern = &qk_grad_kernel<DK, DV>;
-  hipError_t e = set_lds(kern, QkLds<DK>::bytes);
+hipError_t grad_t(const void* q, const void* k, const float* beta, const float* dO,
+                  const float* dv, float* dq, float* dk, float* dbeta, int L, int nc, int bh,
+                  const float* ws, hipStream_t s) {
+  auto* kern = &grad_kernel<DK, DV>;
+  hipError_t e = set_lds(kern, GradLds<DK>::bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(nc, bh), dim3(DK * 4), QkLds<DK>::bytes, s,
-                     static_cast<const bf16*>(q), static_cast<const bf16*>(k), dO, dv, dq, dk, L,
-                     ws);
-  return hipGetLastError();
-}
-
-template <int DK, int DV>
-hipError_t cc_t(const void* k, const float* beta, const float* dO, float* dbeta, int L, int nc,
-                int bh, float* ws, hipStream_t s) {
-  auto* kern = &cc_grad_kernel<DK, DV>;
-  hipError_t e = set_lds(kern, CcLds<DK>::bytes);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(nc, bh), dim3(NTH), CcLds<DK>::bytes, s,
-                     static_cast<const bf16*>(k), beta, dO, dbeta, L, ws);
+  hipLaunchKernelGGL(kern, dim3(nc, bh), dim3(DK * 4), GradLds<DK>::bytes, s,
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k), beta, dO, dv, dq,
+                     dk, dbeta, L, ws);
   return hipGetLastError();
 }
 
@@ -1111,22 +1102,17 @@ hipError_t launch_bwd_scan_mfma(int d_k, int d_v, const void* q, const void* k,
   return mf::bwd_t<128, 128>(q, k, beta, dO, dS_final, dv, dS0, L, nc, bh, ws, stream);
 }
 
-hipError_t launch_qk_grad_mfma(int d_k, int d_v, const void* q, const void* k,
-                               const float* dO, const float* dv, float* dq, float* dk, int L,
-                               int nc, int bh, const float* ws, hipStream_t stream) {
-  if (d_k == 64 && d_v == 64) return mf::qk_t<64, 64>(q, k, dO, dv, dq, dk, L, nc, bh, ws, stream);
-  if (d_k == 64 && d_v == 128) return mf::qk_t<64, 128>(q, k, dO, dv, dq, dk, L, nc, bh, ws, stream);
-  if (d_k == 128 && d_v == 64) return mf::qk_t<128, 64>(q, k, dO, dv, dq, dk, L, nc, bh, ws, stream);
-  return mf::qk_t<128, 128>(q, k, dO, dv, dq, dk, L, nc, bh, ws, stream);
-}
-
-hipError_t launch_cc_grad_mfma(int d_k, int d_v, const void* k, const float* beta,
-                               const float* dO, float* dbeta, int L, int nc, int bh, float* ws,
-                               hipStream_t stream) {
-  if (d_k == 64 && d_v == 64) return mf::cc_t<64, 64>(k, beta, dO, dbeta, L, nc, bh, ws, stream);
-  if (d_k == 64 && d_v == 128) return mf::cc_t<64, 128>(k, beta, dO, dbeta, L, nc, bh, ws, stream);
-  if (d_k == 128 && d_v == 64) return mf::cc_t<128, 64>(k, beta, dO, dbeta, L, nc, bh, ws, stream);
-  return mf::cc_t<128, 128>(k, beta, dO, dbeta, L, nc, bh, ws, stream);
+hipError_t launch_grad_mfma(int d_k, int d_v, const void* q, const void* k, const float* beta,
+                            const float* dO, const float* dv, float* dq, float* dk,
+                            float* dbeta, int L, int nc, int bh, const float* ws,
+                            hipStream_t stream) {
+  if (d_k == 64 && d_v == 64)
+    return mf::grad_t<64, 64>(q, k, beta, dO, dv, dq, dk, dbeta, L, nc, bh, ws, stream);
+  if (d_k == 64 && d_v == 128)
+    return mf::grad_t<64, 128>(q, k, beta, dO, dv, dq, dk, dbeta, L, nc, bh, ws, stream);
+  if (d_k == 128 && d_v == 64)
+    return mf::grad_t<128, 64>(q, k, beta, dO, dv, dq, dk, dbeta, L, nc, bh, ws, stream);
+  return mf::grad_t<128, 128>(q, k, beta, dO, dv, dq, dk, dbeta, L, nc, bh, ws, stream);
 }
 
 hipError_t launch_prep_mfma(int d_k, int d_v, const void* q, const void* k, const float* beta,
