@@ -207,7 +207,11 @@ __global__ __launch_bounds__(NTH) void prep_kernel(const bf16* __restrict__ q,
     }
   }
   inv64::inverse<PF, PF>(As, Xs, scratch);
-  for (int e = t; e < C * C; e += NTH) blk[W.X() + e] = Xs[(e / C) * PF + e % C];
+  for (int e4 = t; e4 < C * C / 4; e4 += NTH) {  // 16-byte stores of X
+    const int r = e4 / (C / 4), c0 = 4 * (e4 % (C / 4));
+    const float* x = Xs + r * PF + c0;
+    *reinterpret_cast<float4*>(blk + W.X() + r * C + c0) = make_float4(x[0], x[1], x[2], x[3]);
+  }
 }
 
 // The state passes' workgroups: a 1-D grid of 8 * ns * ceil(nbh / 8), where
