@@ -59,14 +59,13 @@ constexpr int PNTHR = 1024;
 
 // 8 consecutive values as split pairs, one 16-byte store per plane (i is a
 // multiple of 8).
-// The stores are non-temporal: the workspace is read back only by the scan,
-// a whole kernel later.
+// (Non-temporal stores here measured the same time but 1.8 GB more HBM
+// writes per long-context launch.)
 __device__ __forceinline__ void put_split8(uint16_t* hi, int plane, int i, const float* x) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   bf16x8 h, o;
   lds64::split8(x, h, o);
-  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, h), reinterpret_cast<u32x4*>(hi + i));
-  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, o), reinterpret_cast<u32x4*>(hi + plane + i));
+  *reinterpret_cast<bf16x8*>(hi + i) = h;
+  *reinterpret_cast<bf16x8*>(hi + plane + i) = o;
 }
 
 // x as a split pair: hi[i] = bf16(x), hi[plane + i] = bf16(x - hi[i]).
