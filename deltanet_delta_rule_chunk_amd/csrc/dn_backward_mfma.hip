@@ -651,43 +651,41 @@ __global__ __launch_bounds__(BNTH) void bwd_scan_kernel(
   if (nc < 0) dv[0] = __uint_as_float(pf_acc);
 }
 
-// ---- the chunk's C x C gradients, then dQ and dK, in one kernel ------------
-// One workgroup of d_k / 16 waves per (chunk, head), so that dM and W, and
-// the chunk's dO and Delta rows, never make a round trip through HBM between
-// the two halves.
-//   1. waves 0-3, row tile w of every C x C product, over d_v in passes of
-//      32 columns: dM = tril(dO Delta^T) and dT = tril(dDelta R^T), all four
-//      operands staged split in LDS (the Delta and R rows are the B operands
-//      as stored);
-//   2. waves 0-3: dbeta_i = sum_a X_ai dT_ai; Y = X^T dX with dX = dT diag(beta)
-//      (both operands gathered from fp32 LDS columns and split);
-//      dA = -Y X^T (strictly lower) and W = diag(beta) dA; the Gram tiles
-//      K K^T (exact bf16 products) give dbeta_r += sum_{i<r} dA_ri (k_r . k_i);
-//      dM and W wait in registers, then go into LDS as fp32;
-//   3. every wave owns column tile w (16 columns of d_k) of both outputs, for
-//      all four 16-row tiles; over d_v in passes of 32 columns:
-//      dQ += dO S^T, dK += Delta G'^T - dR S^T, with dO, Delta and -dR rows
-//      staged split in LDS and the S and G' rows each wave's own B operands,
-//      loaded from the workspace straight into registers;
-//   4. over chunk rows: dQ += dM K,  dK += dM^T Q + (W + W^T) K, with dM and W
-//      split per fragment, K and Q staged transposed.
-// LDS: dM and W (fp32) at the start, from step 2's end; the other arrays of
-// steps 3 and 4 after them; steps 1 and 2 use the space from the start
-// (about 72 KB at d_k = 128, two workgroups per CU).
+// ---- the chunk's C x C gradients and dQ, dK in one kernel ------------------
+// One workgroup of d_k / 16 waves per (chunk, head), so that dM and W never
+// make a round trip through HBM and every row of dO, Delta, dDelta, R and
+// dR is read once.
+//   passes over d_v, 32 columns each: dO, Delta, dDelta, R and -dR staged
+//      split in LDS; the S and G' rows of the pass are each wave's own B
+//      operands, loaded from the workspace straight into registers.  Per pass:
+//        - the C x C products dM = tril(dO Delta^T), dT = tril(dDelta R^T):
+//          wave w takes row tile w % 4; with eight waves the pair w, w + 4
+//          splits its column tiles, 0-1 and 2-3;
+//        - dQ += dO S^T, dK += Delta G'^T - dR S^T: every wave owns column
+//          tile w (16 columns of d_k) of both outputs, for all four 16-row
+//          tiles;
+//   then dbeta_i = sum_a X_ai dT_ai; Y = X^T dX with dX = dT diag(beta) (both
+//      operands gathered from fp32 LDS columns and split); dA = -Y X^T
+//      (strictly lower) and W = diag(beta) dA; the Gram tiles K K^T (exact
+//      bf16 products) give dbeta_r += sum_{i<r} dA_ri (k_r . k_i) -- the same
+//      row and column tiles per wave as the C x C products; dM and W go into
+//      LDS as fp32;
+//   then over chunk rows: dQ += dM K,  dK += dM^T Q + (W + W^T) K, with dM and
+//      W split per fragment, K and Q staged transposed.
+// LDS (about 72 KB at d_k = 128, two workgroups per CU): the passes' staging,
+// then X, dT/Y, beta and the K rows, then dM and W with K^T and Q^T.
 template <int DK>
 struct GradLds {
-  static constexpr int HJ = 32;  // d_v columns per pass (steps 1 and 3)
+  static constexpr int HJ = 32;  // d_v columns per pass
   static constexpr int PJ = HJ + 8;
   static constexpr int PF = C + 4;
   static constexpr int PK = DK + 8;
-  static constexpr size_t mw = 2 * (size_t)C * PF * sizeof(float);         // dM, W
-  static constexpr size_t s1 = 8 * (size_t)C * PJ * 2;                     // step 1 staging
-  static constexpr size_t s2 = 2 * (size_t)C * PF * sizeof(float) + 2 * (size_t)C * sizeof(float) +
-                               (size_t)C * PK * 2;                         // X, dT/Y, beta, K rows
-  static constexpr size_t s3 = mw + 6 * (size_t)C * PJ * 2;               // + dO, Delta, -dR
-  static constexpr size_t s4 = mw + 2 * (size_t)DK * PC * 2;              // + K^T, Q^T
-  static constexpr size_t m12 = s1 > s2 ? s1 : s2, m34 = s3 > s4 ? s3 : s4;
-  static constexpr size_t bytes = m12 > m34 ? m12 : m34;
+  static constexpr size_t s1 = 10 * (size_t)C * PJ * 2;                   // five split operands
+  static constexpr size_t s2 = 2 * (size_t)C * PF * sizeof(float) + 3 * (size_t)C * sizeof(float) +
+                               (size_t)C * PK * 2;  // X, dT/Y, beta, dbeta, sums, K rows
+  static constexpr size_t s3 = 2 * (size_t)C * PF * sizeof(float) + 2 * (size_t)DK * PC * 2;  // dM, W, K^T, Q^T
+  static constexpr size_t m12 = s1 > s2 ? s1 : s2;
+  static constexpr size_t bytes = m12 > s3 ? m12 : s3;
 };
 
 template <int DK, int DV>
@@ -698,8 +696,11 @@ __global__ __launch_bounds__(DK * 4) void grad_kernel(
   using LD = GradLds<DK>;
   constexpr int HJ = LD::HJ < DV ? LD::HJ : DV, PJ = LD::PJ, PF = LD::PF, PK = LD::PK;
   constexpr Ws W{DK, DV};
-  constexpr int TPW = 1, NTQ = DK * 4;
+  constexpr int NTQ = DK * 4;
   static_assert(NTQ >= 4 * 64, "four waves for the C x C products");
+  constexpr bool kPairs = NTQ >= 8 * 64;
+  constexpr int NCW = kPairs ? 2 : 4;  // C x C column tiles per wave
+  constexpr int KS = HJ / 32;
   extern __shared__ uint4 lds_u4[];
   const int c = blockIdx.x, bh = blockIdx.y, nc = gridDim.x;
   const int valid = min(C, L - c * C);
@@ -707,36 +708,49 @@ __global__ __launch_bounds__(DK * 4) void grad_kernel(
   const float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
   const int t = threadIdx.x, l = t & 63, n = l & 15, g = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const bool ccw = w < 4;  // the waves of steps 1 and 2
-  const int r0 = 16 * w;
-  float* Ms = reinterpret_cast<float*>(lds_u4);  // dM [C][PF], from step 2's end
-  float* Wm = Ms + C * PF;                        // W  [C][PF]
-  uint16_t* U = reinterpret_cast<uint16_t*>(Wm + C * PF);  // steps 3 and 4
+  const int rt = w & 3, r0 = 16 * rt, half = kPairs ? w >> 2 : 0;
+  auto ctile = [&](int j) { return kPairs ? 2 * half + j : j; };  // this wave's column tiles
 
-  // ---- step 1 -----------------------------------------------------------------
-  f32x4 am[4], at[4];
+  // ---- passes over d_v ----------------------------------------------------------
+  f32x4 am[NCW], at[NCW], aq[4], ak[4];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) am[ct] = at[ct] = zero4();
+  for (int j = 0; j < NCW; ++j) am[j] = at[j] = zero4();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) aq[i] = ak[i] = zero4();
   {
-    uint16_t* Oh = reinterpret_cast<uint16_t*>(lds_u4);
+    uint16_t* Oh = reinterpret_cast<uint16_t*>(lds_u4);  // dO
     uint16_t* Ol = Oh + C * PJ;
-    uint16_t* Dh = Ol + C * PJ;
+    uint16_t* Dh = Ol + C * PJ;                           // Delta
     uint16_t* Dl = Dh + C * PJ;
-    uint16_t* Eh = Dl + C * PJ;
+    uint16_t* Eh = Dl + C * PJ;                           // dDelta
     uint16_t* El = Eh + C * PJ;
-    uint16_t* Rh = El + C * PJ;
+    uint16_t* Rh = El + C * PJ;                           // R
     uint16_t* Rl = Rh + C * PJ;
+    uint16_t* Fh = Rl + C * PJ;                           // -dR
+    uint16_t* Fl = Fh + C * PJ;
     for (int h = 0; h < DV; h += HJ) {
-      if (h > 0) __syncthreads();
+      float4 sv[KS][2], gv[KS][2];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const size_t o = (size_t)(16 * w + n) * DV + h + 32 * ks + 8 * g;
+        sv[ks][0] = *reinterpret_cast<const float4*>(blk + W.S() + o);
+        sv[ks][1] = *reinterpret_cast<const float4*>(blk + W.S() + o + 4);
+        gv[ks][0] = *reinterpret_cast<const float4*>(blk + W.G() + o);
+        gv[ks][1] = *reinterpret_cast<const float4*>(blk + W.G() + o + 4);
+      }
+      if (h > 0) __syncthreads();  // the previous pass is done with the staging
 #pragma unroll
       for (int p = 0; p < C * HJ / 4 / NTQ; ++p) {
         const int f = t + p * NTQ, r = f / (HJ / 4), c4 = f % (HJ / 4);
         const size_t wo = (size_t)r * DV + h + 4 * c4;
-        float4 xo = *reinterpret_cast<const float4*>(dO + (tok0 + min(r, valid - 1)) * DV + h + 4 * c4);
-        if (r >= valid) xo = make_float4(0.f, 0.f, 0.f, 0.f);
+        const size_t go = (tok0 + min(r, valid - 1)) * DV + h + 4 * c4;
+        float4 xo = *reinterpret_cast<const float4*>(dO + go);
+        float4 xf = *reinterpret_cast<const float4*>(dv + go);
         const float4 xd = *reinterpret_cast<const float4*>(blk + W.D() + wo);
         const float4 xe = *reinterpret_cast<const float4*>(blk + W.dD() + wo);
         const float4 xr = *reinterpret_cast<const float4*>(blk + W.R() + wo);
+        if (r >= valid) xo = xf = make_float4(0.f, 0.f, 0.f, 0.f);
+        xf = make_float4(-xf.x, -xf.y, -xf.z, -xf.w);
         const int o = r * PJ + 4 * c4;
         uint2 hh, ll;
         split4(xo, hh, ll);
@@ -751,36 +765,57 @@ __global__ __launch_bounds__(DK * 4) void grad_kernel(
         split4(xr, hh, ll);
         *reinterpret_cast<uint2*>(Rh + o) = hh;
         *reinterpret_cast<uint2*>(Rl + o) = ll;
+        split4(xf, hh, ll);
+        *reinterpret_cast<uint2*>(Fh + o) = hh;
+        *reinterpret_cast<uint2*>(Fl + o) = ll;
       }
       __syncthreads();
-      if (ccw) {
 #pragma unroll
-        for (int ks = 0; ks < HJ / 32; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
+        // The C x C products of row tile rt (column tiles above the diagonal
+        // are zero and skipped).
+        if (ctile(0) <= rt) {
           const bf16x8 oh = frag(Oh, PJ, r0, 32 * ks), ol = frag(Ol, PJ, r0, 32 * ks);
           const bf16x8 eh = frag(Eh, PJ, r0, 32 * ks), el = frag(El, PJ, r0, 32 * ks);
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct) {
-            if (ct > w) continue;  // above the diagonal
-            am[ct] = mfma_split3(oh, ol, frag(Dh, PJ, 16 * ct, 32 * ks), frag(Dl, PJ, 16 * ct, 32 * ks),
-                                 am[ct]);
-            at[ct] = mfma_split3(eh, el, frag(Rh, PJ, 16 * ct, 32 * ks), frag(Rl, PJ, 16 * ct, 32 * ks),
-                                 at[ct]);
+          for (int j = 0; j < NCW; ++j) {
+            const int ct = ctile(j);
+            if (ct > rt) continue;
+            am[j] = mfma_split3(oh, ol, frag(Dh, PJ, 16 * ct, 32 * ks), frag(Dl, PJ, 16 * ct, 32 * ks),
+                                am[j]);
+            at[j] = mfma_split3(eh, el, frag(Rh, PJ, 16 * ct, 32 * ks), frag(Rl, PJ, 16 * ct, 32 * ks),
+                                at[j]);
           }
+        }
+        // dQ += dO S^T, dK += Delta G'^T - dR S^T, column tile w.
+        uint2 h0, l0, h1, l1;
+        split4(sv[ks][0], h0, l0);
+        split4(sv[ks][1], h1, l1);
+        const bf16x8 sh = as_bf16x8(h0, h1), sl = as_bf16x8(l0, l1);
+        split4(gv[ks][0], h0, l0);
+        split4(gv[ks][1], h1, l1);
+        const bf16x8 gh = as_bf16x8(h0, h1), gl = as_bf16x8(l0, l1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          aq[i] = mfma_split3(frag(Oh, PJ, 16 * i, 32 * ks), frag(Ol, PJ, 16 * i, 32 * ks), sh, sl, aq[i]);
+          ak[i] = mfma_split3(frag(Dh, PJ, 16 * i, 32 * ks), frag(Dl, PJ, 16 * i, 32 * ks), gh, gl, ak[i]);
+          ak[i] = mfma_split3(frag(Fh, PJ, 16 * i, 32 * ks), frag(Fl, PJ, 16 * i, 32 * ks), sh, sl, ak[i]);
         }
       }
     }
   }
   __syncthreads();
 
-  // ---- step 2 -----------------------------------------------------------------
-  f32x4 wv[4];  // this wave's row tile of W (columns 16 ct .. 16 ct + 15)
+  // ---- dbeta, Y, dA, W ----------------------------------------------------------
+  f32x4 wv[NCW];  // this wave's tiles of W
   {
     float* Xs = reinterpret_cast<float*>(lds_u4);  // X    [C][PF]
     float* Ts = Xs + C * PF;                        // dT   [C][PF], then Y
     float* Ys = Ts;
     float* bs = Ts + C * PF;
     float* dbs = bs + C;
-    uint16_t* Kb = reinterpret_cast<uint16_t*>(dbs + C);  // K rows [C][PK]
+    float* rsb = dbs + C;                                 // the partner waves' dbeta sums
+    uint16_t* Kb = reinterpret_cast<uint16_t*>(rsb + C);  // K rows [C][PK]
     {
       RowTile<DK, NTQ> tk;
       tk.load(k + tok0 * DK, valid);
@@ -793,188 +828,116 @@ __global__ __launch_bounds__(DK * 4) void grad_kernel(
       if (t < C) bs[t] = t < valid ? beta[tok0 + t] : 0.f;
       tk.put_rows(Kb);
     }
-    if (ccw) {
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+    for (int j = 0; j < NCW; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = r0 + 4 * g + e, i = 16 * ct + n;
-          Ts[r * PF + i] = i <= r ? at[ct][e] : 0.f;
-        }
-    }
+      for (int e = 0; e < 4; ++e) {
+        const int r = r0 + 4 * g + e, i = 16 * ctile(j) + n;
+        Ts[r * PF + i] = i <= r ? at[j][e] : 0.f;
+      }
     __syncthreads();
     if (t < C) {  // dbeta_i from T = X diag(beta)
       float s = 0.f;
       for (int a = t; a < C; ++a) s += Xs[a * PF + t] * Ts[a * PF + t];
       dbs[t] = s;
     }
-    // Y = X^T dX, row tile w: Y_ab = sum_{r >= a} X_ra dT_rb beta_b (held in
-    // registers until every wave is done reading dT, then written over it).
-    f32x4 yt[4];
-    if (ccw) {
+    // Y = X^T dX: Y_ab = sum_{r >= a} X_ra dT_rb beta_b (held in registers
+    // until every wave is done reading dT, then written over it).
+    f32x4 yt[NCW];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        f32x4& y = yt[ct];
-        y = zero4();
-        const int a = r0 + n, b = 16 * ct + n;
-        const float bb = bs[b];
+    for (int j = 0; j < NCW; ++j) {
+      f32x4& y = yt[j];
+      y = zero4();
+      const int a = r0 + n, b = 16 * ctile(j) + n;
+      const float bb = bs[b];
 #pragma unroll
-        for (int ks = w / 2; ks < C / 32; ++ks) {
-          float xa[8], xb[8];
+      for (int ks = rt / 2; ks < C / 32; ++ks) {
+        float xa[8], xb[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 32 * ks + 8 * g + e;
-            xa[e] = Xs[r * PF + a];
-            xb[e] = Ts[r * PF + b] * bb;
-          }
-          bf16x8 ah, al, bh_, bl;
-          split8(xa, ah, al);
-          split8(xb, bh_, bl);
-          y = mfma_split3(ah, al, bh_, bl, y);
+        for (int e = 0; e < 8; ++e) {
+          const int r = 32 * ks + 8 * g + e;
+          xa[e] = Xs[r * PF + a];
+          xb[e] = Ts[r * PF + b] * bb;
         }
+        bf16x8 ah, al, bh_, bl;
+        split8(xa, ah, al);
+        split8(xb, bh_, bl);
+        y = mfma_split3(ah, al, bh_, bl, y);
       }
     }
     __syncthreads();
-    if (ccw) {
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+    for (int j = 0; j < NCW; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Ys[(r0 + 4 * g + e) * PF + 16 * ct + n] = yt[ct][e];
-    }
+      for (int e = 0; e < 4; ++e) Ys[(r0 + 4 * g + e) * PF + 16 * ctile(j) + n] = yt[j][e];
     __syncthreads();
     // dA = -Y X^T (strictly lower), W = diag(beta) dA, and the dbeta row sums
     // against the Gram tiles.
-    if (ccw) {
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        f32x4 acc = zero4(), gr = zero4();
-        if (ct <= w) {
+    for (int j = 0; j < NCW; ++j) {
+      const int ct = ctile(j);
+      f32x4 acc = zero4(), gr = zero4();
+      if (ct <= rt) {
 #pragma unroll
-          for (int ks = 0; ks <= ct / 2; ++ks) {
-            const float* ya = Ys + (r0 + n) * PF + 32 * ks + 8 * g;
-            const float* xb = Xs + (16 * ct + n) * PF + 32 * ks + 8 * g;
-            float va[8], vb[8];
-            *reinterpret_cast<float4*>(va) = *reinterpret_cast<const float4*>(ya);
-            *reinterpret_cast<float4*>(va + 4) = *reinterpret_cast<const float4*>(ya + 4);
-            *reinterpret_cast<float4*>(vb) = *reinterpret_cast<const float4*>(xb);
-            *reinterpret_cast<float4*>(vb + 4) = *reinterpret_cast<const float4*>(xb + 4);
-            bf16x8 ah, al, bh_, bl;
-            split8(va, ah, al);
-            split8(vb, bh_, bl);
-            acc = mfma_split3(ah, al, bh_, bl, acc);
-          }
-#pragma unroll
-          for (int ks = 0; ks < DK / 32; ++ks)
-            gr = mfma16(frag(Kb, PK, r0, 32 * ks), frag(Kb, PK, 16 * ct, 32 * ks), gr);
+        for (int ks = 0; ks <= ct / 2; ++ks) {
+          const float* ya = Ys + (r0 + n) * PF + 32 * ks + 8 * g;
+          const float* xb = Xs + (16 * ct + n) * PF + 32 * ks + 8 * g;
+          float va[8], vb[8];
+          *reinterpret_cast<float4*>(va) = *reinterpret_cast<const float4*>(ya);
+          *reinterpret_cast<float4*>(va + 4) = *reinterpret_cast<const float4*>(ya + 4);
+          *reinterpret_cast<float4*>(vb) = *reinterpret_cast<const float4*>(xb);
+          *reinterpret_cast<float4*>(vb + 4) = *reinterpret_cast<const float4*>(xb + 4);
+          bf16x8 ah, al, bh_, bl;
+          split8(va, ah, al);
+          split8(vb, bh_, bl);
+          acc = mfma_split3(ah, al, bh_, bl, acc);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = r0 + 4 * g + e, i = 16 * ct + n;
-          const float da = i < r ? -acc[e] : 0.f;
-          wv[ct][e] = bs[r] * da;
-          rs[e] += da * gr[e];
-        }
+        for (int ks = 0; ks < DK / 32; ++ks)
+          gr = mfma16(frag(Kb, PK, r0, 32 * ks), frag(Kb, PK, 16 * ct, 32 * ks), gr);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float v = rs[e];
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-        const int r = r0 + 4 * g + e;
-        if (n == 0 && r < valid) dbeta[tok0 + r] = dbs[r] + v;
-      }
-    }
-  }
-  __syncthreads();  // X, dT/Y and the K rows are dead: dM and W go over them
-  if (ccw) {
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = r0 + 4 * g + e, i = 16 * ct + n;
-        Ms[r * PF + i] = i <= r ? am[ct][e] : 0.f;
-        Wm[r * PF + i] = wv[ct][e];
+        const float da = i < r ? -acc[e] : 0.f;
+        wv[j][e] = bs[r] * da;
+        rs[e] += da * gr[e];
       }
-  }
-
-  // ---- step 3 -----------------------------------------------------------------
-  constexpr int KS = HJ / 32;
-  f32x4 aq[4][TPW], ak[4][TPW];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) aq[rt][i] = ak[rt][i] = zero4();
-  {
-    uint16_t* Oh = U;
-    uint16_t* Ol = Oh + C * PJ;
-    uint16_t* Dh = Ol + C * PJ;
-    uint16_t* Dl = Dh + C * PJ;
-    uint16_t* Rh = Dl + C * PJ;
-    uint16_t* Rl = Rh + C * PJ;
-    for (int h = 0; h < DV; h += HJ) {
-      float4 sv[TPW][KS][2], gv[TPW][KS][2];
-#pragma unroll
-      for (int i = 0; i < TPW; ++i)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const size_t o = (size_t)(16 * (w * TPW + i) + n) * DV + h + 32 * ks + 8 * g;
-          sv[i][ks][0] = *reinterpret_cast<const float4*>(blk + W.S() + o);
-          sv[i][ks][1] = *reinterpret_cast<const float4*>(blk + W.S() + o + 4);
-          gv[i][ks][0] = *reinterpret_cast<const float4*>(blk + W.G() + o);
-          gv[i][ks][1] = *reinterpret_cast<const float4*>(blk + W.G() + o + 4);
-        }
-      __syncthreads();  // the previous pass (or step 2) is done with this space
-#pragma unroll
-      for (int p = 0; p < C * HJ / 4 / NTQ; ++p) {
-        const int f = t + p * NTQ, r = f / (HJ / 4), c4 = f % (HJ / 4);
-        const size_t go = (tok0 + min(r, valid - 1)) * DV + h + 4 * c4;
-        float4 xo = *reinterpret_cast<const float4*>(dO + go);
-        float4 xr = *reinterpret_cast<const float4*>(dv + go);
-        const float4 xd = *reinterpret_cast<const float4*>(blk + W.D() + (size_t)r * DV + h + 4 * c4);
-        if (r >= valid) xo = xr = make_float4(0.f, 0.f, 0.f, 0.f);
-        xr = make_float4(-xr.x, -xr.y, -xr.z, -xr.w);
-        uint2 hh, ll;
-        split4(xo, hh, ll);
-        *reinterpret_cast<uint2*>(Oh + r * PJ + 4 * c4) = hh;
-        *reinterpret_cast<uint2*>(Ol + r * PJ + 4 * c4) = ll;
-        split4(xd, hh, ll);
-        *reinterpret_cast<uint2*>(Dh + r * PJ + 4 * c4) = hh;
-        *reinterpret_cast<uint2*>(Dl + r * PJ + 4 * c4) = ll;
-        split4(xr, hh, ll);
-        *reinterpret_cast<uint2*>(Rh + r * PJ + 4 * c4) = hh;
-        *reinterpret_cast<uint2*>(Rl + r * PJ + 4 * c4) = ll;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-          uint2 h0, l0, h1, l1;
-          split4(sv[i][ks][0], h0, l0);
-          split4(sv[i][ks][1], h1, l1);
-          const bf16x8 sh = as_bf16x8(h0, h1), sl = as_bf16x8(l0, l1);
-          split4(gv[i][ks][0], h0, l0);
-          split4(gv[i][ks][1], h1, l1);
-          const bf16x8 gh = as_bf16x8(h0, h1), gl = as_bf16x8(l0, l1);
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            aq[rt][i] = mfma_split3(frag(Oh, PJ, 16 * rt, 32 * ks), frag(Ol, PJ, 16 * rt, 32 * ks), sh,
-                                    sl, aq[rt][i]);
-            ak[rt][i] = mfma_split3(frag(Dh, PJ, 16 * rt, 32 * ks), frag(Dl, PJ, 16 * rt, 32 * ks), gh,
-                                    gl, ak[rt][i]);
-            ak[rt][i] = mfma_split3(frag(Rh, PJ, 16 * rt, 32 * ks), frag(Rl, PJ, 16 * rt, 32 * ks), sh,
-                                    sl, ak[rt][i]);
-          }
-        }
     }
+    // The row sums over the wave's column tiles, then over the wave pair.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) rs[e] += __shfl_xor(rs[e], off, 64);
+    }
+    if (half == 1 && n == 0)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rsb[r0 + 4 * g + e] = rs[e];
+    __syncthreads();
+    if (half == 0 && n == 0)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = r0 + 4 * g + e;
+        if (r < valid) dbeta[tok0 + r] = dbs[r] + rs[e] + (kPairs ? rsb[r] : 0.f);
+      }
   }
-  __syncthreads();
+  __syncthreads();  // X, dT/Y and the K rows are dead: dM and W go over them
 
-  // ---- step 4 -----------------------------------------------------------------
+  // ---- dQ += dM K, dK += dM^T Q + (W + W^T) K ------------------------------------
   {
-    uint16_t* Kt = U;
-    uint16_t* Qt = Kt + DK * PC;
+    float* Ms = reinterpret_cast<float*>(lds_u4);             // dM [C][PF]
+    float* Wm = Ms + C * PF;                                   // W  [C][PF]
+    uint16_t* Kt = reinterpret_cast<uint16_t*>(Wm + C * PF);  // K^T
+    uint16_t* Qt = Kt + DK * PC;                               // Q^T
+#pragma unroll
+    for (int j = 0; j < NCW; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = r0 + 4 * g + e, i = 16 * ctile(j) + n;
+        Ms[r * PF + i] = i <= r ? am[j][e] : 0.f;
+        Wm[r * PF + i] = wv[j][e];
+      }
     {
       RowTile<DK, NTQ> tq, tk;
       tq.load(q + tok0 * DK, valid);
@@ -984,10 +947,10 @@ __global__ __launch_bounds__(DK * 4) void grad_kernel(
     }
     __syncthreads();
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int ks = 0; ks < C / 32; ++ks) {
-        const int r = 16 * rt + n, a0 = 32 * ks + 8 * g;
+        const int r = 16 * i + n, a0 = 32 * ks + 8 * g;
         float m[8], mt[8], ww[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -999,32 +962,26 @@ __global__ __launch_bounds__(DK * 4) void grad_kernel(
         split8(m, mh, ml);
         split8(mt, th, tl);
         split8(ww, wh, wl);
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-          const int d0 = 16 * (w * TPW + i);
-          const bf16x8 bk = fragT<3>(Kt, d0, 32 * ks), bq = fragT<3>(Qt, d0, 32 * ks);
-          aq[rt][i] = mfma16(mh, bk, aq[rt][i]);
-          aq[rt][i] = mfma16(ml, bk, aq[rt][i]);
-          ak[rt][i] = mfma16(th, bq, ak[rt][i]);
-          ak[rt][i] = mfma16(tl, bq, ak[rt][i]);
-          ak[rt][i] = mfma16(wh, bk, ak[rt][i]);
-          ak[rt][i] = mfma16(wl, bk, ak[rt][i]);
-        }
+        const bf16x8 bk = fragT<3>(Kt, 16 * w, 32 * ks), bq = fragT<3>(Qt, 16 * w, 32 * ks);
+        aq[i] = mfma16(mh, bk, aq[i]);
+        aq[i] = mfma16(ml, bk, aq[i]);
+        ak[i] = mfma16(th, bq, ak[i]);
+        ak[i] = mfma16(tl, bq, ak[i]);
+        ak[i] = mfma16(wh, bk, ak[i]);
+        ak[i] = mfma16(wl, bk, ak[i]);
       }
   }
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < TPW; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rt + 4 * g + e;
-        if (r < valid) {
-          const size_t o = (tok0 + r) * DK + 16 * (w * TPW + i) + n;
-          dq[o] = aq[rt][i][e];
-          dk[o] = ak[rt][i][e];
-        }
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * i + 4 * g + e;
+      if (r < valid) {
+        const size_t o = (tok0 + r) * DK + 16 * w + n;
+        dq[o] = aq[i][e];
+        dk[o] = ak[i][e];
       }
+    }
 }
 
 template <typename K>
