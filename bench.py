@@ -57,7 +57,7 @@ KERNEL_SOURCES["kda_decode"] = KERNEL_SOURCES["decode"]
 KERNEL_SOURCES["kda_chunk_prep"] = KERNEL_SOURCES["kda_chunk_scan"] = [
     "dn_kda.hip", "dn_kda.h", "dn_kda_mfma.hip", "dn_lds64.h", "dn_inv64.h", "dn_mfma.h",
     "dn_valu_common.h", "dn_common.h"]
-for _k in ("bwd_prep", "bwd_fwd_scan", "bwd_scan", "bwd_cc", "bwd_qk"):
+for _k in ("bwd_prep", "bwd_fwd_scan", "bwd_scan", "bwd_qk"):
     KERNEL_SOURCES[_k] = ["dn_backward.hip", "dn_backward.h", "dn_backward_mfma.hip", "dn_lds64.h",
                           "dn_inv64.h", "dn_mfma.h", "dn_valu_common.h", "dn_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
