@@ -303,7 +303,7 @@ const char* deltanet_status_string(int status) {
 
 int deltanet_feature_prep(const void* q_raw, const void* k_raw, const float* beta_logit,
                           void* q_hat, void* k_hat, float* beta, int B, int H, int L, int d_k,
-                          int dtype, hipStream_t stream) {
+                          dn_dtype dtype, hipStream_t stream) {
   if (B < 1 || H < 1 || L < 0 || d_k < 1) return DN_ERR_BAD_SHAPE;
   if (!dtype_ok(dtype) || !dim_ok(d_k)) return DN_ERR_UNSUPPORTED;
   const long long rows = (long long)B * H * L;
@@ -331,7 +331,7 @@ int deltanet_feature_prep(const void* q_raw, const void* k_raw, const float* bet
 }
 
 size_t deltanet_chunk_fwd_features_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
-                                                   int in_dtype, int gated) {
+                                                   dn_dtype in_dtype, int gated) {
   ChunkSizes s;
   if (check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, DN_F32, &s) != DN_OK) return 0;
   return ws_layout(B, H, L, d_k, d_v, C, in_dtype, gated != 0, true, s).total;
@@ -340,7 +340,7 @@ size_t deltanet_chunk_fwd_features_workspace_bytes(int B, int H, int L, int d_k,
 int deltanet_chunk_fwd_features(const void* q_raw, const void* k_raw, const void* v,
                                 const float* alpha, const float* beta_logit, const float* S0,
                                 void* o, float* S_final, int B, int H, int L, int d_k, int d_v,
-                                int C, int in_dtype, int out_dtype, void* workspace,
+                                int C, dn_dtype in_dtype, dn_dtype out_dtype, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
   return chunk_fwd_impl(q_raw, k_raw, v, alpha, beta_logit, S0, o, S_final, B, H, L, d_k, d_v, C,
                         in_dtype, out_dtype, workspace, workspace_bytes, stream, true);
@@ -348,14 +348,14 @@ int deltanet_chunk_fwd_features(const void* q_raw, const void* k_raw, const void
 
 int deltanet_decode_step_features(const void* q_raw, const void* k_raw, const void* v,
                                   const float* alpha, const float* beta_logit, float* S, void* o,
-                                  int B, int H, int d_k, int d_v, int in_dtype, int out_dtype,
+                                  int B, int H, int d_k, int d_v, dn_dtype in_dtype, dn_dtype out_dtype,
                                   hipStream_t stream) {
   return decode_impl(q_raw, k_raw, v, alpha, beta_logit, S, o, B, H, d_k, d_v, in_dtype,
                      out_dtype, stream, true);
 }
 
 size_t deltanet_chunk_bwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
-                                          int in_dtype) {
+                                          dn_dtype in_dtype) {
   ChunkSizes s;
   if (check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, DN_F32, &s) != DN_OK) return 0;
   return dn::chunk_bwd_workspace_bytes(B, H, L, d_k, d_v);
@@ -364,7 +364,7 @@ size_t deltanet_chunk_bwd_workspace_bytes(int B, int H, int L, int d_k, int d_v,
 int deltanet_chunk_bwd(const void* q, const void* k, const void* v, const float* beta,
                        const float* S0, const float* dO, const float* dS_final, float* dq,
                        float* dk, float* dv, float* dbeta, float* dS0, int B, int H, int L,
-                       int d_k, int d_v, int C, int in_dtype, void* workspace,
+                       int d_k, int d_v, int C, dn_dtype in_dtype, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
   ChunkSizes s;
   int st = check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, DN_F32, &s);
@@ -410,7 +410,7 @@ int deltanet_chunk_bwd(const void* q, const void* k, const void* v, const float*
 }
 
 size_t deltanet_kda_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
-                                              int in_dtype) {
+                                              dn_dtype in_dtype) {
   ChunkSizes s;
   if (check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, DN_F32, &s) != DN_OK) return 0;
   return dn::kda_workspace_bytes(B, H, L, d_k);
@@ -418,7 +418,7 @@ size_t deltanet_kda_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int 
 
 int deltanet_kda_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
                            const float* beta, const float* S0, void* o, float* S_final, int B,
-                           int H, int L, int d_k, int d_v, int C, int in_dtype, int out_dtype,
+                           int H, int L, int d_k, int d_v, int C, dn_dtype in_dtype, dn_dtype out_dtype,
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (L > 0 && !alpha) return DN_ERR_NULL_ARG;
   return chunk_fwd_impl(q, k, v, alpha, beta, S0, o, S_final, B, H, L, d_k, d_v, C, in_dtype,
@@ -427,21 +427,21 @@ int deltanet_kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
 
 int deltanet_kda_decode_step(const void* q, const void* k, const void* v, const float* alpha,
                              const float* beta, float* S, void* o, int B, int H, int d_k,
-                             int d_v, int in_dtype, int out_dtype, hipStream_t stream) {
+                             int d_v, dn_dtype in_dtype, dn_dtype out_dtype, hipStream_t stream) {
   if (!alpha) return DN_ERR_NULL_ARG;
   return decode_impl(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, in_dtype, out_dtype, stream,
                      false, true);
 }
 
 size_t deltanet_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
-                                          int in_dtype) {
+                                          dn_dtype in_dtype) {
   ChunkSizes s;
   if (check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, DN_F32, &s) != DN_OK) return 0;
   return dn::chunk_workspace_bytes(B, H, L, d_k, d_v, C, in_dtype, false);
 }
 
 size_t deltanet_gated_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
-                                                int in_dtype) {
+                                                dn_dtype in_dtype) {
   ChunkSizes s;
   if (check_chunk_shape(B, H, L, d_k, d_v, C, in_dtype, DN_F32, &s) != DN_OK) return 0;
   return dn::chunk_workspace_bytes(B, H, L, d_k, d_v, C, in_dtype, true);
@@ -449,7 +449,7 @@ size_t deltanet_gated_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, in
 
 int deltanet_chunk_fwd(const void* q, const void* k, const void* v, const float* beta,
                        const float* S0, void* o, float* S_final, int B, int H, int L, int d_k,
-                       int d_v, int C, int in_dtype, int out_dtype, void* workspace,
+                       int d_v, int C, dn_dtype in_dtype, dn_dtype out_dtype, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
   return chunk_fwd_impl(q, k, v, nullptr, beta, S0, o, S_final, B, H, L, d_k, d_v, C, in_dtype,
                         out_dtype, workspace, workspace_bytes, stream);
@@ -457,7 +457,7 @@ int deltanet_chunk_fwd(const void* q, const void* k, const void* v, const float*
 
 int deltanet_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* beta,
                                const float* S0, void* o, float* S_final, int B, int H, int L,
-                               int d_k, int d_v, int C, int in_dtype, int out_dtype,
+                               int d_k, int d_v, int C, dn_dtype in_dtype, dn_dtype out_dtype,
                                hipStream_t stream) {
   return chunk_fwd_impl(q, k, v, nullptr, beta, S0, o, S_final, B, H, L, d_k, d_v, C, in_dtype,
                         out_dtype, nullptr, 0, stream, false, false, true);
@@ -465,7 +465,7 @@ int deltanet_chunk_fwd_noalloc(const void* q, const void* k, const void* v, cons
 
 int deltanet_gated_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
                              const float* beta, const float* S0, void* o, float* S_final, int B,
-                             int H, int L, int d_k, int d_v, int C, int in_dtype, int out_dtype,
+                             int H, int L, int d_k, int d_v, int C, dn_dtype in_dtype, dn_dtype out_dtype,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
   // With L = 0 there is no token to decay and alpha may be null: the call
   // only copies the state, as the plain forward does.
@@ -475,14 +475,14 @@ int deltanet_gated_chunk_fwd(const void* q, const void* k, const void* v, const 
 }
 
 int deltanet_decode_step(const void* q, const void* k, const void* v, const float* beta,
-                         float* S, void* o, int B, int H, int d_k, int d_v, int in_dtype,
-                         int out_dtype, hipStream_t stream) {
+                         float* S, void* o, int B, int H, int d_k, int d_v, dn_dtype in_dtype,
+                         dn_dtype out_dtype, hipStream_t stream) {
   return decode_impl(q, k, v, nullptr, beta, S, o, B, H, d_k, d_v, in_dtype, out_dtype, stream);
 }
 
 int deltanet_gated_decode_step(const void* q, const void* k, const void* v, const float* alpha,
                                const float* beta, float* S, void* o, int B, int H, int d_k,
-                               int d_v, int in_dtype, int out_dtype, hipStream_t stream) {
+                               int d_v, dn_dtype in_dtype, dn_dtype out_dtype, hipStream_t stream) {
   if (!alpha) return DN_ERR_NULL_ARG;
   return decode_impl(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, in_dtype, out_dtype, stream);
 }

@@ -50,7 +50,10 @@ typedef enum {
   DN_ERR_HIP = 7           /* a HIP runtime call failed; see deltanet_last_hip_error */
 } dn_status;
 
-typedef enum { DN_F32 = 0, DN_BF16 = 1 } dn_dtype;
+/* Element types of q, k, v (in_dtype) and o (out_dtype).  The last
+ * enumerator only gives the type the range of an int, so that a value
+ * outside the set reaches the argument checks (DN_ERR_UNSUPPORTED). */
+typedef enum { DN_F32 = 0, DN_BF16 = 1, DN_DTYPE_RANGE_ = 0x7fffffff } dn_dtype;
 
 /*
  * Chunkwise-parallel delta-rule forward over a whole sequence.
@@ -82,13 +85,13 @@ typedef enum { DN_F32 = 0, DN_BF16 = 1 } dn_dtype;
 int deltanet_chunk_fwd(const void* q, const void* k, const void* v, const float* beta,
                        const float* S0, void* o, float* S_final,
                        int B, int H, int L, int d_k, int d_v, int C,
-                       int in_dtype, int out_dtype,
+                       dn_dtype in_dtype, dn_dtype out_dtype,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace deltanet_chunk_fwd needs for these sizes (0 if the
  * sizes are invalid or unsupported). */
 size_t deltanet_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
-                                          int in_dtype);
+                                          dn_dtype in_dtype);
 
 /*
  * deltanet_chunk_fwd that allocates nothing, for callers that cannot allocate
@@ -114,7 +117,7 @@ size_t deltanet_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v,
 int deltanet_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* beta,
                                const float* S0, void* o, float* S_final,
                                int B, int H, int L, int d_k, int d_v, int C,
-                               int in_dtype, int out_dtype, hipStream_t stream);
+                               dn_dtype in_dtype, dn_dtype out_dtype, hipStream_t stream);
 
 /*
  * One decode step for B sequences x H heads (the recurrence at one token),
@@ -128,7 +131,7 @@ int deltanet_chunk_fwd_noalloc(const void* q, const void* k, const void* v, cons
  */
 int deltanet_decode_step(const void* q, const void* k, const void* v, const float* beta,
                          float* S, void* o, int B, int H, int d_k, int d_v,
-                         int in_dtype, int out_dtype, hipStream_t stream);
+                         dn_dtype in_dtype, dn_dtype out_dtype, hipStream_t stream);
 
 /*
  * Gated forms (Gated DeltaNet).  The article "How a Baseten Engineer Traced 7
@@ -155,18 +158,18 @@ int deltanet_decode_step(const void* q, const void* k, const void* v, const floa
 int deltanet_gated_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
                              const float* beta, const float* S0, void* o, float* S_final,
                              int B, int H, int L, int d_k, int d_v, int C,
-                             int in_dtype, int out_dtype,
+                             dn_dtype in_dtype, dn_dtype out_dtype,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace deltanet_gated_chunk_fwd needs (0 if the sizes are
  * invalid or unsupported). */
 size_t deltanet_gated_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
-                                                int in_dtype);
+                                                dn_dtype in_dtype);
 
 /* One gated decode step, S updated in place; o = q S_new.  alpha: [B, H] fp32. */
 int deltanet_gated_decode_step(const void* q, const void* k, const void* v, const float* alpha,
                                const float* beta, float* S, void* o, int B, int H,
-                               int d_k, int d_v, int in_dtype, int out_dtype,
+                               int d_k, int d_v, dn_dtype in_dtype, dn_dtype out_dtype,
                                hipStream_t stream);
 
 /*
@@ -194,13 +197,13 @@ int deltanet_gated_decode_step(const void* q, const void* k, const void* v, cons
 int deltanet_chunk_bwd(const void* q, const void* k, const void* v, const float* beta,
                        const float* S0, const float* dO, const float* dS_final,
                        float* dq, float* dk, float* dv, float* dbeta, float* dS0,
-                       int B, int H, int L, int d_k, int d_v, int C, int in_dtype,
+                       int B, int H, int L, int d_k, int d_v, int C, dn_dtype in_dtype,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace deltanet_chunk_bwd needs (0 if the sizes are invalid or
  * unsupported). */
 size_t deltanet_chunk_bwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
-                                          int in_dtype);
+                                          dn_dtype in_dtype);
 
 /*
  * Per-dimension decay (KDA).  The same article describes Kimi Linear's KDA as
@@ -226,19 +229,19 @@ size_t deltanet_chunk_bwd_workspace_bytes(int B, int H, int L, int d_k, int d_v,
 int deltanet_kda_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
                            const float* beta, const float* S0, void* o, float* S_final,
                            int B, int H, int L, int d_k, int d_v, int C,
-                           int in_dtype, int out_dtype,
+                           dn_dtype in_dtype, dn_dtype out_dtype,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace deltanet_kda_chunk_fwd needs (0 if the sizes are invalid
  * or unsupported). */
 size_t deltanet_kda_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
-                                              int in_dtype);
+                                              dn_dtype in_dtype);
 
 /* One decode step with per-dimension decay, S updated in place; o = q S_new.
  * alpha: [B, H, d_k] fp32. */
 int deltanet_kda_decode_step(const void* q, const void* k, const void* v, const float* alpha,
                              const float* beta, float* S, void* o, int B, int H,
-                             int d_k, int d_v, int in_dtype, int out_dtype,
+                             int d_k, int d_v, dn_dtype in_dtype, dn_dtype out_dtype,
                              hipStream_t stream);
 
 /*
@@ -261,7 +264,7 @@ int deltanet_kda_decode_step(const void* q, const void* k, const void* v, const 
  */
 int deltanet_feature_prep(const void* q_raw, const void* k_raw, const float* beta_logit,
                           void* q_hat, void* k_hat, float* beta,
-                          int B, int H, int L, int d_k, int dtype, hipStream_t stream);
+                          int B, int H, int L, int d_k, dn_dtype dtype, hipStream_t stream);
 
 /*
  * The chunked forward fed by the raw projections: the feature maps above,
@@ -276,13 +279,13 @@ int deltanet_chunk_fwd_features(const void* q_raw, const void* k_raw, const void
                                 const float* alpha, const float* beta_logit, const float* S0,
                                 void* o, float* S_final,
                                 int B, int H, int L, int d_k, int d_v, int C,
-                                int in_dtype, int out_dtype,
+                                dn_dtype in_dtype, dn_dtype out_dtype,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace deltanet_chunk_fwd_features needs (gated != 0 when
  * alpha will be given; 0 if the sizes are invalid or unsupported). */
 size_t deltanet_chunk_fwd_features_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C,
-                                                   int in_dtype, int gated);
+                                                   dn_dtype in_dtype, int gated);
 
 /*
  * One decode step fed by the raw projections: the feature maps are applied
@@ -293,7 +296,7 @@ size_t deltanet_chunk_fwd_features_workspace_bytes(int B, int H, int L, int d_k,
  */
 int deltanet_decode_step_features(const void* q_raw, const void* k_raw, const void* v,
                                   const float* alpha, const float* beta_logit, float* S, void* o,
-                                  int B, int H, int d_k, int d_v, int in_dtype, int out_dtype,
+                                  int B, int H, int d_k, int d_v, dn_dtype in_dtype, dn_dtype out_dtype,
                                   hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
