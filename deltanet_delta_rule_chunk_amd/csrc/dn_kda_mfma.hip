@@ -164,10 +164,14 @@ __global__ __launch_bounds__(PNTHR) __attribute__((amdgpu_waves_per_eu(8))) void
 #pragma unroll
   for (int it = 0; it < NKQ; ++it) {  // into the bf16 tiles as they are (rows past L: zeros)
     const int e8 = t + PNTHR * it, r = e8 / (DK / 8), c8 = e8 % (DK / 8);
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    // (Masked lane by lane: a select between whole uint4 values was lowered
+    // through private memory.)
+    const uint32_t m = r < valid ? ~0u : 0u;
+    const uint4 xkm = make_uint4(xk[it].x & m, xk[it].y & m, xk[it].z & m, xk[it].w & m);
+    const uint4 xqm = make_uint4(xq[it].x & m, xq[it].y & m, xq[it].z & m, xq[it].w & m);
     if (e8 < C * DK / 8) {
-      *reinterpret_cast<uint4*>(Ks + r * LDH + 8 * c8) = r < valid ? xk[it] : z;
-      *reinterpret_cast<uint4*>(Qs + r * LDH + 8 * c8) = r < valid ? xq[it] : z;
+      *reinterpret_cast<uint4*>(Ks + r * LDH + 8 * c8) = xkm;
+      *reinterpret_cast<uint4*>(Qs + r * LDH + 8 * c8) = xqm;
     }
   }
   if (t < C) bs[t] = bt;
