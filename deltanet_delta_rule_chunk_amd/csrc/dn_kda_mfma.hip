@@ -108,6 +108,13 @@ __device__ __forceinline__ float4 bf4(const uint16_t* p) {
                      __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 
+// log2(alpha), floored at log2(FLT_MIN) = -126 (a zero decay, a full wipe,
+// becomes a factor 2^-126), and 2^x on the hardware exponential.
+__device__ __forceinline__ float log2_decay(float alpha) {
+  return alpha > 0.f ? fmaxf(log2f(alpha), -126.f) : -126.f;
+}
+__device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <int DK>
 __global__ __launch_bounds__(PNTHR) __attribute__((amdgpu_waves_per_eu(8))) void prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ alpha,
@@ -119,7 +126,9 @@ __global__ __launch_bounds__(PNTHR) __attribute__((amdgpu_waves_per_eu(8))) void
   uint16_t* Ks = reinterpret_cast<uint16_t*>(smem_f);  // K (bf16)
   uint16_t* Qs = Ks + C * LDH;                           // Q (bf16)
   float* As = smem_f;                                    // A, over K and Q after their last read
-  float* Gs = smem_f + PrepLds<DK>::kq_bytes / 4;        // g (cumulative log-decays), later X
+  // g, the cumulative log-decays, is held in base 2 (the sums of log2(alpha)),
+  // so that every factor e^{g_a - g_b} is a single 2^x instruction.
+  float* Gs = smem_f + PrepLds<DK>::kq_bytes / 4;        // g / ln 2, later X
   float* bs = Gs + C * LD;                               // beta
   float* scratch = bs + C;                               // the inverse's per-wave tiles
 
@@ -182,7 +191,7 @@ __global__ __launch_bounds__(PNTHR) __attribute__((amdgpu_waves_per_eu(8))) void
 #pragma unroll
   for (int it = 0; it < NA; ++it) {
     const int e = t + PNTHR * it, r = e / DK, j = e % DK;
-    Gs[r * LD + j] = r < valid ? log_decay(av[it]) : 0.f;
+    Gs[r * LD + j] = r < valid ? log2_decay(av[it]) : 0.f;
   }
   __syncthreads();
   {
@@ -214,15 +223,15 @@ __global__ __launch_bounds__(PNTHR) __attribute__((amdgpu_waves_per_eu(8))) void
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float gv = Gs[r * LD + j0 + i], gC = Gs[(C - 1) * LD + j0 + i];
-      kd[i] = kv[i] * __expf(gv);
-      qd[i] = qv[i] * __expf(gv);
-      ku[i] = kv[i] * __expf(gC - gv);
+      kd[i] = kv[i] * exp2_raw(gv);
+      qd[i] = qv[i] * exp2_raw(gv);
+      ku[i] = kv[i] * exp2_raw(gC - gv);
     }
     put_split8(Kd, C * DK, 8 * e8, kd);
     put_split8(Qd, C * DK, 8 * e8, qd);
     put_split8(Ku, C * DK, 8 * e8, ku);
   }
-  for (int j = t; j < DK; j += PNTHR) gam[j] = __expf(Gs[(C - 1) * LD + j]);
+  for (int j = t; j < DK; j += PNTHR) gam[j] = exp2_raw(Gs[(C - 1) * LD + j]);
   for (int e = t; e < C * C; e += PNTHR)  // P above the diagonal
     if (e % C > e / C) put_split(Pc, C * C, e, 0.f);
 
@@ -248,10 +257,10 @@ __global__ __launch_bounds__(PNTHR) __attribute__((amdgpu_waves_per_eu(8))) void
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float gm = Gs[m * LD + j + e];
-        const float fr = __expf(Gs[ra * LD + j + e] - gm);
+        const float fr = exp2_raw(Gs[ra * LD + j + e] - gm);
         kt[e] *= fr;
         qt[e] *= fr;
-        kh[e] *= __expf(gm - Gs[ib * LD + j + e]);
+        kh[e] *= exp2_raw(gm - Gs[ib * LD + j + e]);
       }
       bf16x8 kth, ktl, qth, qtl, khh, khl;
       split8(kt, kth, ktl);
@@ -279,13 +288,13 @@ __global__ __launch_bounds__(PNTHR) __attribute__((amdgpu_waves_per_eu(8))) void
       for (int j4 = 0; j4 < DK / 4; ++j4) {  // the sum in order of j
         const float4 gr4 = gr[j4], gi4 = gi[j4];
         const float4 ki4 = bf4(ki + 4 * j4), kr4 = bf4(kr + 4 * j4), qr4 = bf4(qr + 4 * j4);
-        float f = __expf(gr4.x - gi4.x) * ki4.x;
+        float f = exp2_raw(gr4.x - gi4.x) * ki4.x;
         a += kr4.x * f, pv += qr4.x * f;
-        f = __expf(gr4.y - gi4.y) * ki4.y;
+        f = exp2_raw(gr4.y - gi4.y) * ki4.y;
         a += kr4.y * f, pv += qr4.y * f;
-        f = __expf(gr4.z - gi4.z) * ki4.z;
+        f = exp2_raw(gr4.z - gi4.z) * ki4.z;
         a += kr4.z * f, pv += qr4.z * f;
-        f = __expf(gr4.w - gi4.w) * ki4.w;
+        f = exp2_raw(gr4.w - gi4.w) * ki4.w;
         a += kr4.w * f, pv += qr4.w * f;
       }
       put_split(Pc, C * C, r * C + i, pv);
