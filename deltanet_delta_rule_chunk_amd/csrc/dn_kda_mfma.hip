@@ -108,10 +108,13 @@ __device__ __forceinline__ float4 bf4(const uint16_t* p) {
                      __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 
-// log2(alpha), floored at log2(FLT_MIN) = -126 (a zero decay, a full wipe,
-// becomes a factor 2^-126), and 2^x on the hardware exponential.
+// log2(alpha), floored at -120: a zero decay (a full wipe) becomes a factor
+// 2^-120 ~ 7.5e-37.  The floor keeps a one-row factor 2^(g_{r+1} - g_r) a
+// normal number even after the rounding of the summed log-decays (the
+// diagonal pairs below multiply it by its reciprocal), and every difference
+// of summed log-decays finite.  2^x runs on the hardware exponential.
 __device__ __forceinline__ float log2_decay(float alpha) {
-  return alpha > 0.f ? fmaxf(log2f(alpha), -126.f) : -126.f;
+  return alpha > 0.f ? fmaxf(log2f(alpha), -120.f) : -120.f;
 }
 __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -143,7 +146,8 @@ __global__ __launch_bounds__(PNTHR) __attribute__((amdgpu_waves_per_eu(8))) void
   uint16_t* Qd = Kd + 2 * C * DK;  // Q o e^g
   uint16_t* Ku = Qd + 2 * C * DK;  // K o e^{g_C - g}
   float* gam = reinterpret_cast<float*>(Ku + 2 * C * DK);  // e^{g_C}
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
+  const int t = threadIdx.x, l = t & 63, n = l & 15, g = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // (wave-uniform: scalar)
 
   // Every global read of the chunk (q and k rows, 16 bytes per load, the
   // decays, beta) is issued before the first of them is waited on.
@@ -273,33 +277,67 @@ __global__ __launch_bounds__(PNTHR) __attribute__((amdgpu_waves_per_eu(8))) void
     for (int e = 0; e < 4; ++e)
       put_split(Pc, C * C, (16 * br + 4 * g + e) * C + 16 * bi + n, ap[e]);
   } else {
-    // Pairs (r, i), i <= r, inside the diagonal tiles: 4 x 136 of them.
-    const int pidx = t - 6 * 64;
-    if (pidx < 4 * 136) {
-      const int b = pidx / 136, qi = pidx % 136;
-      int rr = 0;
-      while ((rr + 1) * (rr + 2) / 2 <= qi) ++rr;
-      const int r = 16 * b + rr, i = 16 * b + qi - rr * (rr + 1) / 2;
-      const uint16_t *kr = Ks + r * LDH, *ki = Ks + i * LDH, *qr = Qs + r * LDH;
-      const float4 *gr = reinterpret_cast<const float4*>(Gs + r * LD);
-      const float4 *gi = reinterpret_cast<const float4*>(Gs + i * LD);
-      float pv = 0.f;
-#pragma unroll 2
-      for (int j4 = 0; j4 < DK / 4; ++j4) {  // the sum in order of j
-        const float4 gr4 = gr[j4], gi4 = gi[j4];
-        const float4 ki4 = bf4(ki + 4 * j4), kr4 = bf4(kr + 4 * j4), qr4 = bf4(qr + 4 * j4);
-        float f = exp2_raw(gr4.x - gi4.x) * ki4.x;
-        a += kr4.x * f, pv += qr4.x * f;
-        f = exp2_raw(gr4.y - gi4.y) * ki4.y;
-        a += kr4.y * f, pv += qr4.y * f;
-        f = exp2_raw(gr4.z - gi4.z) * ki4.z;
-        a += kr4.z * f, pv += qr4.z * f;
-        f = exp2_raw(gr4.w - gi4.w) * ki4.w;
-        a += kr4.w * f, pv += qr4.w * f;
+    // The pairs (r, i), i <= r, inside the diagonal tiles, in groups of four:
+    // rows r1 = 16 b + 2 u and r1 + 1 against columns i1 = 16 b + 2 v and
+    // i1 + 1 (v <= u: 36 groups per tile; the pair (r1, i1 + 1) of a group
+    // on the diagonal, v = u, lies above it and is dropped).  Four lanes
+    // share a group, each summing every fourth slice of 2 dimensions, so
+    // the K and Q rows are unpacked once for four pairs, and row r1 + 1's
+    // factors come from row r1's:  e^{g_{r1+1} - g_i} = e^{g_{r1} - g_i} e^{g_{r1+1} - g_{r1}}.
+    const int pidx = t - 6 * 64, quarter = pidx & 3, grp = pidx >> 2;
+    if (grp < 4 * 36) {
+      const int b = grp / 36, gg = grp % 36;
+      int u = 0;
+      while ((u + 1) * (u + 2) / 2 <= gg) ++u;
+      const int v = gg - u * (u + 1) / 2;
+      const int r1 = 16 * b + 2 * u, i1 = 16 * b + 2 * v;
+      const uint16_t *kr1 = Ks + r1 * LDH, *qr1 = Qs + r1 * LDH, *ki1 = Ks + i1 * LDH;
+      const float* g1p = Gs + r1 * LD;
+      const float* h1p = Gs + i1 * LD;
+      float a11 = 0.f, a12 = 0.f, a21 = 0.f, a22 = 0.f, p11 = 0.f, p12 = 0.f, p21 = 0.f, p22 = 0.f;
+      auto dim = [&](float g1e, float g2e, float h1e, float h2e, float k1e, float k2e, float q1e,
+                     float q2e, float c1e, float c2e) {
+        const float sd = exp2_raw(g2e - g1e);
+        const float e11 = exp2_raw(g1e - h1e) * c1e, e12 = exp2_raw(g1e - h2e) * c2e;
+        const float e21 = e11 * sd, e22 = e12 * sd;
+        a11 += k1e * e11, p11 += q1e * e11;
+        a12 += k1e * e12, p12 += q1e * e12;
+        a21 += k2e * e21, p21 += q2e * e21;
+        a22 += k2e * e22, p22 += q2e * e22;
+      };
+      auto lo = [](uint32_t x) { return __uint_as_float(x << 16); };
+      auto hi = [](uint32_t x) { return __uint_as_float(x & 0xffff0000u); };
+#pragma unroll 1
+      for (int m = 0; m < DK / 8; ++m) {  // 2-dimension slices 4 m + quarter
+        const int j = 2 * (4 * m + quarter);
+        const float2 g1 = *reinterpret_cast<const float2*>(g1p + j);
+        const float2 g2 = *reinterpret_cast<const float2*>(g1p + LD + j);
+        const float2 h1 = *reinterpret_cast<const float2*>(h1p + j);
+        const float2 h2 = *reinterpret_cast<const float2*>(h1p + LD + j);
+        const uint32_t k1 = *reinterpret_cast<const uint32_t*>(kr1 + j);
+        const uint32_t k2 = *reinterpret_cast<const uint32_t*>(kr1 + LDH + j);
+        const uint32_t q1 = *reinterpret_cast<const uint32_t*>(qr1 + j);
+        const uint32_t q2 = *reinterpret_cast<const uint32_t*>(qr1 + LDH + j);
+        const uint32_t c1 = *reinterpret_cast<const uint32_t*>(ki1 + j);
+        const uint32_t c2 = *reinterpret_cast<const uint32_t*>(ki1 + LDH + j);
+        dim(g1.x, g2.x, h1.x, h2.x, lo(k1), lo(k2), lo(q1), lo(q2), lo(c1), lo(c2));
+        dim(g1.y, g2.y, h1.y, h2.y, hi(k1), hi(k2), hi(q1), hi(q2), hi(c1), hi(c2));
       }
-      put_split(Pc, C * C, r * C + i, pv);
-      ar = r, ai = i;
-      a = i < r ? a * bs[r] : 0.f;
+      float sums[8] = {a11, p11, a21, p21, a22, p22, a12, p12};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sums[e] += __shfl_xor(sums[e], 1, 64);
+        sums[e] += __shfl_xor(sums[e], 2, 64);
+      }
+      // Lane `quarter` keeps pair (r1, i1), (r1+1, i1), (r1+1, i1+1) or (r1, i1+1).
+      const int r = r1 + (quarter == 1 || quarter == 2), i = i1 + (quarter >= 2);
+      const float av_ = quarter == 0 ? sums[0] : quarter == 1 ? sums[2] : quarter == 2 ? sums[4] : sums[6];
+      const float pv = quarter == 0 ? sums[1] : quarter == 1 ? sums[3] : quarter == 2 ? sums[5] : sums[7];
+      if (i <= r) {
+        put_split(Pc, C * C, r * C + i, pv);
+        ar = r, ai = i;
+        a = i < r ? av_ * bs[r] : 0.f;
+      }
     }
   }
   __syncthreads();  // K and Q are dead from here: A goes over them
@@ -311,7 +349,7 @@ __global__ __launch_bounds__(PNTHR) __attribute__((amdgpu_waves_per_eu(8))) void
       const int r = 16 * br + 4 * g + e;
       As[r * LDA + 16 * bi + n] = bs[r] * aa[e];
     }
-  } else if (t - 6 * 64 < 4 * 136) {
+  } else {  // (lanes without a pair write the zero diagonal entry (0, 0))
     As[ar * LDA + ai] = a;
   }
 
