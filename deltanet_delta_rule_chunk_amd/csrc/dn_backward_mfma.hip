@@ -190,21 +190,27 @@ __global__ __launch_bounds__(NTH) void prep_kernel(const bf16* __restrict__ q,
   __syncthreads();
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
+    // gk: tile (w, ct) of K K^T; gq: tile (ct, w) of K Q^T, i.e. M's tile
+    // (w, ct) transposed, so that each lane holds 4 consecutive columns of
+    // one row of M and stores them with one 16-byte write.
     f32x4 gk = zero4(), gq = zero4();
     if (ct <= w) {
 #pragma unroll
       for (int ks = 0; ks < DK / 32; ++ks) {
         const bf16x8 bk = frag(Kb, PK, 16 * ct, 32 * ks);
         gk = mfma16(frag(Kb, PK, r0, 32 * ks), bk, gk);
-        gq = mfma16(frag(Qb, PK, r0, 32 * ks), bk, gq);
+        gq = mfma16(bk, frag(Qb, PK, r0, 32 * ks), gq);
       }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = r0 + 4 * g + e, i = 16 * ct + n;
       As[r * PF + i] = i < r ? bs[r] * gk[e] : 0.f;
-      blk[W.M() + r * C + i] = i <= r ? gq[e] : 0.f;
     }
+    const int mr = r0 + n, mi = 16 * ct + 4 * g;  // M[mr][mi .. mi + 3]
+    *reinterpret_cast<float4*>(blk + W.M() + mr * C + mi) =
+        make_float4(mi <= mr ? gq[0] : 0.f, mi + 1 <= mr ? gq[1] : 0.f, mi + 2 <= mr ? gq[2] : 0.f,
+                    mi + 3 <= mr ? gq[3] : 0.f);
   }
   inv64::inverse<PF, PF>(As, Xs, scratch);
   for (int e4 = t; e4 < C * C / 4; e4 += NTH) {  // 16-byte stores of X
