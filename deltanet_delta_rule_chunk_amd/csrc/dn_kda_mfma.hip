@@ -151,10 +151,10 @@ __global__ __launch_bounds__(PNTHR) __attribute__((amdgpu_waves_per_eu(8))) void
 
   // Every global read of the chunk (q and k rows, 16 bytes per load, the
   // decays, beta) is issued before the first of them is waited on.
-  constexpr int NKQ = (C * DK / 8 + PNTHR - 1) / PNTHR, NA = C * DK / PNTHR;
-  static_assert(C * DK % PNTHR == 0 && (C * DK / 8) % 64 == 0, "load shape");
+  constexpr int NKQ = (C * DK / 8 + PNTHR - 1) / PNTHR, NA = C * DK / (4 * PNTHR);
+  static_assert(C * DK % (4 * PNTHR) == 0 && (C * DK / 8) % 64 == 0, "load shape");
   uint4 xk[NKQ], xq[NKQ];
-  float av[NA];
+  float4 av[NA];  // the decays, 4 consecutive dimensions per load
   {
     const uint4* kg = reinterpret_cast<const uint4*>(k + tok0 * DK);
     const uint4* qg = reinterpret_cast<const uint4*>(q + tok0 * DK);
@@ -169,8 +169,8 @@ __global__ __launch_bounds__(PNTHR) __attribute__((amdgpu_waves_per_eu(8))) void
     }
 #pragma unroll
     for (int it = 0; it < NA; ++it) {
-      const int e = t + PNTHR * it, r = e / DK, j = e % DK;
-      av[it] = alpha[(tok0 + min(r, valid - 1)) * DK + j];
+      const int e = 4 * (t + PNTHR * it), r = e / DK, j = e % DK;
+      av[it] = *reinterpret_cast<const float4*>(alpha + (tok0 + min(r, valid - 1)) * DK + j);
     }
   }
   const float bt = t < C && t < valid ? beta[tok0 + t] : 0.f;
@@ -194,8 +194,11 @@ __global__ __launch_bounds__(PNTHR) __attribute__((amdgpu_waves_per_eu(8))) void
   // (parked in the inverse's scratch, which is used only later).
 #pragma unroll
   for (int it = 0; it < NA; ++it) {
-    const int e = t + PNTHR * it, r = e / DK, j = e % DK;
-    Gs[r * LD + j] = r < valid ? log2_decay(av[it]) : 0.f;
+    const int e = 4 * (t + PNTHR * it), r = e / DK, j = e % DK;
+    const bool in = r < valid;
+    *reinterpret_cast<float4*>(Gs + r * LD + j) =
+        make_float4(in ? log2_decay(av[it].x) : 0.f, in ? log2_decay(av[it].y) : 0.f,
+                    in ? log2_decay(av[it].z) : 0.f, in ? log2_decay(av[it].w) : 0.f);
   }
   __syncthreads();
   {
