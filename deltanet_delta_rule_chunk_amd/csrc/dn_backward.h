@@ -38,13 +38,6 @@ struct Ws {
 hipError_t launch_prep_mfma(int d_k, int d_v, const void* q, const void* k, const float* beta,
                             int L, int nc, int bh, float* ws, hipStream_t stream);
 
-// Forward state pass on the matrix cores (bf16 k, v): writes S_c, R and
-// Delta of every chunk into the workspace, whose X blocks the prep kernel
-// has filled.  nc = ceil(L / C) >= 1; bh = B * H.
-hipError_t launch_fwd_scan_mfma(int d_k, int d_v, const void* k, const void* v,
-                                const float* beta, const float* S0, int L, int nc, int bh,
-                                float* ws, hipStream_t stream);
-
 // Reverse state pass on the matrix cores (bf16 q, k): writes G'_c and
 // dDelta of every chunk, dv (= dR) and dS0 (when not null).  nc >= 1.
 hipError_t launch_bwd_scan_mfma(int d_k, int d_v, const void* q, const void* k,

@@ -37,6 +37,13 @@
 #include "dn_valu_common.h"
 
 namespace dn {
+// The chunked forward's matrix-core kernels (dn_chunk_mfma.hip), which the
+// bf16 backward runs as its forward pass.
+size_t chunk_workspace_bytes_mfma(int B, int H, int L, int C);
+hipError_t launch_chunk_fwd_mfma(const ChunkArgs& a);
+}  // namespace dn
+
+namespace dn {
 namespace bwd {
 
 using valu::load_rows;
@@ -546,7 +553,15 @@ hipError_t launch_t(const BwdArgs& a) {
     prof_mark(kSlotBwdPrep, true, a.stream);
     prof_mark(kSlotBwdFwdScan, false, a.stream);
     if constexpr (kMatrixCores) {
-      DN_TRY(launch_fwd_scan_mfma(DK, DV, k, v, a.beta, a.S0, a.L, nc, bh, ws, a.stream));
+      // The forward pass on the chunked forward's kernels at 128-token
+      // chunks (their T in the workspace past the 64-token blocks), writing
+      // S, R and Delta of every 64-token block.
+      constexpr Ws W{DK, DV};
+      const BwdFwdOut bo{ws, W.per_chunk(), W.S(), W.R(), W.D(), nc};
+      ChunkArgs ca{k, k, v, nullptr, a.beta, a.S0, nullptr, nullptr, a.B, a.H, a.L, DK, DV, 128,
+                   1, 0, ws + (size_t)bh * nc * W.per_chunk(), a.stream, false};
+      ca.bwd_out = &bo;
+      DN_TRY(launch_chunk_fwd_mfma(ca));
     } else {
       DN_TRY(set_smem(&fwd_scan_kernel<DK, DV, IT>, FwdSmem<DK>::bytes));
       hipLaunchKernelGGL((fwd_scan_kernel<DK, DV, IT>), slices, blk, FwdSmem<DK>::bytes, a.stream,
@@ -600,7 +615,10 @@ hipError_t launch_types(const BwdArgs& a) {
 }  // namespace bwd
 
 size_t chunk_bwd_workspace_bytes(int B, int H, int L, int d_k, int d_v) {
-  return (size_t)B * H * cdiv(L, bwd::C) * bwd::Ws{d_k, d_v}.per_chunk() * sizeof(float);
+  // The 64-token blocks, then the T fragments of the forward pass at
+  // 128-token chunks (bf16 path).
+  return (size_t)B * H * cdiv(L, bwd::C) * bwd::Ws{d_k, d_v}.per_chunk() * sizeof(float) +
+         chunk_workspace_bytes_mfma(B, H, L, 128);
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a) {

@@ -1,27 +1,30 @@
-// dn_backward_mfma.hip -- the backward's five kernels on the gfx950 matrix
-// cores, for bf16 q, k, v.
+// dn_backward_mfma.hip -- the backward's kernels on the gfx950 matrix cores,
+// for bf16 q, k, v: the prep (X and M per 64-token chunk), the reverse state
+// pass and the kernel of the chunk's C x C gradients and dQ, dK.  (The
+// forward pass that fills S, R and Delta runs on the chunked forward's own
+// prep and scan at 128-token chunks: dn_scan_mfma.hip, its BWD form.)
 //
 // The products are those of the vector-ALU kernels in dn_backward.hip (the
 // chunk algebra is derived there), taken as 16 x 16 x 32 bf16 MFMAs with
 // fp32 accumulation.  q and k are exact in bf16; every fp32 operand (the
-// state S, its gradient G', X, M, dO, R, Delta, dDelta, dR, dT, Y, W) is
-// carried as a split (hi, lo) bf16 pair (dn_mfma.h), so each product keeps
-// roughly fp32 accuracy.  The 64 x 64 triangular inverse is dn_inv64.h.
+// state gradient G', X, M, dO, Delta, dDelta, dR, R, S, dT, Y, W) is carried
+// as a split (hi, lo) bf16 pair (dn_mfma.h), so each product keeps roughly
+// fp32 accuracy.  The 64 x 64 triangular inverse is dn_inv64.h.
 //
-// The two state passes run one 4-wave workgroup per (head, 16 columns of
-// d_v), all column slices of a head on one XCD.  The slice of the state
-// lives in MFMA accumulators: wave w holds the d_k / 64 row tiles
-// w * d_k / 64 ...  Each chunk step is three phases separated by barriers:
-//   1  wave w forms row tile w (16 chunk rows) of the first product;
-//   2  wave w forms row tile w of the second;
-//   3  every wave advances its state tiles, and the next chunk's operands go
-//      into LDS (row-major and, where a product contracts over chunk rows,
-//      transposed copies); the ones phase 3 itself reads are double
-//      buffered.
-// Each step starts by writing the state out and publishing it to LDS as a
-// split B operand; the following chunk's operands are loaded into registers
-// right after the first barrier, so their latency hides behind the phases.
-//
+// The reverse pass runs one 8-wave workgroup per (head, 16 columns of d_v),
+// all column slices of a head on one XCD; waves 0-3 carry the chain, the
+// slice of the state gradient in MFMA accumulators (wave w holds the
+// d_k / 64 row tiles w * d_k / 64 ...), and waves 4-7 load and deposit the
+// next chunk.  Each chunk step is three phases separated by barriers:
+//   1  chain wave w forms row tile w (16 chunk rows) of the first product;
+//   2  chain wave w forms row tile w of the second;
+//   3  every chain wave advances its state tiles while the next chunk's
+//      operands go into LDS (row-major and, where a product contracts over
+//      chunk rows, transposed copies); the ones phase 3 itself reads are
+//      double buffered.
+// Each step starts by writing the state gradient out and publishing it to
+// LDS as a split B operand.
+
 // LDS operand arrays are bf16 with rows padded by 16 bytes (dn_lds64.h).  A
 // fragment read `frag(a, P, r0, kb)` gives lane l the 8 contraction slots
 // kb + 8 (l / 16) ... of row r0 + l % 16, which is the A layout of the MFMA
@@ -233,200 +236,6 @@ __device__ __forceinline__ bool slice_of(int ns, int nbh, int& j0, int& bh) {
 }
 
 inline dim3 slice_grid(int ns, int nbh) { return dim3(8 * ns * ((nbh + 7) / 8)); }
-
-// ---- forward state pass -----------------------------------------------------
-template <int DK>
-struct FwdLds {
-  static constexpr int PK = DK + 8;
-  static constexpr int PV = NT + 1;
-  static constexpr size_t halves = (size_t)C * PK + 2 * (size_t)DK * PC + 2 * (size_t)C * PC +
-                                   2 * (size_t)NT * PK + 4 * (size_t)NT * PC;
-  static constexpr size_t bytes =
-      halves * 2 + ((size_t)C * PV + C) * sizeof(float);
-};
-
-// Three barriers per chunk: phase 1 (R) | phase 2 (Delta) | phase 3 (state
-// update).  The next chunk's operands are deposited during phase 3: by then
-// only K^T (double buffered) and Delta are still being read.  Eight waves:
-// waves 0-3 carry the chain (the products, the entering state and the
-// stores), waves 4-7 load the next chunk, prefetch the one after into L2 and
-// deposit the next chunk into LDS.
-constexpr int FNTH = 2 * NTH;
-
-template <int DK, int DV>
-__global__ __launch_bounds__(FNTH) void fwd_scan_kernel(const bf16* __restrict__ k,
-                                                       const bf16* __restrict__ v,
-                                                       const float* __restrict__ beta,
-                                                       const float* __restrict__ S0, int L,
-                                                       int nc, int nbh, float* __restrict__ ws) {
-  using LD = FwdLds<DK>;
-  constexpr int PK = LD::PK, PV = LD::PV;
-  constexpr Ws W{DK, DV};
-  constexpr int TPW = DK / 64;  // state row tiles per wave
-  extern __shared__ uint4 lds_u4[];
-  uint16_t* Kb = reinterpret_cast<uint16_t*>(lds_u4);  // K rows     [C][PK]
-  uint16_t* Kt = Kb + C * PK;                           // K^T        [2][DK][PC]
-  uint16_t* Xh = Kt + 2 * DK * PC;                      // X          [C][PC]
-  uint16_t* Xl = Xh + C * PC;
-  uint16_t* Sh = Xl + C * PC;                           // -S^T       [NT][PK]
-  uint16_t* Sl = Sh + NT * PK;
-  uint16_t* Rh = Sl + NT * PK;                          // (beta R)^T [NT][PC]
-  uint16_t* Rl = Rh + NT * PC;
-  uint16_t* Dh = Rl + NT * PC;                          // Delta^T    [NT][PC]
-  uint16_t* Dl = Dh + NT * PC;
-  float* Vs = reinterpret_cast<float*>(Dl + NT * PC);   // V slice    [C][PV]
-  float* bs = Vs + C * PV;
-
-  int j0, bh;
-  if (!slice_of(DV / NT, nbh, j0, bh)) return;
-  const int l = threadIdx.x & 63, n = l & 15, g = l >> 4;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool chain = wid < 4;
-  const int w = wid & 3;                 // a chain wave's row tile and state tiles
-  const int t = threadIdx.x & (NTH - 1);  // index within the role (loads, deposits)
-
-  f32x4 S[TPW];
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int d0 = 16 * (w * TPW + i) + 4 * g;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      S[i][e] = S0 && chain ? S0[((size_t)bh * DK + d0 + e) * DV + j0 + n] : 0.f;
-  }
-
-  RowTile<DK> tk;
-  SqTile tx;
-  tk.tid = tx.tid = t;
-  uint2 pv;
-  float pb = 0.f;
-  auto fetch = [&](int cc) {
-    const int vc = min(C, L - cc * C);
-    const size_t t0 = (size_t)bh * L + (size_t)cc * C;
-    tk.load(k + t0 * DK, vc);
-    tx.load(ws + ((size_t)bh * nc + cc) * W.per_chunk() + W.X());
-    const int r = t % C, c4 = t / C;
-    const uint2 x = *reinterpret_cast<const uint2*>(v + (t0 + min(r, vc - 1)) * DV + j0 + 4 * c4);
-    pv = r < vc ? x : make_uint2(0u, 0u);
-    if (t < C) pb = t < vc ? beta[t0 + t] : 0.f;
-  };
-  // The fetched chunk into LDS (its K^T into buffer kb).
-  auto deposit = [&](int kb) {
-    tk.put_rows(Kb);
-    tk.put_cols(Kt + kb * DK * PC);
-    tx.put_rows(Xh, Xl);
-    const int r = t % C, c4 = t / C;
-    Vs[r * PV + 4 * c4 + 0] = __uint_as_float(pv.x << 16);
-    Vs[r * PV + 4 * c4 + 1] = __uint_as_float(pv.x & 0xffff0000u);
-    Vs[r * PV + 4 * c4 + 2] = __uint_as_float(pv.y << 16);
-    Vs[r * PV + 4 * c4 + 3] = __uint_as_float(pv.y & 0xffff0000u);
-    if (t < C) bs[t] = pb;
-  };
-
-  // L2 prefetch of chunk c + 2: the 128-byte lines of its k, X and v rows
-  // are split over the head's column-slice workgroups (which share an XCD);
-  // thread t touches line slice + ns t with one dword load, folded in a chunk
-  // later and only ever stored under a condition that is false.
-  constexpr int NS = DV / NT;
-  constexpr int KL = C * DK * 2 / 128, XL = C * C * 4 / 128, VL = C * DV * 2 / 128;
-  constexpr int NLINES = KL + XL + VL;
-  constexpr int NPF = ((NLINES + NS - 1) / NS + NTH - 1) / NTH;
-  const int sidx = j0 / NT;
-  uint32_t pf_acc = 0, pf_val[NPF];
-#pragma unroll
-  for (int i = 0; i < NPF; ++i) pf_val[i] = 0;
-  auto prefetch = [&](int cc) {
-    const int vc = min(C, L - cc * C);
-    const size_t t0 = (size_t)bh * L + (size_t)cc * C;
-#pragma unroll
-    for (int i = 0; i < NPF; ++i) {
-      const int ln = min(sidx + NS * (t + NTH * i), NLINES - 1);
-      const uint32_t* src;
-      if (ln < KL) {
-        const int e = ln * 64, row = min(e / DK, vc - 1);
-        src = reinterpret_cast<const uint32_t*>(k + (t0 + row) * DK + e % DK);
-      } else if (ln < KL + XL) {
-        src = reinterpret_cast<const uint32_t*>(ws + ((size_t)bh * nc + cc) * W.per_chunk() + W.X()) +
-              32 * (ln - KL);
-      } else {
-        const int e = (ln - KL - XL) * 64, row = min(e / DV, vc - 1);
-        src = reinterpret_cast<const uint32_t*>(v + (t0 + row) * DV + e % DV);
-      }
-      pf_val[i] = *src;
-    }
-  };
-
-  if (!chain) {
-    fetch(0);
-    deposit(0);
-  }
-  for (int c = 0; c < nc; ++c) {
-    float* blk = ws + ((size_t)bh * nc + c) * W.per_chunk();
-#pragma unroll
-    for (int i = 0; i < NPF; ++i) pf_acc ^= pf_val[i];
-    // The entering state: out to the workspace and into LDS.
-    if (chain) {
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int d0 = 16 * (w * TPW + i);
-        store_tile16(S[i], blk + W.S() + (size_t)d0 * DV + j0, DV);
-        put_split_t(Sh, Sl, PK, d0, -S[i]);
-      }
-    }
-    __syncthreads();
-    if (!chain) {
-      if (c + 1 < nc) fetch(c + 1);
-      prefetch(min(c + 2, nc - 1));
-    }
-
-    // Phase 1: R = V - K S, row tile w.
-    const int r0 = 16 * w;
-    f32x4 acc;
-    if (chain) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = Vs[(r0 + 4 * g + e) * PV + n];
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks)
-      acc = mfma_split2(frag(Kb, PK, r0, 32 * ks), frag(Sh, PK, 0, 32 * ks), frag(Sl, PK, 0, 32 * ks),
-                        acc);
-    f32x4 rb;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) rb[e] = acc[e] * bs[r0 + 4 * g + e];
-    store_tile16(acc, blk + W.R() + (size_t)r0 * DV + j0, DV);
-    put_split_t(Rh, Rl, PC, r0, rb);
-    }
-    __syncthreads();
-
-    // Phase 2: Delta = X diag(beta) R, row tile w (X is lower triangular, so
-    // the contraction stops at the tile's last row).
-    if (chain) {
-    acc = zero4();
-#pragma unroll
-    for (int ks = 0; ks <= w / 2; ++ks)
-      acc = mfma_split3(frag(Xh, PC, r0, 32 * ks), frag(Xl, PC, r0, 32 * ks), frag(Rh, PC, 0, 32 * ks),
-                        frag(Rl, PC, 0, 32 * ks), acc);
-    store_tile16(acc, blk + W.D() + (size_t)r0 * DV + j0, DV);
-    put_split_t(Dh, Dl, PC, r0, acc);
-    }
-    __syncthreads();
-
-    // Phase 3: S += K^T Delta; meanwhile the next chunk goes into LDS (K
-    // rows, X, V and beta were last read in phases 1 and 2).
-    if (chain) {
-      const uint16_t* Kc = Kt + (c & 1) * DK * PC;
-#pragma unroll
-      for (int i = 0; i < TPW; ++i)
-#pragma unroll
-        for (int ks = 0; ks < C / 32; ++ks)
-          S[i] = mfma_split2(fragT<3>(Kc, 16 * (w * TPW + i), 32 * ks), frag(Dh, PC, 0, 32 * ks),
-                             frag(Dl, PC, 0, 32 * ks), S[i]);
-    } else if (c + 1 < nc) {
-      deposit((c + 1) & 1);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < NPF; ++i) pf_acc ^= pf_val[i];
-  if (nc < 0) ws[0] = __uint_as_float(pf_acc);
-}
 
 // ---- reverse state pass -----------------------------------------------------
 template <int DK>
@@ -997,18 +806,6 @@ static hipError_t set_lds(K* kernel, size_t bytes) {
 }
 
 template <int DK, int DV>
-hipError_t fwd_t(const void* k, const void* v, const float* beta, const float* S0, int L, int nc,
-                 int bh, float* ws, hipStream_t s) {
-  auto* kern = &fwd_scan_kernel<DK, DV>;
-  hipError_t e = set_lds(kern, FwdLds<DK>::bytes);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, slice_grid(DV / NT, bh), dim3(FNTH), FwdLds<DK>::bytes, s,
-                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), beta, S0, L, nc, bh,
-                     ws);
-  return hipGetLastError();
-}
-
-template <int DK, int DV>
 hipError_t bwd_t(const void* q, const void* k, const float* beta, const float* dO,
                  const float* dS_final, float* dv, float* dS0, int L, int nc, int bh, float* ws,
                  hipStream_t s) {
@@ -1046,15 +843,6 @@ hipError_t prep_t(const void* q, const void* k, const float* beta, int L, int nc
 }
 
 }  // namespace mf
-
-hipError_t launch_fwd_scan_mfma(int d_k, int d_v, const void* k, const void* v,
-                                const float* beta, const float* S0, int L, int nc, int bh,
-                                float* ws, hipStream_t stream) {
-  if (d_k == 64 && d_v == 64) return mf::fwd_t<64, 64>(k, v, beta, S0, L, nc, bh, ws, stream);
-  if (d_k == 64 && d_v == 128) return mf::fwd_t<64, 128>(k, v, beta, S0, L, nc, bh, ws, stream);
-  if (d_k == 128 && d_v == 64) return mf::fwd_t<128, 64>(k, v, beta, S0, L, nc, bh, ws, stream);
-  return mf::fwd_t<128, 128>(k, v, beta, S0, L, nc, bh, ws, stream);
-}
 
 hipError_t launch_bwd_scan_mfma(int d_k, int d_v, const void* q, const void* k,
                                 const float* beta, const float* dO, const float* dS_final,

@@ -460,7 +460,7 @@ hipError_t launch_g(const ChunkArgs& a, uint4* Tfrag, float* Gws) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
   const FeatureArgs* f = a.feat;
-  prof_mark(kSlotChunkPrep, false, a.stream);
+  if (!a.bwd_out) prof_mark(kSlotChunkPrep, false, a.stream);
   hipLaunchKernelGGL(kern, dim3(nc, BH), dim3(256), sm, a.stream,
                      static_cast<const uint16_t*>(FEAT ? f->k_raw : a.k), a.alpha,
                      FEAT ? f->beta_logit : a.beta, a.L, nc, Tfrag, Gws,
@@ -468,7 +468,7 @@ hipError_t launch_g(const ChunkArgs& a, uint4* Tfrag, float* Gws) {
                      static_cast<uint16_t*>(FEAT ? f->q_hat : nullptr),
                      static_cast<uint16_t*>(FEAT ? f->k_hat : nullptr), FEAT ? f->beta : nullptr);
   e = hipGetLastError();
-  prof_mark(kSlotChunkPrep, true, a.stream);
+  if (!a.bwd_out) prof_mark(kSlotChunkPrep, true, a.stream);
   return e;
 }
 

@@ -26,6 +26,18 @@ struct DecodeArgs {
 
 struct FeatureArgs;
 
+// Outputs of the chunked forward when it runs as the forward pass of the
+// backward (bf16 matrix-core path, C = 128, plain form): for every 64-token
+// block of the backward's workspace, the state entering the block, R = V - K S
+// from that state and Delta, row-major fp32.  o and S_final are then not
+// written.
+struct BwdFwdOut {
+  float* ws;
+  size_t block;    // floats per (head, 64-token block)
+  size_t s, r, d;  // offsets of S [d_k][d_v], R [64][d_v] and Delta [64][d_v]
+  int nb;          // 64-token blocks per head
+};
+
 struct ChunkArgs {
   const void *q, *k, *v;
   const float* alpha;  // per-token decay of the gated form, or null (plain delta rule);
@@ -42,6 +54,8 @@ struct ChunkArgs {
   // WY-prep kernel, from feat's raw inputs into its outputs, which q, k and
   // beta above must then point at (the scan reads them).
   const FeatureArgs* feat = nullptr;
+  // The backward's forward pass (see BwdFwdOut), or null.
+  const BwdFwdOut* bwd_out = nullptr;
 };
 
 hipError_t launch_decode(const DecodeArgs& a);

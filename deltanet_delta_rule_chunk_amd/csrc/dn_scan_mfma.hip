@@ -149,12 +149,23 @@ __device__ __forceinline__ void put_split(uint16_t* base, int plane, int off, f3
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
 
-template <int C, int DK, int DV, typename OT, bool GATED>
+// BWD: the forward pass of the backward (128-token chunks here, 64-token
+// blocks there).  Instead of o, the kernel writes for every 64-token block of
+// the backward's workspace the state entering it, R = V - K S from that
+// state, and Delta (the deltas do not depend on the chunking):
+//   - the chain waves store the entering state of the chunk and, after the
+//     state update's second sub-block, that of the second block; R of the
+//     first block (rows of R = V - K S_c); Delta of both blocks;
+//   - the output waves of sub-blocks 2 and 3 form R of the second block,
+//     V - K S_{c,2} with S_{c,2} the state after 64 rows, in the next
+//     chunk's R phase, as they form outputs otherwise (q is not read).
+template <int C, int DK, int DV, typename OT, bool GATED, bool BWD = false>
 __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ S0, OT* __restrict__ o,
     float* __restrict__ S_final, const uint4* __restrict__ Tfrag, const float* __restrict__ Gws,
-    int L, int nc, int BH) {
+    int L, int nc, int BH, BwdFwdOut bo) {
+  static_assert(!BWD || (C == 128 && !GATED), "the backward's forward pass: plain form, C = 128");
   using CF = Cfg<C, DK, DV>;
   constexpr int NRT = CF::NRT, NSB = CF::NSB, NKB = CF::NKB, NCT = CF::NCT;
   constexpr int RPW = CF::RPW, DPW = CF::DPW, SPT = CF::SPT;
@@ -189,6 +200,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
   const bool chain = w < CF::NCW;
   const size_t sbase = (size_t)bh * DK * DV;
   const size_t tokh = (size_t)bh * L;
+  // BWD: 64-token block nb of this head in the backward's workspace.
+  auto bblk = [&](int nb) { return bo.ws + ((size_t)bh * bo.nb + nb) * bo.block; };
 
   if (nc == 0) {
     if (chain && S_final) {
@@ -292,6 +305,16 @@ __global__ __launch_bounds__(512) void scan_kernel(
       const f32x4 f = *reinterpret_cast<const f32x4*>(Gs + (c & 1) * 4 * C + 2 * C + 16 * rt + 4 * g);
       return x * f;
     };
+    // BWD: Delta rows 16 rt + 4 g + r of chunk c into block 2c or 2c + 1
+    // (a block past the sequence's last is not written).
+    auto store_delta = [&](int rt, f32x4 x, int c) {
+      const int nb = 2 * c + rt / (NRT / 2);
+      if (nb < bo.nb) {
+        float* dd = bblk(nb) + bo.d;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dd[(size_t)(16 * (rt % (NRT / 2)) + 4 * g + r) * DV + j0 + i16] = x[r];
+      }
+    };
     auto step = [&](int c, TRegs& tc) {
       const int cn = min(c + 1, nc - 1);
       const uint16_t* Kc = Kbuf + (c & 1) * KELEMS;
@@ -300,6 +323,13 @@ __global__ __launch_bounds__(512) void scan_kernel(
       // ---- phase A: R = V - K S ----------------------------------------------
       t_load(c, tc);
       stage_load(cn);
+      if constexpr (BWD) {  // the state entering block 2c
+        float* sd = bblk(2 * c) + bo.s;
+#pragma unroll
+        for (int i = 0; i < DPW; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sd[(size_t)(16 * (DPW * w + i) + 4 * g + r) * DV + j0 + i16] = st[i][r];
+      }
       {
         const uint16_t* Sc = Snap + (c & 1) * 2 * SPLANE;
         // All LDS operands of the phase are read up front, then multiplied.
@@ -338,6 +368,13 @@ __global__ __launch_bounds__(512) void scan_kernel(
             R[r] = v4[r] - kv;
           }
           put_split(Rb, RPLANE, fo_d(rt, g, i16), R);
+          if constexpr (BWD) {  // R of block 2c (rows 0..63, from the chunk's entering state)
+            if (rt < NRT / 2) {
+              float* rd = bblk(2 * c) + bo.r;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) rd[(size_t)(16 * rt + 4 * g + r) * DV + j0 + i16] = R[r];
+            }
+          }
         }
       }
       __syncthreads();
@@ -371,8 +408,10 @@ __global__ __launch_bounds__(512) void scan_kernel(
           }
           put_split(Dc, RPLANE, fo_d(rt1, g, i16), e0);
           if constexpr (GATED) put_split(DTb, RPLANE, fo_d(rt1, g, i16), decay_rows(rt1, e0, c));
+          if constexpr (BWD) store_delta(rt1, e0, c);
         }
         put_split(Dc, RPLANE, fo_d(rt0, g, i16), d0);
+        if constexpr (BWD) store_delta(rt0, d0, c);
         if constexpr (GATED) put_split(DTb, RPLANE, fo_d(rt0, g, i16), decay_rows(rt0, d0, c));
       }
       __syncthreads();
@@ -407,6 +446,16 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
             for (int i = 0; i < DPW; ++i)
               *reinterpret_cast<f32x4*>(dst + fo_f(4 * (DPW * w + i) + g, i16)) = st[i];
+            if constexpr (BWD) {  // the state entering block 2c + 1
+              if (b == NSB / 2 - 1 && 2 * c + 1 < bo.nb) {
+                float* sd = bblk(2 * c + 1) + bo.s;
+#pragma unroll
+                for (int i = 0; i < DPW; ++i)
+#pragma unroll
+                  for (int r = 0; r < 4; ++r)
+                    sd[(size_t)(16 * (DPW * w + i) + 4 * g + r) * DV + j0 + i16] = st[i][r];
+              }
+            }
           } else {
             uint16_t* dst = Snap + ((c + 1) & 1) * 2 * SPLANE;
 #pragma unroll
@@ -590,6 +639,46 @@ __global__ __launch_bounds__(512) void scan_kernel(
       }
     };
 
+    // BWD: R of block 2 cc + 1 (rows 64 + ..) for this wave's sub-block,
+    // V - K S_{cc,2} with S_{cc,2} the state after the chunk's first 64 rows
+    // (the snapshot of the second sub-block), in the transposed tile form of
+    // the outputs: lane (i16, g) ends with row 32 a + 16 h + i16, columns
+    // 4 g .. 4 g + 3.
+    auto r_second = [&](int cc) {
+      if (2 * cc + 1 >= bo.nb) return;
+      const uint16_t* Kc = Kbuf + (cc & 1) * KELEMS;
+      const uint16_t* Vc = Vbuf + (cc & 1) * C * 16;
+      const float* Sn = Fsnap + (NSB / 2 - 1) * DK * 16;
+      bf16x8 Sh[NKB], Sl[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(Sn + fo_f(8 * kb + 2 * g, i16));
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(Sn + fo_f(8 * kb + 2 * g + 1, i16));
+        uint2 h0, l0, h1, l1;
+        split4(x0, h0, l0);
+        split4(x1, h1, l1);
+        Sh[kb] = as_bf16x8(h0, h1);
+        Sl[kb] = as_bf16x8(l0, l1);
+      }
+      float* rd = bblk(2 * cc + 1) + bo.r;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 32 * a + 16 * h + i16;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const bf16x8 Kh = lds16(Kc + koff<DK>(row, 4 * kb + g));
+          acc = mfma16(Sh[kb], Kh, acc);
+          acc = mfma16(Sl[kb], Kh, acc);
+        }
+        const uint2 vv = lds8(Vc + row * 16 + 4 * g);
+        const f32x4 r4 = {bf16_to_f32(vv.x & 0xffffu) - acc[0], bf16_to_f32(vv.x >> 16) - acc[1],
+                          bf16_to_f32(vv.y & 0xffffu) - acc[2], bf16_to_f32(vv.y >> 16) - acc[3]};
+        *reinterpret_cast<f32x4*>(rd + (size_t)(row - C / 2) * DV + j0 + 4 * g) = r4;
+      }
+    };
+    const bool bwr = BWD && a >= NSB / 2 && a < NSB;  // the waves of rows 64 ..
+
     // L2 prefetch: the 128-byte lines of chunk cc's k, q, v and T data are
     // split over the head's column-slice workgroups (which share an XCD and
     // its L2); output-wave thread tl touches line ct + NCT tl of the list
@@ -643,46 +732,59 @@ __global__ __launch_bounds__(512) void scan_kernel(
       // ---- phase A: outputs of chunk c-1; q rows of chunk c ------------------
       stage_load(cn);
       v_stage_load(cn);
-      if (outw && c > 0) outputs(c - 1);
-      q_load(c);
+      if constexpr (BWD) {
+        if (bwr && c > 0) r_second(c - 1);
+      } else {
+        if (outw && c > 0) outputs(c - 1);
+        q_load(c);
+      }
       __syncthreads();
       // ---- phase B: L2 prefetch of chunk c+2 ------------------------------------
       pf_acc ^= pf_val;
       prefetch(min(c + 2, nc - 1));
       __syncthreads();
       // ---- phase C: diagonal Q K^T block of chunk c ------------------------------
-      if (outw) diag_qk(c);
+      if (!BWD && outw) diag_qk(c);
       v_stage_store(Vbuf + ((c + 1) & 1) * C * 16, (c + 1) & 1);
       stage_store(Kbuf + ((c + 1) & 1) * KELEMS);
       __syncthreads();
     }
-    if (outw) outputs(nc - 1);
+    if constexpr (BWD) {
+      if (bwr) r_second(nc - 1);
+    } else {
+      if (outw) outputs(nc - 1);
+    }
     pf_acc ^= pf_val;
     if (nc < 0) S_final[0] = __uint_as_float(pf_acc);
   }
 }
 
-template <int C, int DK, int DV, typename OT, bool GATED>
+template <int C, int DK, int DV, typename OT, bool GATED, bool BWD = false>
 hipError_t launch_t(const ChunkArgs& a, const uint4* Tfrag, const float* Gws) {
   using CF = Cfg<C, DK, DV>;
   const int nc = cdiv(a.L, C);
   const int BH = a.B * a.H;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<C, DK, DV, OT, GATED>),
+  auto* kern = &scan_kernel<C, DK, DV, OT, GATED, BWD>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)CF::bytes);
   if (e != hipSuccess) return e;
   const int groups = cdiv(BH, 8) * 8 * CF::NCT;
-  prof_mark(kSlotChunkScan, false, a.stream);
-  hipLaunchKernelGGL((scan_kernel<C, DK, DV, OT, GATED>), dim3(groups), dim3(CF::NTHR), CF::bytes,
-                     a.stream, static_cast<const uint16_t*>(a.q),
+  const BwdFwdOut bo = BWD ? *a.bwd_out : BwdFwdOut{};
+  if (!BWD) prof_mark(kSlotChunkScan, false, a.stream);
+  hipLaunchKernelGGL(kern, dim3(groups), dim3(CF::NTHR), CF::bytes, a.stream,
+                     static_cast<const uint16_t*>(BWD ? a.k : a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.S0,
-                     static_cast<OT*>(a.o), a.S_final, Tfrag, Gws, a.L, nc, BH);
+                     static_cast<OT*>(a.o), a.S_final, Tfrag, Gws, a.L, nc, BH, bo);
   e = hipGetLastError();
-  prof_mark(kSlotChunkScan, true, a.stream);
+  if (!BWD) prof_mark(kSlotChunkScan, true, a.stream);
   return e;
 }
 
 template <int C, int DK, int DV>
 hipError_t launch_o(const ChunkArgs& a, const uint4* Tfrag, const float* Gws) {
+  if constexpr (C == 128) {
+    if (a.bwd_out) return launch_t<C, DK, DV, float, false, true>(a, Tfrag, nullptr);
+  }
   if (Gws)
     return a.out_dtype == 0 ? launch_t<C, DK, DV, float, true>(a, Tfrag, Gws)
                             : launch_t<C, DK, DV, bf16, true>(a, Tfrag, Gws);

@@ -187,12 +187,14 @@ int deltanet_gated_decode_step(const void* q, const void* k, const void* v, cons
  *   dbeta  : [B, H, L] fp32;       dS0 : [B, H, d_k, d_v] fp32 or NULL (not
  *            written)
  * The forward is recomputed inside (nothing from a previous forward call is
- * needed).  64-token chunks whatever C names (C must still be 64 or 128).
- * bf16 inputs run every product on bf16 matrix cores with each fp32 operand
- * split into a (hi, lo) bf16 pair; fp32 inputs run fp32 vector-ALU kernels.  Outputs may not overlap
- * inputs or one another.  The workspace holds, per 64-token chunk, the
- * entering state and the exit gradient (2 d_k d_v floats) besides per-chunk
- * matrices: query deltanet_chunk_bwd_workspace_bytes().
+ * needed).  64-token chunks whatever C names (C must still be 64 or 128);
+ * with bf16 inputs the recomputed forward runs on the chunked forward's
+ * kernels at 128-token chunks.  bf16 inputs run every product on bf16 matrix
+ * cores with each fp32 operand split into a (hi, lo) bf16 pair; fp32 inputs
+ * run fp32 vector-ALU kernels.  Outputs may not overlap inputs or one
+ * another.  The workspace holds, per 64-token chunk, the entering state and
+ * the exit gradient (2 d_k d_v floats) besides per-chunk matrices, and the
+ * forward's T per 128-token chunk: query deltanet_chunk_bwd_workspace_bytes().
  */
 int deltanet_chunk_bwd(const void* q, const void* k, const void* v, const float* beta,
                        const float* S0, const float* dO, const float* dS_final,

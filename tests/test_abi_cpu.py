@@ -285,7 +285,10 @@ def test_chunk_bwd_validation(lib):
     assert _bwd(lib, ws=BASE + 800 * MB) == ALIAS          # workspace over dbeta
     need = lib.deltanet_chunk_bwd_workspace_bytes(1, 2, 256, 64, 64, 64, BF16)
     # per 64-token chunk: X, M, dM, W (64 x 64), the entering state and exit
-    # gradient (d_k x d_v), R, Delta, dDelta (64 x d_v), all fp32
-    assert need == 1 * 2 * 4 * (4 * 64 * 64 + 2 * 64 * 64 + 3 * 64 * 64) * 4
+    # gradient (d_k x d_v), R, Delta, dDelta (64 x d_v), all fp32; then, per
+    # 128-token chunk of the forward pass, T's lower triangle: 20 blocks of
+    # 32 x 32 (row tiles of 16 rows, blocks of 32 columns), hi and lo bf16
+    assert need == (1 * 2 * 4 * (4 * 64 * 64 + 2 * 64 * 64 + 3 * 64 * 64) * 4
+                    + 1 * 2 * 2 * 20 * 2 * 64 * 16)
     assert _bwd(lib, wsb=need - 1) == WS
     assert lib.deltanet_last_hip_error() == 0
