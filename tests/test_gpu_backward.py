@@ -61,6 +61,9 @@ SMALL = [
     ("bf16_L_below_chunk", "bf16", 1, 2, 37, 128, 128, 64, True, True),
     ("bf16_dk64_dv128_ragged", "bf16", 3, 3, 64 * 3 + 19, 64, 128, 64, True, True),
     ("bf16_dk128_dv64_nine_heads", "bf16", 1, 9, 64 * 4, 128, 64, 128, False, True),
+    # an odd number of 64-token blocks: the forward pass's last 128-token
+    # chunk has no second block
+    ("bf16_d128_odd_blocks", "bf16", 1, 2, 64 * 4 + 21, 128, 128, 64, True, True),
 ]
 
 
