@@ -315,9 +315,11 @@ int deltanet_last_hip_error(void);
  * per kernel slot, the summed elapsed milliseconds and the launch count
  * (nslots entries each; slots: 0 = chunk WY-prep kernel, 1 = chunk scan
  * kernel, 2 = decode kernel, 3 = feature-map kernel; the backward's kernels:
- * 4 = prep, 5 = forward state pass, 6 = reverse state pass, 7 = per-chunk
- * matrix gradients, 8 = dq / dk; for bf16 inputs one kernel computes both the
- * matrix gradients and dq / dk and is counted in slot 8).  Recording adds two
+ * 4 = prep, 5 = forward state pass (for bf16 inputs the chunked forward's
+ * prep and scan kernels at 128-token chunks, counted together), 6 = reverse
+ * state pass, 7 = per-chunk matrix gradients, 8 = dq / dk; for bf16 inputs one
+ * kernel computes both the matrix gradients and dq / dk and is counted in
+ * slot 8).  Recording adds two
  * event records per launch.
  * deltanet_profile_start() creates the thread's events up front (4096,
  * enough for 2048 launches; more are created as needed), so it can take a
