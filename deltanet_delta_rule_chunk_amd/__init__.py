@@ -5,6 +5,6 @@ The computation lives in hand-written HIP kernels behind the C ABI of
 to it.  The library is loaded on first use and its absence is an error.
 """
 
-from .binding import chunk_fwd, decode_step, load, workspace_bytes  # noqa: F401
+from .binding import chunk_fwd, decode_step, delta_rule, load, workspace_bytes  # noqa: F401
 
-__all__ = ["chunk_fwd", "decode_step", "load", "workspace_bytes"]
+__all__ = ["chunk_fwd", "decode_step", "delta_rule", "load", "workspace_bytes"]

@@ -211,6 +211,37 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     return dq, dk, dv, db, dS0
 
 
+class _DeltaRule(torch.autograd.Function):
+    """``chunk_fwd`` (fp32 o) with its gradient from ``chunk_bwd``.  Only the
+    inputs are kept for the backward, which recomputes the forward inside the
+    library.  The gradients come back in fp32; autograd casts them to the
+    inputs' dtype."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, beta, S0, C):
+        o, S_final = chunk_fwd(q, k, v, beta, S0, C)
+        ctx.save_for_backward(q, k, v, beta, S0)
+        ctx.C = C
+        return o, S_final
+
+    @staticmethod
+    def backward(ctx, dO, dS_final):
+        q, k, v, beta, S0 = ctx.saved_tensors
+        want_dS0 = S0 is not None and ctx.needs_input_grad[4]
+        dq, dk, dv, db, dS0 = chunk_bwd(q, k, v, beta, S0, dO.contiguous(), dS_final.contiguous(),
+                                        ctx.C, want_dS0=want_dS0)
+        return dq, dk, dv, db, dS0, None
+
+
+def delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+               S0: Optional[torch.Tensor] = None, C: int = 64
+               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Differentiable chunked delta-rule forward for training: ``(o, S_final)``
+    as ``chunk_fwd`` returns them (o in fp32), with gradients for q, k, v,
+    beta and S0 from ``deltanet_chunk_bwd``."""
+    return _DeltaRule.apply(q, k, v, beta, S0, C)
+
+
 def kda_workspace_bytes(B: int, H: int, L: int, d_k: int, d_v: int, C: int = 64,
                         in_dtype: torch.dtype = torch.bfloat16) -> int:
     return int(load().deltanet_kda_chunk_fwd_workspace_bytes(B, H, L, d_k, d_v, C,

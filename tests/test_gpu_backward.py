@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from deltanet_delta_rule_chunk_amd import inputs as I
-from deltanet_delta_rule_chunk_amd.binding import chunk_bwd, chunk_fwd
+from deltanet_delta_rule_chunk_amd.binding import chunk_bwd, chunk_fwd, delta_rule
 from oracle import delta_rule_backward
 from oracle_pool import oracle_heads
 from parity import assert_parity, record, to64
@@ -179,3 +179,29 @@ def test_backward_bitwise_determinism(gpu_lib):
     for n, ga, gb in zip(NAMES, a, b):
         assert torch.equal(ga, gb), n
 
+
+
+@pytest.mark.parametrize("dtype,with_s0", [("f32", True), ("bf16", True), ("bf16", False)])
+def test_autograd_matches_chunk_bwd(gpu_lib, dtype, with_s0):
+    """delta_rule under autograd: its outputs are chunk_fwd's and the
+    gradients it hands back are chunk_bwd's for the same output gradients
+    (cast by autograd to each input's dtype), bit for bit."""
+    _note(f"[bwd] autograd {dtype} S0={with_s0}")
+    w = I.ChunkWorkload("ag", 1, 3, 64 * 3 + 29, 64, 64, 64, dtype, s0_std=0.1 if with_s0 else None)
+    x = I.make_chunk_inputs(w, seed=12)
+    dO, dSf = _grads_in(w, 12)
+    g = {n: (None if t is None else t.to(DEV)) for n, t in x.items()}
+    leaves = {n: (None if t is None else t.clone().requires_grad_(True)) for n, t in g.items()}
+    o, S_final = delta_rule(leaves["q"], leaves["k"], leaves["v"], leaves["beta"], leaves["S0"], 64)
+    o_ref, S_ref = chunk_fwd(g["q"], g["k"], g["v"], g["beta"], g["S0"], 64)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o_ref) and torch.equal(S_final.detach(), S_ref)
+    ((o * dO.to(DEV)).sum() + (S_final * dSf.to(DEV)).sum()).backward()
+    ref = chunk_bwd(g["q"], g["k"], g["v"], g["beta"], g["S0"], dO.to(DEV), dSf.to(DEV), 64)
+    torch.cuda.synchronize()
+    for n, r in zip(("q", "k", "v", "beta", "S0"), ref):
+        if leaves[n] is None:
+            continue
+        got = leaves[n].grad
+        assert got is not None and got.dtype == leaves[n].dtype, n
+        assert torch.equal(got, r.to(got.dtype)), n
