@@ -59,11 +59,13 @@ KERNEL_SOURCES["kda_chunk_prep"] = KERNEL_SOURCES["kda_chunk_scan"] = [
     "dn_valu_common.h", "dn_common.h"]
 for _k in ("bwd_prep", "bwd_scan", "bwd_qk"):
     KERNEL_SOURCES[_k] = ["dn_backward.hip", "dn_backward.h", "dn_backward_mfma.hip", "dn_lds64.h",
-                          "dn_inv64.h", "dn_mfma.h", "dn_valu_common.h", "dn_common.h"]
-# The backward's forward pass is the chunked forward's scan in its BWD form
-# (after the chunked forward's prep kernel, counted in the same slot).
+                          "dn_mfma.h", "dn_valu_common.h", "dn_common.h"]
+# The backward's forward pass is the chunked forward's prep in its form that
+# also writes X of each 64-token block, then the chunked forward's scan in
+# its BWD form; one profiling slot brackets both.
+KERNEL_SOURCES["bwd_fwd_prep"] = KERNEL_SOURCES["chunk_prep"]
 KERNEL_SOURCES["bwd_fwd_scan"] = KERNEL_SOURCES["chunk_scan"]
-SLOT_KERNELS = {"bwd_fwd_scan": ("chunk_prep", "bwd_fwd_scan")}
+SLOT_KERNELS = {"bwd_fwd_scan": ("bwd_fwd_prep", "bwd_fwd_scan")}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters.json")
 
@@ -557,7 +559,7 @@ def main(argv=None) -> int:
             "tokens_per_s": w.B * w.L / (ms_b * 1e-3),
             "kernels_ms": bms,
             "kernels_hbm": {name: hbm_rate(name, t) for name, t in bms.items()},
-            "path": "64-token chunks; the forward recomputed inside on the chunked forward's prep and scan at 128-token chunks (slot bwd_fwd_scan: both kernels); every product on bf16 MFMA (split-precision operands), the triangular inverses' diagonal blocks fp32 vector ALU",
+            "path": "64-token chunks; the forward recomputed inside on the chunked forward's prep (also writing X of each 64-token block) and scan at 128-token chunks (slot bwd_fwd_scan: both kernels); every product on bf16 MFMA (split-precision operands), the triangular inverses' diagonal blocks fp32 vector ALU",
             "grads_in": "dO ~ N(0, 1) (torch generator seeded), no dS_final",
         }
         del bws, dO, grads

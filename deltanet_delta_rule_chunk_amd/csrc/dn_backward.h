@@ -33,10 +33,10 @@ struct Ws {
   __host__ __device__ constexpr size_t dD() const { return D() + (size_t)C * dv; }
 };
 
-// X = (I + A)^{-1} and M = tril(Q K^T) of every chunk, the Gram products on
-// the matrix cores (bf16 q, k).  nc >= 1.
-hipError_t launch_prep_mfma(int d_k, int d_v, const void* q, const void* k, const float* beta,
-                            int L, int nc, int bh, float* ws, hipStream_t stream);
+// M = tril(Q K^T) of every chunk on the matrix cores (bf16 q, k); X comes
+// from the forward pass.  nc >= 1.
+hipError_t launch_prep_mfma(int d_k, int d_v, const void* q, const void* k, int L, int nc, int bh,
+                            float* ws, hipStream_t stream);
 
 // Reverse state pass on the matrix cores (bf16 q, k): writes G'_c and
 // dDelta of every chunk, dv (= dR) and dS0 (when not null).  nc >= 1.

@@ -29,6 +29,10 @@
 //             dDelta, dR (= dV, written out) and dS0;
 //   cc_grad   (chunk, head): dM, dT, dA, W and dbeta;
 //   qk_grad   (chunk, head): dQ and dK.
+// (These are the fp32 path's kernels.  For bf16 inputs, dn_backward_mfma.hip
+// has the prep of M and the last three on the matrix cores, and the
+// chunked forward's own prep and scan at 128-token chunks stand in for the
+// forward pass, writing X, S_c, R and Delta of every 64-row chunk.)
 // A ragged last chunk reads zero rows (k = q = 0, beta = 0, dO = 0).
 
 #include "dn_backward.h"
@@ -543,7 +547,7 @@ hipError_t launch_t(const BwdArgs& a) {
   if (nc > 0) {
     prof_mark(kSlotBwdPrep, false, a.stream);
     if constexpr (kMatrixCores) {
-      DN_TRY(launch_prep_mfma(DK, DV, q, k, a.beta, a.L, nc, bh, ws, a.stream));
+      DN_TRY(launch_prep_mfma(DK, DV, q, k, a.L, nc, bh, ws, a.stream));
     } else {
       DN_TRY(set_smem(&prep_kernel<DK, DV, IT>, PrepSmem<DK>::bytes));
       hipLaunchKernelGGL((prep_kernel<DK, DV, IT>), chunks, blk, PrepSmem<DK>::bytes, a.stream, q,
@@ -555,9 +559,9 @@ hipError_t launch_t(const BwdArgs& a) {
     if constexpr (kMatrixCores) {
       // The forward pass on the chunked forward's kernels at 128-token
       // chunks (their T in the workspace past the 64-token blocks), writing
-      // S, R and Delta of every 64-token block.
+      // X, S, R and Delta of every 64-token block.
       constexpr Ws W{DK, DV};
-      const BwdFwdOut bo{ws, W.per_chunk(), W.S(), W.R(), W.D(), nc};
+      const BwdFwdOut bo{ws, W.per_chunk(), W.X(), W.S(), W.R(), W.D(), nc};
       ChunkArgs ca{k, k, v, nullptr, a.beta, a.S0, nullptr, nullptr, a.B, a.H, a.L, DK, DV, 128,
                    1, 0, ws + (size_t)bh * nc * W.per_chunk(), a.stream, false};
       ca.bwd_out = &bo;

@@ -1,15 +1,16 @@
 // dn_backward_mfma.hip -- the backward's kernels on the gfx950 matrix cores,
-// for bf16 q, k, v: the prep (X and M per 64-token chunk), the reverse state
+// for bf16 q, k, v: the prep (M per 64-token chunk), the reverse state
 // pass and the kernel of the chunk's C x C gradients and dQ, dK.  (The
-// forward pass that fills S, R and Delta runs on the chunked forward's own
-// prep and scan at 128-token chunks: dn_scan_mfma.hip, its BWD form.)
+// forward pass that fills X, S, R and Delta runs on the chunked forward's
+// own prep and scan at 128-token chunks: dn_chunk_mfma.hip and
+// dn_scan_mfma.hip, their backward forms.)
 //
 // The products are those of the vector-ALU kernels in dn_backward.hip (the
 // chunk algebra is derived there), taken as 16 x 16 x 32 bf16 MFMAs with
 // fp32 accumulation.  q and k are exact in bf16; every fp32 operand (the
 // state gradient G', X, M, dO, Delta, dDelta, dR, R, S, dT, Y, W) is carried
 // as a split (hi, lo) bf16 pair (dn_mfma.h), so each product keeps roughly
-// fp32 accuracy.  The 64 x 64 triangular inverse is dn_inv64.h.
+// fp32 accuracy.
 //
 // The reverse pass runs one 8-wave workgroup per (head, 16 columns of d_v),
 // all column slices of a head on one XCD; waves 0-3 carry the chain, the
@@ -32,7 +33,6 @@
 
 #include "dn_backward.h"
 #include "dn_common.h"
-#include "dn_inv64.h"
 #include "dn_lds64.h"
 #include "dn_mfma.h"
 #include "dn_valu_common.h"
@@ -114,8 +114,7 @@ struct SqTile {
     const float4* s = reinterpret_cast<const float4*>(src);
 #pragma unroll
     for (int p = 0; p < N; ++p) x[p] = s[(row0() + p) * CPR + chunk()];
-  }
-  // Split, row-major [C][PC].
+  }  // Split, row-major [C][PC].
   __device__ __forceinline__ void put_rows(uint16_t* hi, uint16_t* lo) const {
 #pragma unroll
     for (int p = 0; p < N; ++p) {
@@ -144,38 +143,27 @@ struct SqTile {
   }
 };
 
-// ---- prep: X = (I + A)^{-1} and M = tril(Q K^T) ---------------------------
-// One 4-wave workgroup per (chunk, head).  Wave w forms row tile w of the
-// Gram products K K^T and Q K^T (exact bf16 products, fp32 sums); then the
-// blocked fp32 inverse of I + A (dn_inv64.h).
+// ---- prep: M = tril(Q K^T) --------------------------------------------------
+// One 4-wave workgroup per (chunk, head): wave w forms row tile w of M from
+// the q and k rows in LDS (exact bf16 products, fp32 sums).  (X = (I + A)^{-1}
+// of every 64-token chunk comes from the forward pass's prep, which inverts
+// the 128-token I + A whose diagonal 64-row blocks these are.)
 template <int DK>
 struct PrepLds {
   static constexpr int PK = DK + 8;
-  static constexpr int PF = C + 1;
-  // K and Q rows, later X and the inverse's scratch (the rows are dead once
-  // the Gram tiles are formed); then A and beta.  ~52 KB at d_k = 128, so
-  // three workgroups share a CU.
-  static constexpr size_t rows_bytes = 2 * (size_t)C * PK * 2;
-  static constexpr size_t x_bytes = ((size_t)C * PF + inv64::SCRATCH_FLOATS) * sizeof(float);
-  static constexpr size_t region0 = rows_bytes > x_bytes ? rows_bytes : x_bytes;
-  static constexpr size_t bytes = region0 + ((size_t)C * PF + C) * sizeof(float);
+  static constexpr size_t bytes = 2 * (size_t)C * PK * 2;  // K and Q rows, ~35 KB at d_k = 128
 };
 
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void prep_kernel(const bf16* __restrict__ q,
-                                                   const bf16* __restrict__ k,
-                                                   const float* __restrict__ beta, int L,
+                                                   const bf16* __restrict__ k, int L,
                                                    float* __restrict__ ws) {
   using LD = PrepLds<DK>;
-  constexpr int PK = LD::PK, PF = LD::PF;
+  constexpr int PK = LD::PK;
   constexpr Ws W{DK, DV};
   extern __shared__ uint4 lds_u4[];
   uint16_t* Kb = reinterpret_cast<uint16_t*>(lds_u4);  // K rows [C][PK]
   uint16_t* Qb = Kb + C * PK;                           // Q rows [C][PK]
-  float* Xs = reinterpret_cast<float*>(lds_u4);         // X      [C][PF], over the rows
-  float* scratch = Xs + C * PF;
-  float* As = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(lds_u4) + LD::region0);
-  float* bs = As + C * PF;                              // A      [C][PF], beta
   const int c = blockIdx.x, bh = blockIdx.y, nc = gridDim.x;
   const int valid = min(C, L - c * C);
   const size_t tok0 = (size_t)bh * L + (size_t)c * C;
@@ -188,38 +176,23 @@ __global__ __launch_bounds__(NTH) void prep_kernel(const bf16* __restrict__ q,
     tk.load(k + tok0 * DK, valid);
     tq.put_rows(Qb);
     tk.put_rows(Kb);
-    if (t < C) bs[t] = t < valid ? beta[tok0 + t] : 0.f;
   }
   __syncthreads();
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    // gk: tile (w, ct) of K K^T; gq: tile (ct, w) of K Q^T, i.e. M's tile
-    // (w, ct) transposed, so that each lane holds 4 consecutive columns of
-    // one row of M and stores them with one 16-byte write.
-    f32x4 gk = zero4(), gq = zero4();
+    // gq: tile (ct, w) of K Q^T, i.e. M's tile (w, ct) transposed, so that
+    // each lane holds 4 consecutive columns of one row of M and stores them
+    // with one 16-byte write.
+    f32x4 gq = zero4();
     if (ct <= w) {
 #pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks) {
-        const bf16x8 bk = frag(Kb, PK, 16 * ct, 32 * ks);
-        gk = mfma16(frag(Kb, PK, r0, 32 * ks), bk, gk);
-        gq = mfma16(bk, frag(Qb, PK, r0, 32 * ks), gq);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = r0 + 4 * g + e, i = 16 * ct + n;
-      As[r * PF + i] = i < r ? bs[r] * gk[e] : 0.f;
+      for (int ks = 0; ks < DK / 32; ++ks)
+        gq = mfma16(frag(Kb, PK, 16 * ct, 32 * ks), frag(Qb, PK, r0, 32 * ks), gq);
     }
     const int mr = r0 + n, mi = 16 * ct + 4 * g;  // M[mr][mi .. mi + 3]
     *reinterpret_cast<float4*>(blk + W.M() + mr * C + mi) =
         make_float4(mi <= mr ? gq[0] : 0.f, mi + 1 <= mr ? gq[1] : 0.f, mi + 2 <= mr ? gq[2] : 0.f,
                     mi + 3 <= mr ? gq[3] : 0.f);
-  }
-  inv64::inverse<PF, PF>(As, Xs, scratch);
-  for (int e4 = t; e4 < C * C / 4; e4 += NTH) {  // 16-byte stores of X
-    const int r = e4 / (C / 4), c0 = 4 * (e4 % (C / 4));
-    const float* x = Xs + r * PF + c0;
-    *reinterpret_cast<float4*>(blk + W.X() + r * C + c0) = make_float4(x[0], x[1], x[2], x[3]);
   }
 }
 
@@ -832,13 +805,12 @@ hipError_t grad_t(const void* q, const void* k, const float* beta, const float* 
 }
 
 template <int DK, int DV>
-hipError_t prep_t(const void* q, const void* k, const float* beta, int L, int nc, int bh,
-                  float* ws, hipStream_t s) {
+hipError_t prep_t(const void* q, const void* k, int L, int nc, int bh, float* ws, hipStream_t s) {
   auto* kern = &prep_kernel<DK, DV>;
   hipError_t e = set_lds(kern, PrepLds<DK>::bytes);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(nc, bh), dim3(NTH), PrepLds<DK>::bytes, s,
-                     static_cast<const bf16*>(q), static_cast<const bf16*>(k), beta, L, ws);
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k), L, ws);
   return hipGetLastError();
 }
 
@@ -870,12 +842,12 @@ hipError_t launch_grad_mfma(int d_k, int d_v, const void* q, const void* k, cons
   return mf::grad_t<128, 128>(q, k, beta, dO, dv, dq, dk, dbeta, L, nc, bh, ws, stream);
 }
 
-hipError_t launch_prep_mfma(int d_k, int d_v, const void* q, const void* k, const float* beta,
-                            int L, int nc, int bh, float* ws, hipStream_t stream) {
-  if (d_k == 64 && d_v == 64) return mf::prep_t<64, 64>(q, k, beta, L, nc, bh, ws, stream);
-  if (d_k == 64 && d_v == 128) return mf::prep_t<64, 128>(q, k, beta, L, nc, bh, ws, stream);
-  if (d_k == 128 && d_v == 64) return mf::prep_t<128, 64>(q, k, beta, L, nc, bh, ws, stream);
-  return mf::prep_t<128, 128>(q, k, beta, L, nc, bh, ws, stream);
+hipError_t launch_prep_mfma(int d_k, int d_v, const void* q, const void* k, int L, int nc, int bh,
+                            float* ws, hipStream_t stream) {
+  if (d_k == 64 && d_v == 64) return mf::prep_t<64, 64>(q, k, L, nc, bh, ws, stream);
+  if (d_k == 64 && d_v == 128) return mf::prep_t<64, 128>(q, k, L, nc, bh, ws, stream);
+  if (d_k == 128 && d_v == 64) return mf::prep_t<128, 64>(q, k, L, nc, bh, ws, stream);
+  return mf::prep_t<128, 128>(q, k, L, nc, bh, ws, stream);
 }
 
 }  // namespace bwd

@@ -168,16 +168,30 @@ __device__ __forceinline__ void gram_wave(const uint16_t* Ks, f32x4 (&acc)[2][C 
 // column layout (lane (i16, g) holds T_kj[4 g + r][i16]), the B operand of
 // the next rows; each T_ij is also formed transposed, R_ij^T Linv_i^T, which
 // is its row layout, and stored as half of fragment block (i, j / 2).
-template <int C, int W>
+// XOUT (C = 128, the forward pass of the backward): the chains carry
+// X = (I + A)^{-1} instead (the same substitution without beta), T_ij =
+// X_ij diag(beta_j) is formed for the store, and the tiles of X inside the
+// two 64-row diagonal blocks go row-major in fp32 to xb0 and xb1 (null: no
+// such block), the tiles above the diagonal as zeros.
+template <int C, int W, bool XOUT>
 __device__ __forceinline__ void cols_wave(const uint2* Atl, const float* Lrow, const float* Lcol,
-                                          const float* bs, uint4* out, int lane, int g, int i16) {
+                                          const float* bs, uint4* out, int lane, int g, int i16,
+                                          float* xb0, float* xb1) {
   constexpr int NT = C / 16;
+  static_assert(!XOUT || C == 128, "X blocks of a 128-row chunk");
   if constexpr (W < NT / 2) {
     constexpr int J[2] = {W, NT - 1 - W};
     auto tstore = [&](int i, int j, uint2 hi, uint2 lo) {
       uint2* blk = reinterpret_cast<uint2*>(out + (size_t)(Frag<C>::base(i) + j / 2) * 128);
       blk[2 * lane + (j & 1)] = hi;
       blk[128 + 2 * lane + (j & 1)] = lo;
+    };
+    // Row layout tile (i, j) of X into its 64-row block (lane (i16, g): row
+    // i16, columns 4 g .. 4 g + 3).
+    auto xstore = [&](int i, int j, f32x4 x) {
+      float* xb = i < 4 ? xb0 : xb1;
+      if ((i >> 2) == (j >> 2) && xb)
+        *reinterpret_cast<f32x4*>(xb + (16 * (i & 3) + i16) * 64 + 16 * (j & 3) + 4 * g) = x;
     };
     const uint2 z = make_uint2(0u, 0u);
     uint2 th[2][NT], tl[2][NT];
@@ -187,7 +201,10 @@ __device__ __forceinline__ void cols_wave(const uint2* Atl, const float* Lrow, c
 #pragma unroll
       for (int t = 0; t < NT; ++t) { th[cw][t] = z; tl[cw][t] = z; }
       const f32x4 lc = *reinterpret_cast<const f32x4*>(Lcol + j * 256 + lane * 4);
-      split4(lc * bs[16 * j + i16], th[cw][j], tl[cw][j]);
+      if constexpr (XOUT)
+        split4(lc, th[cw][j], tl[cw][j]);
+      else
+        split4(lc * bs[16 * j + i16], th[cw][j], tl[cw][j]);
       const f32x4 lr = *reinterpret_cast<const f32x4*>(Lrow + j * 256 + lane * 4);
       const float4 brow = *reinterpret_cast<const float4*>(bs + 16 * j + 4 * g);
       f32x4 trow;
@@ -197,6 +214,12 @@ __device__ __forceinline__ void cols_wave(const uint2* Atl, const float* Lrow, c
       split4(trow, hi, lo);
       tstore(j, j, hi, lo);
       if (j & 1) tstore(j - 1, j, z, z);
+      if constexpr (XOUT) {
+        xstore(j, j, lr);
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+          if (i < j) xstore(i, j, zero4());
+      }
     }
 #pragma unroll
     for (int i = 1; i < NT; ++i) {
@@ -238,6 +261,11 @@ __device__ __forceinline__ void cols_wave(const uint2* Atl, const float* Lrow, c
         f32x4 tr = mfma16(Rh, Lh, zero4());
         tr = mfma16(Rh, Ll, tr);
         tr = mfma16(Rl, Lh, tr);
+        if constexpr (XOUT) {  // tr is X_ij: store it, then T_ij = X_ij diag(beta_j)
+          xstore(i, j, tr);
+          const float4 brow = *reinterpret_cast<const float4*>(bs + 16 * j + 4 * g);
+          tr[0] *= brow.x; tr[1] *= brow.y; tr[2] *= brow.z; tr[3] *= brow.w;
+        }
         uint2 hi, lo;
         split4(tr, hi, lo);
         tstore(i, j, hi, lo);
@@ -250,8 +278,9 @@ __device__ __forceinline__ void cols_wave(const uint2* Atl, const float* Lrow, c
 // layer's feature maps are applied as the rows arrive (the same arithmetic
 // as the streaming feature kernel, so the same bits), and the mapped q, k
 // and beta are written out for the scan.  q_raw, q_hat, k_hat and beta_out
-// are used only then.
-template <int C, int DK, bool GATED, bool FEAT>
+// are used only then.  XOUT: the forward pass of the backward, which also
+// takes X of each 64-token block into the backward's workspace (bo).
+template <int C, int DK, bool GATED, bool FEAT, bool XOUT = false>
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ k,
                                                    const float* __restrict__ alpha,
                                                    const float* __restrict__ beta, int L,
@@ -260,7 +289,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ q_raw,
                                                    uint16_t* __restrict__ q_hat,
                                                    uint16_t* __restrict__ k_hat,
-                                                   float* __restrict__ beta_out) {
+                                                   float* __restrict__ beta_out, BwdFwdOut bo) {
+  static_assert(!XOUT || (C == 128 && !GATED && !FEAT), "the backward's forward pass");
   using CF = Cfg<C, DK>;
   constexpr int NT = CF::NT;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -442,20 +472,25 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
 
   // ---- 4. tile columns of T ------------------------------------------------------
   uint4* const out = Tfrag + ((size_t)bh * nc + c) * Frag<C>::chunk_u4;
+  float *xb0 = nullptr, *xb1 = nullptr;
+  if constexpr (XOUT) {  // blocks 2c and 2c + 1 (the latter only if it exists)
+    xb0 = bo.ws + ((size_t)bh * bo.nb + 2 * c) * bo.block + bo.x;
+    if (2 * c + 1 < bo.nb) xb1 = xb0 + bo.block;
+  }
   switch (w) {
-    case 0: cols_wave<C, 0>(Atl, Lrow, Lcol, bs, out, lane, g, i16); break;
-    case 1: cols_wave<C, 1>(Atl, Lrow, Lcol, bs, out, lane, g, i16); break;
-    case 2: cols_wave<C, 2>(Atl, Lrow, Lcol, bs, out, lane, g, i16); break;
-    default: cols_wave<C, 3>(Atl, Lrow, Lcol, bs, out, lane, g, i16); break;
+    case 0: cols_wave<C, 0, XOUT>(Atl, Lrow, Lcol, bs, out, lane, g, i16, xb0, xb1); break;
+    case 1: cols_wave<C, 1, XOUT>(Atl, Lrow, Lcol, bs, out, lane, g, i16, xb0, xb1); break;
+    case 2: cols_wave<C, 2, XOUT>(Atl, Lrow, Lcol, bs, out, lane, g, i16, xb0, xb1); break;
+    default: cols_wave<C, 3, XOUT>(Atl, Lrow, Lcol, bs, out, lane, g, i16, xb0, xb1); break;
   }
 }
 
-template <int C, int DK, bool GATED, bool FEAT>
+template <int C, int DK, bool GATED, bool FEAT, bool XOUT = false>
 hipError_t launch_g(const ChunkArgs& a, uint4* Tfrag, float* Gws) {
   const int nc = cdiv(a.L, C);
   const int BH = a.B * a.H;
   constexpr size_t sm = Cfg<C, DK>::bytes;
-  auto* kern = &prep_kernel<C, DK, GATED, FEAT>;
+  auto* kern = &prep_kernel<C, DK, GATED, FEAT, XOUT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
@@ -466,7 +501,8 @@ hipError_t launch_g(const ChunkArgs& a, uint4* Tfrag, float* Gws) {
                      FEAT ? f->beta_logit : a.beta, a.L, nc, Tfrag, Gws,
                      static_cast<const uint16_t*>(FEAT ? f->q_raw : nullptr),
                      static_cast<uint16_t*>(FEAT ? f->q_hat : nullptr),
-                     static_cast<uint16_t*>(FEAT ? f->k_hat : nullptr), FEAT ? f->beta : nullptr);
+                     static_cast<uint16_t*>(FEAT ? f->k_hat : nullptr), FEAT ? f->beta : nullptr,
+                     XOUT ? *a.bwd_out : BwdFwdOut{});
   e = hipGetLastError();
   if (!a.bwd_out) prof_mark(kSlotChunkPrep, true, a.stream);
   return e;
@@ -479,8 +515,15 @@ hipError_t launch_c(const ChunkArgs& a) {
   // The gated form's log-decay table follows the T fragments.
   float* Gws = reinterpret_cast<float*>(Tfrag + (size_t)a.B * a.H * nc * Frag<C>::chunk_u4);
   if (nc > 0) {
-    hipError_t e =
-        a.feat ? (a.alpha ? launch_g<C, DK, true, true>(a, Tfrag, Gws)
+    hipError_t e;
+    if constexpr (C == 128) {
+      if (a.bwd_out) {
+        e = launch_g<C, DK, false, false, true>(a, Tfrag, Gws);
+        if (e != hipSuccess) return e;
+        return launch_scan_mfma(a, Tfrag, nullptr);
+      }
+    }
+    e = a.feat ? (a.alpha ? launch_g<C, DK, true, true>(a, Tfrag, Gws)
                           : launch_g<C, DK, false, true>(a, Tfrag, Gws))
                : (a.alpha ? launch_g<C, DK, true, false>(a, Tfrag, Gws)
                           : launch_g<C, DK, false, false>(a, Tfrag, Gws));

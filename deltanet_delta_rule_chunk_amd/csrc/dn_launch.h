@@ -28,14 +28,15 @@ struct FeatureArgs;
 
 // Outputs of the chunked forward when it runs as the forward pass of the
 // backward (bf16 matrix-core path, C = 128, plain form): for every 64-token
-// block of the backward's workspace, the state entering the block, R = V - K S
-// from that state and Delta, row-major fp32.  o and S_final are then not
-// written.
+// block of the backward's workspace, X = (I + A)^{-1} of the block (the
+// block's own diagonal block of the 128-token inverse), the state entering
+// the block, R = V - K S from that state and Delta, row-major fp32.  o and
+// S_final are then not written.
 struct BwdFwdOut {
   float* ws;
-  size_t block;    // floats per (head, 64-token block)
-  size_t s, r, d;  // offsets of S [d_k][d_v], R [64][d_v] and Delta [64][d_v]
-  int nb;          // 64-token blocks per head
+  size_t block;       // floats per (head, 64-token block)
+  size_t x, s, r, d;  // offsets of X [64][64], S [d_k][d_v], R [64][d_v], Delta [64][d_v]
+  int nb;             // 64-token blocks per head
 };
 
 struct ChunkArgs {
