@@ -1,7 +1,6 @@
 // dn_inv64.h -- X = (I + A)^{-1} for a strictly lower-triangular 64 x 64
 // fp32 matrix A in LDS, on the first four waves of a workgroup, for the
-// 64-row-chunk matrix-core kernels (the backward's prep and the
-// per-dimension-decay prep).
+// 64-row-chunk matrix-core prep of the per-dimension decay.
 //
 // By 16 x 16 blocks, with D_b = (I + A_bb)^{-1} the diagonal blocks:
 //   1. wave b forms D_b row by row, D[r][:] = e_r - A_bb[r][0:r] D[0:r][:]:
