@@ -18,7 +18,8 @@
 // d_k / 64 row tiles w * d_k / 64 ...), and waves 4-7 load and deposit the
 // next chunk.  Each chunk step is three phases separated by barriers:
 //   1  chain wave w forms row tile w (16 chunk rows) of the first product;
-//   2  chain wave w forms row tile w of the second;
+//   2  chain wave w forms row tile w of the second, while the other waves
+//      form Q^T dO (it needs no chain result);
 //   3  every chain wave advances its state tiles while the next chunk's
 //      operands go into LDS (row-major and, where a product contracts over
 //      chunk rows, transposed copies); the ones phase 3 itself reads are
@@ -216,16 +217,17 @@ struct BwdLds {
   static constexpr int PK = DK + 8;
   static constexpr size_t halves = (size_t)C * PK + 4 * (size_t)DK * PC + 4 * (size_t)C * PC +
                                    2 * (size_t)NT * PK + 8 * (size_t)NT * PC;
-  static constexpr size_t bytes = halves * 2 + (size_t)C * sizeof(float);
+  static constexpr size_t bytes = halves * 2 + (size_t)C * sizeof(float) + (size_t)DK * NT * sizeof(float);
   static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
 // Three barriers per chunk, as in the forward pass: the next chunk (in
 // reverse order) is deposited during phase 3, with Q^T, K^T and dO^T, which
-// phase 3 still reads, double buffered.  Eight waves: waves 0-3 carry the
-// chain (the three phases' products, the exit gradient and the stores);
-// waves 4-7 load the next chunk, prefetch the one after into L2 and deposit
-// the next chunk into LDS, off the chain's path.
+// are still read in phases 2 and 3, double buffered.  Eight waves: waves 0-3
+// carry the chain (the three phases' products, the exit gradient and the
+// stores); waves 4-7 load the next chunk, prefetch the one after into L2,
+// form the chunk's input-only Q^T dO for the chain's state update and
+// deposit the next chunk into LDS, off the chain's path.
 constexpr int BNTH = 2 * NTH;
 
 template <int DK, int DV>
@@ -253,6 +255,7 @@ __global__ __launch_bounds__(BNTH) void bwd_scan_kernel(
   uint16_t* Fh = El + NT * PC;                          // -dR^T         [NT][PC]
   uint16_t* Fl = Fh + NT * PC;
   float* bs = reinterpret_cast<float*>(Fl + NT * PC);
+  float* Js = bs + C;  // Q^T dO of the chunk, [DK / 4][NT][4] (4-row groups)
 
   int j0, bh;
   if (!slice_of(DV / NT, nbh, j0, bh)) return;
@@ -395,7 +398,19 @@ __global__ __launch_bounds__(BNTH) void bwd_scan_kernel(
     }
     __syncthreads();
 
-    // Phase 2: dR = diag(beta) X^T dDelta, row tile w; dv = dR.
+    // Phase 2: dR = diag(beta) X^T dDelta, row tile w; dv = dR.  The loader
+    // waves meanwhile form J = Q^T dO of the chunk (input only) for phase 3.
+    if (!chain) {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int d0 = 16 * (w * TPW + i);
+        f32x4 jt = zero4();
+#pragma unroll
+        for (int ks = 0; ks < C / 32; ++ks)
+          jt = mfma_split2(fragT<3>(Qc, d0, 32 * ks), frag(Oc, PC, 0, 32 * ks), frag(Ocl, PC, 0, 32 * ks), jt);
+        *reinterpret_cast<f32x4*>(Js + ((d0 / 4 + g) * NT + n) * 4) = jt;
+      }
+    }
     if (chain) {
     acc = zero4();
 #pragma unroll
@@ -415,13 +430,11 @@ __global__ __launch_bounds__(BNTH) void bwd_scan_kernel(
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int d0 = 16 * (w * TPW + i);
+      G[i] += *reinterpret_cast<const f32x4*>(Js + ((d0 / 4 + g) * NT + n) * 4);
 #pragma unroll
-      for (int ks = 0; ks < C / 32; ++ks) {
-        G[i] = mfma_split2(fragT<3>(Qc, d0, 32 * ks), frag(Oc, PC, 0, 32 * ks), frag(Ocl, PC, 0, 32 * ks),
-                           G[i]);
+      for (int ks = 0; ks < C / 32; ++ks)
         G[i] = mfma_split2(fragT<3>(Kc, d0, 32 * ks), frag(Fh, PC, 0, 32 * ks), frag(Fl, PC, 0, 32 * ks),
                            G[i]);
-      }
     }
     } else if (c > 0) {
       deposit((c - 1) & 1);
