@@ -64,6 +64,12 @@ SMALL = [
     # an odd number of 64-token blocks: the forward pass's last 128-token
     # chunk has no second block
     ("bf16_d128_odd_blocks", "bf16", 1, 2, 64 * 4 + 21, 128, 128, 64, True, True),
+    # one token; exactly one 64-token block; a second block of one row; a
+    # last 128-token chunk of one row
+    ("bf16_d128_one_token", "bf16", 1, 2, 1, 128, 128, 64, True, True),
+    ("bf16_d64_one_block", "bf16", 1, 3, 64, 64, 64, 64, False, True),
+    ("bf16_d128_L65", "bf16", 1, 2, 65, 128, 128, 128, True, False),
+    ("bf16_d128_L129", "bf16", 2, 1, 129, 128, 128, 64, True, True),
 ]
 
 
