@@ -47,6 +47,10 @@ SMALL = [
     ("bf16_d128_C128", "bf16", 1, 2, 512, 128, 128, 128, False),
     ("bf16_L_below_C", "bf16", 1, 2, 37, 128, 128, 128, True),
     ("f32_L1", "f32", 1, 1, 1, 64, 64, 64, True),
+    # one token, and a last chunk of one row, on the matrix-core kernels
+    ("bf16_L1_C128", "bf16", 1, 2, 1, 128, 128, 128, True),
+    ("bf16_L129_C128", "bf16", 2, 1, 129, 128, 128, 128, True),
+    ("bf16_L65_C64", "bf16", 1, 3, 65, 64, 128, 64, False),
 ]
 
 

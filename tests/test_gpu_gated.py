@@ -47,6 +47,8 @@ SMALL = [
     ("bf16_d128_C128", "bf16", 1, 2, 512, 128, 128, 128, True),
     ("bf16_dk64_dv128_C128", "bf16", 1, 2, 384, 64, 128, 128, True),
     ("bf16_L_below_C", "bf16", 1, 2, 37, 128, 128, 128, True),
+    ("bf16_L1_C128", "bf16", 1, 2, 1, 128, 128, 128, True),
+    ("bf16_L129_C128", "bf16", 2, 1, 129, 128, 128, 128, True),
 ]
 
 

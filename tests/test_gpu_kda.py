@@ -40,6 +40,8 @@ SMALL = [
     ("bf16_d64_ragged", "bf16", 2, 2, 64 * 5 + 7, 64, 64, 64, False),
     ("bf16_d128_S0", "bf16", 1, 2, 640, 128, 128, 64, True),
     ("bf16_L_below_chunk", "bf16", 1, 2, 37, 128, 128, 128, True),
+    ("bf16_L1", "bf16", 1, 2, 1, 128, 128, 128, True),
+    ("bf16_L65", "bf16", 2, 1, 65, 128, 128, 64, True),
     ("bf16_dk64_dv128_ragged", "bf16", 3, 3, 64 * 4 + 50, 64, 128, 64, True),
     ("bf16_d128_nine_heads", "bf16", 1, 9, 64 * 3, 128, 128, 128, False),
 ]
