@@ -386,9 +386,10 @@ __global__ __launch_bounds__(BNTH) void bwd_scan_kernel(
     f32x4 acc = zero4();
     if (chain) {
 #pragma unroll
-    for (int ks = w / 2; ks < C / 32; ++ks)
-      acc = mfma_split3(fragT<2>(Mh, r0, 32 * ks), fragT<2>(Ml, r0, 32 * ks), frag(Oc, PC, 0, 32 * ks),
-                        frag(Ocl, PC, 0, 32 * ks), acc);
+    for (int ks = 0; ks < C / 32; ++ks)
+      if (ks >= w / 2)
+        acc = mfma_split3(fragT<2>(Mh, r0, 32 * ks), fragT<2>(Ml, r0, 32 * ks), frag(Oc, PC, 0, 32 * ks),
+                          frag(Ocl, PC, 0, 32 * ks), acc);
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks)
       acc = mfma_split2(frag(Kb, PK, r0, 32 * ks), frag(Gh, PK, 0, 32 * ks), frag(Gl, PK, 0, 32 * ks),
@@ -414,9 +415,10 @@ __global__ __launch_bounds__(BNTH) void bwd_scan_kernel(
     if (chain) {
     acc = zero4();
 #pragma unroll
-    for (int ks = w / 2; ks < C / 32; ++ks)
-      acc = mfma_split3(fragT<2>(Xh, r0, 32 * ks), fragT<2>(Xl, r0, 32 * ks), frag(Eh, PC, 0, 32 * ks),
-                        frag(El, PC, 0, 32 * ks), acc);
+    for (int ks = 0; ks < C / 32; ++ks)
+      if (ks >= w / 2)
+        acc = mfma_split3(fragT<2>(Xh, r0, 32 * ks), fragT<2>(Xl, r0, 32 * ks), frag(Eh, PC, 0, 32 * ks),
+                          frag(El, PC, 0, 32 * ks), acc);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] *= bs[r0 + 4 * g + e];
     store_tile16(acc, dv + (tok0 + r0) * DV + j0, DV, valid - r0);
@@ -652,7 +654,8 @@ __global__ __launch_bounds__(DK * 4) void grad_kernel(
       const int a = r0 + n, b = 16 * ctile(j) + n;
       const float bb = bs[b];
 #pragma unroll
-      for (int ks = rt / 2; ks < C / 32; ++ks) {
+      for (int ks = 0; ks < C / 32; ++ks) {
+        if (ks < rt / 2) continue;
         float xa[8], xb[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -681,7 +684,8 @@ __global__ __launch_bounds__(DK * 4) void grad_kernel(
       f32x4 acc = zero4(), gr = zero4();
       if (ct <= rt) {
 #pragma unroll
-        for (int ks = 0; ks <= ct / 2; ++ks) {
+        for (int ks = 0; ks < C / 32; ++ks) {
+          if (ks > ct / 2) continue;
           const float* ya = Ys + (r0 + n) * PF + 32 * ks + 8 * g;
           const float* xb = Xs + (16 * ct + n) * PF + 32 * ks + 8 * g;
           float va[8], vb[8];
